@@ -1,0 +1,175 @@
+"""Logical tensors <-> symbol streams, and symbol tiling (test infrastructure only).
+
+* Integer codes, k codes per symbol ("Single / Pair / Quad" modes): MINE page,
+  Section 4.1, "Data Types" (k-tuples over t values need M >= t^k).  Reading taken:
+  a b-bit code q in [-2^(b-1), 2^(b-1)) maps to the unsigned digit q + 2^(b-1), and
+  the digit of the i-th column of a k-tuple sits at bits [b*i, b*(i+1)) of the
+  symbol (first column in the low bits).
+* BF16: sign/exponent/mantissa layout of Eq. 1 on the DFloat11 page; the 8-bit
+  exponent is the coded symbol and sign + 7-bit mantissa stay a raw byte, as in the
+  DFloat11 format (PackedSignMantissa) and the MINE page, Section 4.1.  The raw
+  byte is sign << 7 | mantissa, and the weight is rebuilt with the bit join of the
+  DFloat11 page's Algorithm 1: (sign << 8) | (exponent << 7) | mantissa, with the
+  sign taken from bit 7 of the raw byte.
+* FP8 E4M3: the byte itself is the symbol (MINE page Section 4.1; OCP E4M3 with
+  bias 7, no infinities, S.1111.111 = NaN).
+* Tiling: rows in groups of 64 (lane l = row r0 + l, the MINE page's lane-per-row
+  grid layout, Section 4 "Grid Layout"), columns in slices; the tile of
+  (row group g, slice c) has index g * n_slices + c.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LANES = 64
+
+
+# ---------------------------------------------------------------- integer codes
+def int_codes_to_symbols(codes: np.ndarray, code_bits: int, k: int) -> np.ndarray:
+    q = np.asarray(codes, dtype=np.int64)
+    n, K = q.shape
+    if K % k:
+        raise ValueError("columns not a multiple of k")
+    half = 1 << (code_bits - 1)
+    if q.size and (q.min() < -half or q.max() >= half):
+        raise ValueError("code outside range")
+    d = (q + half).reshape(n, K // k, k)
+    sym = np.zeros((n, K // k), dtype=np.int64)
+    for i in range(k):
+        sym |= d[:, :, i] << (code_bits * i)
+    return sym
+
+
+def symbols_to_int_codes(sym: np.ndarray, code_bits: int, k: int) -> np.ndarray:
+    s = np.asarray(sym, dtype=np.int64)
+    n, ns = s.shape
+    half = 1 << (code_bits - 1)
+    mask = (1 << code_bits) - 1
+    out = np.zeros((n, ns, k), dtype=np.int64)
+    for i in range(k):
+        out[:, :, i] = ((s >> (code_bits * i)) & mask) - half
+    return out.reshape(n, ns * k).astype(np.int8)
+
+
+# ---------------------------------------------------------------- BF16
+def bf16_split(bits: np.ndarray):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    exponent = (b >> 7) & 0xFF
+    raw = ((b >> 8) & 0x80) | (b & 0x7F)
+    return exponent.astype(np.int64), raw.astype(np.uint8)
+
+
+def bf16_join(exponent: np.ndarray, raw: np.ndarray) -> np.ndarray:
+    e = np.asarray(exponent, dtype=np.uint32)
+    r = np.asarray(raw, dtype=np.uint32)
+    return (((r & 0x80) << 8) | (e << 7) | (r & 0x7F)).astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """Eq. 1 of the DFloat11 page: (-1)^s * 2^(e-127) * 1.m (and the usual specials)."""
+    b = np.asarray(bits, dtype=np.uint32)
+    s = (b >> 15) & 1
+    e = ((b >> 7) & 0xFF).astype(np.int64)
+    m = (b & 0x7F).astype(np.float64)
+    mag = np.where(e == 0, m / 128.0 * 2.0 ** -126, (1.0 + m / 128.0) * np.exp2(e - 127.0))
+    mag = np.where(e == 255, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+def e4m3_value(byte: np.ndarray) -> np.ndarray:
+    b = np.asarray(byte, dtype=np.int64)
+    s = (b >> 7) & 1
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def e4m3_rne(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 byte, ties to the even code, sign kept (so tiny negatives give
+    -0 = 0x80, as IEEE rounding does); |v| <= 448 required."""
+    table = e4m3_value(np.arange(256))
+    pos = np.array([b for b in range(128) if not math.isnan(table[b])])
+    pv = table[pos]
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    if np.any(a > 448.0):
+        raise ValueError("value beyond E4M3 range")
+    i = np.searchsorted(pv, a)
+    i = np.clip(i, 1, len(pv) - 1)
+    lo, hi = pv[i - 1], pv[i]
+    pick_hi = (hi - a < a - lo) | ((hi - a == a - lo) & (pos[i] % 2 == 0))
+    mag_code = np.where(pick_hi, pos[i], pos[i - 1])
+    mag_code = np.where(a == 0, 0, mag_code)
+    neg = np.signbit(np.asarray(v, dtype=np.float64))
+    return (mag_code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+# ---------------------------------------------------------------- tiling
+def tile_plan(n_rows: int, n_sym: int, syms_per_slice: int):
+    n_rg = -(-n_rows // LANES)
+    n_sl = -(-n_sym // syms_per_slice) if n_sym else 0
+    s_last = n_sym - (n_sl - 1) * syms_per_slice if n_sl else 0
+    return n_rg, n_sl, syms_per_slice, s_last
+
+
+def rows_to_tiles(rows: np.ndarray, syms_per_slice: int, fill=0):
+    """[N, n_sym] per-row streams -> list over slice-kind of (tile ids, [T,64,S], active)."""
+    rows = np.asarray(rows)
+    n, n_sym = rows.shape
+    n_rg, n_sl, s_full, s_last = tile_plan(n, n_sym, syms_per_slice)
+    pad = np.full((n_rg * LANES, n_sym), fill, dtype=rows.dtype)
+    pad[:n] = rows
+    active_rows = np.zeros(n_rg * LANES, dtype=bool)
+    active_rows[:n] = True
+    groups = []
+    if n_sl == 0:
+        kinds = []
+    elif s_last == s_full:
+        kinds = [(list(range(n_sl)), s_full)]
+    else:
+        kinds = [(list(range(n_sl - 1)), s_full)] if n_sl > 1 else []
+        kinds.append(([n_sl - 1], s_last))
+    for slices, S in kinds:
+        ids, data, act = [], [], []
+        for g in range(n_rg):
+            for c in slices:
+                ids.append(g * n_sl + c)
+                c0 = c * syms_per_slice
+                data.append(pad[g * LANES:(g + 1) * LANES, c0:c0 + S])
+                act.append(active_rows[g * LANES:(g + 1) * LANES])
+        groups.append((np.array(ids, dtype=np.int64), np.stack(data) if data else
+                       np.zeros((0, LANES, S), rows.dtype), np.stack(act) if act else
+                       np.zeros((0, LANES), bool)))
+    return groups
+
+
+def tiles_to_rows(n_rows: int, n_sym: int, syms_per_slice: int, groups) -> np.ndarray:
+    n_rg, n_sl, _, _ = tile_plan(n_rows, n_sym, syms_per_slice)
+    out = None
+    for ids, data, _ in groups:
+        if out is None:
+            out = np.zeros((n_rg * LANES, n_sym), dtype=data.dtype)
+        for i, t in enumerate(ids):
+            g, c = divmod(int(t), n_sl)
+            c0 = c * syms_per_slice
+            out[g * LANES:(g + 1) * LANES, c0:c0 + data.shape[2]] = data[i]
+    if out is None:
+        out = np.zeros((n_rg * LANES, n_sym), dtype=np.int64)
+    return out[:n_rows]
+
+
+def raw_plane_bytes(raw_tiles: np.ndarray, active: np.ndarray) -> np.ndarray:
+    """Raw bytes of a group of tiles [T, 64, S] -> [T, G, 64, 16] with G = ceil(S/16).
+
+    Lane l's bytes for steps 16g .. 16g+15 sit contiguously at [t, g, l, :] so one
+    wave reads a step group with one 16-byte load per lane.  Padding bytes are 0.
+    """
+    T, lanes, S = raw_tiles.shape
+    G = -(-S // 16)
+    buf = np.zeros((T, lanes, G * 16), dtype=np.uint8)
+    buf[:, :, :S] = np.where(active[:, :, None], raw_tiles, 0)
+    return buf.reshape(T, lanes, G, 16).transpose(0, 2, 1, 3).copy()
