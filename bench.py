@@ -1,0 +1,223 @@
+"""Benchmark: fused rANS decode + batch-1 GEMV over one Llama-3.1-8B-shaped layer set.
+
+One step = one pass of the hot path over the seven linear layers of one transformer
+block (q, k, v, o 4096x4096 / 1024x4096, gate/up 14336x4096, down 4096x14336), each
+stored as 16-level Laplacian codes (2.2 bits of entropy) packed two per rANS symbol,
+decoded and multiplied into y = W x at batch 1.  Launch order follows the block's
+data flow: q, k, v, o, gate, up, down.  Blobs are rotated over >= 512 MiB of copies
+(twice the 256 MiB Infinity Cache), so every step reads its weights from HBM.
+
+Prints one JSON line (stdout).  Per-tensor details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs per fused decode-GEMV layer + effective weight GB/s (% HBM peak), batch 1"
+ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
+
+# per-tensor coding: (log2_m, tile_cols, waves_per_block, tiles_per_wave)
+DEFAULT_CODING = {
+    "q": (12, 256, 8, 1), "k": (12, 256, 8, 1), "v": (12, 256, 8, 1), "o": (12, 256, 8, 1),
+    "gate": (12, 256, 8, 1), "up": (12, 256, 8, 1), "down": (12, 256, 8, 1),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(batch: int, coding: dict):
+    import ecw_inputs as E
+    import entropy_coded_weight_amd as ecw
+    layer = {}
+    for name in ORDER:
+        t = E.config2_tensor(name, layer=0, batch=batch)
+        m, tc, W, R = coding[name]
+        n, k = t.codes.shape
+        c = ecw.Coding(ecw.INT_CODES, n, k, 2, 4, m, tc)
+        blob = ecw.encode(c, t.codes, t.scales)
+        layer[name] = dict(tensor=t, coding=c, blob=blob, launch=(W, R))
+    return layer
+
+
+def cpu_baseline(layer, target_s: float = 12.0):
+    """Time the oracle (numpy decode + fp64 GEMV) on whole 64-row groups of every
+    tensor until about target_s seconds of work, then scale to one full layer by
+    symbol count.  The sampled rows are encoded by the oracle first (untimed)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import gemv as G, pipeline as P
+    done_syms, total_syms, t_used, rows_done = 0, 0, 0.0, 0
+    for name in ORDER:
+        total_syms += layer[name]["tensor"].codes.size // 2
+    with threadpool_limits(limits=1):
+        rg = 0
+        while t_used < target_s and rg < 64:
+            for name in ORDER:
+                t = layer[name]["tensor"]
+                n, K = t.codes.shape
+                r0, r1 = rg * 64, min(rg * 64 + 64, n)
+                if r0 >= n:
+                    continue
+                c = layer[name]["coding"]
+                ocd = P.Coding(P.INT_CODES, r1 - r0, K, k=2, code_bits=4, log2_m=c.log2_m,
+                               tile_cols=c.tile_cols)
+                comp = P.encode(ocd, t.codes[r0:r1], t.scales[r0:r1])
+                t0 = time.perf_counter()
+                q = P.decode(comp)
+                wv = P.weight_values(ocd, q, t.scales[r0:r1])
+                G.gemv_f64(wv, G.x_values(t.x, "f16"))
+                t_used += time.perf_counter() - t0
+                done_syms += q.size // 2
+                rows_done += r1 - r0
+            rg += 1
+    us_layer = t_used / done_syms * total_syms * 1e6
+    return {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} rows in whole 64-row groups of all 7 tensors ({done_syms} symbols, "
+                      f"{t_used:.1f} s): numpy decode + float64 GEMV, BLAS limited to 1 thread, "
+                      f"scaled to the full layer by symbol count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-bytes", type=float, default=512e6)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import entropy_coded_weight_amd as ecw
+    from oracle import gemv as G, pipeline as P
+
+    dev = torch.device("cuda:0")
+    t_build = time.time()
+    layer = build_layer(args.batch, DEFAULT_CODING)
+    log(f"encoded layer set in {time.time() - t_build:.1f} s")
+    stored = {n: 0 for n in ORDER}
+    one = {}
+    for name in ORDER:
+        L = layer[name]
+        ct = ecw.CompressedTensor(L["blob"])
+        ct.set_launch(*L["launch"])
+        stored[name] = ct.stored_bytes()
+        one[name] = ct
+    layer_bytes = sum(stored.values())
+    copies = max(2, int(np.ceil(args.cold_bytes / layer_bytes)))
+    cts = [one] + [{n: ecw.CompressedTensor(layer[n]["blob"]) for n in ORDER} for _ in range(copies - 1)]
+    for c in cts[1:]:
+        for n in ORDER:
+            c[n].set_launch(*layer[n]["launch"])
+    xs, ys, ws = {}, {}, {}
+    for name in ORDER:
+        t = layer[name]["tensor"]
+        xs[name] = torch.from_numpy(t.x).to(dev)
+        ys[name] = torch.empty((args.batch, t.codes.shape[0]), dtype=torch.float32, device=dev)
+        ws[name] = [c[name].workspace(args.batch) for c in cts]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = cts[i % copies]
+        for j, name in enumerate(ORDER):
+            if ev is not None:
+                ev[j].record(stream)
+            ecw.gemv_raw(c[name].t, xs[name], ys[name], ws[name][i % copies])
+        if ev is not None:
+            ev[len(ORDER)].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ORDER) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    per = {n: [] for n in ORDER}
+    for e in evs:
+        for j, n in enumerate(ORDER):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)      # us
+    avg_us = {n: float(np.mean(per[n])) for n in ORDER}
+
+    # parity on the timed blobs: sampled rows of every tensor against float64
+    worst = 0.0
+    for name in ORDER:
+        t = layer[name]["tensor"]
+        y = ys[name].cpu().numpy()
+        rows = np.random.default_rng(1).choice(t.codes.shape[0], 256, replace=False)
+        wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
+        ok, wr = G.check(y[:, rows], wv, G.x_values(t.x, "f16"))
+        worst = max(worst, wr)
+        if not ok:
+            log(f"PARITY FAILURE on {name}: worst err/bound {wr}")
+            sys.exit(1)
+
+    n_weights = sum(layer[n]["tensor"].codes.size for n in ORDER)
+    us_layer = ms_step * 1e3
+    gbs = layer_bytes / (us_layer * 1e-6) / 1e9
+    unc_bytes = sum(layer[n]["tensor"].codes.size * 0.5 + layer[n]["tensor"].codes.shape[0] * 2 for n in ORDER)
+    dom = max(ORDER, key=lambda n: avg_us[n])
+    tdom = layer[dom]["tensor"]
+    dom_bytes = stored[dom] + tdom.x.size * 2 + tdom.codes.shape[0] * 4 * args.batch
+    achieved = dom_bytes / (avg_us[dom] * 1e-6) / 1e9
+    for n in ORDER:
+        c = layer[n]["coding"]
+        log(f"{n:5s} {layer[n]['tensor'].codes.shape} m={c.log2_m} tc={c.tile_cols} "
+            f"launch={layer[n]['launch']} stored={stored[n] / 1e6:.3f} MB "
+            f"avg={avg_us[n]:.2f} us  {stored[n] / (avg_us[n] * 1e-6) / 1e9:.0f} GB/s")
+    out = {
+        "metric": METRIC, "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u32 decode + f32 accumulate", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped layer set (q,k,v,o,gate,up,down) of 16-level "
+                               "Laplacian codes (H=2.2 bits), 2 codes per rANS symbol, fp16 row "
+                               "scales, fp16 x, batch 1, cold cache",
+                   "batch": args.batch, "copies_rotated": copies,
+                   "codings": {n: dict(log2_m=layer[n]["coding"].log2_m,
+                                       tile_cols=layer[n]["coding"].tile_cols,
+                                       waves_per_block=layer[n]["launch"][0],
+                                       tiles_per_wave=layer[n]["launch"][1]) for n in ORDER}},
+        "stored_bytes_per_layer": int(layer_bytes),
+        "stored_bits_per_weight": round(layer_bytes * 8 / n_weights, 4),
+        "gbps_compressed": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "gbps_uncompressed_equiv": round(unc_bytes / (us_layer * 1e-6) / 1e9, 1),
+        "per_tensor_us": {n: round(avg_us[n], 3) for n in ORDER},
+        "host_wall_s": round(host_s, 3),
+        "parity_worst_err_over_bound": worst,
+        "roofline": {"bound": "hbm", "kernel": f"k_decode<INT4,pair> on {dom} {tuple(tdom.codes.shape)}",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(avg_us[dom], 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layer)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

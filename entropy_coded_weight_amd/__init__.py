@@ -1,0 +1,255 @@
+"""Python binding of libecw.so: entropy-coded weights decoded inside a batch-1 GEMV.
+
+Argument marshalling only.  Every step of the path (table building, rANS encoding,
+validation, decoding and the fused GEMV) runs in the C-ABI library; PyTorch only
+provides device memory and the current HIP stream.
+
+    c = Coding(payload=INT_CODES, rows=N, cols=K, weights_per_symbol=2, code_bits=4,
+               log2_m=11, tile_cols=256)
+    blob = encode(c, codes, scales)          # numpy uint8, format v1
+    t = CompressedTensor(blob)               # device copy + validated descriptor
+    y = t.gemv(x)                            # x: cuda fp16/bf16 [batch, K] -> fp32 [batch, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+import torch  # noqa: F401  (load torch's HIP runtime first so the library binds to it)
+
+INT_CODES, BF16_EXP, FP8_E4M3, E8_LATTICE = 1, 2, 3, 4
+DT_F16, DT_BF16, DT_F32, DT_I8, DT_FP8_E4M3 = 1, 2, 3, 4, 5
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "CORRUPT", 4: "BUFFER_TOO_SMALL", 5: "HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libecw.so")
+
+
+class Coding(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in (
+        "payload", "rows", "cols", "weights_per_symbol", "code_bits", "log2_m",
+        "tile_rows", "tile_cols", "recon_dtype")]
+
+    def __init__(self, payload, rows, cols, weights_per_symbol=1, code_bits=0, log2_m=12,
+                 tile_cols=256, recon_dtype=0, tile_rows=64):
+        super().__init__(payload, rows, cols, weights_per_symbol, code_bits, log2_m,
+                         tile_rows, tile_cols, recon_dtype)
+
+
+class Tables(ctypes.Structure):
+    _fields_ = [("n_tables", ctypes.c_uint32),
+                ("alphabet", ctypes.c_uint32 * 17),
+                ("value_offset", ctypes.c_int32 * 17),
+                ("freq", (ctypes.c_uint16 * 256) * 17),
+                ("count", (ctypes.c_uint64 * 256) * 17)]
+
+    def freq_array(self) -> np.ndarray:
+        return np.ctypeslib.as_array(self.freq)[: self.n_tables].astype(np.int64)
+
+    def count_array(self) -> np.ndarray:
+        return np.ctypeslib.as_array(self.count)[: self.n_tables].astype(np.int64)
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("coding", Coding)] + [(n, ctypes.c_uint32) for n in (
+        "n_tables", "n_row_groups", "n_slices", "n_tiles", "steps_full", "steps_last",
+        "lut_entry_bytes", "waves_per_block", "tiles_per_wave", "reserved")] + [
+        ("blob_bytes", ctypes.c_uint64), ("bytes_words", ctypes.c_uint64),
+        ("bytes_raw", ctypes.c_uint64), ("bytes_tile_meta", ctypes.c_uint64),
+        ("bytes_tables", ctypes.c_uint64), ("bytes_scales", ctypes.c_uint64),
+        ("device_blob", ctypes.c_void_p)] + [(n, ctypes.c_uint64) for n in (
+            "off_tables", "off_lut", "off_states", "off_offsets", "off_words", "off_raw",
+            "off_scales")]
+
+
+EXPORTS = ["enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
+           "dec_gemv", "dec_materialize", "ecw_last_error", "ecw_abi_version"]
+
+_lib = None
+
+
+class EcwError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.ecw_last_error().decode() if _lib is not None else ""
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def lib():
+    """Load libecw.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} missing: run __graft_entry__.build() (or "
+                          "python entropy_coded_weight_amd/build.py) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, u32, i32, sz = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.enc_build_tables.argtypes = [P(Coding), vp, P(Tables)]
+    L.enc_encode.argtypes = [P(Coding), P(Tables), vp, vp, vp, P(sz)]
+    L.dec_prepare.argtypes = [vp, sz, vp, P(Tensor)]
+    L.dec_gemv_workspace_size.argtypes = [P(Tensor), i32, P(sz)]
+    L.dec_gemv.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz]
+    L.dec_materialize.argtypes = [vp, P(Tensor), vp, vp, vp]
+    for f in ("enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
+              "dec_gemv", "dec_materialize"):
+        getattr(L, f).restype = ctypes.c_int
+    L.ecw_last_error.argtypes = []
+    L.ecw_last_error.restype = ctypes.c_char_p
+    L.ecw_abi_version.argtypes = []
+    L.ecw_abi_version.restype = u32
+    _lib = L
+    return L
+
+
+def _check(status, where):
+    if status != 0:
+        raise EcwError(status, where)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_logical(coding: Coding, w: np.ndarray) -> np.ndarray:
+    dt = {INT_CODES: np.int8, BF16_EXP: np.uint16, FP8_E4M3: np.uint8, E8_LATTICE: np.int8}[coding.payload]
+    w = np.ascontiguousarray(w, dtype=dt)
+    if w.shape != (coding.rows, coding.cols):
+        raise ValueError(f"weights shape {w.shape} != ({coding.rows}, {coding.cols})")
+    return w
+
+
+# ------------------------------------------------------------------ host calls
+def build_tables(coding: Coding, w: np.ndarray) -> Tables:
+    w = _host_logical(coding, w)
+    t = Tables()
+    _check(lib().enc_build_tables(ctypes.byref(coding), _ptr(w), ctypes.byref(t)), "enc_build_tables")
+    return t
+
+
+def encode(coding: Coding, w: np.ndarray, scales=None, tables: Tables | None = None) -> np.ndarray:
+    w = _host_logical(coding, w)
+    if tables is None:
+        tables = build_tables(coding, w)
+    sc = None
+    if scales is not None:
+        sc = np.ascontiguousarray(scales, dtype=np.float16).view(np.uint16)
+    n = ctypes.c_size_t(0)
+    L = lib()
+    _check(L.enc_encode(ctypes.byref(coding), ctypes.byref(tables), _ptr(w),
+                        _ptr(sc) if sc is not None else None, None, ctypes.byref(n)), "enc_encode")
+    buf = np.zeros(n.value, dtype=np.uint8)
+    _check(L.enc_encode(ctypes.byref(coding), ctypes.byref(tables), _ptr(w),
+                        _ptr(sc) if sc is not None else None, _ptr(buf), ctypes.byref(n)), "enc_encode")
+    return buf[: n.value].copy()
+
+
+def prepare(blob: np.ndarray, device_ptr: int | None = None) -> Tensor:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    t = Tensor()
+    _check(lib().dec_prepare(_ptr(blob), blob.size, device_ptr, ctypes.byref(t)), "dec_prepare")
+    return t
+
+
+def workspace_size(t: Tensor, batch: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dec_gemv_workspace_size(ctypes.byref(t), batch, ctypes.byref(n)), "dec_gemv_workspace_size")
+    return n.value
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def gemv_raw(t: Tensor, x: torch.Tensor, y: torch.Tensor, workspace: torch.Tensor | None, stream=None):
+    """dec_gemv on caller-provided device buffers (x [batch, K] fp16/bf16, y [batch, N] fp32)."""
+    if x.dtype == torch.float16:
+        xd = DT_F16
+    elif x.dtype == torch.bfloat16:
+        xd = DT_BF16
+    else:
+        raise TypeError("x must be float16 or bfloat16")
+    if y.dtype != torch.float32 or not y.is_contiguous() or not x.is_contiguous():
+        raise TypeError("y must be contiguous float32; x contiguous")
+    batch = x.shape[0]
+    ws = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dec_gemv(_stream(stream), ctypes.byref(t), x.data_ptr(), xd, y.data_ptr(), batch,
+                          ws, wsb), "dec_gemv")
+
+
+def materialize_raw(t: Tensor, symbols, w_out, status, stream=None):
+    _check(lib().dec_materialize(_stream(stream), ctypes.byref(t),
+                                 symbols.data_ptr() if symbols is not None else None,
+                                 w_out.data_ptr() if w_out is not None else None,
+                                 status.data_ptr() if status is not None else None), "dec_materialize")
+
+
+# ------------------------------------------------------------------ device tensor
+class CompressedTensor:
+    """A blob resident in device memory plus its validated descriptor."""
+
+    def __init__(self, blob: np.ndarray, device: str = "cuda", waves_per_block=None, tiles_per_wave=None):
+        blob = np.ascontiguousarray(blob, dtype=np.uint8)
+        self.host_blob = blob
+        self.dev = torch.from_numpy(blob).to(device)
+        if self.dev.data_ptr() % 256:
+            raise RuntimeError("device allocation is not 256-byte aligned")
+        self.t = prepare(blob, self.dev.data_ptr())
+        if waves_per_block is not None:
+            self.t.waves_per_block = waves_per_block
+        if tiles_per_wave is not None:
+            self.t.tiles_per_wave = tiles_per_wave
+        self._ws = {}
+
+    @property
+    def rows(self):
+        return self.t.coding.rows
+
+    @property
+    def cols(self):
+        return self.t.coding.cols
+
+    def set_launch(self, waves_per_block: int, tiles_per_wave: int):
+        self.t.waves_per_block = waves_per_block
+        self.t.tiles_per_wave = tiles_per_wave
+
+    def stored_bytes(self) -> int:
+        t = self.t
+        return t.bytes_words + t.bytes_raw + t.bytes_tile_meta + t.bytes_tables + t.bytes_scales
+
+    def workspace(self, batch: int):
+        key = (batch > 1, self.t.waves_per_block, self.t.tiles_per_wave)
+        n = workspace_size(self.t, batch)
+        if n == 0:
+            return None
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < n:
+            ws = torch.zeros(n, dtype=torch.uint8, device=self.dev.device)
+            self._ws[key] = ws
+        return ws
+
+    def gemv(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if y is None:
+            y = torch.empty((x.shape[0], self.rows), dtype=torch.float32, device=x.device)
+        gemv_raw(self.t, x, y, self.workspace(x.shape[0]), stream)
+        return y
+
+    def materialize(self, want_symbols=True, want_weights=True, stream=None):
+        c = self.t.coding
+        n_sym = {INT_CODES: c.cols // max(c.weights_per_symbol, 1), BF16_EXP: c.cols,
+                 FP8_E4M3: c.cols, E8_LATTICE: c.cols // 8 * 9}[c.payload]
+        dev = self.dev.device
+        sym = torch.zeros((c.rows, n_sym), dtype=torch.int16, device=dev) if want_symbols else None
+        wdt = {INT_CODES: torch.int8, BF16_EXP: torch.int16, FP8_E4M3: torch.uint8,
+               E8_LATTICE: torch.int8 if c.recon_dtype == DT_I8 else torch.uint8}[c.payload]
+        w = torch.zeros((c.rows, c.cols), dtype=wdt, device=dev) if want_weights else None
+        st = torch.full((max(self.t.n_tiles, 1),), 0xFFFF, dtype=torch.int32, device=dev)
+        materialize_raw(self.t, sym, w, st, stream)
+        return sym, w, st[: self.t.n_tiles]

@@ -1,0 +1,87 @@
+// Blob format version 1: layout shared by the host encoder, the validator and the
+// device kernels of this library.  All integers little-endian.
+//
+//   [0, 256)        BlobHeader
+//   sections, each starting on a 256-byte boundary, in this order:
+//   TABLES   n_tables x TableRecord                        (alphabet, offset, freq)
+//   LUT      n_tables x M x 8 B decode entries             (derived from freq)
+//   STATES   n_tiles x 64 x u32 decoder start states       (inactive lanes: 2^16)
+//   OFFSETS  (n_tiles + 1) x u32 word offsets into WORDS   (last = total words)
+//   WORDS    u16 payload words of all tiles in tile order, then >= kWordPad bytes of
+//            zero padding (the decoder's chunked loads may read past a tile's end)
+//   RAW      BF16 only: per tile G = ceil(S/16) groups of [64 lanes][16 bytes]
+//   SCALES   rows x fp16 row scales (absent for BF16)
+//
+// Tile t = row_group * n_slices + slice covers rows [64 g, 64 g + 64) and the
+// symbols of columns [slice * tile_cols, ...).  Inside a tile, words are in decoder
+// order: step-major, lanes ascending (EntroPack page, Sections 3.6 and C.3: one
+// wave per independent tile, 32-bit states, 16-bit words).
+//
+// Decode entry of slot i (table t), as two u32:
+//   lo = f | aux << 24   (f <= 2^13 in the low 24 bits, so a 24-bit multiply
+//                         f * (x >> m) ignores aux)
+//   hi = i - cum[s]      (the bias; next state = f * (x >> m) + hi)
+// aux = (symbol + value_offset) & 0xFF: the payload byte the kernel rebuilds the
+// weight from (MINE page, Section 4.1: one table read yields both the state
+// update operands and the payload).
+#pragma once
+#include <stdint.h>
+
+namespace ecw {
+
+constexpr uint32_t kMagic = 0x31574345u;   // "ECW1"
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kHeaderBytes = 256;
+constexpr uint32_t kLanes = 64;
+constexpr uint32_t kStateL = 1u << 16;     // rANS lower bound L
+constexpr uint32_t kSectionAlign = 256;
+constexpr uint32_t kWordPad = 4096;        // zero bytes after the last word
+constexpr uint32_t kMinLog2M = 8;
+constexpr uint32_t kMaxLog2M = 13;
+
+enum Section : uint32_t {
+  kSecTables = 0, kSecLut, kSecStates, kSecOffsets, kSecWords, kSecRaw, kSecScales, kNumSections
+};
+
+struct SectionRef {
+  uint64_t offset;
+  uint64_t bytes;
+};
+
+struct BlobHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint32_t header_bytes;
+  uint32_t n_sections;
+  // coding
+  uint32_t payload, rows, cols, weights_per_symbol, code_bits, log2_m, tile_rows, tile_cols,
+      recon_dtype;
+  // derived geometry
+  uint32_t n_tables, n_row_groups, n_slices, n_tiles, steps_full, steps_last, lut_entry_bytes;
+  uint32_t reserved0, reserved1;
+  uint64_t total_bytes;  // byte offset 88
+  SectionRef sec[8];
+  uint8_t pad[256 - 4 * 4 - 9 * 4 - 9 * 4 - 8 - 8 * 16];  // sections at byte offset 96
+};
+static_assert(sizeof(BlobHeader) == 256, "header must be 256 bytes");
+
+struct TableRecord {          // 520 bytes
+  uint32_t alphabet;
+  int32_t value_offset;
+  uint16_t freq[256];
+};
+static_assert(sizeof(TableRecord) == 520, "table record size");
+
+inline uint32_t symbols_per_row_slice(uint32_t payload, uint32_t k, uint32_t tile_cols) {
+  if (payload == 1) return tile_cols / k;
+  if (payload == 4) return tile_cols / 8 * 9;
+  return tile_cols;
+}
+inline uint32_t symbols_per_row(uint32_t payload, uint32_t k, uint32_t cols) {
+  if (payload == 1) return cols / k;
+  if (payload == 4) return cols / 8 * 9;
+  return cols;
+}
+inline uint64_t raw_group_count(uint32_t steps) { return (steps + 15) / 16; }
+
+}  // namespace ecw

@@ -1,0 +1,544 @@
+// Fused rANS decode + batch-1..4 GEMV for gfx950, and the decode-only test hook.
+//
+// One wave64 decodes one tile at a time: lane l owns row 64g + l (MINE page,
+// Section 4 "Grid Layout": one lane per row, tiles stacked into blocks that share
+// the activation slice), tiles are independent rANS streams with 32-bit states and
+// 16-bit words (EntroPack page, Sections 3.6 and C.3).  Per step and lane:
+//
+//   slot = x & (M-1);  e = LUT[slot]            (LDS, one 8-byte read)
+//   x    = f * (x >> m) + bias                  (v_mad_u32_u24)
+//   weight from e's payload byte                (+ raw byte for BF16)
+//   acc += weight * x_col                        (fp32)
+//   need = x < 2^16; off = popcount(ballot(need) below this lane)
+//   if need: x = x << 16 | word[pos + off];  pos += popcount(ballot)
+//
+// The words of a wave's run of tiles are contiguous in HBM; they are streamed into
+// a per-wave LDS ring in 1 KiB chunks (64 lanes x 16 B, one coalesced load per
+// lane), one chunk prefetched in registers ahead of use.  The table is staged in
+// LDS once per block (MINE page, Section 4.1: decoding tables in shared memory,
+// 1 KiB per-warp chunk buffer for the stream).  No weight tensor is written:
+// weights live in registers between decode and FMA.
+//
+// Cross-wave reduction: the waves of a block cover consecutive column slices of
+// the same 64 rows and are summed in LDS in wave order; when a row group spans
+// several blocks each writes a partial and the last block to arrive (agent-scope
+// counter) sums the partials in block order.  Both orders are fixed, so results do
+// not depend on scheduling.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <string>
+
+#include "ecw_internal.h"
+
+namespace ecw {
+
+constexpr uint32_t kRing = 1024;          // words per wave ring (two chunks)
+constexpr uint32_t kMirror = 64;          // copy of the ring head for reads that wrap
+constexpr uint32_t kRingStride = kRing + kMirror;
+constexpr uint32_t kChunk = 512;          // words per chunk = 64 lanes x 16 bytes
+
+struct KArgs {
+  const uint2* lut;
+  const uint32_t* states;
+  const uint32_t* offsets;
+  const uint16_t* words;
+  const uint8_t* raw;
+  const uint16_t* scales;
+  const void* x;
+  float* y;
+  float* partials;
+  uint32_t* counters;
+  uint16_t* sym_out;
+  void* w_out;
+  uint32_t* status_out;
+  uint32_t rows, cols, n_rg, n_sl, s_full, s_last, log2m, tile_cols;
+  uint32_t tiles_per_wave, n_sg, n_blocks, syms_per_row;
+  uint32_t x_is_bf16, nb, lut_entries, xs_cols;
+  uint32_t raw_full_bytes, raw_rg_bytes;
+};
+
+__device__ __forceinline__ float load_x(const void* x, uint32_t is_bf16, uint64_t i) {
+  const uint16_t h = static_cast<const uint16_t*>(x)[i];
+  if (is_bf16) return __uint_as_float((uint32_t)h << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // fixed xor-butterfly: every lane ends with the same, order-independent-of-timing sum
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// x' = f * (x >> m) + bias in one v_mad_u32_u24 (both factors < 2^24; the payload
+// byte in bits 24..31 of the table word is ignored by the 24-bit multiply).
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Per-wave state of one run of consecutive tiles (same 64 rows).
+struct WaveRun {
+  uint32_t gb, nch, have, nc, rpos;
+  uint4 pre;
+  const uint4* src;
+};
+
+// Decode the tiles [t0, t1) of row group rg with one wave; accumulate (or emit).
+// RAGGED: some lanes of the row group are past the last row and must neither
+// decode nor read words (only the last row group of a matrix whose row count is
+// not a multiple of 64).
+template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED>
+__device__ __forceinline__ void wave_run(const KArgs& a, const uint2* lut, const float* xs,
+                                         uint16_t* ring, uint32_t rg, uint32_t t0, uint32_t t1,
+                                         uint32_t c_lo, uint32_t lane, bool active, float* acc) {
+  constexpr int U = 16;                     // steps per unrolled group (S % 16 == 0)
+  const uint32_t m = a.log2m;
+  const uint32_t mmask = (1u << m) - 1u;
+  const uint32_t row = rg * 64 + lane;
+  const uint4 zero4 = {0u, 0u, 0u, 0u};
+
+  const uint32_t wb = a.offsets[t0], we = a.offsets[t1];
+  const uint32_t gb = wb & ~(kChunk - 1);
+  const uint32_t nch = (we - gb + kChunk - 1) / kChunk;
+  const uint4* src = reinterpret_cast<const uint4*>(a.words + gb) + lane;
+  {
+    uint4 c0 = nch > 0 ? src[0] : zero4;
+    uint4 c1 = nch > 1 ? src[64] : zero4;
+    reinterpret_cast<uint4*>(ring)[lane] = c0;
+    if (lane < 8) reinterpret_cast<uint4*>(ring + kRing)[lane] = c0;
+    reinterpret_cast<uint4*>(ring + kChunk)[lane] = c1;
+  }
+  uint4 pre = nch > 2 ? src[128] : zero4;
+  uint32_t have = 2 * kChunk, nc = 2, rpos = wb - gb;
+  uint32_t st_next = a.states[(uint64_t)t0 * 64 + lane];
+
+  for (uint32_t t = t0; t < t1; ++t) {
+    uint32_t x = st_next;
+    if (t + 1 < t1) st_next = a.states[(uint64_t)(t + 1) * 64 + lane];
+    const uint32_t sl = t - rg * a.n_sl;
+    const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
+    const uint32_t col0 = sl * a.tile_cols - c_lo;     // local staged column of the tile
+    const uint8_t* rawp = nullptr;
+    uint4 rcur = zero4, rnext = zero4;
+    if constexpr (PAY == 2) {
+      rawp = a.raw + (uint64_t)rg * a.raw_rg_bytes + (uint64_t)sl * a.raw_full_bytes + lane * 16;
+      rnext = *reinterpret_cast<const uint4*>(rawp);
+    }
+    for (uint32_t j = 0; j < S; j += U) {
+      if constexpr (PAY == 2) {
+        rcur = rnext;
+        if (j + U < S) rnext = *reinterpret_cast<const uint4*>(rawp + (uint64_t)(j / U + 1) * 1024);
+      }
+      // activations of this 16-step group: KW * U columns x B floats, read as 16-byte
+      // broadcasts (every lane reads the same address) once per 4 steps
+      const float4* xg = reinterpret_cast<const float4*>(xs + (uint64_t)(col0 + KW * j) * B);
+      float4 xq[KW * B];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (!MAT) {
+          if ((u & 3) == 0) {
+#pragma unroll
+            for (int i = 0; i < KW * B; ++i) xq[i] = xg[(u / 4) * KW * B + i];
+          }
+        }
+        // ---- A4: symbol decode (one LDS read gives f, bias and the payload byte)
+        const uint32_t slot = x & mmask;
+        const uint2 e = lut[slot];
+        x = mad_u24(x >> m, e.x, e.y);
+        const uint32_t step = j + u;
+        // ---- A6/A7: payload -> weight (registers only) -> fp32 MAC
+        if constexpr (!MAT) {
+          const float* xp = reinterpret_cast<const float*>(xq) + (u & 3) * KW * B;
+          if constexpr (PAY == 1) {
+            if constexpr (CB == 4 && KW == 1) {
+              const float w = (float)(e.x >> 24);          // digit q + 8
+#pragma unroll
+              for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
+            } else if constexpr (CB == 4 && KW == 2) {
+              const float w01 = (float)(e.x >> 24);        // d0 + 16 d1
+              const float w1 = (float)(e.x >> 28);         // d1
+#pragma unroll
+              for (int b = 0; b < B; ++b) {
+                acc[b] = fmaf(w01, xp[b], acc[b]);
+                acc[b] = fmaf(w1, xp[B + b], acc[b]);
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < KW; ++i) {
+                const float w = (float)((e.x >> (24 + CB * i)) & ((1u << CB) - 1));
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[i * B + b], acc[b]);
+              }
+            }
+          } else if constexpr (PAY == 2) {
+            // bf16 bits = sign << 15 | exponent << 7 | mantissa, as fp32 bits << 16
+            const uint32_t dw = (u < 4) ? rcur.x : (u < 8) ? rcur.y : (u < 12) ? rcur.z : rcur.w;
+            const uint32_t r = (dw >> (8 * (u & 3))) & 0xFFu;
+            const uint32_t bits = ((r << 24) & 0x80000000u) | ((e.x >> 1) & 0x7F800000u) |
+                                  ((r << 16) & 0x007F0000u);
+            const float w = __uint_as_float(bits);
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
+          } else {
+            const float w = __builtin_amdgcn_cvt_f32_fp8((int)e.x, 3);   // OCP E4M3 byte
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
+          }
+        } else {
+          if (!RAGGED || active) {
+            const uint32_t aux = e.x >> 24;
+            const uint64_t sidx = (uint64_t)row * a.syms_per_row + (uint64_t)sl * a.s_full + step;
+            if (a.sym_out) a.sym_out[sidx] = (uint16_t)aux;
+            if (a.w_out) {
+              const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols + (uint64_t)step * KW;
+              if constexpr (PAY == 1) {
+#pragma unroll
+                for (int i = 0; i < KW; ++i)
+                  static_cast<int8_t*>(a.w_out)[wi + i] =
+                      (int8_t)((int)((aux >> (CB * i)) & ((1u << CB) - 1)) - (1 << (CB - 1)));
+              } else if constexpr (PAY == 2) {
+                const uint32_t dw = (u < 4) ? rcur.x : (u < 8) ? rcur.y : (u < 12) ? rcur.z : rcur.w;
+                const uint32_t r = (dw >> (8 * (u & 3))) & 0xFFu;
+                static_cast<uint16_t*>(a.w_out)[wi] = (uint16_t)(((r & 0x80u) << 8) | (aux << 7) | (r & 0x7Fu));
+              } else {
+                static_cast<uint8_t*>(a.w_out)[wi] = (uint8_t)aux;
+              }
+            }
+          }
+        }
+        // ---- A5: renormalise; the stream words come from the LDS ring
+        if (rpos + 64 > have) {            // wave-uniform: next chunk into the ring
+          const uint32_t slot_c = nc & 1u;
+          reinterpret_cast<uint4*>(ring + slot_c * kChunk)[lane] = pre;
+          if (slot_c == 0 && lane < 8) reinterpret_cast<uint4*>(ring + kRing)[lane] = pre;
+          have += kChunk;
+          ++nc;
+          if (nc < nch) pre = src[(uint64_t)nc * 64];
+        }
+        const uint16_t* rp = ring + (rpos & (kRing - 1));
+        if constexpr (RAGGED) {
+          const bool need = active && (x < kStateL);
+          const uint64_t msk = __ballot(need);
+          if (need) x = (x << 16) | rp[lanes_below(msk)];
+          rpos += (uint32_t)__popcll(msk);
+        } else {
+          const bool need = x < kStateL;
+          const uint64_t msk = __builtin_amdgcn_ballot_w64(need);
+          if (need) x = (x << 16) | rp[lanes_below(msk)];
+          rpos += (uint32_t)__popcll(msk);
+        }
+      }
+    }
+    if constexpr (MAT) {
+      const bool ok_lane = !active || x == kStateL;
+      const uint64_t bad = __ballot(!ok_lane);
+      if (lane == 0 && a.status_out)
+        a.status_out[t] = (bad != 0 ? 1u : 0u) | ((rpos != a.offsets[t + 1] - gb) ? 2u : 0u);
+    }
+  }
+}
+
+// PAY: 1 INT codes, 2 BF16 exponent, 3 FP8.  CB/KW: code bits and codes per symbol
+// (INT).  B: batch capacity (1 or 4).  MAT: decode-only test hook.
+template <int PAY, int CB, int KW, int B, bool MAT>
+__global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const uint32_t W = blockDim.x >> 6;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Hardware block b runs on XCD b % 8.  Give each XCD a contiguous range of logical
+  // blocks so the slice groups of a row group (which meet in the partial reduction)
+  // share one L2.  gridDim.x is a multiple of 8; surplus blocks exit at once.
+  const uint32_t per = gridDim.x >> 3;
+  const uint32_t lb = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lb >= a.n_blocks) return;
+  const uint32_t rg = lb / a.n_sg, sg = lb - rg * a.n_sg;
+  const uint32_t R = a.tiles_per_wave;
+  const uint32_t sl_blk = sg * W * R;
+  const uint32_t sl_blk_end = min(sl_blk + W * R, a.n_sl);
+  const uint32_t c_lo = sl_blk * a.tile_cols;
+  const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
+
+  const uint32_t lut_bytes = a.lut_entries * 8;
+  uint2* lut = reinterpret_cast<uint2*>(smem);
+  float* xs = reinterpret_cast<float*>(smem + lut_bytes);
+  const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * 4 + 15) & ~15u);
+  uint16_t* rings = reinterpret_cast<uint16_t*>(smem + lut_bytes + xs_bytes);
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(smem + lut_bytes + xs_bytes + W * kRingStride * 2);
+
+  // ---- A2: stage the decode table; A3: stage the activation slice
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.lut);
+    uint4* dst = reinterpret_cast<uint4*>(lut);
+    for (uint32_t i = tid; i < a.lut_entries / 2; i += blockDim.x) dst[i] = src[i];
+  }
+  if constexpr (!MAT) {
+    const uint32_t nc = a.xs_cols;
+    if constexpr (PAY == 1 && CB == 4 && KW == 2) {
+      // pairs (x0, x1 - 16 x0): acc += (d0 + 16 d1) x0 + d1 (x1 - 16 x0) = d0 x0 + d1 x1
+      for (uint32_t p = tid; p < nc / 2; p += blockDim.x) {
+        const uint32_t c = c_lo + 2 * p;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float x0 = 0.f, x1 = 0.f;
+          if (c < c_hi && (uint32_t)b < a.nb) {
+            x0 = load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c);
+            x1 = load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c + 1);
+          }
+          xs[(2 * p) * B + b] = x0;
+          xs[(2 * p + 1) * B + b] = x1 - 16.f * x0;
+        }
+      }
+    } else {
+      for (uint32_t i = tid; i < nc; i += blockDim.x) {
+        const uint32_t c = c_lo + i;
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          xs[i * B + b] = (c < c_hi && (uint32_t)b < a.nb)
+                              ? load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c) : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const uint32_t row = rg * 64 + lane;
+  const bool active = row < a.rows;
+  const bool ragged = (rg + 1) * 64 > a.rows;     // wave-uniform
+  const uint32_t w_sl0 = sl_blk + wid * R;
+  const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
+  const bool have_work = w_sl0 < w_sl1;
+  float acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = 0.f;
+  uint16_t* ring = rings + wid * kRingStride;
+
+  if (have_work) {
+    const uint32_t t0 = rg * a.n_sl + w_sl0, t1 = rg * a.n_sl + w_sl1;
+    if (ragged)
+      wave_run<PAY, CB, KW, B, MAT, true>(a, lut, xs, ring, rg, t0, t1, c_lo, lane, active, acc);
+    else
+      wave_run<PAY, CB, KW, B, MAT, false>(a, lut, xs, ring, rg, t0, t1, c_lo, lane, active, acc);
+  }
+  if constexpr (MAT) return;
+
+  // ---- A8: epilogue.  Integer digits were accumulated unsigned: subtract
+  // 2^(b-1) * sum(x) over the wave's columns (same for every row).
+  if constexpr (PAY == 1) {
+    if (have_work) {
+      const uint32_t cw0 = (w_sl0 - sl_blk) * a.tile_cols;
+      const uint32_t cw1 = min((w_sl1 - sl_blk) * a.tile_cols, c_hi - c_lo);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float s = 0.f;
+        if ((uint32_t)b < a.nb)
+          for (uint32_t c = cw0 + lane; c < cw1; c += 64)
+            s += load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c_lo + c);
+        acc[b] -= (float)(1 << (CB - 1)) * wave_sum(s);
+      }
+    }
+  }
+  // reuse this wave's ring as its reduction slot (only this wave touched it)
+  float* red = reinterpret_cast<float*>(ring);
+#pragma unroll
+  for (int b = 0; b < B; ++b) red[b * 64 + lane] = have_work ? acc[b] : 0.f;
+  __syncthreads();
+  for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
+    const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
+    float s = 0.f;
+    for (uint32_t w = 0; w < W; ++w) s += reinterpret_cast<const float*>(rings + w * kRingStride)[b * 64 + l];
+    if (a.n_sg == 1) {
+      if (r < a.rows && b < a.nb) {
+        const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
+        a.y[(uint64_t)b * a.rows + r] = s * sc;
+      }
+    } else {
+      a.partials[(((uint64_t)rg * a.n_sg + sg) * B + b) * 64 + l] = s;
+    }
+  }
+  if (a.n_sg == 1) return;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[rg], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    ctl[0] = (prev == a.n_sg - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (ctl[0] == 0) return;
+  __threadfence();
+  for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
+    const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
+    float s = 0.f;
+    for (uint32_t g = 0; g < a.n_sg; ++g)
+      s += __hip_atomic_load(&a.partials[(((uint64_t)rg * a.n_sg + g) * B + b) * 64 + l],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (r < a.rows && b < a.nb) {
+      const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
+      a.y[(uint64_t)b * a.rows + r] = s * sc;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void k_fill_zero(float* y, uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = 0.f;
+}
+
+// ------------------------------------------------------------------ host launch
+using KernelFn = void (*)(const KArgs);
+
+template <int B, bool MAT>
+static KernelFn pick_kernel(const ecw_coding& c) {
+  switch (c.payload) {
+    case ECW_P_INT_CODES:
+      switch (c.code_bits * 16 + c.weights_per_symbol) {
+        case 4 * 16 + 1: return k_decode<1, 4, 1, B, MAT>;
+        case 4 * 16 + 2: return k_decode<1, 4, 2, B, MAT>;
+        case 3 * 16 + 1: return k_decode<1, 3, 1, B, MAT>;
+        case 3 * 16 + 2: return k_decode<1, 3, 2, B, MAT>;
+        case 2 * 16 + 1: return k_decode<1, 2, 1, B, MAT>;
+        case 2 * 16 + 2: return k_decode<1, 2, 2, B, MAT>;
+        case 2 * 16 + 4: return k_decode<1, 2, 4, B, MAT>;
+      }
+      return nullptr;
+    case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT>;
+    case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT>;
+  }
+  return nullptr;
+}
+
+static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t xs_cols, int B, bool mat) {
+  const uint64_t lut = (uint64_t)t->n_tables << t->coding.log2_m;
+  uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * 4 + 15) / 16 * 16;
+  return lut * 8 + xs + (uint64_t)W * kRingStride * 2 + 64;
+}
+
+static ecw_status launch(ecw_stream stream, const ecw_tensor* t, KArgs& a, int B, bool mat,
+                         uint32_t W) {
+  KernelFn fn = mat ? (B == 1 ? pick_kernel<1, true>(t->coding) : nullptr)
+                    : (B == 1 ? pick_kernel<1, false>(t->coding) : pick_kernel<4, false>(t->coding));
+  if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
+  const uint64_t lds = lds_bytes(t, W, a.xs_cols, B, mat);
+  if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "launch shape needs more than 160 KiB of LDS");
+  const uint32_t grid = (a.n_blocks + 7) / 8 * 8;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  return ECW_OK;
+}
+
+static void fill_common(const ecw_tensor* t, KArgs& a) {
+  const uint8_t* base = static_cast<const uint8_t*>(t->device_blob);
+  a.lut = reinterpret_cast<const uint2*>(base + t->off_lut);
+  a.states = reinterpret_cast<const uint32_t*>(base + t->off_states);
+  a.offsets = reinterpret_cast<const uint32_t*>(base + t->off_offsets);
+  a.words = reinterpret_cast<const uint16_t*>(base + t->off_words);
+  a.raw = base + t->off_raw;
+  a.scales = reinterpret_cast<const uint16_t*>(base + t->off_scales);
+  a.rows = t->coding.rows;
+  a.cols = t->coding.cols;
+  a.n_rg = t->n_row_groups;
+  a.n_sl = t->n_slices;
+  a.s_full = t->steps_full;
+  a.s_last = t->steps_last;
+  a.log2m = t->coding.log2_m;
+  a.tile_cols = t->coding.tile_cols;
+  a.syms_per_row = symbols_per_row(t->coding.payload, t->coding.weights_per_symbol, t->coding.cols);
+  a.lut_entries = t->n_tables << t->coding.log2_m;
+  a.raw_full_bytes = (uint32_t)(raw_group_count(t->steps_full) * 1024);
+  a.raw_rg_bytes = t->n_slices ? (uint32_t)((t->n_slices - 1) * raw_group_count(t->steps_full) * 1024 +
+                                            raw_group_count(t->steps_last) * 1024) : 0;
+}
+
+static ecw_status check_tensor(const ecw_tensor* t) {
+  if (!t) return fail(ECW_E_INVALID_ARG, "tensor is NULL");
+  ecw_status st = check_coding(&t->coding);
+  if (st != ECW_OK) return st;
+  if (!t->device_blob) return fail(ECW_E_INVALID_ARG, "tensor has no device blob");
+  if (reinterpret_cast<uintptr_t>(t->device_blob) % 256) return fail(ECW_E_INVALID_ARG, "device blob misaligned");
+  if (t->coding.payload == ECW_P_E8_LATTICE) return fail(ECW_E_UNSUPPORTED, "E8 lattice decode kernel not built");
+  if (t->waves_per_block < 1 || t->waves_per_block > 16 || t->tiles_per_wave < 1 || t->tiles_per_wave > 4096)
+    return fail(ECW_E_INVALID_ARG, "launch shape out of range");
+  if (t->steps_full % 16 || t->steps_last % 16) return fail(ECW_E_UNSUPPORTED, "steps per tile must be a multiple of 16");
+  return ECW_OK;
+}
+
+}  // namespace ecw
+
+using namespace ecw;
+
+extern "C" ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
+                               float* y, int batch, void* workspace, size_t ws_bytes) {
+  clear_error();
+  ecw_status st = check_tensor(t);
+  if (st != ECW_OK) return st;
+  if (batch < 1 || batch > 4) return fail(ECW_E_INVALID_ARG, "batch must be 1..4");
+  if (x_dtype != ECW_DT_F16 && x_dtype != ECW_DT_BF16) return fail(ECW_E_INVALID_ARG, "x dtype must be F16 or BF16");
+  if (t->coding.rows && (!y || reinterpret_cast<uintptr_t>(y) % 16))
+    return fail(ECW_E_INVALID_ARG, "y must be a 16-byte aligned device pointer");
+  if (t->coding.cols && (!x || reinterpret_cast<uintptr_t>(x) % 16))
+    return fail(ECW_E_INVALID_ARG, "x must be a 16-byte aligned device pointer");
+  const uint64_t need = workspace_bytes(t, batch);
+  if (need && (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
+    return fail(ECW_E_INVALID_ARG, "workspace missing, too small or not 256-byte aligned");
+  if (t->coding.rows == 0) return ECW_OK;
+  if (t->n_tiles == 0) {   // K == 0: y = 0 (a fill kernel, so the call stays graph-capturable)
+    const uint64_t n = (uint64_t)batch * t->coding.rows;
+    hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, y, n);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ECW_OK : fail(ECW_E_HIP, "fill launch failed");
+  }
+  const int B = batch > 1 ? 4 : 1;
+  KArgs a{};
+  fill_common(t, a);
+  a.x = x;
+  a.y = y;
+  a.x_is_bf16 = x_dtype == ECW_DT_BF16;
+  a.nb = (uint32_t)batch;
+  a.tiles_per_wave = t->tiles_per_wave;
+  a.n_sg = slice_groups(t);
+  a.n_blocks = a.n_rg * a.n_sg;
+  a.xs_cols = t->waves_per_block * t->tiles_per_wave * t->coding.tile_cols;
+  if (need) {
+    const uint64_t part = (uint64_t)a.n_rg * a.n_sg * (uint64_t)B * 64 * 4;
+    a.partials = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
+  }
+  return launch(stream, t, a, B, false, t->waves_per_block);
+}
+
+extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, uint16_t* symbols,
+                                      void* w_out, uint32_t* tile_status) {
+  clear_error();
+  ecw_status st = check_tensor(t);
+  if (st != ECW_OK) return st;
+  if (t->n_tiles == 0) return ECW_OK;
+  KArgs a{};
+  fill_common(t, a);
+  a.sym_out = symbols;
+  a.w_out = w_out;
+  a.status_out = tile_status;
+  a.nb = 1;
+  a.tiles_per_wave = 1;   // every tile restarts its stream: per-tile status is exact
+  const uint32_t W = std::min<uint32_t>(8, t->n_slices);
+  a.n_sg = (t->n_slices + W - 1) / W;
+  a.n_blocks = a.n_rg * a.n_sg;
+  a.xs_cols = 0;
+  return launch(stream, t, a, 1, true, W);
+}

@@ -1,0 +1,164 @@
+/*
+ * ecw.h -- entropy-coded weights, decoded inside a batch-1 GEMV on MI355X (gfx950).
+ *
+ * Plain C ABI.  No C++ types, exceptions or HIP headers cross it.  Every buffer is
+ * owned by the caller; the library allocates no device memory and keeps no device
+ * state between calls.
+ *
+ * The operation: a weight matrix W [rows][cols] is stored as independent rANS
+ * tiles of 64 rows x tile_cols columns, 32-bit states and 16-bit payload words
+ * (EntroPack page, Sections 3.6 and C.3).  dec_gemv decodes the tiles in parallel,
+ * rebuilds each weight in registers and multiplies it into y = W x straight away,
+ * without writing a weight tensor to memory (MINE page, Section 4.1 "Fused mvm";
+ * EntroPack page, Section D names the fusion as the missing step).  Weights per
+ * symbol, table size M and tile width are the per-tensor tuning axes of the MINE
+ * page (Section 4.2).
+ *
+ * Status convention: every entry point returns ECW_OK or an error code and, on
+ * error, launches nothing and writes no output; ecw_last_error() gives a message
+ * (thread-local).  dec_gemv / dec_materialize are asynchronous on the given stream:
+ * ECW_OK means "enqueued"; a device fault shows at the caller's next
+ * synchronisation.  Calls are reentrant; concurrent calls on different streams are
+ * allowed when they use different workspaces.
+ */
+#ifndef ECW_H
+#define ECW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ECW_ABI_VERSION 1u
+#define ECW_MAX_TABLES 17
+#define ECW_MAX_ALPHABET 256
+
+typedef struct ihipStream_t* ecw_stream; /* same type as hipStream_t; NULL = default */
+
+typedef enum {
+  ECW_OK = 0,
+  ECW_E_INVALID_ARG = 1,     /* null pointer, bad size, misaligned buffer, bad dtype */
+  ECW_E_UNSUPPORTED = 2,     /* legal coding this build does not implement */
+  ECW_E_CORRUPT = 3,         /* blob fails validation */
+  ECW_E_BUFFER_TOO_SMALL = 4,
+  ECW_E_HIP = 5              /* the HIP runtime refused a launch */
+} ecw_status;
+
+typedef enum {
+  ECW_P_INT_CODES = 1,       /* signed b-bit integer codes, k per symbol, fp16 row scale */
+  ECW_P_BF16_EXP = 2,        /* BF16: 8-bit exponent coded, sign+mantissa byte raw     */
+  ECW_P_FP8_E4M3 = 3,        /* OCP E4M3 bytes coded, fp16 row scale                   */
+  ECW_P_E8_LATTICE = 4       /* E8 lattice fields, 17 coset-conditioned tables          */
+} ecw_payload;
+
+typedef enum {
+  ECW_DT_F16 = 1, ECW_DT_BF16 = 2, ECW_DT_F32 = 3, ECW_DT_I8 = 4, ECW_DT_FP8_E4M3 = 5
+} ecw_dtype;
+
+/* One coding of one tensor (one point of the per-tensor tuning space). */
+typedef struct {
+  uint32_t payload;            /* ecw_payload */
+  uint32_t rows, cols;         /* N (outputs) x K (inputs); W is row-major [N][K] */
+  uint32_t weights_per_symbol; /* k: INT 1|2|4 with code_bits*k <= 8; BF16/FP8 1; E8 8 */
+  uint32_t code_bits;          /* INT only: 2, 3 or 4; else 0 */
+  uint32_t log2_m;             /* table size M = 2^log2_m, 8..13 */
+  uint32_t tile_rows;          /* must be 64 (one wave64 lane per row) */
+  uint32_t tile_cols;          /* columns per tile: multiple of 64 (and of 8k) */
+  uint32_t recon_dtype;        /* E8 only: ECW_DT_I8 (2v) or ECW_DT_FP8_E4M3 (v); else 0 */
+} ecw_coding;
+
+/* Frequency tables of a coding (host POD).  Table 0 serves every payload except
+ * E8, where table 0 codes the coset and table 1 + 8c + j codes field j (z1..z7, then
+ * m = floor(z8/2)) given coset c (EntroPack page, Sections 3.3 and A.3). */
+typedef struct {
+  uint32_t n_tables;
+  uint32_t alphabet[ECW_MAX_TABLES];          /* symbols in use per table (<= 256)   */
+  int32_t value_offset[ECW_MAX_TABLES];       /* field value = symbol + value_offset */
+  uint16_t freq[ECW_MAX_TABLES][ECW_MAX_ALPHABET];   /* f > 0 iff count > 0; sum = M */
+  uint64_t count[ECW_MAX_TABLES][ECW_MAX_ALPHABET];  /* histogram the freqs come from */
+} ecw_tables;
+
+/* Validated, device-ready view of one blob (host POD, filled by dec_prepare). */
+typedef struct {
+  ecw_coding coding;
+  uint32_t n_tables, n_row_groups, n_slices, n_tiles;
+  uint32_t steps_full, steps_last;   /* symbols per lane in a full / the last slice */
+  uint32_t lut_entry_bytes;
+  uint32_t waves_per_block;          /* launch shape; dec_prepare sets a default and */
+  uint32_t tiles_per_wave;           /* the caller may change it (autotuning)        */
+  uint32_t reserved;
+  uint64_t blob_bytes;
+  /* byte ledger of the stored representation */
+  uint64_t bytes_words, bytes_raw, bytes_tile_meta, bytes_tables, bytes_scales;
+  const void* device_blob;           /* the caller's device copy of the blob */
+  uint64_t off_tables, off_lut, off_states, off_offsets, off_words, off_raw, off_scales;
+} ecw_tensor;
+
+/* Histogram + frequency normalisation of the logical tensor `w`.
+ *   c: coding; w: host, row-major [rows][cols], element type by payload:
+ *      INT: int8 codes in [-2^(b-1), 2^(b-1)); BF16: uint16 bit patterns;
+ *      FP8: uint8 e4m3fn bytes; E8: int8 doubled coordinates 2v, each block of 8
+ *      columns all even or all odd with sum(v) even.
+ *   out: filled.  Frequencies minimise the cross-entropy size bound (MINE page,
+ *   Section 4.2, "Compressed Size Prediction"); ties go to the smaller symbol.
+ * Errors: INVALID_ARG (nulls, bad coding, values out of range), UNSUPPORTED (more
+ * distinct symbols than M slots, alphabet > 256). */
+ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_tables* out);
+
+/* Encode `w` into a self-describing blob (format version 1, little-endian).
+ *   t: tables from enc_build_tables for the same w (or any tables with f > 0 for
+ *      every occurring symbol); row_scales: host fp16 [rows] (NULL for BF16).
+ *   Two-call protocol: blob == NULL -> *blob_bytes = required size, ECW_OK;
+ *   otherwise *blob_bytes is the capacity (BUFFER_TOO_SMALL if short) and is set
+ *   to the bytes written.
+ * Tiles are rANS-coded independently on up to hardware_concurrency host threads. */
+ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const void* w,
+                      const uint16_t* row_scales, void* blob, size_t* blob_bytes);
+
+/* Validate a blob and describe it.
+ *   host_blob / blob_bytes: the blob in host memory (read only during the call).
+ *   device_blob: the same bytes already copied to device memory, 256-byte aligned
+ *   (may be NULL for host-only inspection; dec_gemv then refuses the tensor).
+ * Checks, before anything is used: magic, version, checked 64-bit section
+ * arithmetic, section bounds and overlap, table sums (sum f = M), the decode table
+ * against the frequencies, monotone tile offsets, start states in [2^16, 2^32).
+ * Errors: INVALID_ARG, CORRUPT, UNSUPPORTED. */
+ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, const void* device_blob,
+                       ecw_tensor* out);
+
+/* Bytes of device workspace dec_gemv needs for this tensor, launch shape and batch
+ * (0 when each row group fits one block).  The workspace holds per-block partial
+ * sums and one arrival counter per row group; it must be zero-filled once before
+ * its first use, and every completed dec_gemv leaves the counters at zero again. */
+ecw_status dec_gemv_workspace_size(const ecw_tensor* t, int batch, size_t* bytes);
+
+/* Fused decode + matrix-vector product: y[b][r] = sum_c W[r][c] * x[b][c].
+ *   x: device [batch][cols], ECW_DT_F16 or ECW_DT_BF16, 16-byte aligned.
+ *   y: device fp32 [batch][rows], overwritten, 16-byte aligned.
+ *   batch: 1..4.  workspace: device, >= dec_gemv_workspace_size bytes (NULL if 0).
+ * Weight reconstruction (never stored): INT q * scale_r; BF16 the exact bf16 value;
+ * FP8 e4m3(q) * scale_r; E8 (2v) * scale_r / 2 or e4m3(v) * scale_r.  Accumulation
+ * in fp32; per-row sums are reduced in a fixed order (deterministic).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
+                    float* y, int batch, void* workspace, size_t workspace_bytes);
+
+/* Test hook: the same decode core, writing what dec_gemv keeps in registers.
+ *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices);
+ *   w_out: nullable device [rows][cols] in the logical dtype (INT int8 codes, BF16
+ *          uint16 bits, FP8 uint8 bytes, E8 int8 2v or uint8 e4m3 per recon_dtype);
+ *   tile_status: nullable device uint32 [n_tiles], 0 when the tile ended with every
+ *          active state back at 2^16 and exactly its words read, else nonzero.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, uint16_t* symbols,
+                           void* w_out, uint32_t* tile_status);
+
+const char* ecw_last_error(void);
+uint32_t ecw_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ECW_H */

@@ -1,0 +1,90 @@
+"""Coding variants shared by the CPU byte-parity tests and the GPU parity tests.
+
+Each case gives a logical tensor, row scales, the coding, and the activation dtype.
+Inputs come from ecw_inputs (seeded) or plain seeded numpy draws.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+import ecw_inputs as E
+
+INT, BF16, FP8, E8 = 1, 2, 3, 4
+
+
+@dataclass
+class Case:
+    name: str
+    payload: int
+    rows: int
+    cols: int
+    k: int
+    code_bits: int
+    log2_m: int
+    tile_cols: int
+    logical: np.ndarray
+    scales: np.ndarray | None
+    x_dtype: str = "f16"
+    recon_dtype: int = 0
+
+    def oracle_coding(self):
+        from oracle import pipeline as P
+        return P.Coding(self.payload, self.rows, self.cols, k=self.k, code_bits=self.code_bits,
+                        log2_m=self.log2_m, tile_cols=self.tile_cols, recon_dtype=self.recon_dtype)
+
+    def lib_coding(self):
+        import entropy_coded_weight_amd as ecw
+        return ecw.Coding(self.payload, self.rows, self.cols, self.k,
+                          self.code_bits if self.payload == INT else 0, self.log2_m,
+                          self.tile_cols, self.recon_dtype)
+
+
+def _int(name, rows, cols, k, bits, m, tc, dist="laplace", seed=0):
+    rng = np.random.default_rng([0, 200, seed])
+    if bits == 4:
+        t = E.laplace_codes((rows, cols), rng) if dist == "laplace" else E.gaussian_codes((rows, cols), rng)
+        q, s = t.codes, t.scales
+    else:
+        half = 1 << (bits - 1)
+        q = np.clip(np.rint(rng.laplace(0, 0.7, (rows, cols))), -half, half - 1).astype(np.int8)
+        s = (0.01 * rng.uniform(0.5, 1.5, rows)).astype(np.float16)
+    return Case(name, INT, rows, cols, k, bits, m, tc, q, s)
+
+
+def small_cases():
+    cases = []
+    t = E.config1()
+    cases.append(Case("cfg1_gauss_k1_m12", INT, 1024, 1024, 1, 4, 12, 256, t.codes, t.scales))
+    cases.append(_int("pair_m10", 256, 1024, 2, 4, 10, 256, seed=1))
+    cases.append(_int("pair_m11_ragged", 200, 416, 2, 4, 11, 128, seed=2))
+    cases.append(_int("pair_m12_gauss", 128, 512, 2, 4, 12, 128, dist="gauss", seed=3))
+    cases.append(_int("quad_int2", 70, 256, 4, 2, 10, 128, seed=4))
+    cases.append(_int("pair_int3", 64, 192, 2, 3, 8, 64, seed=5))
+    cases.append(_int("single_int2", 65, 320, 1, 2, 9, 64, seed=6))
+    # one symbol only: f = M, the stream holds no words
+    q = np.full((96, 256), 3, np.int8)
+    cases.append(Case("single_symbol", INT, 96, 256, 1, 4, 12, 128, q, np.full(96, 0.5, np.float16)))
+    # maximal skew: one symbol almost everywhere
+    rng = np.random.default_rng(77)
+    q = np.where(rng.random((64, 512)) < 0.999, 0, rng.integers(-8, 8, (64, 512))).astype(np.int8)
+    cases.append(Case("max_skew_pair", INT, 64, 512, 2, 4, 12, 256, q, np.full(64, 0.25, np.float16)))
+    b = E.bf16_weights((130, 512), np.random.default_rng([0, 300, 1]))
+    cases.append(Case("bf16_m12", BF16, 130, 512, 1, 0, 12, 256, b.bits, None, "bf16"))
+    b = E.bf16_weights((64, 1536), np.random.default_rng([0, 300, 2]))
+    cases.append(Case("bf16_m10_ragged_k", BF16, 64, 1536, 1, 0, 10, 1024, b.bits, None, "bf16"))
+    f = E.fp8_weights((96, 768), np.random.default_rng([0, 400, 1]))
+    cases.append(Case("fp8_m12", FP8, 96, 768, 1, 0, 12, 256, f.codes, f.scales, "bf16"))
+    f = E.fp8_weights((64, 512), np.random.default_rng([0, 400, 2]))
+    cases.append(Case("fp8_m9", FP8, 64, 512, 1, 0, 9, 64, f.codes, f.scales, "bf16"))
+    return cases
+
+
+def e8_case():
+    from oracle import e8
+    rng = np.random.default_rng([0, 500, 1])
+    c, z = e8.nearest_e8(rng.normal(0, 3.0, (96 * 24, 8)))
+    v2 = e8.doubled_coords(c, z).reshape(96, 192).astype(np.int8)
+    return Case("e8_i8", E8, 96, 192, 8, 0, 11, 64, v2, (0.01 * rng.uniform(0.5, 1.5, 96)).astype(np.float16),
+                recon_dtype=4)

@@ -1,0 +1,137 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+* decode parity (bit-exact): dec_materialize's symbols and weights equal the
+  oracle's decode / the encoded logical tensor; every tile ends on its invariant.
+* operator parity: dec_gemv within |y - y_ref| <= 1e-3 * sum|w x| per output, with
+  y_ref the float64 product of the oracle's weight values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import entropy_coded_weight_amd as ecw
+import ecw_inputs as E
+from oracle import gemv, pipeline as P
+from tests import cases
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _x(case, batch, seed=0):
+    rng = np.random.default_rng([0, 900, seed, batch])
+    xv = rng.standard_normal((batch, case.cols))
+    if case.x_dtype == "f16":
+        host = xv.astype(np.float16)
+        dev = torch.from_numpy(host).cuda()
+        return dev, gemv.x_values(host, "f16")
+    import torch as T
+    bits = T.from_numpy(xv.astype(np.float32)).to(T.bfloat16)
+    host = bits.view(T.int16).numpy().view(np.uint16)
+    return bits.cuda(), gemv.x_values(host, "bf16")
+
+
+def _logical_view(case, w):
+    a = w.cpu().numpy()
+    if case.payload == cases.BF16:
+        return a.view(np.uint16)
+    return a
+
+
+@pytest.mark.parametrize("case", cases.small_cases(), ids=lambda c: c.name)
+def test_materialize_bit_exact(case):
+    print(f"[gpu] materialize {case.name}", flush=True)
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    ct = ecw.CompressedTensor(blob)
+    sym, w, st = ct.materialize()
+    torch.cuda.synchronize()
+    assert int(st.abs().sum()) == 0
+    assert np.array_equal(_logical_view(case, w), case.logical)
+    comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+    ref_sym, ok = P.decode_symbols(comp)
+    assert ok.all()
+    assert np.array_equal(sym.cpu().numpy().view(np.uint16).astype(np.int64), ref_sym)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4])
+@pytest.mark.parametrize("case", cases.small_cases(), ids=lambda c: c.name)
+def test_gemv_within_bound(case, batch):
+    print(f"[gpu] gemv {case.name} batch={batch}", flush=True)
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    ct = ecw.CompressedTensor(blob)
+    xd, xv = _x(case, batch)
+    y = ct.gemv(xd)
+    torch.cuda.synchronize()
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    ok, worst = gemv.check(y.cpu().numpy(), wv, xv)
+    assert ok, f"worst error / bound = {worst}"
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (2, 3), (3, 1), (8, 1), (16, 1), (4, 2), (1, 16)])
+def test_launch_shapes_agree_and_reduction_is_deterministic(shape):
+    W, R = shape
+    print(f"[gpu] launch shape W={W} R={R}", flush=True)
+    case = cases._int("shapes", 200, 2048, 2, 4, 11, 128, seed=9)
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    ct = ecw.CompressedTensor(blob, waves_per_block=W, tiles_per_wave=R)
+    xd, xv = _x(case, 1)
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    ys = []
+    for _ in range(3):                       # counters must return to zero each call
+        ys.append(ct.gemv(xd).cpu().numpy())
+    for y in ys:
+        ok, worst = gemv.check(y, wv, xv)
+        assert ok, worst
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+
+
+def test_fp8_every_code_value():
+    # row r repeats E4M3 code r: y[r] = K * e4m3(r) * scale, so any mis-decoded
+    # code (subnormals included) breaks its own row's bound
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    n, K = codes.size, 64
+    q = np.repeat(codes[:, None], K, axis=1)
+    sc = np.full(n, 1.0, np.float16)
+    c = ecw.Coding(ecw.FP8_E4M3, n, K, 1, 0, 9, 64)
+    ct = ecw.CompressedTensor(ecw.encode(c, q, sc))
+    xd = torch.ones((1, K), dtype=torch.bfloat16, device="cuda")
+    y = ct.gemv(xd).cpu().numpy()[0]
+    wv = P.weight_values(P.Coding(P.FP8_E4M3, n, K), q, sc)
+    assert np.array_equal(y.astype(np.float64), wv.sum(axis=1))
+
+
+def test_bf16_every_exponent_and_sign():
+    # every finite bf16 exponent with both signs and a few mantissas
+    vals = []
+    for e in range(0, 255):
+        for s in (0, 1):
+            for m in (0, 1, 0x55, 0x7F):
+                vals.append((s << 15) | (e << 7) | m)
+    vals = np.array(vals, np.uint16)
+    n = vals.size // 16
+    bits = vals[: n * 16].reshape(n, 16)
+    bits = np.repeat(bits, 4, axis=1)              # K = 64
+    c = ecw.Coding(ecw.BF16_EXP, n, 64, 1, 0, 9, 64)
+    ct = ecw.CompressedTensor(ecw.encode(c, bits))
+    sym, w, st = ct.materialize()
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), bits)
+
+
+def test_degenerate_shapes():
+    # K == 0: y must be zero; N == 0: nothing happens
+    c = ecw.Coding(ecw.INT_CODES, 70, 0, 1, 4, 10, 64)
+    ct = ecw.CompressedTensor(ecw.encode(c, np.zeros((70, 0), np.int8), np.ones(70, np.float16)))
+    y = torch.full((1, 70), 7.0, device="cuda")
+    ecw.gemv_raw(ct.t, torch.zeros((1, 16), dtype=torch.float16, device="cuda")[:, :0].contiguous(), y, None)
+    torch.cuda.synchronize()
+    assert float(y.abs().max()) == 0.0
+    c = ecw.Coding(ecw.INT_CODES, 0, 64, 1, 4, 10, 64)
+    ct = ecw.CompressedTensor(ecw.encode(c, np.zeros((0, 64), np.int8), np.zeros(0, np.float16)))
+    y = torch.empty((1, 0), device="cuda")
+    ecw.gemv_raw(ct.t, torch.zeros((1, 64), dtype=torch.float16, device="cuda"), y, None)
+    torch.cuda.synchronize()

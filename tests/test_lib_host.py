@@ -1,0 +1,259 @@
+"""CPU tests of the C-ABI library: symbols, byte parity with the oracle, validation.
+
+No GPU is touched: only the host entry points run, and the device entry points are
+called only with arguments they must reject before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import entropy_coded_weight_amd as ecw
+from oracle import pipeline as P, rans
+from tests import blobfmt, cases
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "ecw.h")).read()
+    declared = set(re.findall(r"^\w[\w\s\*]*?\b(\w+)\s*\(", header, flags=re.M))
+    declared -= {"if", "while"}
+    assert {"enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv", "dec_materialize",
+            "dec_gemv_workspace_size", "ecw_last_error", "ecw_abi_version"} <= declared
+    L = ecw.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.ecw_abi_version() == 1
+
+
+def test_tile_metadata_bytes_match_page_formula():
+    rows = [list(map(int, l.split())) for l in open(os.path.join(GOLDEN, "tile_metadata_bytes.txt"))
+            if l.strip() and not l.startswith("#")]
+    for lanes, sb, ob, total in rows:
+        assert lanes * sb + ob == total
+    c = cases.small_cases()[0]
+    t = ecw.prepare(ecw.encode(c.lib_coding(), c.logical, c.scales))
+    # 64 states + 1 offset per tile, plus the closing boundary offset
+    assert t.bytes_tile_meta == t.n_tiles * 260 + 4
+
+
+@pytest.mark.parametrize("case", cases.small_cases() + [cases.e8_case()], ids=lambda c: c.name)
+def test_byte_parity_with_oracle_and_oracle_decodes_library_blob(case):
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+    bl = blobfmt.parse(blob)
+    assert bl.h["magic"] == 0x31574345 and bl.h["version"] == 1
+    assert bl.h["total_bytes"] == blob.size
+    alphabet, voff, freq = blobfmt.tables(bl)
+    assert np.array_equal(freq, comp.freq)
+    assert np.array_equal(voff, comp.value_offset)
+    assert np.array_equal(blobfmt.states(bl), comp.states)
+    assert np.array_equal(blobfmt.offsets(bl), comp.offsets)
+    assert np.array_equal(blobfmt.words(bl), comp.words)
+    if comp.raw is not None:
+        assert np.array_equal(bl.section("raw"), comp.raw)
+    if case.scales is not None:
+        assert np.array_equal(blobfmt.scales(bl).view(np.uint16), case.scales.view(np.uint16))
+    # code parity: the oracle's decoder reads the library's sections
+    comp2 = P.Components(comp.coding, comp.n_tables, alphabet, voff, freq, comp.n_rg, comp.n_sl,
+                         comp.s_full, comp.s_last, blobfmt.states(bl), blobfmt.offsets(bl),
+                         blobfmt.words(bl), bl.section("raw") if comp.raw is not None else None,
+                         blobfmt.scales(bl))
+    _, ok = P.decode_symbols(comp2)
+    assert ok.all()
+    assert np.array_equal(P.decode(comp2), case.logical)
+
+
+def test_tables_match_oracle_histogram_and_frequencies():
+    for case in cases.small_cases()[:6]:
+        t = ecw.build_tables(case.lib_coding(), case.logical)
+        comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+        assert np.array_equal(t.count_array(), comp.counts)
+        assert np.array_equal(t.freq_array(), comp.freq)
+
+
+def test_decode_table_entries_follow_the_frequencies():
+    case = cases.small_cases()[1]
+    bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    _, voff, freq = blobfmt.tables(bl)
+    lut = blobfmt.lut(bl)[0]
+    cum = np.concatenate([[0], np.cumsum(freq[0])[:-1]])
+    sym = np.repeat(np.arange(256), freq[0])
+    assert np.array_equal(lut[:, 0] & 0xFFFFFF, freq[0][sym])
+    assert np.array_equal(lut[:, 0] >> 24, sym & 0xFF)
+    assert np.array_equal(lut[:, 1], np.arange(lut.shape[0]) - cum[sym])
+
+
+def test_prepare_ledger_and_defaults():
+    case = cases.small_cases()[0]
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    t = ecw.prepare(blob)
+    assert t.blob_bytes == blob.size
+    assert t.n_tiles == 16 * 4 and t.steps_full == 256 and t.steps_last == 256
+    assert t.bytes_scales == 2 * 1024 and t.bytes_raw == 0
+    assert t.bytes_tables == 520 + (1 << 12) * 8
+    assert 1 <= t.waves_per_block <= 16 and t.tiles_per_wave >= 1
+
+
+# ------------------------------------------------------------------ fault injection
+def _blob():
+    case = cases.small_cases()[2]
+    return ecw.encode(case.lib_coding(), case.logical, case.scales)
+
+
+def _prep_status(blob):
+    t = ecw.Tensor()
+    b = np.ascontiguousarray(blob)
+    return ecw.lib().dec_prepare(b.ctypes.data_as(ctypes.c_void_p), b.size, None, ctypes.byref(t))
+
+
+def _mutate(fn):
+    b = _blob().copy()
+    fn(b)
+    return b
+
+
+def _u32(b, off, v):
+    b[off:off + 4] = np.array([v], np.uint32).view(np.uint8)
+
+
+def _u64(b, off, v):
+    b[off:off + 8] = np.array([v], np.uint64).view(np.uint8)
+
+
+def test_prepare_accepts_valid_blob():
+    assert _prep_status(_blob()) == 0
+
+
+@pytest.mark.parametrize("name,fn,expect", [
+    ("truncated", None, 3),
+    ("bad_magic", lambda b: _u32(b, 0, 0xDEADBEEF), 3),
+    ("bad_version", lambda b: _u32(b, 4, 2), 2),
+    ("bad_section_count", lambda b: _u32(b, 12, 6), 3),
+    ("bad_tile_rows", lambda b: _u32(b, 40, 32), 2),
+    ("geometry_mismatch", lambda b: _u32(b, 64, 7), 3),
+    ("section_misaligned", lambda b: _u64(b, 96 + 16 * 2, 300), 3),
+    ("section_out_of_range", lambda b: _u64(b, 96 + 16 * 6, 1 << 40), 3),
+    ("section_size_overflow", lambda b: _u64(b, 96 + 16 * 4 + 8, (1 << 64) - 16), 3),
+    ("sections_overlap", lambda b: _u64(b, 96 + 16 * 3, 256), 3),
+])
+def test_prepare_rejects_corrupt_header(name, fn, expect):
+    if name == "truncated":
+        b = _blob()[:-300]
+    else:
+        b = _mutate(fn)
+    assert _prep_status(b) == expect, name
+    assert ecw.lib().ecw_last_error()
+
+
+def test_prepare_rejects_corrupt_contents():
+    base = _blob()
+    bl = blobfmt.parse(base)
+    off_t, _ = bl.sec["tables"]
+    off_l, _ = bl.sec["lut"]
+    off_s, _ = bl.sec["states"]
+    off_o, _ = bl.sec["offsets"]
+    # frequencies no longer sum to M
+    b = base.copy()
+    f = b[off_t + 8: off_t + 10].view(np.uint16)
+    f[0] += 1
+    assert _prep_status(b) == 3
+    # decode entry inconsistent with the frequencies
+    b = base.copy()
+    b[off_l + 4: off_l + 8] = np.array([5], np.uint32).view(np.uint8)
+    assert _prep_status(b) == 3
+    # frequency beyond the alphabet
+    b = base.copy()
+    _u32(b, off_t, 4)
+    assert _prep_status(b) == 3
+    # start state below L
+    b = base.copy()
+    _u32(b, off_s + 4 * 5, 123)
+    assert _prep_status(b) == 3
+    # inactive lane (row >= rows) with a state other than L: last row group of 200 rows
+    t = ecw.prepare(base)
+    last_rg_tile = (t.n_row_groups - 1) * t.n_slices
+    b = base.copy()
+    _u32(b, off_s + (last_rg_tile * 64 + 63) * 4, 0x20000)
+    assert _prep_status(b) == 3
+    # tile offsets not monotone
+    b = base.copy()
+    offs = b[off_o: off_o + 4 * 3].view(np.uint32)
+    offs[1], offs[2] = offs[2] + 1, offs[1]
+    assert _prep_status(b) == 3
+    # more words than symbols claimed by one tile
+    b = base.copy()
+    _u32(b, off_o + 4, 10 ** 7)
+    assert _prep_status(b) == 3
+
+
+def test_prepare_rejects_bad_arguments():
+    L = ecw.lib()
+    t = ecw.Tensor()
+    b = _blob()
+    assert L.dec_prepare(None, b.size, None, ctypes.byref(t)) == 1
+    # misaligned device pointer is rejected before anything else
+    assert L.dec_prepare(b.ctypes.data_as(ctypes.c_void_p), b.size, 8, ctypes.byref(t)) == 1
+
+
+def test_device_entry_points_reject_bad_arguments_without_launching():
+    L = ecw.lib()
+    b = _blob()
+    t = ecw.prepare(b)        # no device blob
+    y = ctypes.c_void_p(256)
+    assert L.dec_gemv(None, ctypes.byref(t), 256, 1, y, 1, None, 0) == 1
+    t.device_blob = 256
+    assert L.dec_gemv(None, ctypes.byref(t), 256, 1, y, 5, None, 0) == 1      # batch
+    assert L.dec_gemv(None, ctypes.byref(t), 256, 3, y, 1, None, 0) == 1      # x dtype
+    assert L.dec_gemv(None, ctypes.byref(t), 8, 1, y, 1, None, 0) == 1        # x misaligned
+    t.waves_per_block = 17
+    assert L.dec_gemv(None, ctypes.byref(t), 256, 1, y, 1, None, 0) == 1
+    t.waves_per_block, t.tiles_per_wave = 1, 1
+    n = ctypes.c_size_t()
+    assert L.dec_gemv_workspace_size(ctypes.byref(t), 1, ctypes.byref(n)) == 0 and n.value > 0
+    assert L.dec_gemv(None, ctypes.byref(t), 256, 1, y, 1, None, 0) == 1      # workspace needed
+    assert L.dec_materialize(None, None, None, None, None) == 1
+
+
+def test_encoder_rejects_bad_inputs():
+    c = ecw.Coding(ecw.INT_CODES, 64, 64, 1, 4, 12, 64)
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(c, np.full((64, 64), 9, np.int8), np.ones(64, np.float16))   # code out of range
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(ecw.Coding(ecw.INT_CODES, 64, 64, 2, 4, 7, 64), np.zeros((64, 64), np.int8),
+                   np.ones(64, np.float16))                                      # M < alphabet^k
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(ecw.Coding(ecw.INT_CODES, 64, 64, 1, 4, 12, 96), np.zeros((64, 64), np.int8),
+                   np.ones(64, np.float16))                                      # tile_cols % 64
+    v2 = np.zeros((8, 8), np.int8)
+    v2[0, 0] = 1                                                                 # mixed parity
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(ecw.Coding(ecw.E8_LATTICE, 8, 8, 8, 0, 11, 64, 4), v2, np.ones(8, np.float16))
+    # buffer too small in the second call
+    c = ecw.Coding(ecw.INT_CODES, 64, 64, 1, 4, 12, 64)
+    q = np.zeros((64, 64), np.int8)
+    t = ecw.build_tables(c, q)
+    buf = np.zeros(512, np.uint8)
+    n = ctypes.c_size_t(512)
+    st = ecw.lib().enc_encode(ctypes.byref(c), ctypes.byref(t), q.ctypes.data_as(ctypes.c_void_p),
+                              np.ones(64, np.float16).ctypes.data_as(ctypes.c_void_p),
+                              buf.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
+    assert st == 4 and n.value > 512
+
+
+def test_empty_tensor_encodes_and_validates():
+    c = ecw.Coding(ecw.INT_CODES, 0, 64, 1, 4, 10, 64)
+    blob = ecw.encode(c, np.zeros((0, 64), np.int8), np.zeros(0, np.float16))
+    t = ecw.prepare(blob)
+    assert t.n_tiles == 0 and t.bytes_words == 0
+
+
+def test_encode_is_deterministic_and_threads_agree():
+    case = cases.small_cases()[1]
+    a = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    b = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    assert np.array_equal(a, b)
