@@ -27,10 +27,7 @@ METRIC = "µs per fused decode-GEMV layer + effective weight GB/s (% HBM peak), 
 ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
 
 # per-tensor coding: (log2_m, tile_cols, waves_per_block, tiles_per_wave)
-DEFAULT_CODING = {
-    "q": (12, 256, 8, 1), "k": (12, 256, 8, 1), "v": (12, 256, 8, 1), "o": (12, 256, 8, 1),
-    "gate": (12, 256, 8, 1), "up": (12, 256, 8, 1), "down": (12, 256, 8, 1),
-}
+DEFAULT_CODING = {n: (12, 128, 16, 1) for n in ORDER}
 
 
 def log(*a):
@@ -96,6 +93,12 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-bytes", type=float, default=512e6)
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="after timing, run N plain device copies of 64 MiB (a kernel of known "
+                         "traffic that scales the profiler's FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--tensors", default=",".join(ORDER),
+                    help="subset of the layer to run (profiling); the JSON line is only "
+                         "meaningful for the full set")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -106,6 +109,7 @@ def main():
     import entropy_coded_weight_amd as ecw
     from oracle import gemv as G, pipeline as P
 
+    ORDER[:] = [n for n in ORDER if n in args.tensors.split(",")]
     dev = torch.device("cuda:0")
     t_build = time.time()
     layer = build_layer(args.batch, DEFAULT_CODING)
@@ -214,6 +218,12 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(avg_us[dom], 3)},
     }
+    if args.calibrate_copy:
+        src = torch.ones(64 << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.calibrate_copy):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(out), flush=True)

@@ -17,13 +17,17 @@
 // order: step-major, lanes ascending (EntroPack page, Sections 3.6 and C.3: one
 // wave per independent tile, 32-bit states, 16-bit words).
 //
-// Decode entry of slot i (table t), as two u32:
-//   lo = f | aux << 24   (f <= 2^13 in the low 24 bits, so a 24-bit multiply
-//                         f * (x >> m) ignores aux)
-//   hi = i - cum[s]      (the bias; next state = f * (x >> m) + hi)
-// aux = (symbol + value_offset) & 0xFF: the payload byte the kernel rebuilds the
-// weight from (MINE page, Section 4.1: one table read yields both the state
-// update operands and the payload).
+// Decode entry of slot i (table t), symbol s, as two u32 (MINE page, Section 4.1:
+// one table read yields both the state-update operands and the payload):
+//   lo = f | a8 << 24     f <= 2^13 sits in the low 24 bits, so the 24-bit multiply
+//                         f * (x >> m) ignores a8
+//   hi = bias | h16 << 16 bias = i - cum[s] < 2^13; next state = f * (x >> m) + bias
+// a8 / h16 per payload (h16 is an fp16 bit pattern, exact for every value here):
+//   INT, k = 1 or 2:  a8 = first code q0 (int8), h16 = fp16(q_{k-1})
+//   INT, k = 4:       a8 = symbol (packed unsigned digits), h16 = 0
+//   BF16:             a8 = exponent byte, h16 = 0
+//   FP8 E4M3:         a8 = code byte, h16 = fp16(e4m3 value) (NaN codes: 0x7E00)
+//   E8:               a8 = field value (int8), h16 = 0
 #pragma once
 #include <stdint.h>
 
@@ -83,5 +87,60 @@ inline uint32_t symbols_per_row(uint32_t payload, uint32_t k, uint32_t cols) {
   return cols;
 }
 inline uint64_t raw_group_count(uint32_t steps) { return (steps + 15) / 16; }
+
+// fp16 bit pattern of a small integer |v| <= 2048 (exact).
+inline uint16_t fp16_of_int(int v) {
+  if (v == 0) return 0;
+  uint16_t sign = v < 0 ? 0x8000 : 0;
+  uint32_t a = (uint32_t)(v < 0 ? -v : v);
+  int e = 31 - __builtin_clz(a);                 // a = 2^e * 1.m
+  uint32_t mant = (a << (10 - e)) & 0x3FF;
+  return (uint16_t)(sign | ((uint32_t)(e + 15) << 10) | mant);
+}
+
+// fp16 bit pattern of an OCP E4M3 byte's value (every finite E4M3 value is an fp16
+// value: 3 mantissa bits, exponents 2^-9 .. 2^8).
+inline uint16_t fp16_of_e4m3(uint8_t b) {
+  const uint16_t sign = (b & 0x80) ? 0x8000 : 0;
+  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
+  if (e == 15 && m == 7) return 0x7E00;                       // NaN
+  if (e == 0) {
+    if (m == 0) return sign;                                  // +-0
+    // m * 2^-9 = 1.f * 2^k with k = msb(m) - 9
+    int k = 31 - __builtin_clz(m);
+    uint32_t mant = (m << (10 - k)) & 0x3FF;
+    return (uint16_t)(sign | ((uint32_t)(k - 9 + 15) << 10) | mant);
+  }
+  return (uint16_t)(sign | ((e - 7 + 15) << 10) | (m << 7));
+}
+
+// Table entry payload of symbol s (see the layout above).
+inline void entry_payload(uint32_t payload, uint32_t code_bits, uint32_t k, int32_t value_offset,
+                          uint32_t s, uint32_t* a8, uint32_t* h16) {
+  switch (payload) {
+    case 1: {
+      const int half = 1 << (code_bits - 1);
+      const uint32_t mask = (1u << code_bits) - 1;
+      if (k == 4) {
+        *a8 = s & 0xFF;
+        *h16 = 0;
+      } else {
+        const int q0 = (int)(s & mask) - half;
+        const int ql = (int)((s >> (code_bits * (k - 1))) & mask) - half;
+        *a8 = (uint32_t)(q0 & 0xFF);
+        *h16 = fp16_of_int(ql);
+      }
+      return;
+    }
+    case 3:
+      *a8 = s & 0xFF;
+      *h16 = fp16_of_e4m3((uint8_t)s);
+      return;
+    default:
+      *a8 = (uint32_t)((int32_t)s + value_offset) & 0xFF;
+      *h16 = 0;
+      return;
+  }
+}
 
 }  // namespace ecw

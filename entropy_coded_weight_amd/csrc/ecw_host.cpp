@@ -527,10 +527,11 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     uint32_t slot = 0;
     for (uint32_t s = 0; s < 256; ++s) {
       const uint32_t f = t->freq[k][s];
-      const uint32_t aux = (uint32_t)((int32_t)s + t->value_offset[k]) & 0xFF;
+      uint32_t a8, h16;
+      entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], s, &a8, &h16);
       for (uint32_t i = 0; i < f; ++i, ++slot) {
-        lut[2 * slot] = f | (aux << 24);
-        lut[2 * slot + 1] = i;   // slot - cum[s]
+        lut[2 * slot] = f | (a8 << 24);
+        lut[2 * slot + 1] = i | (h16 << 16);   // bias = slot - cum[s]
       }
     }
   }
@@ -556,10 +557,13 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
 // ------------------------------------------------------------------ dec_prepare
 namespace ecw {
 
+// Default launch shape: one wave per tile, up to 16 waves (consecutive slices of
+// one row group) per block.  Measured on MI355X this was the fastest shape for every
+// Llama-8B-shaped tensor; per-tensor tuning may change it.
 void default_launch(ecw_tensor* t) {
   const uint32_t n_sl = t->n_slices;
   t->tiles_per_wave = 1;
-  t->waves_per_block = std::max(1u, std::min(8u, n_sl));
+  t->waves_per_block = std::max(1u, std::min(16u, n_sl));
 }
 
 uint32_t slice_groups(const ecw_tensor* t) {
@@ -571,8 +575,7 @@ uint64_t workspace_bytes(const ecw_tensor* t, int batch) {
   const uint32_t nsg = slice_groups(t);
   if (nsg <= 1) return 0;
   const uint64_t B = batch > 1 ? 4 : 1;   // kernels are built for batch capacity 1 or 4
-  const uint64_t part = (uint64_t)t->n_row_groups * nsg * B * 64 * 4;
-  return align_up(part, 256) + align_up((uint64_t)t->n_row_groups * 4, 256);
+  return align_up((uint64_t)t->n_row_groups * nsg * B * 64 * 4, 256);
 }
 
 }  // namespace ecw
@@ -649,9 +652,10 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     if (sum == M) {
       uint32_t slot = 0;
       for (uint32_t s = 0; s < 256; ++s) {
-        const uint32_t aux = (uint32_t)((int32_t)s + rec.value_offset) & 0xFF;
+        uint32_t a8, h16;
+        entry_payload(c.payload, c.code_bits, c.weights_per_symbol, rec.value_offset, s, &a8, &h16);
         for (uint32_t i = 0; i < rec.freq[s]; ++i, ++slot)
-          if (lut[2 * slot] != (rec.freq[s] | (aux << 24)) || lut[2 * slot + 1] != i)
+          if (lut[2 * slot] != (rec.freq[s] | (a8 << 24)) || lut[2 * slot + 1] != (i | (h16 << 16)))
             return fail(ECW_E_CORRUPT, "decode table does not match the frequencies");
       }
     }

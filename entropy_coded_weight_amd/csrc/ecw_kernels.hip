@@ -21,9 +21,8 @@
 //
 // Cross-wave reduction: the waves of a block cover consecutive column slices of
 // the same 64 rows and are summed in LDS in wave order; when a row group spans
-// several blocks each writes a partial and the last block to arrive (agent-scope
-// counter) sums the partials in block order.  Both orders are fixed, so results do
-// not depend on scheduling.
+// several blocks each block writes a partial and a second small kernel sums them in
+// block order.  Both orders are fixed, so results do not depend on scheduling.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -48,7 +47,6 @@ struct KArgs {
   const void* x;
   float* y;
   float* partials;
-  uint32_t* counters;
   uint16_t* sym_out;
   void* w_out;
   uint32_t* status_out;
@@ -76,6 +74,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t d;
   asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// acc + f16(h >> 16) * x in fp32 (v_fma_mix_f32: operand 0 is the fp16 in the high
+// half of h, operands 1 and 2 are fp32).  Exact widening of the fp16 weight.
+__device__ __forceinline__ float fma_mix_hi(uint32_t h, float x, float acc) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=v"(d) : "v"(h), "v"(x), "v"(acc));
   return d;
 }
 
@@ -152,28 +159,26 @@ __device__ __forceinline__ void wave_run(const KArgs& a, const uint2* lut, const
         // ---- A4: symbol decode (one LDS read gives f, bias and the payload byte)
         const uint32_t slot = x & mmask;
         const uint2 e = lut[slot];
-        x = mad_u24(x >> m, e.x, e.y);
+        x = mad_u24(x >> m, e.x, e.y & 0xFFFFu);
         const uint32_t step = j + u;
         // ---- A6/A7: payload -> weight (registers only) -> fp32 MAC
         if constexpr (!MAT) {
           const float* xp = reinterpret_cast<const float*>(xq) + (u & 3) * KW * B;
           if constexpr (PAY == 1) {
-            if constexpr (CB == 4 && KW == 1) {
-              const float w = (float)(e.x >> 24);          // digit q + 8
+            if constexpr (KW == 1) {
 #pragma unroll
-              for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
-            } else if constexpr (CB == 4 && KW == 2) {
-              const float w01 = (float)(e.x >> 24);        // d0 + 16 d1
-              const float w1 = (float)(e.x >> 28);         // d1
+              for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);   // q0
+            } else if constexpr (KW == 2) {
+              const float w0 = (float)(int8_t)(e.x >> 24);                           // q0
 #pragma unroll
               for (int b = 0; b < B; ++b) {
-                acc[b] = fmaf(w01, xp[b], acc[b]);
-                acc[b] = fmaf(w1, xp[B + b], acc[b]);
+                acc[b] = fmaf(w0, xp[b], acc[b]);
+                acc[b] = fma_mix_hi(e.y, xp[B + b], acc[b]);                        // q1
               }
             } else {
 #pragma unroll
               for (int i = 0; i < KW; ++i) {
-                const float w = (float)((e.x >> (24 + CB * i)) & ((1u << CB) - 1));
+                const float w = (float)((int)((e.x >> (24 + CB * i)) & ((1u << CB) - 1)) - (1 << (CB - 1)));
 #pragma unroll
                 for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[i * B + b], acc[b]);
               }
@@ -188,22 +193,34 @@ __device__ __forceinline__ void wave_run(const KArgs& a, const uint2* lut, const
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
           } else {
-            const float w = __builtin_amdgcn_cvt_f32_fp8((int)e.x, 3);   // OCP E4M3 byte
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
+            for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);    // e4m3 value
           }
         } else {
           if (!RAGGED || active) {
             const uint32_t aux = e.x >> 24;
+            uint32_t symbol = aux;
+            int q[KW > 0 ? KW : 1];
+            if constexpr (PAY == 1) {
+              constexpr int half = 1 << (CB - 1);
+              if constexpr (KW == 4) {
+#pragma unroll
+                for (int i = 0; i < KW; ++i) q[i] = (int)((aux >> (CB * i)) & ((1u << CB) - 1)) - half;
+              } else {
+                q[0] = (int)(int8_t)aux;
+                if constexpr (KW == 2) q[1] = (int)(float)__builtin_bit_cast(_Float16, (uint16_t)(e.y >> 16));
+                symbol = 0;
+#pragma unroll
+                for (int i = 0; i < KW; ++i) symbol |= (uint32_t)(q[i] + half) << (CB * i);
+              }
+            }
             const uint64_t sidx = (uint64_t)row * a.syms_per_row + (uint64_t)sl * a.s_full + step;
-            if (a.sym_out) a.sym_out[sidx] = (uint16_t)aux;
+            if (a.sym_out) a.sym_out[sidx] = (uint16_t)symbol;
             if (a.w_out) {
               const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols + (uint64_t)step * KW;
               if constexpr (PAY == 1) {
 #pragma unroll
-                for (int i = 0; i < KW; ++i)
-                  static_cast<int8_t*>(a.w_out)[wi + i] =
-                      (int8_t)((int)((aux >> (CB * i)) & ((1u << CB) - 1)) - (1 << (CB - 1)));
+                for (int i = 0; i < KW; ++i) static_cast<int8_t*>(a.w_out)[wi + i] = (int8_t)q[i];
               } else if constexpr (PAY == 2) {
                 const uint32_t dw = (u < 4) ? rcur.x : (u < 8) ? rcur.y : (u < 12) ? rcur.z : rcur.w;
                 const uint32_t r = (dw >> (8 * (u & 3))) & 0xFFu;
@@ -274,7 +291,6 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   float* xs = reinterpret_cast<float*>(smem + lut_bytes);
   const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * 4 + 15) & ~15u);
   uint16_t* rings = reinterpret_cast<uint16_t*>(smem + lut_bytes + xs_bytes);
-  uint32_t* ctl = reinterpret_cast<uint32_t*>(smem + lut_bytes + xs_bytes + W * kRingStride * 2);
 
   // ---- A2: stage the decode table; A3: stage the activation slice
   {
@@ -284,29 +300,12 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   }
   if constexpr (!MAT) {
     const uint32_t nc = a.xs_cols;
-    if constexpr (PAY == 1 && CB == 4 && KW == 2) {
-      // pairs (x0, x1 - 16 x0): acc += (d0 + 16 d1) x0 + d1 (x1 - 16 x0) = d0 x0 + d1 x1
-      for (uint32_t p = tid; p < nc / 2; p += blockDim.x) {
-        const uint32_t c = c_lo + 2 * p;
+    for (uint32_t i = tid; i < nc; i += blockDim.x) {
+      const uint32_t c = c_lo + i;
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          float x0 = 0.f, x1 = 0.f;
-          if (c < c_hi && (uint32_t)b < a.nb) {
-            x0 = load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c);
-            x1 = load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c + 1);
-          }
-          xs[(2 * p) * B + b] = x0;
-          xs[(2 * p + 1) * B + b] = x1 - 16.f * x0;
-        }
-      }
-    } else {
-      for (uint32_t i = tid; i < nc; i += blockDim.x) {
-        const uint32_t c = c_lo + i;
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-          xs[i * B + b] = (c < c_hi && (uint32_t)b < a.nb)
-                              ? load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c) : 0.f;
-      }
+      for (int b = 0; b < B; ++b)
+        xs[i * B + b] = (c < c_hi && (uint32_t)b < a.nb)
+                            ? load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c) : 0.f;
     }
   }
   __syncthreads();
@@ -331,22 +330,7 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   }
   if constexpr (MAT) return;
 
-  // ---- A8: epilogue.  Integer digits were accumulated unsigned: subtract
-  // 2^(b-1) * sum(x) over the wave's columns (same for every row).
-  if constexpr (PAY == 1) {
-    if (have_work) {
-      const uint32_t cw0 = (w_sl0 - sl_blk) * a.tile_cols;
-      const uint32_t cw1 = min((w_sl1 - sl_blk) * a.tile_cols, c_hi - c_lo);
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        float s = 0.f;
-        if ((uint32_t)b < a.nb)
-          for (uint32_t c = cw0 + lane; c < cw1; c += 64)
-            s += load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c_lo + c);
-        acc[b] -= (float)(1 << (CB - 1)) * wave_sum(s);
-      }
-    }
-  }
+  // ---- A8: epilogue
   // reuse this wave's ring as its reduction slot (only this wave touched it)
   float* red = reinterpret_cast<float*>(ring);
 #pragma unroll
@@ -365,29 +349,25 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
       a.partials[(((uint64_t)rg * a.n_sg + sg) * B + b) * 64 + l] = s;
     }
   }
-  if (a.n_sg == 1) return;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[rg], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    ctl[0] = (prev == a.n_sg - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (ctl[0] == 0) return;
-  __threadfence();
-  for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
-    const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
+}
+
+// Fixed-order sum of the per-block partials of each row (row groups that span
+// several blocks), times the row scale.  A separate launch: the kernel boundary
+// makes the partials visible without device-wide cache flushes.
+template <int B>
+__global__ void __launch_bounds__(256) k_reduce(const float* partials, const uint16_t* scales, float* y,
+                                                uint32_t rows, uint32_t n_sg, uint32_t nb, uint32_t unit_scale) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;   // = rg * 64 + lane
+  const uint32_t r = i, rg = i >> 6, l = i & 63;
+  if (r >= rows) return;
+  const float sc = unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, scales[r]);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    if ((uint32_t)b >= nb) break;
     float s = 0.f;
-    for (uint32_t g = 0; g < a.n_sg; ++g)
-      s += __hip_atomic_load(&a.partials[(((uint64_t)rg * a.n_sg + g) * B + b) * 64 + l],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (r < a.rows && b < a.nb) {
-      const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
-      a.y[(uint64_t)b * a.rows + r] = s * sc;
-    }
+    for (uint32_t g = 0; g < n_sg; ++g) s += partials[(((uint64_t)rg * n_sg + g) * B + b) * 64 + l];
+    y[(uint64_t)b * rows + r] = s * sc;
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void k_fill_zero(float* y, uint64_t n) {
@@ -440,6 +420,18 @@ static ecw_status launch(ecw_stream stream, const ecw_tensor* t, KArgs& a, int B
   hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  if (!mat && a.n_sg > 1) {
+    const uint32_t unit = t->coding.payload == ECW_P_BF16_EXP;
+    const dim3 rgrid((a.rows + 255) / 256);
+    if (B == 1)
+      hipLaunchKernelGGL(k_reduce<1>, rgrid, dim3(256), 0, (hipStream_t)stream, a.partials, a.scales, a.y,
+                         a.rows, a.n_sg, a.nb, unit);
+    else
+      hipLaunchKernelGGL(k_reduce<4>, rgrid, dim3(256), 0, (hipStream_t)stream, a.partials, a.scales, a.y,
+                         a.rows, a.n_sg, a.nb, unit);
+    err = hipGetLastError();
+    if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  }
   return ECW_OK;
 }
 
@@ -516,9 +508,7 @@ extern "C" ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const voi
   a.n_blocks = a.n_rg * a.n_sg;
   a.xs_cols = t->waves_per_block * t->tiles_per_wave * t->coding.tile_cols;
   if (need) {
-    const uint64_t part = (uint64_t)a.n_rg * a.n_sg * (uint64_t)B * 64 * 4;
     a.partials = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
   }
   return launch(stream, t, a, B, false, t->waves_per_block);
 }

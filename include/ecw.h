@@ -129,9 +129,9 @@ ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, const void* dev
                        ecw_tensor* out);
 
 /* Bytes of device workspace dec_gemv needs for this tensor, launch shape and batch
- * (0 when each row group fits one block).  The workspace holds per-block partial
- * sums and one arrival counter per row group; it must be zero-filled once before
- * its first use, and every completed dec_gemv leaves the counters at zero again. */
+ * (0 when each row group fits one block).  The workspace holds the per-block
+ * partial sums of row groups that span several blocks; dec_gemv then enqueues a
+ * second small kernel that adds them in block order.  No initialisation needed. */
 ecw_status dec_gemv_workspace_size(const ecw_tensor* t, int batch, size_t* bytes);
 
 /* Fused decode + matrix-vector product: y[b][r] = sum_c W[r][c] * x[b][c].

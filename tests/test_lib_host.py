@@ -84,8 +84,25 @@ def test_decode_table_entries_follow_the_frequencies():
     cum = np.concatenate([[0], np.cumsum(freq[0])[:-1]])
     sym = np.repeat(np.arange(256), freq[0])
     assert np.array_equal(lut[:, 0] & 0xFFFFFF, freq[0][sym])
-    assert np.array_equal(lut[:, 0] >> 24, sym & 0xFF)
-    assert np.array_equal(lut[:, 1], np.arange(lut.shape[0]) - cum[sym])
+    assert np.array_equal(lut[:, 1] & 0xFFFF, np.arange(lut.shape[0]) - cum[sym])
+    # Pair mode payload: a8 = first code (int8), h16 = fp16 of the second code
+    q0 = (sym & 15) - 8
+    q1 = (sym >> 4) - 8
+    assert np.array_equal((lut[:, 0] >> 24).astype(np.uint8).view(np.int8), q0)
+    h = (lut[:, 1] >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    assert np.array_equal(h, q1)
+
+
+def test_fp8_entry_payload_is_the_code_value():
+    case = [c for c in cases.small_cases() if c.name == "fp8_m12"][0]
+    bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    _, _, freq = blobfmt.tables(bl)
+    lut = blobfmt.lut(bl)[0]
+    sym = np.repeat(np.arange(256), freq[0])
+    h = (lut[:, 1] >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    from oracle import symbols
+    assert np.array_equal(h, symbols.e4m3_value(sym))
+    assert np.array_equal(lut[:, 0] >> 24, sym)
 
 
 def test_prepare_ledger_and_defaults():
