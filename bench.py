@@ -5,7 +5,8 @@ block (q, k, v, o 4096x4096 / 1024x4096, gate/up 14336x4096, down 4096x14336), e
 stored as 16-level Laplacian codes (2.2 bits of entropy) packed two per rANS symbol,
 decoded and multiplied into y = W x at batch 1.  Launch order follows the block's
 data flow: q, k, v, o, gate, up, down.  Blobs are rotated over >= 512 MiB of copies
-(twice the 256 MiB Infinity Cache), so every step reads its weights from HBM.
+(twice the 256 MiB Infinity Cache), so every step reads its weights from HBM.  Each
+step is captured once per rotated copy as a HIP graph; the timed region replays them.
 
 Prints one JSON line (stdout).  Per-tensor details go to stderr.
 """
@@ -134,37 +135,59 @@ def main():
         xs[name] = torch.from_numpy(t.x).to(dev)
         ys[name] = torch.empty((args.batch, t.codes.shape[0]), dtype=torch.float32, device=dev)
         ws[name] = [c[name].workspace(args.batch) for c in cts]
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
+    def step(i):
         c = cts[i % copies]
-        for j, name in enumerate(ORDER):
-            if ev is not None:
-                ev[j].record(stream)
+        for name in ORDER:
             ecw.gemv_raw(c[name].t, xs[name], ys[name], ws[name][i % copies])
-        if ev is not None:
-            ev[len(ORDER)].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ORDER) + 1)] for _ in range(args.steps)]
+    # One HIP graph per rotated copy: each replay is one full step (all launches of
+    # the layer set, in order), so the timed loop measures device time, not the
+    # Python launch loop.
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(c)
+        graphs.append(g)
+    for c in range(copies):
+        graphs[c].replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        graphs[i % copies].replay()
     t_end.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
+
+    # Per-launch device time of each tensor: a graph of its launches over all rotated
+    # copies, timed with events on the launch stream around replays.
     per = {n: [] for n in ORDER}
-    for e in evs:
-        for j, n in enumerate(ORDER):
-            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)      # us
+    for name in ORDER:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(copies):
+                ecw.gemv_raw(cts[c][name].t, xs[name], ys[name], ws[name][c])
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // (4 * copies))
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per[name].append(e0.elapsed_time(e1) * 1e3 / (reps * copies))     # us per launch
     avg_us = {n: float(np.mean(per[n])) for n in ORDER}
 
     # parity on the timed blobs: sampled rows of every tensor against float64

@@ -557,9 +557,9 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
 // ------------------------------------------------------------------ dec_prepare
 namespace ecw {
 
-// Default launch shape: one wave per tile, up to 16 waves (consecutive slices of
-// one row group) per block.  Measured on MI355X this was the fastest shape for every
-// Llama-8B-shaped tensor; per-tensor tuning may change it.
+// Default launch shape: one tile per wave, up to 16 waves (consecutive slices of
+// one row group) per block: the fastest shape measured on MI355X for every
+// Llama-8B-shaped tensor.  Per-tensor tuning may change it.
 void default_launch(ecw_tensor* t) {
   const uint32_t n_sl = t->n_slices;
   t->tiles_per_wave = 1;

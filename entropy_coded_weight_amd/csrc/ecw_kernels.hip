@@ -26,7 +26,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
+#include <unordered_set>
 
 #include "ecw_internal.h"
 
@@ -86,119 +88,215 @@ __device__ __forceinline__ float fma_mix_hi(uint32_t h, float x, float acc) {
   return d;
 }
 
+// Per lane: mask bit set ? t : f (v_cndmask on a wave-uniform lane mask).  Inline
+// asm so the compiler cannot turn it back into an exec-masked branch.
+__device__ __forceinline__ uint32_t select_lanes(uint64_t mask, uint32_t t, uint32_t f) {
+  uint32_t d;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(f), "v"(t), "s"(mask));
+  return d;
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Per-wave state of one run of consecutive tiles (same 64 rows).
-struct WaveRun {
-  uint32_t gb, nch, have, nc, rpos;
-  uint4 pre;
-  const uint4* src;
-};
+// ---- the per-stream pieces of one decode step (scalar state, kept in registers)
 
-// Decode the tiles [t0, t1) of row group rg with one wave; accumulate (or emit).
-// RAGGED: some lanes of the row group are past the last row and must neither
-// decode nor read words (only the last row group of a matrix whose row count is
-// not a multiple of 64).
-template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED>
-__device__ __forceinline__ void wave_run(const KArgs& a, const uint2* lut, const float* xs,
-                                         uint16_t* ring, uint32_t rg, uint32_t t0, uint32_t t1,
-                                         uint32_t c_lo, uint32_t lane, bool active, float* acc) {
-  constexpr int U = 16;                     // steps per unrolled group (S % 16 == 0)
-  const uint32_t m = a.log2m;
-  const uint32_t mmask = (1u << m) - 1u;
-  const uint32_t row = rg * 64 + lane;
-  const uint4 zero4 = {0u, 0u, 0u, 0u};
+// A4: one symbol decode.  Returns the table entry (f | a8 << 24, bias | h16 << 16).
+__device__ __forceinline__ uint2 decode_step(uint32_t& x, const uint2* lut, uint32_t m, uint32_t mmask) {
+  const uint2 e = lut[x & mmask];
+  x = mad_u24(x >> m, e.x, e.y & 0xFFFFu);
+  return e;
+}
 
-  const uint32_t wb = a.offsets[t0], we = a.offsets[t1];
-  const uint32_t gb = wb & ~(kChunk - 1);
-  const uint32_t nch = (we - gb + kChunk - 1) / kChunk;
-  const uint4* src = reinterpret_cast<const uint4*>(a.words + gb) + lane;
-  {
-    uint4 c0 = nch > 0 ? src[0] : zero4;
-    uint4 c1 = nch > 1 ? src[64] : zero4;
-    reinterpret_cast<uint4*>(ring)[lane] = c0;
-    if (lane < 8) reinterpret_cast<uint4*>(ring + kRing)[lane] = c0;
-    reinterpret_cast<uint4*>(ring + kChunk)[lane] = c1;
+// A5: renormalise the wave's 64 states against the stream's LDS ring; refill the
+// ring one chunk ahead of the read position (the chunk was loaded into `pre`
+// one chunk-consumption earlier).
+template <bool RAGGED>
+__device__ __forceinline__ void renorm_step(uint32_t& x, uint32_t& rpos, uint32_t& have, uint32_t& nc,
+                                            uint4& pre, uint16_t* ring, const uint4* src, uint32_t nch,
+                                            uint32_t lane, bool active) {
+  if (rpos + 64 > have) {            // wave-uniform
+    const uint32_t slot_c = nc & 1u;
+    reinterpret_cast<uint4*>(ring + slot_c * kChunk)[lane] = pre;
+    if (slot_c == 0 && lane < 8) reinterpret_cast<uint4*>(ring + kRing)[lane] = pre;
+    have += kChunk;
+    ++nc;
+    if (nc < nch) pre = src[(uint64_t)nc * 64];
   }
-  uint4 pre = nch > 2 ? src[128] : zero4;
-  uint32_t have = 2 * kChunk, nc = 2, rpos = wb - gb;
-  uint32_t st_next = a.states[(uint64_t)t0 * 64 + lane];
+  // Branch-free: every lane reads the word at its prefix offset (always inside the
+  // ring plus its mirror) and keeps it only if it needs one, so no exec-mask
+  // change or LDS wait splits the step.
+  const uint16_t* rp = ring + (rpos & (kRing - 1));
+  uint64_t msk;
+  if constexpr (RAGGED)
+    msk = __ballot(active && (x < kStateL));
+  else
+    msk = __builtin_amdgcn_ballot_w64(x < kStateL);
+  const uint32_t w = rp[lanes_below(msk)];
+  x = select_lanes(msk, (x << 16) | w, x);
+  rpos += (uint32_t)__popcll(msk);
+}
 
-  for (uint32_t t = t0; t < t1; ++t) {
-    uint32_t x = st_next;
-    if (t + 1 < t1) st_next = a.states[(uint64_t)(t + 1) * 64 + lane];
-    const uint32_t sl = t - rg * a.n_sl;
-    const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
-    const uint32_t col0 = sl * a.tile_cols - c_lo;     // local staged column of the tile
-    const uint8_t* rawp = nullptr;
-    uint4 rcur = zero4, rnext = zero4;
-    if constexpr (PAY == 2) {
-      rawp = a.raw + (uint64_t)rg * a.raw_rg_bytes + (uint64_t)sl * a.raw_full_bytes + lane * 16;
-      rnext = *reinterpret_cast<const uint4*>(rawp);
-    }
-    for (uint32_t j = 0; j < S; j += U) {
-      if constexpr (PAY == 2) {
-        rcur = rnext;
-        if (j + U < S) rnext = *reinterpret_cast<const uint4*>(rawp + (uint64_t)(j / U + 1) * 1024);
+// A6 + A7: rebuild the weight(s) of one symbol in registers and accumulate.
+// xp: this symbol's activations, [KW][B] floats.  r: BF16 raw byte.
+template <int PAY, int CB, int KW, int B>
+__device__ __forceinline__ void mac(const uint2 e, const float* xp, uint32_t r, float* acc) {
+  if constexpr (PAY == 1) {
+    if constexpr (KW == 1) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);        // q0
+    } else if constexpr (KW == 2) {
+      const float w0 = (float)(int8_t)(e.x >> 24);                                // q0
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        acc[b] = fmaf(w0, xp[b], acc[b]);
+        acc[b] = fma_mix_hi(e.y, xp[B + b], acc[b]);                             // q1
       }
-      // activations of this 16-step group: KW * U columns x B floats, read as 16-byte
-      // broadcasts (every lane reads the same address) once per 4 steps
-      const float4* xg = reinterpret_cast<const float4*>(xs + (uint64_t)(col0 + KW * j) * B);
-      float4 xq[KW * B];
+    } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int i = 0; i < KW; ++i) {
+        const float w = (float)((int)((e.x >> (24 + CB * i)) & ((1u << CB) - 1)) - (1 << (CB - 1)));
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[i * B + b], acc[b]);
+      }
+    }
+  } else if constexpr (PAY == 2) {
+    // bf16 bits = sign << 15 | exponent << 7 | mantissa, as fp32 bits << 16
+    const uint32_t bits = ((r << 24) & 0x80000000u) | ((e.x >> 1) & 0x7F800000u) | ((r << 16) & 0x007F0000u);
+    const float w = __uint_as_float(bits);
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
+  } else {
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);          // e4m3 value
+  }
+}
+
+__device__ __forceinline__ uint32_t raw_byte(const uint4& g, int u) {
+  const uint32_t dw = (u < 4) ? g.x : (u < 8) ? g.y : (u < 12) ? g.z : g.w;
+  return (dw >> (8 * (u & 3))) & 0xFFu;
+}
+
+__device__ __forceinline__ const uint8_t* raw_tile(const KArgs& a, uint32_t rg, uint32_t sl, uint32_t lane) {
+  return a.raw + (uint64_t)rg * a.raw_rg_bytes + (uint64_t)sl * a.raw_full_bytes + lane * 16;
+}
+
+// Word range of a run of tiles [t0, t1): chunk-aligned start, chunk count, first
+// read position.
+__device__ __forceinline__ void run_words(const KArgs& a, uint32_t t0, uint32_t t1, uint32_t& gb,
+                                          uint32_t& nch, uint32_t& rpos) {
+  if (t0 >= t1) {
+    gb = 0; nch = 0; rpos = 0;
+    return;
+  }
+  const uint32_t wb = a.offsets[t0], we = a.offsets[t1];
+  gb = wb & ~(kChunk - 1);
+  nch = (we - gb + kChunk - 1) / kChunk;
+  rpos = wb - gb;
+}
+
+// The wave body.  NS = 1: the wave's tiles [t0, t1) are one stream.  NS = 2: the
+// first half (stream A) and the second half (stream B) are decoded in lockstep, two
+// independent dependency chains per wave.  MAT: decode-only test hook (NS = 1).
+// The first two chunks of each stream (c0*, c1*) were loaded by the caller before
+// the block's staging barrier and are committed to the rings here.
+template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED, int NS>
+__device__ __forceinline__ void wave_body(const KArgs& a, const uint2* lut, const float* xs, uint16_t* ring,
+                                          uint32_t rg, uint32_t tA0, uint32_t tA1, uint32_t tB0,
+                                          uint32_t tB1, uint32_t c_lo, uint32_t lane, bool active,
+                                          float* acc) {
+  constexpr int U = 16;
+  const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
+  const uint32_t row = rg * 64 + lane;
+  const uint32_t sl0 = rg * a.n_sl;
+  const uint4 zero4 = {0u, 0u, 0u, 0u};
+  uint16_t* ringA = ring;
+  uint16_t* ringB = ring + kRingStride;
+
+  uint32_t gbA, nchA, rposA, gbB = 0, nchB = 0, rposB = 0;
+  run_words(a, tA0, tA1, gbA, nchA, rposA);
+  if constexpr (NS == 2) run_words(a, tB0, tB1, gbB, nchB, rposB);
+  const uint4* srcA = reinterpret_cast<const uint4*>(a.words + gbA) + lane;
+  const uint4* srcB = reinterpret_cast<const uint4*>(a.words + gbB) + lane;
+  // first chunks (issued together; they travel while the previous stream's
+  // staging finishes) and the one-ahead prefetch
+  {
+    const uint4 c0 = nchA > 0 ? srcA[0] : zero4;
+    const uint4 c1 = nchA > 1 ? srcA[64] : zero4;
+    uint4 d0 = zero4, d1 = zero4;
+    if constexpr (NS == 2) {
+      d0 = nchB > 0 ? srcB[0] : zero4;
+      d1 = nchB > 1 ? srcB[64] : zero4;
+    }
+    reinterpret_cast<uint4*>(ringA)[lane] = c0;
+    if (lane < 8) reinterpret_cast<uint4*>(ringA + kRing)[lane] = c0;
+    reinterpret_cast<uint4*>(ringA + kChunk)[lane] = c1;
+    if constexpr (NS == 2) {
+      reinterpret_cast<uint4*>(ringB)[lane] = d0;
+      if (lane < 8) reinterpret_cast<uint4*>(ringB + kRing)[lane] = d0;
+      reinterpret_cast<uint4*>(ringB + kChunk)[lane] = d1;
+    }
+  }
+  uint4 preA = nchA > 2 ? srcA[128] : zero4;
+  uint4 preB = zero4;
+  if constexpr (NS == 2) preB = nchB > 2 ? srcB[128] : zero4;
+  uint32_t haveA = 2 * kChunk, ncA = 2, haveB = 2 * kChunk, ncB = 2;
+  uint32_t stA = tA0 < tA1 ? a.states[(uint64_t)tA0 * 64 + lane] : kStateL;
+  uint32_t stB = kStateL;
+  if constexpr (NS == 2) stB = tB0 < tB1 ? a.states[(uint64_t)tB0 * 64 + lane] : kStateL;
+
+  uint32_t tA = tA0, tB = tB0;
+  while (tA < tA1) {
+    const bool pairB = (NS == 2) && (tB < tB1);           // wave-uniform
+    uint32_t xA = stA, xB = stB;
+    if (tA + 1 < tA1) stA = a.states[(uint64_t)(tA + 1) * 64 + lane];
+    if constexpr (NS == 2) {
+      if (pairB && tB + 1 < tB1) stB = a.states[(uint64_t)(tB + 1) * 64 + lane];
+    }
+    const uint32_t slA = tA - sl0, slB = tB - sl0;
+    const uint32_t SA = (slA + 1 == a.n_sl) ? a.s_last : a.s_full;
+    const uint32_t SB = pairB ? ((slB + 1 == a.n_sl) ? a.s_last : a.s_full) : 0;   // SB <= SA
+    const uint32_t colA = slA * a.tile_cols - c_lo, colB = slB * a.tile_cols - c_lo;
+    const uint8_t* rawA = raw_tile(a, rg, slA, lane);
+    const uint8_t* rawB = raw_tile(a, rg, slB, lane);
+
+    for (uint32_t j = 0; j < SA; j += U) {
+      const bool dualB = j < SB;                            // wave-uniform
+      uint4 rgA = zero4, rgB = zero4;
+      if constexpr (PAY == 2) {
+        rgA = *reinterpret_cast<const uint4*>(rawA + (uint64_t)(j / U) * 1024);
+        if (NS == 2 && dualB) rgB = *reinterpret_cast<const uint4*>(rawB + (uint64_t)(j / U) * 1024);
+      }
+      const float4* xgA = reinterpret_cast<const float4*>(xs + (uint64_t)(colA + KW * j) * B);
+      const float4* xgB = reinterpret_cast<const float4*>(xs + (uint64_t)(colB + KW * j) * B);
+#pragma unroll
+      for (int qtr = 0; qtr < U / 4; ++qtr) {
+        float4 xqA[MAT ? 1 : KW * B], xqB[MAT ? 1 : KW * B];
         if constexpr (!MAT) {
-          if ((u & 3) == 0) {
 #pragma unroll
-            for (int i = 0; i < KW * B; ++i) xq[i] = xg[(u / 4) * KW * B + i];
+          for (int i = 0; i < KW * B; ++i) xqA[i] = xgA[qtr * KW * B + i];
+          if (NS == 2 && dualB) {
+#pragma unroll
+            for (int i = 0; i < KW * B; ++i) xqB[i] = xgB[qtr * KW * B + i];
           }
         }
-        // ---- A4: symbol decode (one LDS read gives f, bias and the payload byte)
-        const uint32_t slot = x & mmask;
-        const uint2 e = lut[slot];
-        x = mad_u24(x >> m, e.x, e.y & 0xFFFFu);
-        const uint32_t step = j + u;
-        // ---- A6/A7: payload -> weight (registers only) -> fp32 MAC
-        if constexpr (!MAT) {
-          const float* xp = reinterpret_cast<const float*>(xq) + (u & 3) * KW * B;
-          if constexpr (PAY == 1) {
-            if constexpr (KW == 1) {
 #pragma unroll
-              for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);   // q0
-            } else if constexpr (KW == 2) {
-              const float w0 = (float)(int8_t)(e.x >> 24);                           // q0
-#pragma unroll
-              for (int b = 0; b < B; ++b) {
-                acc[b] = fmaf(w0, xp[b], acc[b]);
-                acc[b] = fma_mix_hi(e.y, xp[B + b], acc[b]);                        // q1
-              }
-            } else {
-#pragma unroll
-              for (int i = 0; i < KW; ++i) {
-                const float w = (float)((int)((e.x >> (24 + CB * i)) & ((1u << CB) - 1)) - (1 << (CB - 1)));
-#pragma unroll
-                for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[i * B + b], acc[b]);
-              }
-            }
-          } else if constexpr (PAY == 2) {
-            // bf16 bits = sign << 15 | exponent << 7 | mantissa, as fp32 bits << 16
-            const uint32_t dw = (u < 4) ? rcur.x : (u < 8) ? rcur.y : (u < 12) ? rcur.z : rcur.w;
-            const uint32_t r = (dw >> (8 * (u & 3))) & 0xFFu;
-            const uint32_t bits = ((r << 24) & 0x80000000u) | ((e.x >> 1) & 0x7F800000u) |
-                                  ((r << 16) & 0x007F0000u);
-            const float w = __uint_as_float(bits);
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
-          } else {
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);    // e4m3 value
-          }
-        } else {
-          if (!RAGGED || active) {
-            const uint32_t aux = e.x >> 24;
+        for (int u4 = 0; u4 < 4; ++u4) {
+          const int u = qtr * 4 + u4;
+          const uint32_t step = j + u;
+          const uint2 eA = decode_step(xA, lut, m, mmask);
+          uint2 eB = {0u, 0u};
+          if (NS == 2 && dualB) eB = decode_step(xB, lut, m, mmask);
+          if constexpr (!MAT) {
+            mac<PAY, CB, KW, B>(eA, reinterpret_cast<const float*>(xqA) + u4 * KW * B,
+                                PAY == 2 ? raw_byte(rgA, u) : 0u, acc);
+            if (NS == 2 && dualB)
+              mac<PAY, CB, KW, B>(eB, reinterpret_cast<const float*>(xqB) + u4 * KW * B,
+                                  PAY == 2 ? raw_byte(rgB, u) : 0u, acc);
+          } else if (!RAGGED || active) {
+            const uint32_t aux = eA.x >> 24;
             uint32_t symbol = aux;
             int q[KW > 0 ? KW : 1];
             if constexpr (PAY == 1) {
@@ -208,63 +306,47 @@ __device__ __forceinline__ void wave_run(const KArgs& a, const uint2* lut, const
                 for (int i = 0; i < KW; ++i) q[i] = (int)((aux >> (CB * i)) & ((1u << CB) - 1)) - half;
               } else {
                 q[0] = (int)(int8_t)aux;
-                if constexpr (KW == 2) q[1] = (int)(float)__builtin_bit_cast(_Float16, (uint16_t)(e.y >> 16));
+                if constexpr (KW == 2) q[1] = (int)(float)__builtin_bit_cast(_Float16, (uint16_t)(eA.y >> 16));
                 symbol = 0;
 #pragma unroll
                 for (int i = 0; i < KW; ++i) symbol |= (uint32_t)(q[i] + half) << (CB * i);
               }
             }
-            const uint64_t sidx = (uint64_t)row * a.syms_per_row + (uint64_t)sl * a.s_full + step;
-            if (a.sym_out) a.sym_out[sidx] = (uint16_t)symbol;
+            if (a.sym_out) a.sym_out[(uint64_t)row * a.syms_per_row + (uint64_t)slA * a.s_full + step] = (uint16_t)symbol;
             if (a.w_out) {
-              const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols + (uint64_t)step * KW;
+              const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)slA * a.tile_cols + (uint64_t)step * KW;
               if constexpr (PAY == 1) {
 #pragma unroll
                 for (int i = 0; i < KW; ++i) static_cast<int8_t*>(a.w_out)[wi + i] = (int8_t)q[i];
               } else if constexpr (PAY == 2) {
-                const uint32_t dw = (u < 4) ? rcur.x : (u < 8) ? rcur.y : (u < 12) ? rcur.z : rcur.w;
-                const uint32_t r = (dw >> (8 * (u & 3))) & 0xFFu;
+                const uint32_t r = raw_byte(rgA, u);
                 static_cast<uint16_t*>(a.w_out)[wi] = (uint16_t)(((r & 0x80u) << 8) | (aux << 7) | (r & 0x7Fu));
               } else {
                 static_cast<uint8_t*>(a.w_out)[wi] = (uint8_t)aux;
               }
             }
           }
-        }
-        // ---- A5: renormalise; the stream words come from the LDS ring
-        if (rpos + 64 > have) {            // wave-uniform: next chunk into the ring
-          const uint32_t slot_c = nc & 1u;
-          reinterpret_cast<uint4*>(ring + slot_c * kChunk)[lane] = pre;
-          if (slot_c == 0 && lane < 8) reinterpret_cast<uint4*>(ring + kRing)[lane] = pre;
-          have += kChunk;
-          ++nc;
-          if (nc < nch) pre = src[(uint64_t)nc * 64];
-        }
-        const uint16_t* rp = ring + (rpos & (kRing - 1));
-        if constexpr (RAGGED) {
-          const bool need = active && (x < kStateL);
-          const uint64_t msk = __ballot(need);
-          if (need) x = (x << 16) | rp[lanes_below(msk)];
-          rpos += (uint32_t)__popcll(msk);
-        } else {
-          const bool need = x < kStateL;
-          const uint64_t msk = __builtin_amdgcn_ballot_w64(need);
-          if (need) x = (x << 16) | rp[lanes_below(msk)];
-          rpos += (uint32_t)__popcll(msk);
+          renorm_step<RAGGED>(xA, rposA, haveA, ncA, preA, ringA, srcA, nchA, lane, active);
+          if (NS == 2 && dualB) renorm_step<RAGGED>(xB, rposB, haveB, ncB, preB, ringB, srcB, nchB, lane, active);
         }
       }
     }
     if constexpr (MAT) {
-      const bool ok_lane = !active || x == kStateL;
+      const bool ok_lane = !active || xA == kStateL;
       const uint64_t bad = __ballot(!ok_lane);
       if (lane == 0 && a.status_out)
-        a.status_out[t] = (bad != 0 ? 1u : 0u) | ((rpos != a.offsets[t + 1] - gb) ? 2u : 0u);
+        a.status_out[tA] = (bad != 0 ? 1u : 0u) | ((rposA != a.offsets[tA + 1] - gbA) ? 2u : 0u);
     }
+    ++tA;
+    if (pairB) ++tB;
   }
 }
 
 // PAY: 1 INT codes, 2 BF16 exponent, 3 FP8.  CB/KW: code bits and codes per symbol
 // (INT).  B: batch capacity (1 or 4).  MAT: decode-only test hook.
+// Block = W waves on consecutive slices of one row group; wave w owns R tiles,
+// decoded as one stream or, when R >= 2 and the payload allows, two interleaved
+// streams (the host sizes the LDS rings the same way).
 template <int PAY, int CB, int KW, int B, bool MAT>
 __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -274,8 +356,8 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Hardware block b runs on XCD b % 8.  Give each XCD a contiguous range of logical
-  // blocks so the slice groups of a row group (which meet in the partial reduction)
-  // share one L2.  gridDim.x is a multiple of 8; surplus blocks exit at once.
+  // blocks (the slice groups of one row group are adjacent).  gridDim.x is a
+  // multiple of 8; surplus blocks exit at once.
   const uint32_t per = gridDim.x >> 3;
   const uint32_t lb = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lb >= a.n_blocks) return;
@@ -285,68 +367,98 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   const uint32_t sl_blk_end = min(sl_blk + W * R, a.n_sl);
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
+  constexpr bool kTwoCapable = !MAT && PAY != 2 && KW != 4;
+  const uint32_t NSr = (kTwoCapable && R >= 2) ? 2 : 1;
 
   const uint32_t lut_bytes = a.lut_entries * 8;
   uint2* lut = reinterpret_cast<uint2*>(smem);
   float* xs = reinterpret_cast<float*>(smem + lut_bytes);
   const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * 4 + 15) & ~15u);
   uint16_t* rings = reinterpret_cast<uint16_t*>(smem + lut_bytes + xs_bytes);
+  uint16_t* ring = rings + (wid * NSr) * kRingStride;
 
-  // ---- A2: stage the decode table; A3: stage the activation slice
+  // ---- A2: stage the decode table (two 16-byte loads in flight per thread)
   {
     const uint4* src = reinterpret_cast<const uint4*>(a.lut);
     uint4* dst = reinterpret_cast<uint4*>(lut);
-    for (uint32_t i = tid; i < a.lut_entries / 2; i += blockDim.x) dst[i] = src[i];
+    const uint32_t n = a.lut_entries / 2, bd = blockDim.x;
+    for (uint32_t i = tid; i < n; i += 2 * bd) {
+      const uint32_t i2 = i + bd;
+      const uint4 v0 = src[i];
+      const uint4 v1 = src[i2 < n ? i2 : i];
+      dst[i] = v0;
+      if (i2 < n) dst[i2] = v1;
+    }
   }
+  // ---- A3: stage the block's activation columns as fp32 [col][b], 8 columns
+  // (16 bytes) per load
   if constexpr (!MAT) {
-    const uint32_t nc = a.xs_cols;
-    for (uint32_t i = tid; i < nc; i += blockDim.x) {
-      const uint32_t c = c_lo + i;
+    const uint32_t nvec = a.xs_cols / 8;
+    for (uint32_t v = tid; v < nvec * B; v += blockDim.x) {
+      const uint32_t b = v / nvec, c8 = v - b * nvec, col = c_lo + 8 * c8;
+      uint4 raw = {0u, 0u, 0u, 0u};
+      if (col < c_hi && b < a.nb)
+        raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (uint64_t)b * a.cols + col);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int b = 0; b < B; ++b)
-        xs[i * B + b] = (c < c_hi && (uint32_t)b < a.nb)
-                            ? load_x(a.x, a.x_is_bf16, (uint64_t)b * a.cols + c) : 0.f;
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t h = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
+        xs[(8 * c8 + i) * B + b] = a.x_is_bf16 ? __uint_as_float((uint32_t)h << 16)
+                                               : (float)__builtin_bit_cast(_Float16, h);
+      }
     }
   }
   __syncthreads();
 
+  const uint32_t w_sl0 = min(sl_blk + wid * R, sl_blk_end);
+  const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
+  const uint32_t w_mid = NSr == 1 ? w_sl1 : w_sl0 + (w_sl1 - w_sl0 + 1) / 2;
+  const uint32_t tb = rg * a.n_sl;
   const uint32_t row = rg * 64 + lane;
   const bool active = row < a.rows;
   const bool ragged = (rg + 1) * 64 > a.rows;     // wave-uniform
-  const uint32_t w_sl0 = sl_blk + wid * R;
-  const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
-  const bool have_work = w_sl0 < w_sl1;
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.f;
-  uint16_t* ring = rings + wid * kRingStride;
-
-  if (have_work) {
-    const uint32_t t0 = rg * a.n_sl + w_sl0, t1 = rg * a.n_sl + w_sl1;
-    if (ragged)
-      wave_run<PAY, CB, KW, B, MAT, true>(a, lut, xs, ring, rg, t0, t1, c_lo, lane, active, acc);
-    else
-      wave_run<PAY, CB, KW, B, MAT, false>(a, lut, xs, ring, rg, t0, t1, c_lo, lane, active, acc);
-  }
-  if constexpr (MAT) return;
-
-  // ---- A8: epilogue
-  // reuse this wave's ring as its reduction slot (only this wave touched it)
-  float* red = reinterpret_cast<float*>(ring);
-#pragma unroll
-  for (int b = 0; b < B; ++b) red[b * 64 + lane] = have_work ? acc[b] : 0.f;
-  __syncthreads();
-  for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
-    const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
-    float s = 0.f;
-    for (uint32_t w = 0; w < W; ++w) s += reinterpret_cast<const float*>(rings + w * kRingStride)[b * 64 + l];
-    if (a.n_sg == 1) {
-      if (r < a.rows && b < a.nb) {
-        const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
-        a.y[(uint64_t)b * a.rows + r] = s * sc;
+  if (w_sl0 < w_sl1) {
+    if constexpr (kTwoCapable) {
+      if (NSr == 2) {
+        if (ragged)
+          wave_body<PAY, CB, KW, B, MAT, true, 2>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_mid, tb + w_mid,
+                                                  tb + w_sl1, c_lo, lane, active, acc);
+        else
+          wave_body<PAY, CB, KW, B, MAT, false, 2>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_mid, tb + w_mid,
+                                                   tb + w_sl1, c_lo, lane, active, acc);
       }
-    } else {
-      a.partials[(((uint64_t)rg * a.n_sg + sg) * B + b) * 64 + l] = s;
+    }
+    if (NSr == 1) {
+      if (ragged)
+        wave_body<PAY, CB, KW, B, MAT, true, 1>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, 0, 0, c_lo,
+                                                lane, active, acc);
+      else
+        wave_body<PAY, CB, KW, B, MAT, false, 1>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, 0, 0, c_lo,
+                                                 lane, active, acc);
+    }
+  }
+  if constexpr (!MAT) {
+    // ---- A8: epilogue.  Reuse this wave's first ring as its reduction slot.
+    float* red = reinterpret_cast<float*>(ring);
+#pragma unroll
+    for (int b = 0; b < B; ++b) red[b * 64 + lane] = acc[b];
+    __syncthreads();
+    for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
+      const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
+      float s = 0.f;
+      for (uint32_t w = 0; w < W; ++w)
+        s += reinterpret_cast<const float*>(rings + (w * NSr) * kRingStride)[b * 64 + l];
+      if (a.n_sg == 1) {
+        if (r < a.rows && b < a.nb) {
+          const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
+          a.y[(uint64_t)b * a.rows + r] = s * sc;
+        }
+      } else {
+        a.partials[(((uint64_t)rg * a.n_sg + sg) * B + b) * 64 + l] = s;
+      }
     }
   }
 }
@@ -398,10 +510,30 @@ static KernelFn pick_kernel(const ecw_coding& c) {
   return nullptr;
 }
 
-static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t xs_cols, int B, bool mat) {
+static uint32_t streams_per_wave(const ecw_coding& c, bool mat, uint32_t R) {
+  return (mat || c.payload == ECW_P_BF16_EXP || c.weights_per_symbol == 4 || R < 2) ? 1 : 2;
+}
+
+static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat) {
   const uint64_t lut = (uint64_t)t->n_tables << t->coding.log2_m;
   uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * 4 + 15) / 16 * 16;
-  return lut * 8 + xs + (uint64_t)W * kRingStride * 2 + 64;
+  return lut * 8 + xs + (uint64_t)W * streams_per_wave(t->coding, mat, R) * kRingStride * 2;
+}
+
+// Allow each kernel the whole 160 KiB LDS once (a host call, not a stream
+// operation, so launches stay capturable).
+static bool lds_attribute_set(KernelFn fn) {
+  static std::mutex mu;
+  static std::unordered_set<const void*> done;
+  std::lock_guard<std::mutex> lock(mu);
+  const void* key = reinterpret_cast<const void*>(fn);
+  if (done.count(key)) return true;
+  if (hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  done.insert(key);
+  return true;
 }
 
 static ecw_status launch(ecw_stream stream, const ecw_tensor* t, KArgs& a, int B, bool mat,
@@ -409,14 +541,10 @@ static ecw_status launch(ecw_stream stream, const ecw_tensor* t, KArgs& a, int B
   KernelFn fn = mat ? (B == 1 ? pick_kernel<1, true>(t->coding) : nullptr)
                     : (B == 1 ? pick_kernel<1, false>(t->coding) : pick_kernel<4, false>(t->coding));
   if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
-  const uint64_t lds = lds_bytes(t, W, a.xs_cols, B, mat);
+  const uint64_t lds = lds_bytes(t, W, a.tiles_per_wave, a.xs_cols, B, mat);
   if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "launch shape needs more than 160 KiB of LDS");
   const uint32_t grid = (a.n_blocks + 7) / 8 * 8;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
-  }
+  if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));

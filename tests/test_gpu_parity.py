@@ -135,3 +135,28 @@ def test_degenerate_shapes():
     y = torch.empty((1, 0), device="cuda")
     ecw.gemv_raw(ct.t, torch.zeros((1, 64), dtype=torch.float16, device="cuda"), y, None)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", [(16, 1), (4, 1)])
+def test_graph_capture_replays_match_eager(shape):
+    # the fused GEMV (and, when a row group spans blocks, its reduction kernel) is
+    # captured in a HIP graph and replayed several times with eager work between
+    W, R = shape
+    case = cases._int("graph", 192, 4096, 2, 4, 12, 128, seed=12)
+    ct = ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
+                              waves_per_block=W, tiles_per_wave=R)
+    xd, xv = _x(case, 1)
+    y_eager = ct.gemv(xd).clone()
+    y = torch.empty_like(y_eager)
+    ws = ct.workspace(1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ecw.gemv_raw(ct.t, xd, y, ws)
+    for i in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i} differs"
+        ct.gemv(xd * 2.0)                  # eager work between replays
+        torch.cuda.synchronize()
