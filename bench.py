@@ -26,9 +26,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs per fused decode-GEMV layer + effective weight GB/s (% HBM peak), batch 1"
 ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
+# launches of one decode step, in data-flow order; tensors of a launch share x
+LAUNCHES = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
 
 # per-tensor coding: (log2_m, tile_cols, waves_per_block, tiles_per_wave)
-DEFAULT_CODING = {n: (12, 128, 16, 1) for n in ORDER}
+DEFAULT_CODING = {"q": (12, 128, 16, 1), "k": (12, 128, 16, 1), "v": (12, 128, 16, 1),
+                  "o": (12, 128, 16, 1), "gate": (12, 256, 16, 1), "up": (12, 256, 16, 1),
+                  "down": (12, 256, 16, 1)}
 
 
 def log(*a):
@@ -115,30 +119,39 @@ def main():
     t_build = time.time()
     layer = build_layer(args.batch, DEFAULT_CODING)
     log(f"encoded layer set in {time.time() - t_build:.1f} s")
-    stored = {n: 0 for n in ORDER}
-    one = {}
+    global LAUNCHES
+    LAUNCHES = [(ln, [n for n in names if n in ORDER]) for ln, names in LAUNCHES]
+    LAUNCHES = [(ln, names) for ln, names in LAUNCHES if names]
+    stored = {}
     for name in ORDER:
-        L = layer[name]
-        ct = ecw.CompressedTensor(L["blob"])
-        ct.set_launch(*L["launch"])
-        stored[name] = ct.stored_bytes()
-        one[name] = ct
-    layer_bytes = sum(stored.values())
+        stored[name] = ecw.prepare(layer[name]["blob"]).blob_bytes
+    layer_bytes = 0
+    for name in ORDER:
+        t = ecw.prepare(layer[name]["blob"])
+        stored[name] = t.bytes_words + t.bytes_raw + t.bytes_tile_meta + t.bytes_tables + t.bytes_scales
+        layer_bytes += stored[name]
     copies = max(2, int(np.ceil(args.cold_bytes / layer_bytes)))
-    cts = [one] + [{n: ecw.CompressedTensor(layer[n]["blob"]) for n in ORDER} for _ in range(copies - 1)]
-    for c in cts[1:]:
+    cts = []
+    for _ in range(copies):
+        c = {n: ecw.CompressedTensor(layer[n]["blob"]) for n in ORDER}
         for n in ORDER:
             c[n].set_launch(*layer[n]["launch"])
-    xs, ys, ws = {}, {}, {}
-    for name in ORDER:
-        t = layer[name]["tensor"]
-        xs[name] = torch.from_numpy(t.x).to(dev)
-        ys[name] = torch.empty((args.batch, t.codes.shape[0]), dtype=torch.float32, device=dev)
-        ws[name] = [c[name].workspace(args.batch) for c in cts]
+        cts.append(c)
+    groups = [{ln: ecw.GemvGroup([c[n] for n in names]) for ln, names in LAUNCHES} for c in cts]
+    xs, ys = {}, {}
+    for ln, names in LAUNCHES:
+        xs[ln] = torch.from_numpy(layer[names[0]]["tensor"].x).to(dev)
+        for n in names:
+            ys[n] = torch.empty((args.batch, layer[n]["tensor"].codes.shape[0]), dtype=torch.float32, device=dev)
+    wss = [{ln: g[ln].workspace(args.batch) for ln, _ in LAUNCHES} for g in groups]
+
+    def launch(i, ln, names):
+        c = i % copies
+        ecw.gemv_group_raw([cts[c][n].t for n in names], xs[ln], [ys[n] for n in names], wss[c][ln])
+
     def step(i):
-        c = cts[i % copies]
-        for name in ORDER:
-            ecw.gemv_raw(c[name].t, xs[name], ys[name], ws[name][i % copies])
+        for ln, names in LAUNCHES:
+            launch(i, ln, names)
 
     for i in range(args.warmup):
         step(i)
@@ -169,14 +182,14 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
 
-    # Per-launch device time of each tensor: a graph of its launches over all rotated
-    # copies, timed with events on the launch stream around replays.
-    per = {n: [] for n in ORDER}
-    for name in ORDER:
+    # Per-launch device time: a graph of that launch over all rotated copies, timed
+    # with events on the launch stream around replays.
+    avg_us = {}
+    for ln, names in LAUNCHES:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for c in range(copies):
-                ecw.gemv_raw(cts[c][name].t, xs[name], ys[name], ws[name][c])
+                launch(c, ln, names)
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -187,35 +200,40 @@ def main():
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        per[name].append(e0.elapsed_time(e1) * 1e3 / (reps * copies))     # us per launch
-    avg_us = {n: float(np.mean(per[n])) for n in ORDER}
+        avg_us[ln] = e0.elapsed_time(e1) * 1e3 / (reps * copies)     # us per launch
 
-    # parity on the timed blobs: sampled rows of every tensor against float64
+    # parity on the timed blobs: sampled rows of every tensor against float64, with
+    # the activations its launch used
     worst = 0.0
-    for name in ORDER:
-        t = layer[name]["tensor"]
-        y = ys[name].cpu().numpy()
-        rows = np.random.default_rng(1).choice(t.codes.shape[0], 256, replace=False)
-        wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
-        ok, wr = G.check(y[:, rows], wv, G.x_values(t.x, "f16"))
-        worst = max(worst, wr)
-        if not ok:
-            log(f"PARITY FAILURE on {name}: worst err/bound {wr}")
-            sys.exit(1)
+    for ln, names in LAUNCHES:
+        xv = G.x_values(layer[names[0]]["tensor"].x, "f16")
+        for name in names:
+            t = layer[name]["tensor"]
+            y = ys[name].cpu().numpy()
+            rows = np.random.default_rng(1).choice(t.codes.shape[0], 256, replace=False)
+            wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
+            ok, wr = G.check(y[:, rows], wv, xv)
+            worst = max(worst, wr)
+            if not ok:
+                log(f"PARITY FAILURE on {name}: worst err/bound {wr}")
+                sys.exit(1)
 
     n_weights = sum(layer[n]["tensor"].codes.size for n in ORDER)
     us_layer = ms_step * 1e3
     gbs = layer_bytes / (us_layer * 1e-6) / 1e9
     unc_bytes = sum(layer[n]["tensor"].codes.size * 0.5 + layer[n]["tensor"].codes.shape[0] * 2 for n in ORDER)
-    dom = max(ORDER, key=lambda n: avg_us[n])
-    tdom = layer[dom]["tensor"]
-    dom_bytes = stored[dom] + tdom.x.size * 2 + tdom.codes.shape[0] * 4 * args.batch
-    achieved = dom_bytes / (avg_us[dom] * 1e-6) / 1e9
+    launch_bytes = {}
+    for ln, names in LAUNCHES:
+        launch_bytes[ln] = sum(stored[n] + layer[n]["tensor"].codes.shape[0] * 4 * args.batch for n in names) \
+            + layer[names[0]]["tensor"].x.size * 2
+    dom = max(avg_us, key=lambda ln: avg_us[ln])
+    achieved = launch_bytes[dom] / (avg_us[dom] * 1e-6) / 1e9
     for n in ORDER:
         c = layer[n]["coding"]
         log(f"{n:5s} {layer[n]['tensor'].codes.shape} m={c.log2_m} tc={c.tile_cols} "
-            f"launch={layer[n]['launch']} stored={stored[n] / 1e6:.3f} MB "
-            f"avg={avg_us[n]:.2f} us  {stored[n] / (avg_us[n] * 1e-6) / 1e9:.0f} GB/s")
+            f"launch={layer[n]['launch']} stored={stored[n] / 1e6:.3f} MB")
+    for ln, names in LAUNCHES:
+        log(f"launch {ln:8s} avg={avg_us[ln]:.2f} us  {launch_bytes[ln] / (avg_us[ln] * 1e-6) / 1e9:.0f} GB/s")
     out = {
         "metric": METRIC, "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -223,7 +241,8 @@ def main():
         "dtype": "u32 decode + f32 accumulate", "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B-shaped layer set (q,k,v,o,gate,up,down) of 16-level "
                                "Laplacian codes (H=2.2 bits), 2 codes per rANS symbol, fp16 row "
-                               "scales, fp16 x, batch 1, cold cache",
+                               "scales, fp16 x, batch 1, cold cache; 4 launches per step "
+                               "(q/k/v, o, gate/up, down)",
                    "batch": args.batch, "copies_rotated": copies,
                    "codings": {n: dict(log2_m=layer[n]["coding"].log2_m,
                                        tile_cols=layer[n]["coding"].tile_cols,
@@ -233,13 +252,13 @@ def main():
         "stored_bits_per_weight": round(layer_bytes * 8 / n_weights, 4),
         "gbps_compressed": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gbps_uncompressed_equiv": round(unc_bytes / (us_layer * 1e-6) / 1e9, 1),
-        "per_tensor_us": {n: round(avg_us[n], 3) for n in ORDER},
+        "per_launch_us": {ln: round(v, 3) for ln, v in avg_us.items()},
         "host_wall_s": round(host_s, 3),
         "parity_worst_err_over_bound": worst,
-        "roofline": {"bound": "hbm", "kernel": f"k_decode<INT4,pair> on {dom} {tuple(tdom.codes.shape)}",
+        "roofline": {"bound": "hbm", "kernel": f"k_decode<INT4 pair> launch {dom}",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(avg_us[dom], 3)},
+                     "bytes_per_launch": int(launch_bytes[dom]), "avg_launch_us": round(avg_us[dom], 3)},
     }
     if args.calibrate_copy:
         src = torch.ones(64 << 18, dtype=torch.float32, device=dev)

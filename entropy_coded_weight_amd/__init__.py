@@ -65,7 +65,8 @@ class Tensor(ctypes.Structure):
 
 
 EXPORTS = ["enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
-           "dec_gemv", "dec_materialize", "ecw_last_error", "ecw_abi_version"]
+           "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize",
+           "ecw_last_error", "ecw_abi_version"]
 
 _lib = None
 
@@ -94,8 +95,10 @@ def lib():
     L.dec_gemv_workspace_size.argtypes = [P(Tensor), i32, P(sz)]
     L.dec_gemv.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz]
     L.dec_materialize.argtypes = [vp, P(Tensor), vp, vp, vp]
+    L.dec_gemv_group_workspace_size.argtypes = [P(P(Tensor)), i32, i32, P(sz)]
+    L.dec_gemv_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz]
     for f in ("enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
-              "dec_gemv", "dec_materialize"):
+              "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []
     L.ecw_last_error.restype = ctypes.c_char_p
@@ -180,6 +183,57 @@ def gemv_raw(t: Tensor, x: torch.Tensor, y: torch.Tensor, workspace: torch.Tenso
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dec_gemv(_stream(stream), ctypes.byref(t), x.data_ptr(), xd, y.data_ptr(), batch,
                           ws, wsb), "dec_gemv")
+
+
+def _tensor_array(ts):
+    arr = (ctypes.POINTER(Tensor) * len(ts))(*[ctypes.pointer(t) for t in ts])
+    return arr
+
+
+def group_workspace_size(ts, batch: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dec_gemv_group_workspace_size(_tensor_array(ts), len(ts), batch, ctypes.byref(n)),
+           "dec_gemv_group_workspace_size")
+    return n.value
+
+
+def gemv_group_raw(ts, x: torch.Tensor, ys, workspace: torch.Tensor | None, stream=None):
+    """dec_gemv_group: tensors ts share x [batch, K]; ys[i] fp32 [batch, N_i]."""
+    xd = DT_F16 if x.dtype == torch.float16 else DT_BF16 if x.dtype == torch.bfloat16 else None
+    if xd is None:
+        raise TypeError("x must be float16 or bfloat16")
+    yarr = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    ws = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dec_gemv_group(_stream(stream), _tensor_array(ts), len(ts), x.data_ptr(), xd, yarr,
+                                x.shape[0], ws, wsb), "dec_gemv_group")
+
+
+class GemvGroup:
+    """Compressed tensors sharing one activation vector, run as one launch."""
+
+    def __init__(self, tensors):
+        self.tensors = list(tensors)
+        self._ws = {}
+
+    def workspace(self, batch: int):
+        n = group_workspace_size([c.t for c in self.tensors], batch)
+        if n == 0:
+            return None
+        key = (batch > 1, tuple((c.t.waves_per_block, c.t.tiles_per_wave) for c in self.tensors))
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < n:
+            ws = torch.zeros(n, dtype=torch.uint8, device=self.tensors[0].dev.device)
+            self._ws[key] = ws
+        return ws
+
+    def gemv(self, x: torch.Tensor, ys=None, stream=None):
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if ys is None:
+            ys = [torch.empty((x.shape[0], c.rows), dtype=torch.float32, device=x.device) for c in self.tensors]
+        gemv_group_raw([c.t for c in self.tensors], x, ys, self.workspace(x.shape[0]), stream)
+        return ys
 
 
 def materialize_raw(t: Tensor, symbols, w_out, status, stream=None):

@@ -39,7 +39,10 @@ constexpr uint32_t kMirror = 64;          // copy of the ring head for reads tha
 constexpr uint32_t kRingStride = kRing + kMirror;
 constexpr uint32_t kChunk = 512;          // words per chunk = 64 lanes x 16 bytes
 
-struct KArgs {
+constexpr int kMaxGroup = 8;
+
+// Per-tensor launch arguments (one entry per tensor of a grouped launch).
+struct TArgs {
   const uint2* lut;
   const uint32_t* states;
   const uint32_t* offsets;
@@ -53,9 +56,15 @@ struct KArgs {
   void* w_out;
   uint32_t* status_out;
   uint32_t rows, cols, n_rg, n_sl, s_full, s_last, log2m, tile_cols;
-  uint32_t tiles_per_wave, n_sg, n_blocks, syms_per_row;
+  uint32_t tiles_per_wave, n_sg, n_blocks, block_begin, syms_per_row;
   uint32_t x_is_bf16, nb, lut_entries, xs_cols;
   uint32_t raw_full_bytes, raw_rg_bytes;
+};
+
+struct KArgs {
+  TArgs t[kMaxGroup];
+  uint32_t nt;           // tensors in the launch
+  uint32_t n_blocks;     // total logical blocks
 };
 
 __device__ __forceinline__ float load_x(const void* x, uint32_t is_bf16, uint64_t i) {
@@ -179,13 +188,13 @@ __device__ __forceinline__ uint32_t raw_byte(const uint4& g, int u) {
   return (dw >> (8 * (u & 3))) & 0xFFu;
 }
 
-__device__ __forceinline__ const uint8_t* raw_tile(const KArgs& a, uint32_t rg, uint32_t sl, uint32_t lane) {
+__device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, uint32_t sl, uint32_t lane) {
   return a.raw + (uint64_t)rg * a.raw_rg_bytes + (uint64_t)sl * a.raw_full_bytes + lane * 16;
 }
 
 // Word range of a run of tiles [t0, t1): chunk-aligned start, chunk count, first
 // read position.
-__device__ __forceinline__ void run_words(const KArgs& a, uint32_t t0, uint32_t t1, uint32_t& gb,
+__device__ __forceinline__ void run_words(const TArgs& a, uint32_t t0, uint32_t t1, uint32_t& gb,
                                           uint32_t& nch, uint32_t& rpos) {
   if (t0 >= t1) {
     gb = 0; nch = 0; rpos = 0;
@@ -203,7 +212,7 @@ __device__ __forceinline__ void run_words(const KArgs& a, uint32_t t0, uint32_t 
 // The first two chunks of each stream (c0*, c1*) were loaded by the caller before
 // the block's staging barrier and are committed to the rings here.
 template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED, int NS>
-__device__ __forceinline__ void wave_body(const KArgs& a, const uint2* lut, const float* xs, uint16_t* ring,
+__device__ __forceinline__ void wave_body(const TArgs& a, const uint2* lut, const float* xs, uint16_t* ring,
                                           uint32_t rg, uint32_t tA0, uint32_t tA1, uint32_t tB0,
                                           uint32_t tB1, uint32_t c_lo, uint32_t lane, bool active,
                                           float* acc) {
@@ -348,7 +357,7 @@ __device__ __forceinline__ void wave_body(const KArgs& a, const uint2* lut, cons
 // decoded as one stream or, when R >= 2 and the payload allows, two interleaved
 // streams (the host sizes the LDS rings the same way).
 template <int PAY, int CB, int KW, int B, bool MAT>
-__global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
+__global__ void __launch_bounds__(1024) k_decode(const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
   const uint32_t W = blockDim.x >> 6;
   const uint32_t tid = threadIdx.x;
@@ -359,8 +368,14 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
   // blocks (the slice groups of one row group are adjacent).  gridDim.x is a
   // multiple of 8; surplus blocks exit at once.
   const uint32_t per = gridDim.x >> 3;
-  const uint32_t lb = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lb >= a.n_blocks) return;
+  const uint32_t gl = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (gl >= ka.n_blocks) return;
+  // tensor of a grouped launch: blocks are numbered tensor by tensor
+  uint32_t ti = 0;
+  for (uint32_t i = 1; i < ka.nt; ++i)
+    if (gl >= ka.t[i].block_begin) ti = i;
+  const TArgs& a = ka.t[ti];
+  const uint32_t lb = gl - a.block_begin;
   const uint32_t rg = lb / a.n_sg, sg = lb - rg * a.n_sg;
   const uint32_t R = a.tiles_per_wave;
   const uint32_t sl_blk = sg * W * R;
@@ -465,20 +480,31 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs a) {
 
 // Fixed-order sum of the per-block partials of each row (row groups that span
 // several blocks), times the row scale.  A separate launch: the kernel boundary
-// makes the partials visible without device-wide cache flushes.
+// makes the partials visible without device-wide cache flushes.  One launch covers
+// every tensor of a group that needs it.
+struct RArgs {
+  const float* partials[kMaxGroup];
+  const uint16_t* scales[kMaxGroup];
+  float* y[kMaxGroup];
+  uint32_t rows[kMaxGroup], n_sg[kMaxGroup], row_begin[kMaxGroup];
+  uint32_t nt, nb, unit_scale, total_rows;
+};
+
 template <int B>
-__global__ void __launch_bounds__(256) k_reduce(const float* partials, const uint16_t* scales, float* y,
-                                                uint32_t rows, uint32_t n_sg, uint32_t nb, uint32_t unit_scale) {
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;   // = rg * 64 + lane
-  const uint32_t r = i, rg = i >> 6, l = i & 63;
-  if (r >= rows) return;
-  const float sc = unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, scales[r]);
+__global__ void __launch_bounds__(256) k_reduce(const RArgs ra) {
+  const uint32_t gi = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= ra.total_rows) return;
+  uint32_t ti = 0;
+  for (uint32_t i = 1; i < ra.nt; ++i)
+    if (gi >= ra.row_begin[i]) ti = i;
+  const uint32_t r = gi - ra.row_begin[ti], rg = r >> 6, l = r & 63, n_sg = ra.n_sg[ti];
+  const float sc = ra.unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, ra.scales[ti][r]);
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    if ((uint32_t)b >= nb) break;
+    if ((uint32_t)b >= ra.nb) break;
     float s = 0.f;
-    for (uint32_t g = 0; g < n_sg; ++g) s += partials[(((uint64_t)rg * n_sg + g) * B + b) * 64 + l];
-    y[(uint64_t)b * rows + r] = s * sc;
+    for (uint32_t g = 0; g < n_sg; ++g) s += ra.partials[ti][(((uint64_t)rg * n_sg + g) * B + b) * 64 + l];
+    ra.y[ti][(uint64_t)b * ra.rows[ti] + r] = s * sc;
   }
 }
 
@@ -514,6 +540,7 @@ static uint32_t streams_per_wave(const ecw_coding& c, bool mat, uint32_t R) {
   return (mat || c.payload == ECW_P_BF16_EXP || c.weights_per_symbol == 4 || R < 2) ? 1 : 2;
 }
 
+// Dynamic LDS of one block: decode table, staged activations, word rings.
 static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat) {
   const uint64_t lut = (uint64_t)t->n_tables << t->coding.log2_m;
   uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * 4 + 15) / 16 * 16;
@@ -536,34 +563,7 @@ static bool lds_attribute_set(KernelFn fn) {
   return true;
 }
 
-static ecw_status launch(ecw_stream stream, const ecw_tensor* t, KArgs& a, int B, bool mat,
-                         uint32_t W) {
-  KernelFn fn = mat ? (B == 1 ? pick_kernel<1, true>(t->coding) : nullptr)
-                    : (B == 1 ? pick_kernel<1, false>(t->coding) : pick_kernel<4, false>(t->coding));
-  if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
-  const uint64_t lds = lds_bytes(t, W, a.tiles_per_wave, a.xs_cols, B, mat);
-  if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "launch shape needs more than 160 KiB of LDS");
-  const uint32_t grid = (a.n_blocks + 7) / 8 * 8;
-  if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
-  if (!mat && a.n_sg > 1) {
-    const uint32_t unit = t->coding.payload == ECW_P_BF16_EXP;
-    const dim3 rgrid((a.rows + 255) / 256);
-    if (B == 1)
-      hipLaunchKernelGGL(k_reduce<1>, rgrid, dim3(256), 0, (hipStream_t)stream, a.partials, a.scales, a.y,
-                         a.rows, a.n_sg, a.nb, unit);
-    else
-      hipLaunchKernelGGL(k_reduce<4>, rgrid, dim3(256), 0, (hipStream_t)stream, a.partials, a.scales, a.y,
-                         a.rows, a.n_sg, a.nb, unit);
-    err = hipGetLastError();
-    if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
-  }
-  return ECW_OK;
-}
-
-static void fill_common(const ecw_tensor* t, KArgs& a) {
+static void fill_tensor(const ecw_tensor* t, TArgs& a) {
   const uint8_t* base = static_cast<const uint8_t*>(t->device_blob);
   a.lut = reinterpret_cast<const uint2*>(base + t->off_lut);
   a.states = reinterpret_cast<const uint32_t*>(base + t->off_states);
@@ -599,6 +599,120 @@ static ecw_status check_tensor(const ecw_tensor* t) {
   return ECW_OK;
 }
 
+static uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace layout of a group: each tensor whose row groups span several blocks
+// gets its partials, in tensor order, 256-byte aligned.
+static uint64_t group_workspace(const ecw_tensor* const* ts, int n, int batch, uint64_t* off) {
+  uint64_t pos = 0;
+  for (int i = 0; i < n; ++i) {
+    const uint64_t w = workspace_bytes(ts[i], batch);
+    if (off) off[i] = pos;
+    pos += align256(w);
+  }
+  return pos;
+}
+
+static ecw_status check_group(const ecw_tensor* const* ts, int n, int batch, int x_dtype, const void* x,
+                              float* const* ys) {
+  if (!ts || n < 1 || n > kMaxGroup) return fail(ECW_E_INVALID_ARG, "group must hold 1..8 tensors");
+  if (batch < 1 || batch > 4) return fail(ECW_E_INVALID_ARG, "batch must be 1..4");
+  if (x_dtype != ECW_DT_F16 && x_dtype != ECW_DT_BF16) return fail(ECW_E_INVALID_ARG, "x dtype must be F16 or BF16");
+  if (!ys) return fail(ECW_E_INVALID_ARG, "y array is NULL");
+  for (int i = 0; i < n; ++i) {
+    ecw_status st = check_tensor(ts[i]);
+    if (st != ECW_OK) return st;
+    const ecw_coding& c = ts[i]->coding, &c0 = ts[0]->coding;
+    if (c.payload != c0.payload || c.code_bits != c0.code_bits || c.weights_per_symbol != c0.weights_per_symbol ||
+        c.cols != c0.cols || ts[i]->waves_per_block != ts[0]->waves_per_block)
+      return fail(ECW_E_INVALID_ARG, "grouped tensors must share payload, code width, cols and waves per block");
+    if (c.rows && (!ys[i] || reinterpret_cast<uintptr_t>(ys[i]) % 16))
+      return fail(ECW_E_INVALID_ARG, "y must be a 16-byte aligned device pointer");
+  }
+  if (ts[0]->coding.cols && (!x || reinterpret_cast<uintptr_t>(x) % 16))
+    return fail(ECW_E_INVALID_ARG, "x must be a 16-byte aligned device pointer");
+  return ECW_OK;
+}
+
+// Fused decode + GEMV of a group of tensors that read the same x (one launch),
+// then one launch that adds the cross-block partials where a row group spans
+// several blocks.
+static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, int n, const void* x,
+                               int x_dtype, float* const* ys, int batch, void* workspace, size_t ws_bytes) {
+  ecw_status st = check_group(ts, n, batch, x_dtype, x, ys);
+  if (st != ECW_OK) return st;
+  uint64_t woff[kMaxGroup];
+  const uint64_t need = group_workspace(ts, n, batch, woff);
+  if (need && (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
+    return fail(ECW_E_INVALID_ARG, "workspace missing, too small or not 256-byte aligned");
+  const int B = batch > 1 ? 4 : 1;
+  const uint32_t W = ts[0]->waves_per_block;
+  KArgs ka{};
+  RArgs ra{};
+  uint64_t lds = 0;
+  uint32_t blocks = 0, red_rows = 0;
+  for (int i = 0; i < n; ++i) {
+    const ecw_tensor* t = ts[i];
+    if (t->coding.rows == 0) continue;
+    if (t->n_tiles == 0) {   // K == 0: y = 0 (a fill kernel keeps the call graph-capturable)
+      const uint64_t cnt = (uint64_t)batch * t->coding.rows;
+      hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)((cnt + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                         ys[i], cnt);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(ECW_E_HIP, "fill launch failed");
+      continue;
+    }
+    TArgs& a = ka.t[ka.nt];
+    fill_tensor(t, a);
+    a.x = x;
+    a.y = ys[i];
+    a.x_is_bf16 = x_dtype == ECW_DT_BF16;
+    a.nb = (uint32_t)batch;
+    a.tiles_per_wave = t->tiles_per_wave;
+    a.n_sg = slice_groups(t);
+    a.n_blocks = a.n_rg * a.n_sg;
+    a.block_begin = blocks;
+    a.xs_cols = W * t->tiles_per_wave * t->coding.tile_cols;
+    blocks += a.n_blocks;
+    lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false));
+    if (a.n_sg > 1) {
+      a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + woff[i]);
+      const uint32_t j = ra.nt++;
+      ra.partials[j] = a.partials;
+      ra.scales[j] = a.scales;
+      ra.y[j] = ys[i];
+      ra.rows[j] = a.rows;
+      ra.n_sg[j] = a.n_sg;
+      ra.row_begin[j] = red_rows;
+      red_rows += a.rows;
+    }
+    ++ka.nt;
+  }
+  if (ka.nt == 0) return ECW_OK;
+  ka.n_blocks = blocks;
+  KernelFn fn = B == 1 ? pick_kernel<1, false>(ts[0]->coding) : pick_kernel<4, false>(ts[0]->coding);
+  if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
+  if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "launch shape needs more than 160 KiB of LDS");
+  if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
+  const uint32_t grid = (blocks + 7) / 8 * 8;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  if (ra.nt) {
+    ra.nb = (uint32_t)batch;
+    ra.unit_scale = ts[0]->coding.payload == ECW_P_BF16_EXP;
+    ra.total_rows = red_rows;
+    const dim3 rgrid((red_rows + 255) / 256);
+    if (B == 1)
+      hipLaunchKernelGGL(k_reduce<1>, rgrid, dim3(256), 0, (hipStream_t)stream, ra);
+    else
+      hipLaunchKernelGGL(k_reduce<4>, rgrid, dim3(256), 0, (hipStream_t)stream, ra);
+    err = hipGetLastError();
+    if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  }
+  return ECW_OK;
+}
+
 }  // namespace ecw
 
 using namespace ecw;
@@ -606,39 +720,26 @@ using namespace ecw;
 extern "C" ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
                                float* y, int batch, void* workspace, size_t ws_bytes) {
   clear_error();
-  ecw_status st = check_tensor(t);
-  if (st != ECW_OK) return st;
+  return launch_group(stream, &t, 1, x, x_dtype, &y, batch, workspace, ws_bytes);
+}
+
+extern "C" ecw_status dec_gemv_group_workspace_size(const ecw_tensor* const* t, int n, int batch,
+                                                    size_t* bytes) {
+  clear_error();
+  if (!t || !bytes || n < 1 || n > kMaxGroup) return fail(ECW_E_INVALID_ARG, "bad arguments");
   if (batch < 1 || batch > 4) return fail(ECW_E_INVALID_ARG, "batch must be 1..4");
-  if (x_dtype != ECW_DT_F16 && x_dtype != ECW_DT_BF16) return fail(ECW_E_INVALID_ARG, "x dtype must be F16 or BF16");
-  if (t->coding.rows && (!y || reinterpret_cast<uintptr_t>(y) % 16))
-    return fail(ECW_E_INVALID_ARG, "y must be a 16-byte aligned device pointer");
-  if (t->coding.cols && (!x || reinterpret_cast<uintptr_t>(x) % 16))
-    return fail(ECW_E_INVALID_ARG, "x must be a 16-byte aligned device pointer");
-  const uint64_t need = workspace_bytes(t, batch);
-  if (need && (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
-    return fail(ECW_E_INVALID_ARG, "workspace missing, too small or not 256-byte aligned");
-  if (t->coding.rows == 0) return ECW_OK;
-  if (t->n_tiles == 0) {   // K == 0: y = 0 (a fill kernel, so the call stays graph-capturable)
-    const uint64_t n = (uint64_t)batch * t->coding.rows;
-    hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, y, n);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? ECW_OK : fail(ECW_E_HIP, "fill launch failed");
-  }
-  const int B = batch > 1 ? 4 : 1;
-  KArgs a{};
-  fill_common(t, a);
-  a.x = x;
-  a.y = y;
-  a.x_is_bf16 = x_dtype == ECW_DT_BF16;
-  a.nb = (uint32_t)batch;
-  a.tiles_per_wave = t->tiles_per_wave;
-  a.n_sg = slice_groups(t);
-  a.n_blocks = a.n_rg * a.n_sg;
-  a.xs_cols = t->waves_per_block * t->tiles_per_wave * t->coding.tile_cols;
-  if (need) {
-    a.partials = static_cast<float*>(workspace);
-  }
-  return launch(stream, t, a, B, false, t->waves_per_block);
+  for (int i = 0; i < n; ++i)
+    if (!t[i] || t[i]->waves_per_block < 1 || t[i]->waves_per_block > 16 || t[i]->tiles_per_wave < 1)
+      return fail(ECW_E_INVALID_ARG, "bad tensor or launch shape");
+  *bytes = (size_t)group_workspace(t, n, batch, nullptr);
+  return ECW_OK;
+}
+
+extern "C" ecw_status dec_gemv_group(ecw_stream stream, const ecw_tensor* const* t, int n, const void* x,
+                                     int x_dtype, float* const* y, int batch, void* workspace,
+                                     size_t ws_bytes) {
+  clear_error();
+  return launch_group(stream, t, n, x, x_dtype, y, batch, workspace, ws_bytes);
 }
 
 extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, uint16_t* symbols,
@@ -647,8 +748,9 @@ extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, ui
   ecw_status st = check_tensor(t);
   if (st != ECW_OK) return st;
   if (t->n_tiles == 0) return ECW_OK;
-  KArgs a{};
-  fill_common(t, a);
+  KArgs ka{};
+  TArgs& a = ka.t[0];
+  fill_tensor(t, a);
   a.sym_out = symbols;
   a.w_out = w_out;
   a.status_out = tile_status;
@@ -658,5 +760,16 @@ extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, ui
   a.n_sg = (t->n_slices + W - 1) / W;
   a.n_blocks = a.n_rg * a.n_sg;
   a.xs_cols = 0;
-  return launch(stream, t, a, 1, true, W);
+  ka.nt = 1;
+  ka.n_blocks = a.n_blocks;
+  KernelFn fn = pick_kernel<1, true>(t->coding);
+  if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
+  const uint64_t lds = lds_bytes(t, W, 1, 0, 1, true);
+  if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "decode table needs more than 160 KiB of LDS");
+  if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
+  const uint32_t grid = (ka.n_blocks + 7) / 8 * 8;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  return ECW_OK;
 }

@@ -145,6 +145,20 @@ ecw_status dec_gemv_workspace_size(const ecw_tensor* t, int batch, size_t* bytes
 ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
                     float* y, int batch, void* workspace, size_t workspace_bytes);
 
+/* Grouped launch: several tensors that read the same activations, decoded and
+ * multiplied in one kernel launch (MINE page, Section 4.2 "Launch": sections with
+ * the same input dimension and quantisation share a launch, e.g. q/k/v and
+ * gate/up).  t[0..n): 1 <= n <= 8 tensors with the same payload, code width, cols
+ * and waves_per_block (each keeps its own table size, tile width and tiles per
+ * wave); y[i]: device fp32 [batch][t[i]->coding.rows].  x, batch, workspace as for
+ * dec_gemv; the workspace size comes from dec_gemv_group_workspace_size.  Results
+ * are bit-identical to separate dec_gemv calls with the same launch shapes.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ecw_status dec_gemv_group_workspace_size(const ecw_tensor* const* t, int n, int batch, size_t* bytes);
+ecw_status dec_gemv_group(ecw_stream stream, const ecw_tensor* const* t, int n, const void* x,
+                          int x_dtype, float* const* y, int batch, void* workspace,
+                          size_t workspace_bytes);
+
 /* Test hook: the same decode core, writing what dec_gemv keeps in registers.
  *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices);
  *   w_out: nullable device [rows][cols] in the logical dtype (INT int8 codes, BF16

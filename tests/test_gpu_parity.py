@@ -160,3 +160,26 @@ def test_graph_capture_replays_match_eager(shape):
         assert torch.equal(y, y_eager), f"replay {i} differs"
         ct.gemv(xd * 2.0)                  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_grouped_launch_matches_separate_launches(batch):
+    # q/k/v-like group: different rows, table sizes and tile widths, shared x
+    specs = [(256, 11, 128, 1), (64, 12, 256, 1), (130, 10, 128, 2)]
+    cts, cs = [], []
+    for i, (n, m, tc, R) in enumerate(specs):
+        case = cases._int(f"g{i}", n, 1024, 2, 4, m, tc, seed=20 + i)
+        ct = ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
+                                  waves_per_block=4, tiles_per_wave=R)
+        cts.append(ct)
+        cs.append(case)
+    xd, xv = _x(cs[0], batch)
+    ys = ecw.GemvGroup(cts).gemv(xd)
+    torch.cuda.synchronize()
+    for ct, case, y in zip(cts, cs, ys):
+        y_sep = ct.gemv(xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_sep)
+        wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+        ok, worst = gemv.check(y.cpu().numpy(), wv, xv)
+        assert ok, worst

@@ -274,3 +274,19 @@ def test_encode_is_deterministic_and_threads_agree():
     a = ecw.encode(case.lib_coding(), case.logical, case.scales)
     b = ecw.encode(case.lib_coding(), case.logical, case.scales)
     assert np.array_equal(a, b)
+
+
+def test_group_rejects_mismatched_tensors_without_launching():
+    a = ecw.prepare(_blob())
+    case = cases.small_cases()[1]                      # different cols
+    b = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    a.device_blob = 256
+    b.device_blob = 256
+    L = ecw.lib()
+    arr = ecw._tensor_array([a, b])
+    ys = (ctypes.c_void_p * 2)(256, 512)
+    assert L.dec_gemv_group(None, arr, 2, 256, 1, ys, 1, None, 0) == 1
+    assert L.dec_gemv_group(None, arr, 0, 256, 1, ys, 1, None, 0) == 1
+    assert L.dec_gemv_group(None, arr, 9, 256, 1, ys, 1, None, 0) == 1
+    n = ctypes.c_size_t()
+    assert L.dec_gemv_group_workspace_size(arr, 2, 1, ctypes.byref(n)) == 0
