@@ -23,8 +23,12 @@
 //                         f * (x >> m) ignores a8
 //   hi = bias | h16 << 16 bias = i - cum[s] < 2^13; next state = f * (x >> m) + bias
 // a8 / h16 per payload (h16 is an fp16 bit pattern, exact for every value here):
-//   INT, k = 1 or 2:  a8 = first code q0 (int8), h16 = fp16(q_{k-1})
-//   INT, k = 4:       a8 = symbol (packed unsigned digits), h16 = 0
+//   INT, k = 1:       a8 = the code q0 (int8), h16 = fp16(q0)
+//   INT, k = 2:       a8 = symbol (packed unsigned digits, first code lowest),
+//                     h16 = hi8(fp16(q0)) | hi8(fp16(q1)) << 8 (the fp16 of a code
+//                     |q| <= 8 has a zero low byte, so the two high bytes are the
+//                     whole values)
+//   INT, k = 4:       a8 = symbol, h16 = 0
 //   BF16:             a8 = exponent byte, h16 = 0
 //   FP8 E4M3:         a8 = code byte, h16 = fp16(e4m3 value) (NaN codes: 0x7E00)
 //   E8:               a8 = field value (int8), h16 = 0
@@ -124,11 +128,15 @@ inline void entry_payload(uint32_t payload, uint32_t code_bits, uint32_t k, int3
       if (k == 4) {
         *a8 = s & 0xFF;
         *h16 = 0;
+      } else if (k == 2) {
+        const int q0 = (int)(s & mask) - half;
+        const int q1 = (int)((s >> code_bits) & mask) - half;
+        *a8 = s & 0xFF;
+        *h16 = (uint32_t)(fp16_of_int(q0) >> 8) | (uint32_t)(fp16_of_int(q1) & 0xFF00u);
       } else {
         const int q0 = (int)(s & mask) - half;
-        const int ql = (int)((s >> (code_bits * (k - 1))) & mask) - half;
         *a8 = (uint32_t)(q0 & 0xFF);
-        *h16 = fp16_of_int(ql);
+        *h16 = fp16_of_int(q0);
       }
       return;
     }

@@ -34,12 +34,50 @@
 
 namespace ecw {
 
-constexpr uint32_t kRing = 1024;          // words per wave ring (two chunks)
-constexpr uint32_t kMirror = 64;          // copy of the ring head for reads that wrap
-constexpr uint32_t kRingStride = kRing + kMirror;
-constexpr uint32_t kChunk = 512;          // words per chunk = 64 lanes x 16 bytes
+constexpr uint32_t kChunk = 256;           // words per chunk = 64 lanes x 8 bytes
+constexpr uint32_t kRing = 512;            // words per wave ring (two chunks)
+constexpr uint32_t kMirror = 64;           // copy of the ring head for reads that wrap
+constexpr uint32_t kRingStride = kRing + kMirror;   // 1152 bytes per stream
+constexpr uint32_t kPairTableBytes = 2048; // 256 symbols x up to 8 bytes
 
 constexpr int kMaxGroup = 8;
+
+// Payloads whose symbols carry several codes are multiplied with packed 16-bit dot
+// products.  With fp16 activations and two codes per symbol the pair comes from the
+// table entry itself (the high bytes of both codes' fp16 values); otherwise the
+// entry's payload byte is the symbol and a 256-entry side table in LDS maps it to
+// its codes as 16-bit floats of the activations' type.
+template <int PAY, int KW>
+constexpr bool kDot = PAY == 1 && KW >= 2;
+template <int PAY, int KW, bool XBF>
+constexpr bool kPairTable = PAY == 1 && (KW == 4 || (KW == 2 && XBF));
+// Table entries whose high word is the bias alone (no payload bits beside it).
+template <int PAY, int KW>
+constexpr bool kCleanBias = (PAY == 1 && KW == 4) || PAY == 2 || PAY == 4;
+
+#define ECW_LDS __attribute__((address_space(3)))
+template <typename T>
+__device__ __forceinline__ ECW_LDS T* lds_ptr(uint32_t addr) {
+  return (ECW_LDS T*)addr;
+}
+// 8- and 16-byte LDS accesses (clang vector types: HIP's vector classes cannot be
+// addressed in LDS address space)
+typedef uint32_t ecw_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t ecw_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_load2(uint32_t addr) {
+  const ecw_u32x2 v = *lds_ptr<const ecw_u32x2>(addr);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 lds_load4(uint32_t addr) {
+  const ecw_u32x4 v = *lds_ptr<const ecw_u32x4>(addr);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void lds_store2(uint32_t addr, uint2 v) {
+  *lds_ptr<ecw_u32x2>(addr) = ecw_u32x2{v.x, v.y};
+}
+__device__ __forceinline__ void lds_store4(uint32_t addr, uint4 v) {
+  *lds_ptr<ecw_u32x4>(addr) = ecw_u32x4{v.x, v.y, v.z, v.w};
+}
 
 // Per-tensor launch arguments (one entry per tensor of a grouped launch).
 struct TArgs {
@@ -67,19 +105,6 @@ struct KArgs {
   uint32_t n_blocks;     // total logical blocks
 };
 
-__device__ __forceinline__ float load_x(const void* x, uint32_t is_bf16, uint64_t i) {
-  const uint16_t h = static_cast<const uint16_t*>(x)[i];
-  if (is_bf16) return __uint_as_float((uint32_t)h << 16);
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  // fixed xor-butterfly: every lane ends with the same, order-independent-of-timing sum
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // x' = f * (x >> m) + bias in one v_mad_u32_u24 (both factors < 2^24; the payload
 // byte in bits 24..31 of the table word is ignored by the 24-bit multiply).
 __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
@@ -97,12 +122,26 @@ __device__ __forceinline__ float fma_mix_hi(uint32_t h, float x, float acc) {
   return d;
 }
 
-// Per lane: mask bit set ? t : f (v_cndmask on a wave-uniform lane mask).  Inline
-// asm so the compiler cannot turn it back into an exec-masked branch.
-__device__ __forceinline__ uint32_t select_lanes(uint64_t mask, uint32_t t, uint32_t f) {
-  uint32_t d;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(f), "v"(t), "s"(mask));
-  return d;
+typedef _Float16 ecw_half2 __attribute__((ext_vector_type(2)));
+typedef short ecw_short2 __attribute__((ext_vector_type(2)));
+
+// acc + w.lo * x.lo + w.hi * x.hi, 16-bit operands (fp16 or bf16), fp32 accumulate.
+template <bool XBF>
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+  if constexpr (XBF)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ecw_short2, w), __builtin_bit_cast(ecw_short2, x),
+                                           acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(ecw_half2, w), __builtin_bit_cast(ecw_half2, x), acc, false);
+}
+
+// x = (x << 16) | w on the lanes of `mask` only (exec-masked v_lshl_or).  Inline asm
+// so the update stays one VALU op under a scalar exec swap instead of a select.
+__device__ __forceinline__ uint32_t shift_in(uint64_t mask, uint32_t x, uint32_t w) {
+  uint64_t save;
+  asm("s_and_saveexec_b64 %1, %2\n\tv_lshl_or_b32 %0, %0, 16, %3\n\ts_mov_b64 exec, %1"
+      : "+v"(x), "=&s"(save) : "s"(mask), "v"(w) : "scc");
+  return x;
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
@@ -112,74 +151,82 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 // ---- the per-stream pieces of one decode step (scalar state, kept in registers)
 
-// A4: one symbol decode.  Returns the table entry (f | a8 << 24, bias | h16 << 16).
-__device__ __forceinline__ uint2 decode_step(uint32_t& x, const uint2* lut, uint32_t m, uint32_t mmask) {
-  const uint2 e = lut[x & mmask];
-  x = mad_u24(x >> m, e.x, e.y & 0xFFFFu);
+// A4: one symbol decode.  Returns the table entry (f | a8 << 24, bias [| h16 << 16]).
+template <bool CLEAN>
+__device__ __forceinline__ uint2 decode_step(uint32_t& x, uint32_t lut, uint32_t m, uint32_t mmask) {
+  const uint2 e = lds_load2(lut + ((x & mmask) << 3));
+  x = mad_u24(x >> m, e.x, CLEAN ? e.y : (e.y & 0xFFFFu));
   return e;
 }
 
-// A5: renormalise the wave's 64 states against the stream's LDS ring; refill the
-// ring one chunk ahead of the read position (the chunk was loaded into `pre`
-// one chunk-consumption earlier).
+// A5: renormalise the wave's 64 states against the stream's LDS ring.  Every lane
+// reads the word at its prefix offset (always inside the ring plus its mirror) and
+// keeps it only if it needs one.  rposb: read position in bytes.
 template <bool RAGGED>
-__device__ __forceinline__ void renorm_step(uint32_t& x, uint32_t& rpos, uint32_t& have, uint32_t& nc,
-                                            uint4& pre, uint16_t* ring, const uint4* src, uint32_t nch,
-                                            uint32_t lane, bool active) {
-  if (rpos + 64 > have) {            // wave-uniform
-    const uint32_t slot_c = nc & 1u;
-    reinterpret_cast<uint4*>(ring + slot_c * kChunk)[lane] = pre;
-    if (slot_c == 0 && lane < 8) reinterpret_cast<uint4*>(ring + kRing)[lane] = pre;
-    have += kChunk;
-    ++nc;
-    if (nc < nch) pre = src[(uint64_t)nc * 64];
-  }
-  // Branch-free: every lane reads the word at its prefix offset (always inside the
-  // ring plus its mirror) and keeps it only if it needs one, so no exec-mask
-  // change or LDS wait splits the step.
-  const uint16_t* rp = ring + (rpos & (kRing - 1));
+__device__ __forceinline__ void renorm_step(uint32_t& x, uint32_t& rposb, uint32_t ring, bool active) {
   uint64_t msk;
   if constexpr (RAGGED)
     msk = __ballot(active && (x < kStateL));
   else
     msk = __builtin_amdgcn_ballot_w64(x < kStateL);
-  const uint32_t w = rp[lanes_below(msk)];
-  x = select_lanes(msk, (x << 16) | w, x);
-  rpos += (uint32_t)__popcll(msk);
+  const uint32_t base = ring + (rposb & (2 * kRing - 2));
+  const uint32_t w = *lds_ptr<const uint16_t>(base + (lanes_below(msk) << 1));
+  x = shift_in(msk, x, w);
+  rposb += (uint32_t)__popcll(msk) << 1;
+}
+
+// Keep the next four steps' reads inside committed ring data: commit the chunk held
+// in `pre` when fewer than 256 words are ahead of the read position, and load the
+// next one into `pre` (one chunk of prefetch distance).
+__device__ __forceinline__ void refill(uint32_t rposb, uint32_t& haveb, uint32_t& nc, uint2& pre, uint32_t ring,
+                                       const uint2* src, uint32_t nch, uint32_t lane) {
+  if (rposb + 8 * 64 > haveb) {      // wave-uniform
+    const uint32_t slot = nc & 1u;
+    lds_store2(ring + slot * (2 * kChunk) + lane * 8, pre);
+    if (slot == 0 && lane < 16) lds_store2(ring + 2 * kRing + lane * 8, pre);
+    haveb += 2 * kChunk;
+    ++nc;
+    if (nc < nch) pre = src[(uint64_t)nc * 64];
+  }
 }
 
 // A6 + A7: rebuild the weight(s) of one symbol in registers and accumulate.
-// xp: this symbol's activations, [KW][B] floats.  r: BF16 raw byte.
-template <int PAY, int CB, int KW, int B>
-__device__ __forceinline__ void mac(const uint2 e, const float* xp, uint32_t r, float* acc) {
-  if constexpr (PAY == 1) {
-    if constexpr (KW == 1) {
+// xw: this symbol's activations as 32-bit words (fp32 [KW][B], or for the dot path
+// packed 16-bit pairs [KW/2][B]).  r: BF16 raw byte.
+template <int PAY, int CB, int KW, int B, bool XBF>
+__device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t r, float* acc) {
+  if constexpr (kDot<PAY, KW> && !kPairTable<PAY, KW, XBF>) {
+    // fp16 (q0, q1) = bytes (0, hi8 q0, 0, hi8 q1) from the entry's high half
+    const uint32_t wp = __builtin_amdgcn_perm(e.y, e.y, 0x030C020Cu);
 #pragma unroll
-      for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);        // q0
-    } else if constexpr (KW == 2) {
-      const float w0 = (float)(int8_t)(e.x >> 24);                                // q0
+    for (int b = 0; b < B; ++b) acc[b] = dot2<false>(wp, xw[b], acc[b]);
+  } else if constexpr (kDot<PAY, KW>) {
+    // pair table at LDS address 0: entry of symbol s at s * 4 (KW 2) or s * 8 (KW 4);
+    // bits 22..23 of e.x are zero because f < 2^14
+    if constexpr (KW == 2) {
+      const uint32_t wp = *lds_ptr<const uint32_t>(e.x >> 22);
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[b] = dot2<XBF>(wp, xw[b], acc[b]);
+    } else {
+      const uint2 wp = lds_load2(e.x >> 21);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        acc[b] = fmaf(w0, xp[b], acc[b]);
-        acc[b] = fma_mix_hi(e.y, xp[B + b], acc[b]);                             // q1
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KW; ++i) {
-        const float w = (float)((int)((e.x >> (24 + CB * i)) & ((1u << CB) - 1)) - (1 << (CB - 1)));
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[i * B + b], acc[b]);
+        acc[b] = dot2<XBF>(wp.x, xw[b], acc[b]);
+        acc[b] = dot2<XBF>(wp.y, xw[B + b], acc[b]);
       }
     }
+  } else if constexpr (PAY == 1) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, __uint_as_float(xw[b]), acc[b]);   // q0
   } else if constexpr (PAY == 2) {
     // bf16 bits = sign << 15 | exponent << 7 | mantissa, as fp32 bits << 16
     const uint32_t bits = ((r << 24) & 0x80000000u) | ((e.x >> 1) & 0x7F800000u) | ((r << 16) & 0x007F0000u);
     const float w = __uint_as_float(bits);
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = fmaf(w, xp[b], acc[b]);
+    for (int b = 0; b < B; ++b) acc[b] = fmaf(w, __uint_as_float(xw[b]), acc[b]);
   } else {
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, xp[b], acc[b]);          // e4m3 value
+    for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, __uint_as_float(xw[b]), acc[b]);   // e4m3 value
   }
 }
 
@@ -193,172 +240,148 @@ __device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, 
 }
 
 // Word range of a run of tiles [t0, t1): chunk-aligned start, chunk count, first
-// read position.
+// read position (bytes from the aligned start).
 __device__ __forceinline__ void run_words(const TArgs& a, uint32_t t0, uint32_t t1, uint32_t& gb,
-                                          uint32_t& nch, uint32_t& rpos) {
+                                          uint32_t& nch, uint32_t& rposb) {
   if (t0 >= t1) {
-    gb = 0; nch = 0; rpos = 0;
+    gb = 0; nch = 0; rposb = 0;
     return;
   }
   const uint32_t wb = a.offsets[t0], we = a.offsets[t1];
   gb = wb & ~(kChunk - 1);
   nch = (we - gb + kChunk - 1) / kChunk;
-  rpos = wb - gb;
+  rposb = (wb - gb) * 2;
 }
 
-// The wave body.  NS = 1: the wave's tiles [t0, t1) are one stream.  NS = 2: the
-// first half (stream A) and the second half (stream B) are decoded in lockstep, two
-// independent dependency chains per wave.  MAT: decode-only test hook (NS = 1).
-// The first two chunks of each stream (c0*, c1*) were loaded by the caller before
-// the block's staging barrier and are committed to the rings here.
-template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED, int NS>
-__device__ __forceinline__ void wave_body(const TArgs& a, const uint2* lut, const float* xs, uint16_t* ring,
-                                          uint32_t rg, uint32_t tA0, uint32_t tA1, uint32_t tB0,
-                                          uint32_t tB1, uint32_t c_lo, uint32_t lane, bool active,
-                                          float* acc) {
+// The wave body: the wave's tiles [t0, t1) (consecutive slices of one row group)
+// are decoded as one stream of words; each tile starts from its own states.
+// MAT: decode-only test hook.  ring: LDS byte address of the wave's ring.  xs: LDS
+// byte address of the staged activations.
+template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED, bool XBF>
+__device__ __forceinline__ void wave_body(const TArgs& a, uint32_t lut, uint32_t xs, uint32_t ring,
+                                          uint32_t rg, uint32_t t0, uint32_t t1, uint32_t c_lo,
+                                          uint32_t lane, bool active, float* acc) {
   constexpr int U = 16;
+  constexpr bool DOT = kDot<PAY, KW>;
+  constexpr bool CLEAN = kCleanBias<PAY, KW>;
+  constexpr int XW = DOT ? (KW / 2) * B : KW * B;   // 32-bit activation words per step
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
   const uint32_t row = rg * 64 + lane;
   const uint32_t sl0 = rg * a.n_sl;
+  const uint2 zero2 = {0u, 0u};
   const uint4 zero4 = {0u, 0u, 0u, 0u};
-  uint16_t* ringA = ring;
-  uint16_t* ringB = ring + kRingStride;
 
-  uint32_t gbA, nchA, rposA, gbB = 0, nchB = 0, rposB = 0;
-  run_words(a, tA0, tA1, gbA, nchA, rposA);
-  if constexpr (NS == 2) run_words(a, tB0, tB1, gbB, nchB, rposB);
-  const uint4* srcA = reinterpret_cast<const uint4*>(a.words + gbA) + lane;
-  const uint4* srcB = reinterpret_cast<const uint4*>(a.words + gbB) + lane;
-  // first chunks (issued together; they travel while the previous stream's
-  // staging finishes) and the one-ahead prefetch
+  uint32_t gb, nch, rposb;
+  run_words(a, t0, t1, gb, nch, rposb);
+  const uint2* src = reinterpret_cast<const uint2*>(a.words + gb) + lane;
+  // first two chunks straight into the ring, the third into the prefetch register
   {
-    const uint4 c0 = nchA > 0 ? srcA[0] : zero4;
-    const uint4 c1 = nchA > 1 ? srcA[64] : zero4;
-    uint4 d0 = zero4, d1 = zero4;
-    if constexpr (NS == 2) {
-      d0 = nchB > 0 ? srcB[0] : zero4;
-      d1 = nchB > 1 ? srcB[64] : zero4;
-    }
-    reinterpret_cast<uint4*>(ringA)[lane] = c0;
-    if (lane < 8) reinterpret_cast<uint4*>(ringA + kRing)[lane] = c0;
-    reinterpret_cast<uint4*>(ringA + kChunk)[lane] = c1;
-    if constexpr (NS == 2) {
-      reinterpret_cast<uint4*>(ringB)[lane] = d0;
-      if (lane < 8) reinterpret_cast<uint4*>(ringB + kRing)[lane] = d0;
-      reinterpret_cast<uint4*>(ringB + kChunk)[lane] = d1;
-    }
+    const uint2 c0 = nch > 0 ? src[0] : zero2;
+    const uint2 c1 = nch > 1 ? src[64] : zero2;
+    lds_store2(ring + lane * 8, c0);
+    if (lane < 16) lds_store2(ring + 2 * kRing + lane * 8, c0);
+    lds_store2(ring + 2 * kChunk + lane * 8, c1);
   }
-  uint4 preA = nchA > 2 ? srcA[128] : zero4;
-  uint4 preB = zero4;
-  if constexpr (NS == 2) preB = nchB > 2 ? srcB[128] : zero4;
-  uint32_t haveA = 2 * kChunk, ncA = 2, haveB = 2 * kChunk, ncB = 2;
-  uint32_t stA = tA0 < tA1 ? a.states[(uint64_t)tA0 * 64 + lane] : kStateL;
-  uint32_t stB = kStateL;
-  if constexpr (NS == 2) stB = tB0 < tB1 ? a.states[(uint64_t)tB0 * 64 + lane] : kStateL;
+  uint2 pre = nch > 2 ? src[128] : zero2;
+  uint32_t haveb = 4 * kChunk, nc = 2;
+  uint32_t st = t0 < t1 ? a.states[(uint64_t)t0 * 64 + lane] : kStateL;
 
-  uint32_t tA = tA0, tB = tB0;
-  while (tA < tA1) {
-    const bool pairB = (NS == 2) && (tB < tB1);           // wave-uniform
-    uint32_t xA = stA, xB = stB;
-    if (tA + 1 < tA1) stA = a.states[(uint64_t)(tA + 1) * 64 + lane];
-    if constexpr (NS == 2) {
-      if (pairB && tB + 1 < tB1) stB = a.states[(uint64_t)(tB + 1) * 64 + lane];
-    }
-    const uint32_t slA = tA - sl0, slB = tB - sl0;
-    const uint32_t SA = (slA + 1 == a.n_sl) ? a.s_last : a.s_full;
-    const uint32_t SB = pairB ? ((slB + 1 == a.n_sl) ? a.s_last : a.s_full) : 0;   // SB <= SA
-    const uint32_t colA = slA * a.tile_cols - c_lo, colB = slB * a.tile_cols - c_lo;
-    const uint8_t* rawA = raw_tile(a, rg, slA, lane);
-    const uint8_t* rawB = raw_tile(a, rg, slB, lane);
+  for (uint32_t t = t0; t < t1; ++t) {
+    uint32_t x = st;
+    if (t + 1 < t1) st = a.states[(uint64_t)(t + 1) * 64 + lane];
+    const uint32_t sl = t - sl0;
+    const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
+    const uint32_t col = sl * a.tile_cols - c_lo;
+    const uint8_t* rawp = raw_tile(a, rg, sl, lane);
 
-    for (uint32_t j = 0; j < SA; j += U) {
-      const bool dualB = j < SB;                            // wave-uniform
-      uint4 rgA = zero4, rgB = zero4;
-      if constexpr (PAY == 2) {
-        rgA = *reinterpret_cast<const uint4*>(rawA + (uint64_t)(j / U) * 1024);
-        if (NS == 2 && dualB) rgB = *reinterpret_cast<const uint4*>(rawB + (uint64_t)(j / U) * 1024);
-      }
-      const float4* xgA = reinterpret_cast<const float4*>(xs + (uint64_t)(colA + KW * j) * B);
-      const float4* xgB = reinterpret_cast<const float4*>(xs + (uint64_t)(colB + KW * j) * B);
+    for (uint32_t j = 0; j < S; j += U) {
+      uint4 rgp = zero4;
+      if constexpr (PAY == 2) rgp = *reinterpret_cast<const uint4*>(rawp + (uint64_t)(j / U) * 1024);
+      // activation words of step j: fp32 [col][B], or packed pairs [col / 2][B]
+      const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
-        float4 xqA[MAT ? 1 : KW * B], xqB[MAT ? 1 : KW * B];
+        refill(rposb, haveb, nc, pre, ring, src, nch, lane);
+        uint4 xq[MAT ? 1 : XW];
         if constexpr (!MAT) {
 #pragma unroll
-          for (int i = 0; i < KW * B; ++i) xqA[i] = xgA[qtr * KW * B + i];
-          if (NS == 2 && dualB) {
-#pragma unroll
-            for (int i = 0; i < KW * B; ++i) xqB[i] = xgB[qtr * KW * B + i];
-          }
+          for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
         }
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
           const uint32_t step = j + u;
-          const uint2 eA = decode_step(xA, lut, m, mmask);
-          uint2 eB = {0u, 0u};
-          if (NS == 2 && dualB) eB = decode_step(xB, lut, m, mmask);
+          const uint2 e = decode_step<CLEAN>(x, lut, m, mmask);
           if constexpr (!MAT) {
-            mac<PAY, CB, KW, B>(eA, reinterpret_cast<const float*>(xqA) + u4 * KW * B,
-                                PAY == 2 ? raw_byte(rgA, u) : 0u, acc);
-            if (NS == 2 && dualB)
-              mac<PAY, CB, KW, B>(eB, reinterpret_cast<const float*>(xqB) + u4 * KW * B,
-                                  PAY == 2 ? raw_byte(rgB, u) : 0u, acc);
+            mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW,
+                                     PAY == 2 ? raw_byte(rgp, u) : 0u, acc);
           } else if (!RAGGED || active) {
-            const uint32_t aux = eA.x >> 24;
+            const uint32_t aux = e.x >> 24;
             uint32_t symbol = aux;
             int q[KW > 0 ? KW : 1];
             if constexpr (PAY == 1) {
               constexpr int half = 1 << (CB - 1);
-              if constexpr (KW == 4) {
+              if constexpr (KW == 1) {
+                q[0] = (int)(int8_t)aux;
+                symbol = (uint32_t)(q[0] + half);
+              } else {
 #pragma unroll
                 for (int i = 0; i < KW; ++i) q[i] = (int)((aux >> (CB * i)) & ((1u << CB) - 1)) - half;
-              } else {
-                q[0] = (int)(int8_t)aux;
-                if constexpr (KW == 2) q[1] = (int)(float)__builtin_bit_cast(_Float16, (uint16_t)(eA.y >> 16));
-                symbol = 0;
-#pragma unroll
-                for (int i = 0; i < KW; ++i) symbol |= (uint32_t)(q[i] + half) << (CB * i);
               }
             }
-            if (a.sym_out) a.sym_out[(uint64_t)row * a.syms_per_row + (uint64_t)slA * a.s_full + step] = (uint16_t)symbol;
+            if (a.sym_out) a.sym_out[(uint64_t)row * a.syms_per_row + (uint64_t)sl * a.s_full + step] = (uint16_t)symbol;
             if (a.w_out) {
-              const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)slA * a.tile_cols + (uint64_t)step * KW;
+              const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols + (uint64_t)step * KW;
               if constexpr (PAY == 1) {
 #pragma unroll
                 for (int i = 0; i < KW; ++i) static_cast<int8_t*>(a.w_out)[wi + i] = (int8_t)q[i];
               } else if constexpr (PAY == 2) {
-                const uint32_t r = raw_byte(rgA, u);
+                const uint32_t r = raw_byte(rgp, u);
                 static_cast<uint16_t*>(a.w_out)[wi] = (uint16_t)(((r & 0x80u) << 8) | (aux << 7) | (r & 0x7Fu));
               } else {
                 static_cast<uint8_t*>(a.w_out)[wi] = (uint8_t)aux;
               }
             }
           }
-          renorm_step<RAGGED>(xA, rposA, haveA, ncA, preA, ringA, srcA, nchA, lane, active);
-          if (NS == 2 && dualB) renorm_step<RAGGED>(xB, rposB, haveB, ncB, preB, ringB, srcB, nchB, lane, active);
+          renorm_step<RAGGED>(x, rposb, ring, active);
         }
       }
     }
     if constexpr (MAT) {
-      const bool ok_lane = !active || xA == kStateL;
+      const bool ok_lane = !active || x == kStateL;
       const uint64_t bad = __ballot(!ok_lane);
       if (lane == 0 && a.status_out)
-        a.status_out[tA] = (bad != 0 ? 1u : 0u) | ((rposA != a.offsets[tA + 1] - gbA) ? 2u : 0u);
+        a.status_out[t] = (bad != 0 ? 1u : 0u) | ((rposb != (a.offsets[t + 1] - gb) * 2) ? 2u : 0u);
     }
-    ++tA;
-    if (pairB) ++tB;
   }
 }
 
+// 16-bit float bits of a small integer, in the activations' type.
+template <bool XBF>
+__device__ __forceinline__ uint32_t small_int_bits(int q) {
+  if constexpr (XBF) return __float_as_uint((float)q) >> 16;     // exact for |q| < 2^8
+  else return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q);
+}
+
 // PAY: 1 INT codes, 2 BF16 exponent, 3 FP8.  CB/KW: code bits and codes per symbol
-// (INT).  B: batch capacity (1 or 4).  MAT: decode-only test hook.
-// Block = W waves on consecutive slices of one row group; wave w owns R tiles,
-// decoded as one stream or, when R >= 2 and the payload allows, two interleaved
-// streams (the host sizes the LDS rings the same way).
-template <int PAY, int CB, int KW, int B, bool MAT>
-__global__ void __launch_bounds__(1024) k_decode(const KArgs ka) {
+// (INT).  B: batch capacity (1 or 4).  MAT: decode-only test hook.  XBF: the dot path
+// multiplies bf16 activations (else fp16).
+// Block = W waves on consecutive slices of one row group; wave w owns R consecutive
+// tiles, decoded one after the other as one word stream.
+// LDS, from address 0 (the kernel declares no static LDS): [pair side table]
+// [decode table] [activations] [rings].
+// Register budget: batch-1 kernels are held to 64 VGPRs so 8 waves fit per SIMD (two
+// 16-wave blocks per CU) and hide the LDS latency of the decode chain.
+template <int B>
+constexpr int kWavesPerEU = B == 1 ? 8 : 4;
+
+template <int PAY, int CB, int KW, int B, bool MAT, bool XBF>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<B>)))
+k_decode(const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
+  (void)smem;
+  constexpr bool DOT = kDot<PAY, KW> && !MAT;
+  constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT;
   const uint32_t W = blockDim.x >> 6;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -382,31 +405,47 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs ka) {
   const uint32_t sl_blk_end = min(sl_blk + W * R, a.n_sl);
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
-  constexpr bool kTwoCapable = !MAT && PAY != 2 && KW != 4;
-  const uint32_t NSr = (kTwoCapable && R >= 2) ? 2 : 1;
-
+  const uint32_t pair_bytes = PTAB ? kPairTableBytes : 0;
+  const uint32_t lut = pair_bytes;
   const uint32_t lut_bytes = a.lut_entries * 8;
-  uint2* lut = reinterpret_cast<uint2*>(smem);
-  float* xs = reinterpret_cast<float*>(smem + lut_bytes);
-  const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * 4 + 15) & ~15u);
-  uint16_t* rings = reinterpret_cast<uint16_t*>(smem + lut_bytes + xs_bytes);
-  uint16_t* ring = rings + (wid * NSr) * kRingStride;
+  const uint32_t xs = lut + lut_bytes;
+  const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * (DOT ? 2 : 4) + 15) & ~15u);
+  const uint32_t rings = xs + xs_bytes;
+  // wave-uniform LDS address, pinned to a scalar register (the compiler otherwise
+  // may carry it in a VGPR and pay a vector add per ring read)
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(rings + wid * (2 * kRingStride));
 
   // ---- A2: stage the decode table (two 16-byte loads in flight per thread)
   {
     const uint4* src = reinterpret_cast<const uint4*>(a.lut);
-    uint4* dst = reinterpret_cast<uint4*>(lut);
     const uint32_t n = a.lut_entries / 2, bd = blockDim.x;
     for (uint32_t i = tid; i < n; i += 2 * bd) {
       const uint32_t i2 = i + bd;
       const uint4 v0 = src[i];
       const uint4 v1 = src[i2 < n ? i2 : i];
-      dst[i] = v0;
-      if (i2 < n) dst[i2] = v1;
+      lds_store4(lut + i * 16, v0);
+      if (i2 < n) lds_store4(lut + i2 * 16, v1);
     }
   }
-  // ---- A3: stage the block's activation columns as fp32 [col][b], 8 columns
-  // (16 bytes) per load
+  if constexpr (PTAB) {
+    // symbol -> its codes as 16-bit floats, packed two per word (digits low first)
+    // (blocks may have fewer than 256 threads)
+    for (uint32_t sy = tid; sy < 256; sy += blockDim.x) {
+      constexpr int half = 1 << (CB - 1);
+      constexpr uint32_t dmask = (1u << CB) - 1;
+      uint32_t w[KW / 2];
+#pragma unroll
+      for (int p = 0; p < KW / 2; ++p)
+        w[p] = small_int_bits<XBF>((int)((sy >> (CB * 2 * p)) & dmask) - half) |
+               (small_int_bits<XBF>((int)((sy >> (CB * (2 * p + 1))) & dmask) - half) << 16);
+      if constexpr (KW == 2)
+        *lds_ptr<uint32_t>(sy * 4) = w[0];
+      else
+        lds_store2(sy * 8, make_uint2(w[0], w[1]));
+    }
+  }
+  // ---- A3: stage the block's activation columns, 8 columns (16 bytes) per load:
+  // as fp32 [col][b], or for the dot path as the packed 16-bit pairs [col / 2][b]
   if constexpr (!MAT) {
     const uint32_t nvec = a.xs_cols / 8;
     for (uint32_t v = tid; v < nvec * B; v += blockDim.x) {
@@ -415,11 +454,20 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs ka) {
       if (col < c_hi && b < a.nb)
         raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (uint64_t)b * a.cols + col);
       const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+      if constexpr (DOT) {
+        if constexpr (B == 1) {
+          lds_store4(xs + c8 * 16, raw);
+        } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint16_t h = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
-        xs[(8 * c8 + i) * B + b] = a.x_is_bf16 ? __uint_as_float((uint32_t)h << 16)
-                                               : (float)__builtin_bit_cast(_Float16, h);
+          for (int i = 0; i < 4; ++i) *lds_ptr<uint32_t>(xs + ((4 * c8 + i) * B + b) * 4) = w4[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint16_t h = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
+          const float f = a.x_is_bf16 ? __uint_as_float((uint32_t)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+          *lds_ptr<float>(xs + ((8 * c8 + i) * B + b) * 4) = f;
+        }
       }
     }
   }
@@ -427,7 +475,6 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs ka) {
 
   const uint32_t w_sl0 = min(sl_blk + wid * R, sl_blk_end);
   const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
-  const uint32_t w_mid = NSr == 1 ? w_sl1 : w_sl0 + (w_sl1 - w_sl0 + 1) / 2;
   const uint32_t tb = rg * a.n_sl;
   const uint32_t row = rg * 64 + lane;
   const bool active = row < a.rows;
@@ -436,36 +483,23 @@ __global__ void __launch_bounds__(1024) k_decode(const KArgs ka) {
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.f;
   if (w_sl0 < w_sl1) {
-    if constexpr (kTwoCapable) {
-      if (NSr == 2) {
-        if (ragged)
-          wave_body<PAY, CB, KW, B, MAT, true, 2>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_mid, tb + w_mid,
-                                                  tb + w_sl1, c_lo, lane, active, acc);
-        else
-          wave_body<PAY, CB, KW, B, MAT, false, 2>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_mid, tb + w_mid,
-                                                   tb + w_sl1, c_lo, lane, active, acc);
-      }
-    }
-    if (NSr == 1) {
-      if (ragged)
-        wave_body<PAY, CB, KW, B, MAT, true, 1>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, 0, 0, c_lo,
-                                                lane, active, acc);
-      else
-        wave_body<PAY, CB, KW, B, MAT, false, 1>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, 0, 0, c_lo,
-                                                 lane, active, acc);
-    }
+    if (ragged)
+      wave_body<PAY, CB, KW, B, MAT, true, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
+                                                acc);
+    else
+      wave_body<PAY, CB, KW, B, MAT, false, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
+                                                 acc);
   }
   if constexpr (!MAT) {
     // ---- A8: epilogue.  Reuse this wave's first ring as its reduction slot.
-    float* red = reinterpret_cast<float*>(ring);
 #pragma unroll
-    for (int b = 0; b < B; ++b) red[b * 64 + lane] = acc[b];
+    for (int b = 0; b < B; ++b) *lds_ptr<float>(ring + (b * 64 + lane) * 4) = acc[b];
     __syncthreads();
     for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
       const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
       float s = 0.f;
       for (uint32_t w = 0; w < W; ++w)
-        s += reinterpret_cast<const float*>(rings + (w * NSr) * kRingStride)[b * 64 + l];
+        s += *lds_ptr<const float>(rings + w * (2 * kRingStride) + (b * 64 + l) * 4);
       if (a.n_sg == 1) {
         if (r < a.rows && b < a.nb) {
           const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
@@ -516,35 +550,48 @@ __global__ void k_fill_zero(float* y, uint64_t n) {
 // ------------------------------------------------------------------ host launch
 using KernelFn = void (*)(const KArgs);
 
-template <int B, bool MAT>
+template <int B, bool MAT, bool XBF>
 static KernelFn pick_kernel(const ecw_coding& c) {
   switch (c.payload) {
     case ECW_P_INT_CODES:
       switch (c.code_bits * 16 + c.weights_per_symbol) {
-        case 4 * 16 + 1: return k_decode<1, 4, 1, B, MAT>;
-        case 4 * 16 + 2: return k_decode<1, 4, 2, B, MAT>;
-        case 3 * 16 + 1: return k_decode<1, 3, 1, B, MAT>;
-        case 3 * 16 + 2: return k_decode<1, 3, 2, B, MAT>;
-        case 2 * 16 + 1: return k_decode<1, 2, 1, B, MAT>;
-        case 2 * 16 + 2: return k_decode<1, 2, 2, B, MAT>;
-        case 2 * 16 + 4: return k_decode<1, 2, 4, B, MAT>;
+        case 4 * 16 + 1: return k_decode<1, 4, 1, B, MAT, false>;
+        case 4 * 16 + 2: return k_decode<1, 4, 2, B, MAT, XBF>;
+        case 3 * 16 + 1: return k_decode<1, 3, 1, B, MAT, false>;
+        case 3 * 16 + 2: return k_decode<1, 3, 2, B, MAT, XBF>;
+        case 2 * 16 + 1: return k_decode<1, 2, 1, B, MAT, false>;
+        case 2 * 16 + 2: return k_decode<1, 2, 2, B, MAT, XBF>;
+        case 2 * 16 + 4: return k_decode<1, 2, 4, B, MAT, XBF>;
       }
       return nullptr;
-    case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT>;
-    case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT>;
+    case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT, false>;
+    case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT, false>;
   }
   return nullptr;
 }
 
-static uint32_t streams_per_wave(const ecw_coding& c, bool mat, uint32_t R) {
-  return (mat || c.payload == ECW_P_BF16_EXP || c.weights_per_symbol == 4 || R < 2) ? 1 : 2;
+static KernelFn pick_gemv_kernel(const ecw_coding& c, int B, bool xbf) {
+  if (B == 1) return xbf ? pick_kernel<1, false, true>(c) : pick_kernel<1, false, false>(c);
+  return xbf ? pick_kernel<4, false, true>(c) : pick_kernel<4, false, false>(c);
 }
 
-// Dynamic LDS of one block: decode table, staged activations, word rings.
-static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat) {
+static bool dot_path(const ecw_coding& c) {
+  return c.payload == ECW_P_INT_CODES && c.weights_per_symbol >= 2;
+}
+static bool pair_table(const ecw_coding& c, bool xbf) {
+  return c.payload == ECW_P_INT_CODES && (c.weights_per_symbol == 4 || (c.weights_per_symbol == 2 && xbf));
+}
+
+// Dynamic LDS of one block: pair side table, decode table, staged activations,
+// word rings.  Mirrors the layout k_decode computes.
+static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat,
+                          bool xbf) {
+  const bool dot = !mat && dot_path(t->coding);
+  const uint64_t pair = (!mat && pair_table(t->coding, xbf)) ? kPairTableBytes : 0;
   const uint64_t lut = (uint64_t)t->n_tables << t->coding.log2_m;
-  uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * 4 + 15) / 16 * 16;
-  return lut * 8 + xs + (uint64_t)W * streams_per_wave(t->coding, mat, R) * kRingStride * 2;
+  const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
+  (void)R;
+  return pair + lut * 8 + xs + (uint64_t)W * kRingStride * 2;
 }
 
 // Allow each kernel the whole 160 KiB LDS once (a host call, not a stream
@@ -674,7 +721,7 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
     a.block_begin = blocks;
     a.xs_cols = W * t->tiles_per_wave * t->coding.tile_cols;
     blocks += a.n_blocks;
-    lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false));
+    lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false, x_dtype == ECW_DT_BF16));
     if (a.n_sg > 1) {
       a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + woff[i]);
       const uint32_t j = ra.nt++;
@@ -690,7 +737,7 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
   }
   if (ka.nt == 0) return ECW_OK;
   ka.n_blocks = blocks;
-  KernelFn fn = B == 1 ? pick_kernel<1, false>(ts[0]->coding) : pick_kernel<4, false>(ts[0]->coding);
+  KernelFn fn = pick_gemv_kernel(ts[0]->coding, B, x_dtype == ECW_DT_BF16);
   if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
   if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "launch shape needs more than 160 KiB of LDS");
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
@@ -762,9 +809,9 @@ extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, ui
   a.xs_cols = 0;
   ka.nt = 1;
   ka.n_blocks = a.n_blocks;
-  KernelFn fn = pick_kernel<1, true>(t->coding);
+  KernelFn fn = pick_kernel<1, true, false>(t->coding);
   if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
-  const uint64_t lds = lds_bytes(t, W, 1, 0, 1, true);
+  const uint64_t lds = lds_bytes(t, W, 1, 0, 1, true, false);
   if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "decode table needs more than 160 KiB of LDS");
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   const uint32_t grid = (ka.n_blocks + 7) / 8 * 8;

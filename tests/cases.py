@@ -63,6 +63,13 @@ def small_cases():
     cases.append(_int("quad_int2", 70, 256, 4, 2, 10, 128, seed=4))
     cases.append(_int("pair_int3", 64, 192, 2, 3, 8, 64, seed=5))
     cases.append(_int("single_int2", 65, 320, 1, 2, 9, 64, seed=6))
+    # one slice per row group: one-wave blocks (64 threads stage the 256-entry pair table)
+    cases.append(_int("pair_one_wave", 100, 128, 2, 4, 11, 128, seed=13))
+    cases.append(_int("quad_one_wave", 64, 128, 4, 2, 9, 128, seed=14))
+    # bf16 activations on the packed-pair path
+    c = _int("pair_bf16_x", 192, 768, 2, 4, 12, 256, seed=15)
+    c.x_dtype = "bf16"
+    cases.append(c)
     # one symbol only: f = M, the stream holds no words
     q = np.full((96, 256), 3, np.int8)
     cases.append(Case("single_symbol", INT, 96, 256, 1, 4, 12, 128, q, np.full(96, 0.5, np.float16)))

@@ -85,12 +85,23 @@ def test_decode_table_entries_follow_the_frequencies():
     sym = np.repeat(np.arange(256), freq[0])
     assert np.array_equal(lut[:, 0] & 0xFFFFFF, freq[0][sym])
     assert np.array_equal(lut[:, 1] & 0xFFFF, np.arange(lut.shape[0]) - cum[sym])
-    # Pair mode payload: a8 = first code (int8), h16 = fp16 of the second code
-    q0 = (sym & 15) - 8
-    q1 = (sym >> 4) - 8
-    assert np.array_equal((lut[:, 0] >> 24).astype(np.uint8).view(np.int8), q0)
-    h = (lut[:, 1] >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
-    assert np.array_equal(h, q1)
+    # Pair mode payload: a8 = the symbol (first code in the low digit); h16 holds the
+    # high bytes of the two codes' fp16 values (their low bytes are zero)
+    assert np.array_equal(lut[:, 0] >> 24, sym)
+    h = (lut[:, 1] >> 16).astype(np.uint32)
+    f0 = ((h & 0xFF) << 8).astype(np.uint16).view(np.float16).astype(np.float64)
+    f1 = (h & 0xFF00).astype(np.uint16).view(np.float16).astype(np.float64)
+    assert np.array_equal(f0, (sym & 15) - 8)
+    assert np.array_equal(f1, (sym >> 4) - 8)
+    # single-code payload: a8 = the code (int8), h16 = its fp16 value
+    case1 = cases.small_cases()[0]
+    bl1 = blobfmt.parse(ecw.encode(case1.lib_coding(), case1.logical, case1.scales))
+    _, _, freq1 = blobfmt.tables(bl1)
+    lut1 = blobfmt.lut(bl1)[0]
+    sym1 = np.repeat(np.arange(256), freq1[0])
+    q = sym1 - 8
+    assert np.array_equal((lut1[:, 0] >> 24).astype(np.uint8).view(np.int8), q)
+    assert np.array_equal((lut1[:, 1] >> 16).astype(np.uint16).view(np.float16).astype(np.float64), q)
 
 
 def test_fp8_entry_payload_is_the_code_value():
