@@ -108,9 +108,7 @@ struct KArgs {
 // x' = f * (x >> m) + bias in one v_mad_u32_u24 (both factors < 2^24; the payload
 // byte in bits 24..31 of the table word is ignored by the 24-bit multiply).
 __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
+  return __umul24(a, b) + c;
 }
 
 // acc + f16(h >> 16) * x in fp32 (v_fma_mix_f32: operand 0 is the fp16 in the high
@@ -172,7 +170,10 @@ __device__ __forceinline__ void renorm_step(uint32_t& x, uint32_t& rposb, uint32
   const uint32_t base = ring + (rposb & (2 * kRing - 2));
   const uint32_t w = *lds_ptr<const uint16_t>(base + (lanes_below(msk) << 1));
   x = shift_in(msk, x, w);
-  rposb += (uint32_t)__popcll(msk) << 1;
+  // rposb += 2 * popcount(mask) as one scalar op (kept opaque so the compiler does
+  // not rebuild the pointer from a running count every step)
+  const uint32_t cnt = (uint32_t)__popcll(msk);
+  asm("s_lshl1_add_u32 %0, %1, %0" : "+s"(rposb) : "s"(cnt) : "scc");
 }
 
 // Keep the next four steps' reads inside committed ring data: commit the chunk held
@@ -533,11 +534,20 @@ __global__ void __launch_bounds__(256) k_reduce(const RArgs ra) {
     if (gi >= ra.row_begin[i]) ti = i;
   const uint32_t r = gi - ra.row_begin[ti], rg = r >> 6, l = r & 63, n_sg = ra.n_sg[ti];
   const float sc = ra.unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, ra.scales[ti][r]);
+  const float* p = ra.partials[ti] + (uint64_t)rg * n_sg * B * 64 + l;
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     if ((uint32_t)b >= ra.nb) break;
+    // loads of up to 8 partials are issued together, then summed in block order
     float s = 0.f;
-    for (uint32_t g = 0; g < n_sg; ++g) s += ra.partials[ti][(((uint64_t)rg * n_sg + g) * B + b) * 64 + l];
+    for (uint32_t g0 = 0; g0 < n_sg; g0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (g0 + i < n_sg) ? p[((uint64_t)(g0 + i) * B + b) * 64] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (g0 + i < n_sg) s += v[i];
+    }
     ra.y[ti][(uint64_t)b * ra.rows[ti] + r] = s * sc;
   }
 }
