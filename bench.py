@@ -29,10 +29,53 @@ ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
 # launches of one decode step, in data-flow order; tensors of a launch share x
 LAUNCHES = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
 
-# per-tensor coding: (log2_m, tile_cols, waves_per_block, tiles_per_wave)
-DEFAULT_CODING = {"q": (12, 128, 16, 1), "k": (12, 128, 16, 1), "v": (12, 128, 16, 1),
-                  "o": (12, 128, 16, 1), "gate": (12, 256, 16, 1), "up": (12, 256, 16, 1),
-                  "down": (12, 256, 16, 1)}
+# per-tensor coding: (k, log2_m, tile_cols, waves_per_block, tiles_per_wave).  Used
+# when no tune file exists; `--tune` measures every candidate on the device and
+# writes TUNE_FILE, which later runs load.
+DEFAULT_CODING = {"q": (2, 12, 128, 16, 1), "k": (2, 12, 128, 16, 1), "v": (2, 12, 128, 16, 1),
+                  "o": (2, 12, 128, 16, 1), "gate": (2, 12, 256, 16, 1), "up": (2, 12, 256, 16, 1),
+                  "down": (2, 12, 256, 16, 1)}
+TUNE_FILE = os.path.join(ROOT, "entropy_coded_weight_amd", "tuned", "llama8b_int4_laplace_batch1.json")
+
+
+def load_coding(path: str):
+    if not os.path.exists(path):
+        return dict(DEFAULT_CODING), "defaults"
+    with open(path) as f:
+        d = json.load(f)
+    coding = dict(DEFAULT_CODING)
+    for n, p in d["picks"].items():
+        coding[n] = (p["k"], p["log2_m"], p["tile_cols"], p["waves_per_block"], p["tiles_per_wave"])
+    return coding, os.path.relpath(path, ROOT)
+
+
+def run_tuner(path: str, batch: int):
+    """Autotune every tensor of the layer set (k in {1, 2}, M in {2^10, 2^11, 2^12},
+    tile width in {64..512}, waves per block, tiles per wave) and write the picks."""
+    import torch
+    import ecw_inputs as E
+    from entropy_coded_weight_amd import autotune as A, INT_CODES
+    cands, specs, xs = {}, {}, {}
+    for name in ORDER:
+        t = E.config2_tensor(name, layer=0, batch=batch)
+        xs[name] = torch.from_numpy(t.x).cuda()
+        specs[name] = (INT_CODES, t.codes, t.scales, 4)
+        log(f"tuning {name} {t.codes.shape}")
+        cands[name] = A.tune_tensor(INT_CODES, t.codes, t.scales, xs[name], code_bits=4, ks=(1, 2), log=log)
+    picks = {}
+    for ln, names in LAUNCHES:
+        log(f"tuning launch {ln}")
+        g = A.tune_group({n: specs[n] for n in names}, {n: cands[n] for n in names}, xs[names[0]], log=log)
+        picks.update(g)
+    table = {n: [dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, stored_bytes=c.stored_bytes,
+                      shapes={f"{w}x{r}": round(us, 3) for (w, r), us in c.shape_us.items()})
+                 for c in cands[n]] for n in ORDER}
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump({"workload": "Llama-3.1-8B-shaped layer set, 16-level Laplacian codes (H=2.2 bits), "
+                               f"fp16 row scales, fp16 x, batch {batch}",
+                   "device": torch.cuda.get_device_name(0), "picks": picks, "candidates": table}, f, indent=1)
+    log(f"wrote {path}")
 
 
 def log(*a):
@@ -45,9 +88,9 @@ def build_layer(batch: int, coding: dict):
     layer = {}
     for name in ORDER:
         t = E.config2_tensor(name, layer=0, batch=batch)
-        m, tc, W, R = coding[name]
+        kk, m, tc, W, R = coding[name]
         n, k = t.codes.shape
-        c = ecw.Coding(ecw.INT_CODES, n, k, 2, 4, m, tc)
+        c = ecw.Coding(ecw.INT_CODES, n, k, kk, 4, m, tc)
         blob = ecw.encode(c, t.codes, t.scales)
         layer[name] = dict(tensor=t, coding=c, blob=blob, launch=(W, R))
     return layer
@@ -61,7 +104,7 @@ def cpu_baseline(layer, target_s: float = 12.0):
     from oracle import gemv as G, pipeline as P
     done_syms, total_syms, t_used, rows_done = 0, 0, 0.0, 0
     for name in ORDER:
-        total_syms += layer[name]["tensor"].codes.size // 2
+        total_syms += layer[name]["tensor"].codes.size // layer[name]["coding"].weights_per_symbol
     with threadpool_limits(limits=1):
         rg = 0
         while t_used < target_s and rg < 64:
@@ -72,7 +115,8 @@ def cpu_baseline(layer, target_s: float = 12.0):
                 if r0 >= n:
                     continue
                 c = layer[name]["coding"]
-                ocd = P.Coding(P.INT_CODES, r1 - r0, K, k=2, code_bits=4, log2_m=c.log2_m,
+                kk = c.weights_per_symbol
+                ocd = P.Coding(P.INT_CODES, r1 - r0, K, k=kk, code_bits=4, log2_m=c.log2_m,
                                tile_cols=c.tile_cols)
                 comp = P.encode(ocd, t.codes[r0:r1], t.scales[r0:r1])
                 t0 = time.perf_counter()
@@ -80,7 +124,7 @@ def cpu_baseline(layer, target_s: float = 12.0):
                 wv = P.weight_values(ocd, q, t.scales[r0:r1])
                 G.gemv_f64(wv, G.x_values(t.x, "f16"))
                 t_used += time.perf_counter() - t0
-                done_syms += q.size // 2
+                done_syms += q.size // kk
                 rows_done += r1 - r0
             rg += 1
     us_layer = t_used / done_syms * total_syms * 1e6
@@ -101,6 +145,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="after timing, run N plain device copies of 64 MiB (a kernel of known "
                          "traffic that scales the profiler's FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--tune", action="store_true",
+                    help="autotune every tensor on this device first and rewrite the tune file")
+    ap.add_argument("--tune-file", default=TUNE_FILE)
     ap.add_argument("--tensors", default=",".join(ORDER),
                     help="subset of the layer to run (profiling); the JSON line is only "
                          "meaningful for the full set")
@@ -115,13 +162,16 @@ def main():
     from oracle import gemv as G, pipeline as P
 
     ORDER[:] = [n for n in ORDER if n in args.tensors.split(",")]
-    dev = torch.device("cuda:0")
-    t_build = time.time()
-    layer = build_layer(args.batch, DEFAULT_CODING)
-    log(f"encoded layer set in {time.time() - t_build:.1f} s")
     global LAUNCHES
     LAUNCHES = [(ln, [n for n in names if n in ORDER]) for ln, names in LAUNCHES]
     LAUNCHES = [(ln, names) for ln, names in LAUNCHES if names]
+    dev = torch.device("cuda:0")
+    if args.tune:
+        run_tuner(args.tune_file, args.batch)
+    coding, coding_src = load_coding(args.tune_file)
+    t_build = time.time()
+    layer = build_layer(args.batch, coding)
+    log(f"encoded layer set in {time.time() - t_build:.1f} s (codings: {coding_src})")
     stored = {}
     for name in ORDER:
         stored[name] = ecw.prepare(layer[name]["blob"]).blob_bytes
@@ -240,11 +290,12 @@ def main():
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "u32 decode + f32 accumulate", "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B-shaped layer set (q,k,v,o,gate,up,down) of 16-level "
-                               "Laplacian codes (H=2.2 bits), 2 codes per rANS symbol, fp16 row "
+                               "Laplacian codes (H=2.2 bits), autotuned codes per rANS symbol, fp16 row "
                                "scales, fp16 x, batch 1, cold cache; 4 launches per step "
                                "(q/k/v, o, gate/up, down)",
-                   "batch": args.batch, "copies_rotated": copies,
-                   "codings": {n: dict(log2_m=layer[n]["coding"].log2_m,
+                   "batch": args.batch, "copies_rotated": copies, "codings_from": coding_src,
+                   "codings": {n: dict(k=layer[n]["coding"].weights_per_symbol,
+                                       log2_m=layer[n]["coding"].log2_m,
                                        tile_cols=layer[n]["coding"].tile_cols,
                                        waves_per_block=layer[n]["launch"][0],
                                        tiles_per_wave=layer[n]["launch"][1]) for n in ORDER}},
@@ -255,7 +306,8 @@ def main():
         "per_launch_us": {ln: round(v, 3) for ln, v in avg_us.items()},
         "host_wall_s": round(host_s, 3),
         "parity_worst_err_over_bound": worst,
-        "roofline": {"bound": "hbm", "kernel": f"k_decode<INT4 pair> launch {dom}",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"k_decode<INT4 k={layer[LAUNCHES[[l for l, _ in LAUNCHES].index(dom)][1][0]]['coding'].weights_per_symbol}> launch {dom}",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": int(launch_bytes[dom]), "avg_launch_us": round(avg_us[dom], 3)},

@@ -97,8 +97,13 @@ def lib():
     L.dec_materialize.argtypes = [vp, P(Tensor), vp, vp, vp]
     L.dec_gemv_group_workspace_size.argtypes = [P(P(Tensor)), i32, i32, P(sz)]
     L.dec_gemv_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz]
+    L.dec_tune_launch.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz, P(u32), i32, i32,
+                                  P(ctypes.c_float)]
+    L.dec_time_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz, i32,
+                                 P(ctypes.c_float)]
     for f in ("enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
-              "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize"):
+              "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize",
+              "dec_tune_launch", "dec_time_group"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []
     L.ecw_last_error.restype = ctypes.c_char_p

@@ -1,0 +1,207 @@
+"""Per-tensor autotuner: weights per symbol, table size, tile width and launch shape.
+
+The coding axes (weights per symbol k, table size M = 2^m, tile width) change the
+stored blob, so each candidate is encoded on the host through the C ABI.  The launch
+axes (waves per block, tiles per wave) are timed on the device by the library's
+dec_tune_launch, which replays each shape as a captured HIP graph.  The fastest
+candidate wins; when two are within `tie` of each other the smaller blob wins.  This
+is the per-tensor tuning the MINE page describes (Section 4.2: tile width, table
+size and symbol packing chosen per tensor by measurement, with the cross-entropy
+size as the tie-breaker).
+
+Tensors that share a launch (q/k/v, gate/up) must agree on waves per block;
+tune_group times the real grouped launch for combinations of each member's best
+single-tensor candidates at each common value.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+
+import torch
+
+from . import (INT_CODES, BF16_EXP, FP8_E4M3, Coding, CompressedTensor, EcwError, encode, lib,
+               workspace_size, _check, DT_F16, DT_BF16)
+
+DEFAULT_LOG2_M = (10, 11, 12)
+DEFAULT_TILE_COLS = (64, 128, 256, 512)
+DEFAULT_SHAPES = tuple((w, r) for w in (4, 8, 16) for r in (1, 2, 4))
+
+
+@dataclass
+class Candidate:
+    k: int
+    log2_m: int
+    tile_cols: int
+    stored_bytes: int
+    shape_us: dict = field(default_factory=dict)     # (W, R) -> us per call (launchable shapes)
+
+    def best(self, waves=None):
+        items = [(us, s) for s, us in self.shape_us.items() if waves is None or s[0] == waves]
+        return min(items) if items else (float("inf"), None)
+
+
+def legal_ks(payload: int, code_bits: int, ks=None):
+    if payload != INT_CODES:
+        return (1,)
+    out = [k for k in (1, 2, 4) if code_bits * k <= 8]
+    return tuple(k for k in out if ks is None or k in ks)
+
+
+def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT_LOG2_M,
+                      tile_cols=DEFAULT_TILE_COLS):
+    """Every (k, m, tile width) the format accepts for this tensor."""
+    for k in legal_ks(payload, code_bits, ks):
+        for m in log2_ms:
+            for tc in tile_cols:
+                if tc % 64 or tc % (8 * k) or tc > max(64, ((cols + 63) // 64) * 64):
+                    continue
+                yield k, m, tc
+
+
+def _tune_launch(ct: CompressedTensor, x: torch.Tensor, shapes, reps: int, stream: torch.cuda.Stream):
+    batch = x.shape[0]
+    ws_need = 0
+    for w, r in shapes:
+        ct.set_launch(w, r)
+        ws_need = max(ws_need, workspace_size(ct.t, batch))
+    ws = torch.zeros(max(ws_need, 1), dtype=torch.uint8, device=x.device)
+    y = torch.empty((batch, ct.rows), dtype=torch.float32, device=x.device)
+    flat = (ctypes.c_uint32 * (2 * len(shapes)))(*[v for s in shapes for v in s])
+    us = (ctypes.c_float * len(shapes))()
+    xd = DT_F16 if x.dtype == torch.float16 else DT_BF16
+    _check(lib().dec_tune_launch(ctypes.c_void_p(stream.cuda_stream), ctypes.byref(ct.t), x.data_ptr(), xd,
+                                 y.data_ptr(), batch, ws.data_ptr(), ws.numel(), flat, len(shapes), reps, us),
+           "dec_tune_launch")
+    return {tuple(s): float(u) for s, u in zip(shapes, us) if u >= 0}
+
+
+def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks=None,
+                log2_ms=DEFAULT_LOG2_M, tile_cols=DEFAULT_TILE_COLS, shapes=DEFAULT_SHAPES,
+                reps: int = 20, log=None):
+    """Search the codings of one logical tensor `w` (host array as enc_encode takes it)
+    with activations `x` (device [batch, cols]).  Returns the list of Candidates."""
+    rows, cols = w.shape
+    stream = torch.cuda.Stream()
+    out = []
+    for k, m, tc in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols):
+        c = Coding(payload, rows, cols, k, code_bits if payload == INT_CODES else 0, m, tc)
+        try:
+            blob = encode(c, w, scales)
+        except EcwError:
+            continue          # e.g. more distinct symbols than table slots
+        ct = CompressedTensor(blob)
+        cand = Candidate(k, m, tc, ct.stored_bytes())
+        with torch.cuda.stream(stream):
+            cand.shape_us = _tune_launch(ct, x, shapes, reps, stream)
+        stream.synchronize()
+        if log:
+            us, s = cand.best()
+            log(f"  k={k} m={m} tc={tc:4d} stored={cand.stored_bytes / 1e6:8.3f} MB best {s} {us:8.2f} us")
+        out.append(cand)
+        del ct
+    return out
+
+
+def pick(cands, waves=None, tie: float = 0.02):
+    """Fastest candidate (optionally restricted to one waves-per-block value); within
+    `tie` of the fastest, the smallest blob."""
+    scored = [(c.best(waves), c) for c in cands]
+    scored = [(us, s, c) for (us, s), c in scored if s is not None]
+    if not scored:
+        return None
+    t_min = min(us for us, _, _ in scored)
+    near = [(c.stored_bytes, us, s, c) for us, s, c in scored if us <= t_min * (1 + tie)]
+    near.sort(key=lambda v: (v[0], v[1]))
+    _, us, s, c = near[0]
+    return dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
+                us=us, stored_bytes=c.stored_bytes)
+
+
+def time_group(cts, x: torch.Tensor, reps: int = 20, stream: torch.cuda.Stream | None = None) -> float:
+    """Microseconds per grouped launch of CompressedTensors `cts` (current launch
+    shapes), timed natively as a captured graph (dec_time_group)."""
+    from . import GemvGroup, _tensor_array
+    stream = stream or torch.cuda.Stream()
+    grp = GemvGroup(cts)
+    ys = [torch.empty((x.shape[0], c.rows), dtype=torch.float32, device=x.device) for c in cts]
+    ws = grp.workspace(x.shape[0])
+    yarr = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    us = ctypes.c_float(0)
+    xd = DT_F16 if x.dtype == torch.float16 else DT_BF16
+    with torch.cuda.stream(stream):
+        _check(lib().dec_time_group(ctypes.c_void_p(stream.cuda_stream), _tensor_array([c.t for c in cts]),
+                                    len(cts), x.data_ptr(), xd, yarr, x.shape[0],
+                                    ws.data_ptr() if ws is not None else None,
+                                    ws.numel() if ws is not None else 0, reps, ctypes.byref(us)),
+               "dec_time_group")
+    stream.synchronize()
+    return us.value
+
+
+def _ranked(cands, waves, top):
+    """The `top` fastest (candidate, shape) pairs at a given waves per block."""
+    items = []
+    for c in cands:
+        for s, us in c.shape_us.items():
+            if s[0] == waves:
+                items.append((us, c.stored_bytes, id(c), c, s))
+    items.sort(key=lambda v: (v[0], v[1]))
+    out, seen = [], set()
+    for us, _, cid, c, s in items:
+        if cid not in seen:
+            seen.add(cid)
+            out.append((c, s))
+        if len(out) == top:
+            break
+    return out
+
+
+def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | None = None, reps: int = 20,
+               tie: float = 0.02, log=None):
+    """Tensors sharing one launch (same activations) must share waves per block.  For
+    each common waves-per-block value, every combination of each member's `top`
+    fastest single-tensor candidates at that value is timed as the real grouped
+    launch; the fastest group wins (ties within `tie`: fewer stored bytes).
+    specs[name] = (payload, w, scales, code_bits) re-encodes a candidate.  By default
+    `top` keeps the number of timed combinations near 16 per waves-per-block value."""
+    import itertools
+    names = list(cands_by_name)
+    if top is None:
+        top = {1: 16, 2: 4, 3: 2}.get(len(names), 1)
+    if len(names) == 1:
+        return {names[0]: pick(cands_by_name[names[0]], tie=tie)}
+    waves = sorted({s[0] for n in names for c in cands_by_name[n] for s in c.shape_us})
+    stream = torch.cuda.Stream()
+    blobs = {}
+
+    def tensor_for(name, c, shape):
+        key = (name, c.k, c.log2_m, c.tile_cols)
+        if key not in blobs:
+            payload, w, scales, cb = specs[name]
+            coding = Coding(payload, w.shape[0], w.shape[1], c.k, cb if payload == INT_CODES else 0,
+                            c.log2_m, c.tile_cols)
+            blobs[key] = encode(coding, w, scales)
+        return CompressedTensor(blobs[key], waves_per_block=shape[0], tiles_per_wave=shape[1])
+
+    results = []
+    for w in waves:
+        ranked = [_ranked(cands_by_name[n], w, top) for n in names]
+        if any(not r for r in ranked):
+            continue
+        for combo in itertools.product(*ranked):
+            cts = [tensor_for(n, c, s) for n, (c, s) in zip(names, combo)]
+            us = time_group(cts, x, reps, stream)
+            nbytes = sum(c.stored_bytes for c, _ in combo)
+            results.append((us, nbytes, combo))
+            if log:
+                log(f"  group W={w}: " + ", ".join(f"{n}:m={c.log2_m},tc={c.tile_cols},R={s[1]}"
+                                                   for n, (c, s) in zip(names, combo)) + f" -> {us:.2f} us")
+            del cts
+    if not results:
+        return None
+    t_min = min(r[0] for r in results)
+    near = sorted([r for r in results if r[0] <= t_min * (1 + tie)], key=lambda r: (r[1], r[0]))
+    us, _, combo = near[0]
+    return {n: dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
+                    us=round(us, 3), stored_bytes=c.stored_bytes) for n, (c, s) in zip(names, combo)}

@@ -799,6 +799,90 @@ extern "C" ecw_status dec_gemv_group(ecw_stream stream, const ecw_tensor* const*
   return launch_group(stream, t, n, x, x_dtype, y, batch, workspace, ws_bytes);
 }
 
+// Mean microseconds per call of `reps` grouped launches captured as one graph (so
+// host launch cost is not measured); one warm-up replay first.
+static ecw_status time_group(ecw_stream stream, const ecw_tensor* const* ts, int n, const void* x, int x_dtype,
+                             float* const* ys, int batch, void* ws, size_t ws_bytes, int reps, float* us) {
+  hipStream_t s = (hipStream_t)stream;
+  // a direct call first: reports an unlaunchable group with its own status
+  ecw_status st = launch_group(stream, ts, n, x, x_dtype, ys, batch, ws, ws_bytes);
+  if (st != ECW_OK) return st;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(ECW_E_HIP, "hipEventCreate failed");
+  }
+  hipGraph_t g = nullptr;
+  hipGraphExec_t ge = nullptr;
+  bool ok = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) == hipSuccess;
+  bool launched = ok;
+  for (int r = 0; launched && r < reps; ++r)
+    launched = launch_group(stream, ts, n, x, x_dtype, ys, batch, ws, ws_bytes) == ECW_OK;
+  if (ok) ok = hipStreamEndCapture(s, &g) == hipSuccess && launched;
+  float ms = 0.f;
+  ok = ok && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) == hipSuccess;
+  ok = ok && hipGraphLaunch(ge, s) == hipSuccess;
+  ok = ok && hipEventRecord(e0, s) == hipSuccess;
+  ok = ok && hipGraphLaunch(ge, s) == hipSuccess;
+  ok = ok && hipEventRecord(e1, s) == hipSuccess;
+  ok = ok && hipEventSynchronize(e1) == hipSuccess;
+  ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+  if (ge) (void)hipGraphExecDestroy(ge);
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (!ok) return fail(ECW_E_HIP, "timing a captured launch failed");
+  *us = ms * 1000.f / (float)reps;
+  return ECW_OK;
+}
+
+extern "C" ecw_status dec_time_group(ecw_stream stream, const ecw_tensor* const* t, int n, const void* x,
+                                     int x_dtype, float* const* y, int batch, void* workspace, size_t ws_bytes,
+                                     int reps, float* us_out) {
+  clear_error();
+  if (!us_out || reps < 1 || reps > 1000) return fail(ECW_E_INVALID_ARG, "bad timing arguments");
+  if (!stream) return fail(ECW_E_INVALID_ARG, "timing captures a graph: pass a created stream, not the default one");
+  return time_group(stream, t, n, x, x_dtype, y, batch, workspace, ws_bytes, reps, us_out);
+}
+
+// Times each candidate launch shape of one tensor and keeps the fastest.
+extern "C" ecw_status dec_tune_launch(ecw_stream stream, ecw_tensor* t, const void* x, int x_dtype, float* y,
+                                      int batch, void* workspace, size_t ws_bytes, const uint32_t* shapes,
+                                      int n_shapes, int reps, float* us_out) {
+  clear_error();
+  if (!t || !shapes || !us_out || n_shapes < 1 || reps < 1 || reps > 1000)
+    return fail(ECW_E_INVALID_ARG, "bad tuning arguments");
+  if (!stream) return fail(ECW_E_INVALID_ARG, "tuning captures a graph: pass a created stream, not the default one");
+  const uint32_t W0 = t->waves_per_block, R0 = t->tiles_per_wave;
+  float best = -1.f;
+  uint32_t bestW = W0, bestR = R0;
+  ecw_status result = ECW_OK;
+  for (int i = 0; i < n_shapes; ++i) {
+    us_out[i] = -1.f;
+    t->waves_per_block = shapes[2 * i];
+    t->tiles_per_wave = shapes[2 * i + 1];
+    float us = 0.f;
+    const ecw_status st = time_group(stream, &t, 1, x, x_dtype, &y, batch, workspace, ws_bytes, reps, &us);
+    if (st == ECW_E_HIP) {
+      result = st;
+      break;
+    }
+    if (st != ECW_OK) continue;                 // shape not launchable: skipped
+    us_out[i] = us;
+    if (best < 0.f || us < best) {
+      best = us;
+      bestW = t->waves_per_block;
+      bestR = t->tiles_per_wave;
+    }
+  }
+  t->waves_per_block = bestW;
+  t->tiles_per_wave = bestR;
+  if (result != ECW_OK) return result;
+  if (best < 0.f) return fail(ECW_E_INVALID_ARG, "no launchable candidate shape");
+  clear_error();
+  return ECW_OK;
+}
+
 extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, uint16_t* symbols,
                                       void* w_out, uint32_t* tile_status) {
   clear_error();

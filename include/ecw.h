@@ -159,6 +159,29 @@ ecw_status dec_gemv_group(ecw_stream stream, const ecw_tensor* const* t, int n, 
                           int x_dtype, float* const* y, int batch, void* workspace,
                           size_t workspace_bytes);
 
+/* Launch-shape autotuning for one tensor (MINE page, Section 4.2: per-tensor
+ * tuning of the kernel configuration by measured time).  For each candidate shape
+ * shapes[2i] = waves_per_block, shapes[2i+1] = tiles_per_wave, the fused GEMV is
+ * captured `reps` times into a HIP graph on `stream` and replayed; us_out[i] receives
+ * the mean microseconds per call, or -1 when the shape is not launchable (e.g. it
+ * needs more than 160 KiB of LDS).  x, y, batch as for dec_gemv; the workspace must
+ * hold the largest dec_gemv_workspace_size over the candidates.  On return t's
+ * launch shape is the fastest candidate.  Host-blocking (synchronises the stream);
+ * not itself capturable.  Errors: INVALID_ARG (bad arguments, no launchable
+ * candidate or a NULL stream, which cannot be captured), HIP. */
+ecw_status dec_tune_launch(ecw_stream stream, ecw_tensor* t, const void* x, int x_dtype, float* y,
+                           int batch, void* workspace, size_t workspace_bytes,
+                           const uint32_t* shapes, int n_shapes, int reps, float* us_out);
+
+/* Time a grouped launch as tuned: `reps` dec_gemv_group calls with the tensors'
+ * current launch shapes are captured into a HIP graph on `stream` (not the NULL
+ * stream) and replayed once after a warm-up replay; *us_out = microseconds per call.
+ * Arguments otherwise as dec_gemv_group.  Host-blocking.  Errors: INVALID_ARG, HIP,
+ * and whatever dec_gemv_group returns for the group. */
+ecw_status dec_time_group(ecw_stream stream, const ecw_tensor* const* t, int n, const void* x, int x_dtype,
+                          float* const* y, int batch, void* workspace, size_t workspace_bytes, int reps,
+                          float* us_out);
+
 /* Test hook: the same decode core, writing what dec_gemv keeps in registers.
  *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices);
  *   w_out: nullable device [rows][cols] in the logical dtype (INT int8 codes, BF16

@@ -1,0 +1,85 @@
+"""Autotuner: candidate enumeration and selection rules (CPU), device timing (GPU)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import entropy_coded_weight_amd as ecw
+from entropy_coded_weight_amd import autotune as A
+from tests import cases
+
+
+def test_candidates_respect_the_format():
+    got = list(A.coding_candidates(ecw.INT_CODES, 256, 1024, code_bits=4))
+    # 16-level codes: k = 4 would need 16-bit symbols; tile widths must be multiples
+    # of 64 and of 8k
+    assert {k for k, _, _ in got} == {1, 2}
+    assert all(tc % 64 == 0 for _, _, tc in got)
+    assert len(got) == 2 * 3 * 4
+    got2 = list(A.coding_candidates(ecw.INT_CODES, 64, 256, code_bits=2, log2_ms=(10,), tile_cols=(64, 128)))
+    assert {k for k, _, _ in got2} == {1, 2, 4}
+    # tiles wider than the (64-rounded) row are pointless
+    assert all(tc <= 256 for _, _, tc in got2)
+    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256)]
+
+
+def _cand(k, m, tc, nbytes, shapes):
+    c = A.Candidate(k, m, tc, nbytes)
+    c.shape_us = shapes
+    return c
+
+
+def test_pick_prefers_speed_then_size_within_tie():
+    a = _cand(2, 12, 128, 1000, {(16, 1): 10.0, (8, 1): 12.0})
+    b = _cand(2, 11, 128, 900, {(16, 1): 10.1})          # within 2%, smaller: wins
+    c = _cand(2, 10, 128, 500, {(16, 1): 11.0})          # 10% slower: loses despite size
+    p = A.pick([a, b, c])
+    assert (p["log2_m"], p["waves_per_block"], p["stored_bytes"]) == (11, 16, 900)
+    p8 = A.pick([a, b, c], waves=8)
+    assert (p8["log2_m"], p8["waves_per_block"]) == (12, 8)
+    assert A.pick([_cand(2, 12, 64, 1, {})]) is None
+
+
+def test_ranked_takes_the_fastest_shapes_per_candidate():
+    a = _cand(2, 12, 128, 1, {(16, 1): 10.0, (16, 2): 9.0, (8, 1): 11.0})
+    b = _cand(2, 11, 128, 1, {(16, 1): 9.5})
+    r = A._ranked([a, b], 16, 2)
+    assert [(c.log2_m, s) for c, s in r] == [(12, (16, 2)), (11, (16, 1))]
+    assert A._ranked([a, b], 4, 2) == []
+
+
+def test_tune_rejects_null_stream_without_launching():
+    case = cases.small_cases()[1]
+    ct = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    us = (ctypes.c_float * 1)()
+    shapes = (ctypes.c_uint32 * 2)(4, 1)
+    st = ecw.lib().dec_tune_launch(None, ctypes.byref(ct), None, ecw.DT_F16, None, 1, None, 0, shapes, 1, 5, us)
+    assert st == 1   # ECW_E_INVALID_ARG
+
+
+@pytest.mark.gpu
+def test_device_tuning_picks_a_shape_that_stays_correct():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oracle import gemv, pipeline as P
+    case = cases._int("tune", 256, 2048, 2, 4, 11, 128, seed=21)
+    rng = np.random.default_rng([0, 901])
+    xh = rng.standard_normal((1, case.cols)).astype(np.float16)
+    x = torch.from_numpy(xh).cuda()
+    cands = A.tune_tensor(ecw.INT_CODES, case.logical, case.scales, x, code_bits=4, ks=(2,),
+                          log2_ms=(11, 12), tile_cols=(128, 256), shapes=((4, 1), (8, 1), (16, 2)), reps=5)
+    assert len(cands) == 4 and all(c.shape_us for c in cands)
+    # a two-member group of the same tensor shares one waves-per-block value
+    g = A.tune_group({"a": (ecw.INT_CODES, case.logical, case.scales, 4),
+                      "b": (ecw.INT_CODES, case.logical, case.scales, 4)}, {"a": cands, "b": cands}, x,
+                     top=1, reps=5)
+    assert g["a"]["waves_per_block"] == g["b"]["waves_per_block"]
+    p = A.pick(cands)
+    c = ecw.Coding(ecw.INT_CODES, case.rows, case.cols, p["k"], 4, p["log2_m"], p["tile_cols"])
+    ct = ecw.CompressedTensor(ecw.encode(c, case.logical, case.scales),
+                              waves_per_block=p["waves_per_block"], tiles_per_wave=p["tiles_per_wave"])
+    y = ct.gemv(x).cpu().numpy()
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    ok, worst = gemv.check(y, wv, gemv.x_values(xh, "f16"))
+    assert ok, worst
