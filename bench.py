@@ -36,6 +36,7 @@ DEFAULT_CODING = {"q": (2, 12, 128, 16, 1), "k": (2, 12, 128, 16, 1), "v": (2, 1
                   "o": (2, 12, 128, 16, 1), "gate": (2, 12, 256, 16, 1), "up": (2, 12, 256, 16, 1),
                   "down": (2, 12, 256, 16, 1)}
 TUNE_FILE = os.path.join(ROOT, "entropy_coded_weight_amd", "tuned", "llama8b_int4_laplace_batch1.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_llama8b_int4_gate_up_traffic.txt")
 
 
 def load_coding(path: str):
@@ -105,9 +106,10 @@ def cpu_baseline(layer, target_s: float = 12.0):
     done_syms, total_syms, t_used, rows_done = 0, 0, 0.0, 0
     for name in ORDER:
         total_syms += layer[name]["tensor"].codes.size // layer[name]["coding"].weights_per_symbol
+    max_rg = max((layer[n]["tensor"].codes.shape[0] + 63) // 64 for n in ORDER)
     with threadpool_limits(limits=1):
         rg = 0
-        while t_used < target_s and rg < 64:
+        while t_used < target_s and rg < max_rg:
             for name in ORDER:
                 t = layer[name]["tensor"]
                 n, K = t.codes.shape
@@ -134,6 +136,56 @@ def cpu_baseline(layer, target_s: float = 12.0):
                       f"scaled to the full layer by symbol count"}
 
 
+def summarize_rocprof(directory: str):
+    """Print per-(kernel, grid size) averages from rocprofv3 CSV output under
+    `directory`: kernel durations from *_kernel_trace.csv and counter values from
+    *_counter_collection.csv (one line per kernel and counter)."""
+    import csv
+    import collections
+    import glob
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*_kernel_trace.csv"), recursive=True)):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size_X"]))
+            d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"# kernel durations from {os.path.relpath(path, directory)}")
+        print(f"{'kernel':48s} {'grid':>8s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s}")
+        for (k, g), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+            v.sort()
+            print(f"{k[:48]:48s} {g:8d} {len(v):6d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} {v[0]:8.2f}")
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True)):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size"]))
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for did, cs in per.items():
+            for c, v in cs.items():
+                agg[names[did]][c].append(v)
+        print(f"# counters from {os.path.relpath(path, directory)} (mean per dispatch)")
+        for (k, g), cs in sorted(agg.items()):
+            for c, v in sorted(cs.items()):
+                print(f"{k[:48]:48s} {g:8d} {c:24s} n={len(v):4d} {sum(v) / len(v):16.1f}")
+
+
+def measured_traffic(path: str):
+    """HBM bytes per launch of the dominant launch from a committed profile record,
+    valid only while the kernel source and tune file hash to what was profiled."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    rec = dict(l.split("=", 1) for l in open(path).read().split("\n") if "=" in l and not l.startswith("#"))
+    rec = {k.strip(): v.strip() for k, v in rec.items()}
+    def sha(p):
+        return hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest()
+    if rec.get("kernel_sha256") != sha("entropy_coded_weight_amd/csrc/ecw_kernels.hip"):
+        return None
+    if rec.get("tune_sha256") != sha(os.path.relpath(TUNE_FILE, ROOT)):
+        return None
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,10 +200,15 @@ def main():
     ap.add_argument("--tune", action="store_true",
                     help="autotune every tensor on this device first and rewrite the tune file")
     ap.add_argument("--tune-file", default=TUNE_FILE)
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="print per-launch averages of rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--tensors", default=",".join(ORDER),
                     help="subset of the layer to run (profiling); the JSON line is only "
                          "meaningful for the full set")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
@@ -278,6 +335,13 @@ def main():
             + layer[names[0]]["tensor"].x.size * 2
     dom = max(avg_us, key=lambda ln: avg_us[ln])
     achieved = launch_bytes[dom] / (avg_us[dom] * 1e-6) / 1e9
+    # measured HBM traffic of that launch (calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE),
+    # if the committed record still describes this kernel and these codings
+    dom_names = dict(LAUNCHES)[dom]
+    dom_label = (f"k_decode<INT4, {layer[dom_names[0]]['coding'].weights_per_symbol} codes/symbol>"
+                 + (" + k_reduce" if wss[0][dom] is not None else "") + f" (launch {dom}: {'+'.join(dom_names)})")
+    rec = measured_traffic(TRAFFIC_FILE) if args.tune_file == TUNE_FILE and args.batch == 1 else None
+    traffic = int(rec["traffic_bytes"]) if rec and rec.get("launch") == dom else None
     for n in ORDER:
         c = layer[n]["coding"]
         log(f"{n:5s} {layer[n]['tensor'].codes.shape} m={c.log2_m} tc={c.tile_cols} "
@@ -306,10 +370,9 @@ def main():
         "per_launch_us": {ln: round(v, 3) for ln, v in avg_us.items()},
         "host_wall_s": round(host_s, 3),
         "parity_worst_err_over_bound": worst,
-        "roofline": {"bound": "hbm",
-                     "kernel": f"k_decode<INT4 k={layer[LAUNCHES[[l for l, _ in LAUNCHES].index(dom)][1][0]]['coding'].weights_per_symbol}> launch {dom}",
+        "roofline": {"bound": "hbm", "kernel": dom_label,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(launch_bytes[dom]), "avg_launch_us": round(avg_us[dom], 3)},
     }
     if args.calibrate_copy:
