@@ -97,6 +97,7 @@ struct TArgs {
   uint32_t tiles_per_wave, n_sg, n_blocks, block_begin, syms_per_row;
   uint32_t x_is_bf16, nb, lut_entries, xs_cols;
   uint32_t raw_full_bytes, raw_rg_bytes;
+  const uint8_t* tables;   // TABLES section (E8 decode-only hook: value offsets)
 };
 
 struct KArgs {
@@ -357,6 +358,158 @@ __device__ __forceinline__ void wave_body(const TArgs& a, uint32_t lut, uint32_t
   }
 }
 
+// ---- E8 lattice fields (EntroPack page, Sections 3.2, 3.3 and A.3)
+//
+// Per block of 8 weights a lane decodes 9 symbols: the coset c (table 0), then
+// z1..z7 and m = floor(z8 / 2) from table 1 + 8c + j.  The inverse of the parity
+// reduction is z8 = 2m + ((z1 + .. + z7) mod 2); the doubled coordinates are
+// 2v = 2z + c.  Reconstruction: INT8 route 2v (the row scale is halved in the
+// epilogue), FP8 route e4m3_rne(v) from a 256-entry LDS table indexed by 2v.
+// Table entries are staged compactly as 4 bytes: f (12 bits) | bias (11 bits) << 12 |
+// field value (int8) << 24, which needs M <= 2^11.
+constexpr uint32_t kE8F8TableBytes = 1024;   // 256 x u32, fp16 value in the high half
+
+template <bool MAT>
+__device__ __forceinline__ int e8_decode(uint32_t& x, uint32_t addr, uint32_t m) {
+  const uint32_t e = *lds_ptr<const uint32_t>(addr);
+  x = mad_u24(x >> m, e & 0xFFFu, (e >> 12) & 0x7FFu);
+  return (int)e >> 24;
+}
+
+template <int B, bool MAT, bool RAGGED, bool F8>
+__device__ __forceinline__ void wave_body_e8(const TArgs& a, uint32_t lut, uint32_t xs, uint32_t ring,
+                                             uint32_t f8tab, uint32_t rg, uint32_t t0, uint32_t t1,
+                                             uint32_t c_lo, uint32_t lane, bool active, float* acc) {
+  const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
+  const uint32_t tbytes = 4u << m;                 // bytes per compact table
+  const uint32_t row = rg * 64 + lane;
+  const uint32_t sl0 = rg * a.n_sl;
+  const uint2 zero2 = {0u, 0u};
+
+  uint32_t gb, nch, rposb;
+  run_words(a, t0, t1, gb, nch, rposb);
+  const uint2* src = reinterpret_cast<const uint2*>(a.words + gb) + lane;
+  {
+    const uint2 c0 = nch > 0 ? src[0] : zero2;
+    const uint2 c1 = nch > 1 ? src[64] : zero2;
+    lds_store2(ring + lane * 8, c0);
+    if (lane < 16) lds_store2(ring + 2 * kRing + lane * 8, c0);
+    lds_store2(ring + 2 * kChunk + lane * 8, c1);
+  }
+  uint2 pre = nch > 2 ? src[128] : zero2;
+  uint32_t haveb = 4 * kChunk, nc = 2;
+  uint32_t st = t0 < t1 ? a.states[(uint64_t)t0 * 64 + lane] : kStateL;
+
+  for (uint32_t t = t0; t < t1; ++t) {
+    uint32_t x = st;
+    if (t + 1 < t1) st = a.states[(uint64_t)(t + 1) * 64 + lane];
+    const uint32_t sl = t - sl0;
+    const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
+    const uint32_t col0 = sl * a.tile_cols - c_lo;
+    for (uint32_t blk = 0; blk < S / 9; ++blk) {
+      const uint32_t step0 = blk * 9;
+      // activations of the block's 8 columns: fp32 [col][B]
+      float xv[MAT ? 1 : 8 * B];
+      if constexpr (!MAT) {
+#pragma unroll
+        for (int i = 0; i < 2 * B; ++i) {
+          const uint4 q = lds_load4(xs + ((col0 + 8 * blk) * B) * 4 + i * 16);
+          xv[4 * i] = __uint_as_float(q.x);
+          xv[4 * i + 1] = __uint_as_float(q.y);
+          xv[4 * i + 2] = __uint_as_float(q.z);
+          xv[4 * i + 3] = __uint_as_float(q.w);
+        }
+      }
+      refill(rposb, haveb, nc, pre, ring, src, nch, lane);
+      const int c = e8_decode<MAT>(x, lut + ((x & mmask) << 2), m) & 1;    // coset, table 0
+      if constexpr (MAT) {
+        if ((!RAGGED || active) && a.sym_out) {
+          const int32_t off0 = *reinterpret_cast<const int32_t*>(a.tables + 4);
+          a.sym_out[(uint64_t)row * a.syms_per_row + (uint64_t)sl * a.s_full + step0] = (uint16_t)(c - off0);
+        }
+      }
+      renorm_step<RAGGED>(x, rposb, ring, active);
+      const uint32_t tb = lut + (1u + 8u * (uint32_t)c) * tbytes;          // table 1 + 8c
+      int zsum = 0;
+#pragma unroll
+      for (int j = 1; j <= 8; ++j) {
+        if (j == 4 || j == 8) refill(rposb, haveb, nc, pre, ring, src, nch, lane);
+        const int v = e8_decode<MAT>(x, tb + (uint32_t)(j - 1) * tbytes + ((x & mmask) << 2), m);
+        int z;
+        if (j < 8) {
+          z = v;
+          zsum += v;
+        } else {
+          z = 2 * v + (zsum & 1);                                         // z8 from m and parity
+        }
+        const int w2 = 2 * z + c;                                         // doubled coordinate
+        if constexpr (!MAT) {
+          if constexpr (F8) {
+            const uint32_t h = *lds_ptr<const uint32_t>(f8tab + ((uint32_t)(w2 + 128) & 255u) * 4);
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(h, xv[(j - 1) * B + b], acc[b]);
+          } else {
+            const float wf = (float)w2;
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[b] = fmaf(wf, xv[(j - 1) * B + b], acc[b]);
+          }
+        } else if (!RAGGED || active) {
+          const uint32_t step = step0 + (uint32_t)j;
+          if (a.sym_out) {
+            const uint32_t tbl = 1u + 8u * (uint32_t)c + (uint32_t)(j - 1);
+            const int32_t off = *reinterpret_cast<const int32_t*>(a.tables + (uint64_t)tbl * 520 + 4);
+            a.sym_out[(uint64_t)row * a.syms_per_row + (uint64_t)sl * a.s_full + step] = (uint16_t)(v - off);
+          }
+          if (a.w_out) {
+            const uint64_t wi = (uint64_t)row * a.cols + (uint64_t)col0 + c_lo + 8ull * blk + (uint64_t)(j - 1);
+            if constexpr (F8)
+              static_cast<uint8_t*>(a.w_out)[wi] =
+                  (uint8_t)(*lds_ptr<const uint32_t>(f8tab + ((uint32_t)(w2 + 128) & 255u) * 4));
+            else
+              static_cast<int8_t*>(a.w_out)[wi] = (int8_t)w2;
+          }
+        }
+        renorm_step<RAGGED>(x, rposb, ring, active);
+      }
+    }
+    if constexpr (MAT) {
+      const bool ok_lane = !active || x == kStateL;
+      const uint64_t bad = __ballot(!ok_lane);
+      if (lane == 0 && a.status_out)
+        a.status_out[t] = (bad != 0 ? 1u : 0u) | ((rposb != (a.offsets[t + 1] - gb) * 2) ? 2u : 0u);
+    }
+  }
+}
+
+// E4M3 byte nearest to t / 2 (t = 0..128), ties to the even code: t is rounded to a
+// 4-bit significand (implicit one and 3 fraction bits) with round-half-even.
+__device__ inline uint32_t e4m3_of_half_int(uint32_t t) {
+  if (t == 0) return 0;
+  int e2 = 31 - __builtin_clz(t);                  // t = 2^e2 * 1.f
+  uint32_t q;
+  if (e2 <= 3) {
+    q = t << (3 - e2);                             // exact: 1.fff in 4 bits
+  } else {
+    const int sh = e2 - 3;
+    q = t >> sh;
+    const uint32_t rem = t & ((1u << sh) - 1), half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    if (q == 16) {
+      q = 8;
+      ++e2;
+    }
+  }
+  // value = q * 2^(e2 - 3) / 2 = (q / 8) * 2^(e2 - 1); biased exponent e2 - 1 + 7
+  return ((uint32_t)(e2 + 6) << 3) | (q & 7u);
+}
+
+// fp16 bits of a normal E4M3 byte's value (the table only holds normal codes and 0)
+__device__ inline uint32_t fp16_of_e4m3_normal(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xF, mnt = b & 7, sign = (b & 0x80) << 8;
+  if ((b & 0x7F) == 0) return sign;
+  return sign | ((e - 7 + 15) << 10) | (mnt << 7);
+}
+
 // 16-bit float bits of a small integer, in the activations' type.
 template <bool XBF>
 __device__ __forceinline__ uint32_t small_int_bits(int q) {
@@ -406,9 +559,11 @@ k_decode(const KArgs ka) {
   const uint32_t sl_blk_end = min(sl_blk + W * R, a.n_sl);
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
-  const uint32_t pair_bytes = PTAB ? kPairTableBytes : 0;
+  constexpr bool E8 = PAY == 4;
+  constexpr bool E8F8 = E8 && CB == 1;            // E8: CB selects the FP8 reconstruction
+  const uint32_t pair_bytes = PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
   const uint32_t lut = pair_bytes;
-  const uint32_t lut_bytes = a.lut_entries * 8;
+  const uint32_t lut_bytes = a.lut_entries * (E8 ? 4 : 8);
   const uint32_t xs = lut + lut_bytes;
   const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * (DOT ? 2 : 4) + 15) & ~15u);
   const uint32_t rings = xs + xs_bytes;
@@ -416,8 +571,23 @@ k_decode(const KArgs ka) {
   // may carry it in a VGPR and pay a vector add per ring read)
   const uint32_t ring = __builtin_amdgcn_readfirstlane(rings + wid * (2 * kRingStride));
 
-  // ---- A2: stage the decode table (two 16-byte loads in flight per thread)
-  {
+  // ---- A2: stage the decode table (two 16-byte loads in flight per thread); E8
+  // tables are packed to 4-byte entries on the way
+  if constexpr (E8) {
+    const uint2* src = a.lut;
+    for (uint32_t i = tid; i < a.lut_entries; i += blockDim.x) {
+      const uint2 e = src[i];
+      *lds_ptr<uint32_t>(lut + i * 4) = (e.x & 0xFFFu) | ((e.y & 0x7FFu) << 12) | (e.x & 0xFF000000u);
+    }
+    if constexpr (E8F8) {
+      for (uint32_t i = tid; i < 256; i += blockDim.x) {
+        const int w2 = (int)i - 128;                 // doubled coordinate
+        const uint32_t mag = e4m3_of_half_int((uint32_t)(w2 < 0 ? -w2 : w2));
+        const uint32_t b = mag | (w2 < 0 ? 0x80u : 0u);
+        *lds_ptr<uint32_t>(i * 4) = b | (fp16_of_e4m3_normal(b) << 16);
+      }
+    }
+  } else {
     const uint4* src = reinterpret_cast<const uint4*>(a.lut);
     const uint32_t n = a.lut_entries / 2, bd = blockDim.x;
     for (uint32_t i = tid; i < n; i += 2 * bd) {
@@ -484,12 +654,19 @@ k_decode(const KArgs ka) {
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.f;
   if (w_sl0 < w_sl1) {
-    if (ragged)
-      wave_body<PAY, CB, KW, B, MAT, true, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
-                                                acc);
-    else
-      wave_body<PAY, CB, KW, B, MAT, false, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
-                                                 acc);
+    if constexpr (E8) {
+      if (ragged)
+        wave_body_e8<B, MAT, true, E8F8>(a, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active, acc);
+      else
+        wave_body_e8<B, MAT, false, E8F8>(a, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active, acc);
+    } else {
+      if (ragged)
+        wave_body<PAY, CB, KW, B, MAT, true, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
+                                                  acc);
+      else
+        wave_body<PAY, CB, KW, B, MAT, false, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane,
+                                                   active, acc);
+    }
   }
   if constexpr (!MAT) {
     // ---- A8: epilogue.  Reuse this wave's first ring as its reduction slot.
@@ -503,7 +680,8 @@ k_decode(const KArgs ka) {
         s += *lds_ptr<const float>(rings + w * (2 * kRingStride) + (b * 64 + l) * 4);
       if (a.n_sg == 1) {
         if (r < a.rows && b < a.nb) {
-          const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
+          float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
+          if constexpr (E8 && !E8F8) sc *= 0.5f;    // INT8 route: weights are 2v
           a.y[(uint64_t)b * a.rows + r] = s * sc;
         }
       } else {
@@ -523,6 +701,7 @@ struct RArgs {
   float* y[kMaxGroup];
   uint32_t rows[kMaxGroup], n_sg[kMaxGroup], row_begin[kMaxGroup];
   uint32_t nt, nb, unit_scale, total_rows;
+  float scale_mul;       // 0.5 for the E8 INT8 route (weights are 2v), else 1
 };
 
 template <int B>
@@ -533,7 +712,7 @@ __global__ void __launch_bounds__(256) k_reduce(const RArgs ra) {
   for (uint32_t i = 1; i < ra.nt; ++i)
     if (gi >= ra.row_begin[i]) ti = i;
   const uint32_t r = gi - ra.row_begin[ti], rg = r >> 6, l = r & 63, n_sg = ra.n_sg[ti];
-  const float sc = ra.unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, ra.scales[ti][r]);
+  const float sc = ra.unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, ra.scales[ti][r]) * ra.scale_mul;
   const float* p = ra.partials[ti] + (uint64_t)rg * n_sg * B * 64 + l;
 #pragma unroll
   for (int b = 0; b < B; ++b) {
@@ -576,6 +755,8 @@ static KernelFn pick_kernel(const ecw_coding& c) {
       return nullptr;
     case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT, false>;
     case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT, false>;
+    case ECW_P_E8_LATTICE:
+      return c.recon_dtype == ECW_DT_FP8_E4M3 ? k_decode<4, 1, 8, B, MAT, false> : k_decode<4, 0, 8, B, MAT, false>;
   }
   return nullptr;
 }
@@ -597,8 +778,10 @@ static bool pair_table(const ecw_coding& c, bool xbf) {
 static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat,
                           bool xbf) {
   const bool dot = !mat && dot_path(t->coding);
-  const uint64_t pair = (!mat && pair_table(t->coding, xbf)) ? kPairTableBytes : 0;
-  const uint64_t lut = (uint64_t)t->n_tables << t->coding.log2_m;
+  const bool e8 = t->coding.payload == ECW_P_E8_LATTICE;
+  uint64_t pair = (!mat && pair_table(t->coding, xbf)) ? kPairTableBytes : 0;
+  if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
+  const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
   (void)R;
   return pair + lut * 8 + xs + (uint64_t)W * kRingStride * 2;
@@ -628,6 +811,7 @@ static void fill_tensor(const ecw_tensor* t, TArgs& a) {
   a.words = reinterpret_cast<const uint16_t*>(base + t->off_words);
   a.raw = base + t->off_raw;
   a.scales = reinterpret_cast<const uint16_t*>(base + t->off_scales);
+  a.tables = base + t->off_tables;
   a.rows = t->coding.rows;
   a.cols = t->coding.cols;
   a.n_rg = t->n_row_groups;
@@ -649,10 +833,12 @@ static ecw_status check_tensor(const ecw_tensor* t) {
   if (st != ECW_OK) return st;
   if (!t->device_blob) return fail(ECW_E_INVALID_ARG, "tensor has no device blob");
   if (reinterpret_cast<uintptr_t>(t->device_blob) % 256) return fail(ECW_E_INVALID_ARG, "device blob misaligned");
-  if (t->coding.payload == ECW_P_E8_LATTICE) return fail(ECW_E_UNSUPPORTED, "E8 lattice decode kernel not built");
+  if (t->coding.payload == ECW_P_E8_LATTICE && t->coding.log2_m > 11)
+    return fail(ECW_E_UNSUPPORTED, "E8 decode stages 4-byte table entries: M must be at most 2^11");
   if (t->waves_per_block < 1 || t->waves_per_block > 16 || t->tiles_per_wave < 1 || t->tiles_per_wave > 4096)
     return fail(ECW_E_INVALID_ARG, "launch shape out of range");
-  if (t->steps_full % 16 || t->steps_last % 16) return fail(ECW_E_UNSUPPORTED, "steps per tile must be a multiple of 16");
+  if (t->coding.payload != ECW_P_E8_LATTICE && (t->steps_full % 16 || t->steps_last % 16))
+    return fail(ECW_E_UNSUPPORTED, "steps per tile must be a multiple of 16");
   return ECW_OK;
 }
 
@@ -758,6 +944,7 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
   if (ra.nt) {
     ra.nb = (uint32_t)batch;
     ra.unit_scale = ts[0]->coding.payload == ECW_P_BF16_EXP;
+    ra.scale_mul = (ts[0]->coding.payload == ECW_P_E8_LATTICE && ts[0]->coding.recon_dtype == ECW_DT_I8) ? 0.5f : 1.f;
     ra.total_rows = red_rows;
     const dim3 rgrid((red_rows + 255) / 256);
     if (B == 1)

@@ -88,10 +88,30 @@ def small_cases():
     return cases
 
 
-def e8_case():
+def e8_case(recon_dtype=4, rows=96, cols=192, m=11, tc=64, sigma=3.0, seed=1):
     from oracle import e8
-    rng = np.random.default_rng([0, 500, 1])
-    c, z = e8.nearest_e8(rng.normal(0, 3.0, (96 * 24, 8)))
-    v2 = e8.doubled_coords(c, z).reshape(96, 192).astype(np.int8)
-    return Case("e8_i8", E8, 96, 192, 8, 0, 11, 64, v2, (0.01 * rng.uniform(0.5, 1.5, 96)).astype(np.float16),
-                recon_dtype=4)
+    rng = np.random.default_rng([0, 500, seed])
+    c, z = e8.nearest_e8(rng.normal(0, sigma, (rows * cols // 8, 8)))
+    v2 = e8.doubled_coords(c, z).reshape(rows, cols).astype(np.int8)
+    name = "e8_i8" if recon_dtype == 4 else "e8_fp8"
+    return Case(f"{name}_{rows}x{cols}_m{m}_tc{tc}", E8, rows, cols, 8, 0, m, tc, v2,
+                (0.01 * rng.uniform(0.5, 1.5, rows)).astype(np.float16), recon_dtype=recon_dtype)
+
+
+def e8_cases():
+    """E8 variants for the GPU tests: both reconstruction routes, a ragged row group,
+    wider tiles, a small table, and blocks covering every doubled coordinate."""
+    out = [e8_case(4), e8_case(5), e8_case(4, rows=130, cols=384, m=10, tc=128, seed=2),
+           e8_case(5, rows=64, cols=512, m=9, tc=256, sigma=1.5, seed=3)]
+    # every doubled coordinate -127..127 once, as blocks of 8 equal values (same
+    # parity; sum of v = 4 * value is even)
+    vals = np.arange(-127, 128)
+    blocks = np.repeat(vals[:, None], 8, axis=1)
+    pad = (-len(blocks)) % 16
+    blocks = np.concatenate([blocks, np.zeros((pad, 8), np.int64)])
+    v2 = blocks.reshape(-1, 128).astype(np.int8)
+    sc = np.full(v2.shape[0], 0.125, np.float16)
+    for rd in (4, 5):
+        out.append(Case(f"e8_every_coord_{'i8' if rd == 4 else 'fp8'}", E8, v2.shape[0], 128, 8, 0, 10, 128,
+                        v2, sc, recon_dtype=rd))
+    return out

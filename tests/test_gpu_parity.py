@@ -183,3 +183,34 @@ def test_grouped_launch_matches_separate_launches(batch):
         wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
         ok, worst = gemv.check(y.cpu().numpy(), wv, xv)
         assert ok, worst
+
+
+@pytest.mark.parametrize("case", cases.e8_cases(), ids=lambda c: c.name)
+def test_e8_materialize_bit_exact(case):
+    # symbols, reconstructed weights (INT8 2v or E4M3 bytes) and tile ends vs the oracle
+    print(f"[gpu] e8 materialize {case.name}", flush=True)
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    ct = ecw.CompressedTensor(blob)
+    sym, w, st = ct.materialize()
+    torch.cuda.synchronize()
+    assert int(st.abs().sum()) == 0
+    want = P.reconstructed_dtype_tensor(case.oracle_coding(), case.logical)
+    assert np.array_equal(w.cpu().numpy().view(want.dtype), want)
+    comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+    ref_sym, ok = P.decode_symbols(comp)
+    assert ok.all()
+    assert np.array_equal(sym.cpu().numpy().view(np.uint16).astype(np.int64), ref_sym)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("case", cases.e8_cases(), ids=lambda c: c.name)
+def test_e8_gemv_within_bound(case, batch):
+    print(f"[gpu] e8 gemv {case.name} batch={batch}", flush=True)
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    ct = ecw.CompressedTensor(blob)
+    xd, xv = _x(case, batch)
+    y = ct.gemv(xd)
+    torch.cuda.synchronize()
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    ok, worst = gemv.check(y.cpu().numpy(), wv, xv)
+    assert ok, f"worst error / bound = {worst}"

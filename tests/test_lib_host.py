@@ -41,7 +41,7 @@ def test_tile_metadata_bytes_match_page_formula():
     assert t.bytes_tile_meta == t.n_tiles * 260 + 4
 
 
-@pytest.mark.parametrize("case", cases.small_cases() + [cases.e8_case()], ids=lambda c: c.name)
+@pytest.mark.parametrize("case", cases.small_cases() + cases.e8_cases(), ids=lambda c: c.name)
 def test_byte_parity_with_oracle_and_oracle_decodes_library_blob(case):
     blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
     comp = P.encode(case.oracle_coding(), case.logical, case.scales)
