@@ -558,12 +558,15 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
 namespace ecw {
 
 // Default launch shape: one tile per wave, up to 16 waves (consecutive slices of
-// one row group) per block: the fastest shape measured on MI355X for every
-// Llama-8B-shaped tensor.  Per-tensor tuning may change it.
+// one row group) per block, halved until the block's LDS (decode tables, staged
+// activations at batch capacity 4, word rings) fits the CU's 160 KiB.  Per-tensor
+// tuning may change it.
 void default_launch(ecw_tensor* t) {
   const uint32_t n_sl = t->n_slices;
   t->tiles_per_wave = 1;
-  t->waves_per_block = std::max(1u, std::min(16u, n_sl));
+  uint32_t W = std::max(1u, std::min(16u, n_sl));
+  while (W > 1 && launch_lds_bytes(t, W, 1, 4, false, true) > 160u * 1024u) W /= 2;
+  t->waves_per_block = W;
 }
 
 uint32_t slice_groups(const ecw_tensor* t) {

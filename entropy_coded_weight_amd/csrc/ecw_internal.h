@@ -24,6 +24,9 @@ Geometry geometry_of(const ecw_coding& c);
 
 // launch shape helpers
 void default_launch(ecw_tensor* t);
+// LDS bytes of one block of the fused kernel (or, with mat, the decode-only hook)
+// for W waves of R tiles at batch capacity B (1 or 4); xbf: bf16 activations.
+uint64_t launch_lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, int B, bool mat, bool xbf);
 uint32_t slice_groups(const ecw_tensor* t);
 uint64_t workspace_bytes(const ecw_tensor* t, int batch);
 

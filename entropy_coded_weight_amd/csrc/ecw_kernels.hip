@@ -787,6 +787,11 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   return pair + lut * 8 + xs + (uint64_t)W * kRingStride * 2;
 }
 
+uint64_t launch_lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, int B, bool mat, bool xbf) {
+  const uint32_t xs_cols = mat ? 0 : W * R * t->coding.tile_cols;
+  return lds_bytes(t, W, R, xs_cols, B > 1 ? 4 : 1, mat, xbf);
+}
+
 // Allow each kernel the whole 160 KiB LDS once (a host call, not a stream
 // operation, so launches stay capturable).
 static bool lds_attribute_set(KernelFn fn) {

@@ -5,6 +5,7 @@ Inputs come from ecw_inputs (seeded) or plain seeded numpy draws.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -115,3 +116,58 @@ def e8_cases():
         out.append(Case(f"e8_every_coord_{'i8' if rd == 4 else 'fp8'}", E8, v2.shape[0], 128, 8, 0, 10, 128,
                         v2, sc, recon_dtype=rd))
     return out
+
+
+# ---------------------------------------------------------------- full-size configs
+_CFG5 = {}
+
+
+def config5():
+    """The lattice workload at its full size.  w = N(0, 0.02^2) [3072, 12288]; rows
+    are normalised by their RMS; the lattice step s comes from 12 steps of geometric
+    bisection on [1e-3, 8] such that the plug-in entropy of the block fields (coset,
+    then the eight fields given the coset) on 2^18 sampled blocks is 4.0 bits per
+    weight; v = nearest E8 point of u / s; the fp16 row scale is the least-squares
+    refit <w_r, v_r> / <v_r, v_r>.  Returns (2v as int8 [N, K], fp16 scales, fp16 x
+    [1, K]).  Test-side generation (it uses the oracle's nearest-point routine)."""
+    if not _CFG5:
+        from oracle import coding, e8
+        n, k = 3072, 12288
+        rng = E.rng_for(5, 0, 0)
+        w = E.normal_matrix((n, k), rng)
+        x = rng.standard_normal((1, k)).astype(np.float16)
+        rms = np.sqrt((w * w).mean(axis=1))
+        u = (w / rms[:, None]).reshape(-1, 8)
+        srng = np.random.default_rng([0, 5, n, k])
+        sample = u[srng.choice(u.shape[0], 1 << 18, replace=False)]
+
+        def bits_per_weight(s):
+            c, z = e8.nearest_e8(sample / s)
+            f = e8.point_to_fields(c, z)
+            total = coding.entropy_bits(np.bincount(c, minlength=2)) * len(c)
+            for cc in (0, 1):
+                sel = f[c == cc]
+                for j in range(1, 9):
+                    vals = sel[:, j] - sel[:, j].min() if len(sel) else sel[:, j]
+                    total += coding.entropy_bits(np.bincount(vals)) * len(sel)
+            return total / (8 * len(c))
+
+        lo, hi = 1e-3, 8.0
+        for _ in range(12):
+            mid = math.sqrt(lo * hi)
+            if bits_per_weight(mid) > 4.0:
+                lo = mid
+            else:
+                hi = mid
+        s = math.sqrt(lo * hi)
+        v2 = np.empty((u.shape[0], 8), np.int64)
+        for b0 in range(0, u.shape[0], 1 << 18):          # chunks keep temporaries small
+            c, z = e8.nearest_e8(u[b0:b0 + (1 << 18)] / s)
+            v2[b0:b0 + len(c)] = e8.doubled_coords(c, z)
+        v2 = v2.reshape(n, k)
+        if np.abs(v2).max() > 127:
+            raise ValueError("lattice step too fine for int8 doubled coordinates")
+        v = v2 / 2.0
+        scales = ((w * v).sum(axis=1) / np.maximum((v * v).sum(axis=1), 1e-30)).astype(np.float16)
+        _CFG5.update(v2=v2.astype(np.int8), scales=scales, x=x, step=s, bpw=bits_per_weight(s))
+    return _CFG5["v2"], _CFG5["scales"], _CFG5["x"]
