@@ -94,16 +94,22 @@ struct TArgs {
   void* w_out;
   uint32_t* status_out;
   uint32_t rows, cols, n_rg, n_sl, s_full, s_last, log2m, tile_cols;
-  uint32_t tiles_per_wave, n_sg, n_blocks, block_begin, syms_per_row;
+  uint32_t tiles_per_wave, n_sg, n_blocks, syms_per_row;
   uint32_t x_is_bf16, nb, lut_entries, xs_cols;
   uint32_t raw_full_bytes, raw_rg_bytes;
   const uint8_t* tables;   // TABLES section (E8 decode-only hook: value offsets)
 };
 
+// Launch arguments.  The fields a block needs to find its tensor come first, so one
+// scalar load fetches them; the launch shape is passed here instead of being read
+// from the dispatch packet.
 struct KArgs {
+  uint32_t n_blocks;                 // total logical blocks
+  uint32_t nt;                       // tensors in the launch
+  uint32_t waves;                    // waves per block (blockDim.x / 64)
+  uint32_t grid;                     // blocks launched (a multiple of 8)
+  uint32_t block_begin[kMaxGroup];   // first logical block of each tensor
   TArgs t[kMaxGroup];
-  uint32_t nt;           // tensors in the launch
-  uint32_t n_blocks;     // total logical blocks
 };
 
 // x' = f * (x >> m) + bias in one v_mad_u32_u24 (both factors < 2^24; the payload
@@ -241,18 +247,46 @@ __device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, 
   return a.raw + (uint64_t)rg * a.raw_rg_bytes + (uint64_t)sl * a.raw_full_bytes + lane * 16;
 }
 
-// Word range of a run of tiles [t0, t1): chunk-aligned start, chunk count, first
-// read position (bytes from the aligned start).
-__device__ __forceinline__ void run_words(const TArgs& a, uint32_t t0, uint32_t t1, uint32_t& gb,
-                                          uint32_t& nch, uint32_t& rposb) {
-  if (t0 >= t1) {
-    gb = 0; nch = 0; rposb = 0;
-    return;
+// Start of a wave's word stream over tiles [t0, t1): chunk-aligned word start gb,
+// chunk count nch, first read position rposb (bytes from gb), the first tile's
+// start state, the first two chunks and the one-ahead prefetch.  Filled in two
+// phases so the loads overlap the block's table staging: head_begin issues the
+// tile offsets and start state, head_chunks (after staging, before the barrier)
+// the first chunk loads.
+struct StreamHead {
+  uint32_t gb, nch, rposb, st;
+  uint2 c0, c1, pre;
+  const uint2* src;
+};
+
+__device__ __forceinline__ void head_begin(const TArgs& a, uint32_t t0, uint32_t t1, uint32_t lane, StreamHead& h) {
+  h.gb = 0;          // word offset of t0 until head_chunks
+  h.nch = 0;         // word offset of t1 until head_chunks
+  h.st = kStateL;
+  if (t0 < t1) {
+    h.gb = a.offsets[t0];
+    h.nch = a.offsets[t1];
+    h.st = a.states[(uint64_t)t0 * 64 + lane];
   }
-  const uint32_t wb = a.offsets[t0], we = a.offsets[t1];
-  gb = wb & ~(kChunk - 1);
-  nch = (we - gb + kChunk - 1) / kChunk;
-  rposb = (wb - gb) * 2;
+}
+
+__device__ __forceinline__ void head_chunks(const TArgs& a, uint32_t lane, StreamHead& h) {
+  const uint32_t wb = h.gb, we = h.nch;
+  h.gb = wb & ~(kChunk - 1);
+  h.nch = (we - h.gb + kChunk - 1) / kChunk;
+  h.rposb = (wb - h.gb) * 2;
+  h.src = reinterpret_cast<const uint2*>(a.words + h.gb) + lane;
+  const uint2 zero2 = {0u, 0u};
+  h.c0 = h.nch > 0 ? h.src[0] : zero2;
+  h.c1 = h.nch > 1 ? h.src[64] : zero2;
+  h.pre = h.nch > 2 ? h.src[128] : zero2;
+}
+
+// First two chunks into the ring (and the head mirror); after the block barrier.
+__device__ __forceinline__ void head_ring(const StreamHead& h, uint32_t ring, uint32_t lane) {
+  lds_store2(ring + lane * 8, h.c0);
+  if (lane < 16) lds_store2(ring + 2 * kRing + lane * 8, h.c0);
+  lds_store2(ring + 2 * kChunk + lane * 8, h.c1);
 }
 
 // The wave body: the wave's tiles [t0, t1) (consecutive slices of one row group)
@@ -260,8 +294,8 @@ __device__ __forceinline__ void run_words(const TArgs& a, uint32_t t0, uint32_t 
 // MAT: decode-only test hook.  ring: LDS byte address of the wave's ring.  xs: LDS
 // byte address of the staged activations.
 template <int PAY, int CB, int KW, int B, bool MAT, bool RAGGED, bool XBF>
-__device__ __forceinline__ void wave_body(const TArgs& a, uint32_t lut, uint32_t xs, uint32_t ring,
-                                          uint32_t rg, uint32_t t0, uint32_t t1, uint32_t c_lo,
+__device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, uint32_t lut, uint32_t xs,
+                                          uint32_t ring, uint32_t rg, uint32_t t0, uint32_t t1, uint32_t c_lo,
                                           uint32_t lane, bool active, float* acc) {
   constexpr int U = 16;
   constexpr bool DOT = kDot<PAY, KW>;
@@ -270,23 +304,15 @@ __device__ __forceinline__ void wave_body(const TArgs& a, uint32_t lut, uint32_t
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
   const uint32_t row = rg * 64 + lane;
   const uint32_t sl0 = rg * a.n_sl;
-  const uint2 zero2 = {0u, 0u};
   const uint4 zero4 = {0u, 0u, 0u, 0u};
 
-  uint32_t gb, nch, rposb;
-  run_words(a, t0, t1, gb, nch, rposb);
-  const uint2* src = reinterpret_cast<const uint2*>(a.words + gb) + lane;
-  // first two chunks straight into the ring, the third into the prefetch register
-  {
-    const uint2 c0 = nch > 0 ? src[0] : zero2;
-    const uint2 c1 = nch > 1 ? src[64] : zero2;
-    lds_store2(ring + lane * 8, c0);
-    if (lane < 16) lds_store2(ring + 2 * kRing + lane * 8, c0);
-    lds_store2(ring + 2 * kChunk + lane * 8, c1);
-  }
-  uint2 pre = nch > 2 ? src[128] : zero2;
+  head_ring(h, ring, lane);
+  const uint32_t gb = h.gb, nch = h.nch;
+  const uint2* src = h.src;
+  uint32_t rposb = h.rposb;
+  uint2 pre = h.pre;
   uint32_t haveb = 4 * kChunk, nc = 2;
-  uint32_t st = t0 < t1 ? a.states[(uint64_t)t0 * 64 + lane] : kStateL;
+  uint32_t st = h.st;
 
   for (uint32_t t = t0; t < t1; ++t) {
     uint32_t x = st;
@@ -358,6 +384,78 @@ __device__ __forceinline__ void wave_body(const TArgs& a, uint32_t lut, uint32_t
   }
 }
 
+// Two word streams per wave (fused GEMV only): tiles [tA0, tA1) and [tB0, tB1) of
+// the same row group are decoded in lockstep, two independent dependency chains per
+// wave, each with its own ring.  B's tiles follow A's, so only B can hold the short
+// last slice (SB <= SA).
+template <int PAY, int CB, int KW, int B, bool RAGGED, bool XBF>
+__device__ __forceinline__ void wave_body_two(const TArgs& a, const StreamHead& hA, const StreamHead& hB,
+                                              uint32_t lut, uint32_t xs, uint32_t ringA, uint32_t ringB,
+                                              uint32_t rg, uint32_t tA0, uint32_t tA1, uint32_t tB0, uint32_t tB1,
+                                              uint32_t c_lo, uint32_t lane, bool active, float* acc) {
+  constexpr int U = 16;
+  constexpr bool DOT = kDot<PAY, KW>;
+  constexpr bool CLEAN = kCleanBias<PAY, KW>;
+  constexpr int XW = DOT ? (KW / 2) * B : KW * B;
+  const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
+  const uint32_t sl0 = rg * a.n_sl;
+
+  head_ring(hA, ringA, lane);
+  head_ring(hB, ringB, lane);
+  const uint32_t nchA = hA.nch, nchB = hB.nch;
+  const uint2* srcA = hA.src;
+  const uint2* srcB = hB.src;
+  uint32_t rposA = hA.rposb, rposB = hB.rposb;
+  uint2 preA = hA.pre, preB = hB.pre;
+  uint32_t haveA = 4 * kChunk, ncA = 2, haveB = 4 * kChunk, ncB = 2;
+  uint32_t stA = hA.st, stB = hB.st;
+
+  uint32_t tB = tB0;
+  for (uint32_t tA = tA0; tA < tA1; ++tA) {
+    const bool pairB = tB < tB1;                          // wave-uniform
+    uint32_t xA = stA, xB = stB;
+    if (tA + 1 < tA1) stA = a.states[(uint64_t)(tA + 1) * 64 + lane];
+    if (pairB && tB + 1 < tB1) stB = a.states[(uint64_t)(tB + 1) * 64 + lane];
+    const uint32_t slA = tA - sl0, slB = tB - sl0;
+    const uint32_t SA = (slA + 1 == a.n_sl) ? a.s_last : a.s_full;
+    const uint32_t SB = pairB ? ((slB + 1 == a.n_sl) ? a.s_last : a.s_full) : 0;
+    const uint32_t xgA0 = xs + ((slA * a.tile_cols - c_lo) * B / (DOT ? 2 : 1)) * 4;
+    const uint32_t xgB0 = xs + ((slB * a.tile_cols - c_lo) * B / (DOT ? 2 : 1)) * 4;
+    for (uint32_t j = 0; j < SA; j += U) {
+      const bool dualB = j < SB;                            // wave-uniform
+      const uint32_t xgA = xgA0 + ((KW * j) * B / (DOT ? 2 : 1)) * 4;
+      const uint32_t xgB = xgB0 + ((KW * j) * B / (DOT ? 2 : 1)) * 4;
+#pragma unroll
+      for (int qtr = 0; qtr < U / 4; ++qtr) {
+        refill(rposA, haveA, ncA, preA, ringA, srcA, nchA, lane);
+        if (dualB) refill(rposB, haveB, ncB, preB, ringB, srcB, nchB, lane);
+        uint4 xqA[XW], xqB[XW];
+#pragma unroll
+        for (int i = 0; i < XW; ++i) xqA[i] = lds_load4(xgA + (qtr * XW + i) * 16);
+        if (dualB) {
+#pragma unroll
+          for (int i = 0; i < XW; ++i) xqB[i] = lds_load4(xgB + (qtr * XW + i) * 16);
+        }
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) {
+          const uint2 eA = decode_step<CLEAN>(xA, lut, m, mmask);
+          if (dualB) {
+            const uint2 eB = decode_step<CLEAN>(xB, lut, m, mmask);
+            mac<PAY, CB, KW, B, XBF>(eA, reinterpret_cast<const uint32_t*>(xqA) + u4 * XW, 0u, acc);
+            mac<PAY, CB, KW, B, XBF>(eB, reinterpret_cast<const uint32_t*>(xqB) + u4 * XW, 0u, acc);
+            renorm_step<RAGGED>(xA, rposA, ringA, active);
+            renorm_step<RAGGED>(xB, rposB, ringB, active);
+          } else {
+            mac<PAY, CB, KW, B, XBF>(eA, reinterpret_cast<const uint32_t*>(xqA) + u4 * XW, 0u, acc);
+            renorm_step<RAGGED>(xA, rposA, ringA, active);
+          }
+        }
+      }
+    }
+    if (pairB) ++tB;
+  }
+}
+
 // ---- E8 lattice fields (EntroPack page, Sections 3.2, 3.3 and A.3)
 //
 // Per block of 8 weights a lane decodes 9 symbols: the coset c (table 0), then
@@ -377,28 +475,21 @@ __device__ __forceinline__ int e8_decode(uint32_t& x, uint32_t addr, uint32_t m)
 }
 
 template <int B, bool MAT, bool RAGGED, bool F8>
-__device__ __forceinline__ void wave_body_e8(const TArgs& a, uint32_t lut, uint32_t xs, uint32_t ring,
-                                             uint32_t f8tab, uint32_t rg, uint32_t t0, uint32_t t1,
+__device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h, uint32_t lut, uint32_t xs,
+                                             uint32_t ring, uint32_t f8tab, uint32_t rg, uint32_t t0, uint32_t t1,
                                              uint32_t c_lo, uint32_t lane, bool active, float* acc) {
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
   const uint32_t tbytes = 4u << m;                 // bytes per compact table
   const uint32_t row = rg * 64 + lane;
   const uint32_t sl0 = rg * a.n_sl;
-  const uint2 zero2 = {0u, 0u};
 
-  uint32_t gb, nch, rposb;
-  run_words(a, t0, t1, gb, nch, rposb);
-  const uint2* src = reinterpret_cast<const uint2*>(a.words + gb) + lane;
-  {
-    const uint2 c0 = nch > 0 ? src[0] : zero2;
-    const uint2 c1 = nch > 1 ? src[64] : zero2;
-    lds_store2(ring + lane * 8, c0);
-    if (lane < 16) lds_store2(ring + 2 * kRing + lane * 8, c0);
-    lds_store2(ring + 2 * kChunk + lane * 8, c1);
-  }
-  uint2 pre = nch > 2 ? src[128] : zero2;
+  head_ring(h, ring, lane);
+  const uint32_t gb = h.gb, nch = h.nch;
+  const uint2* src = h.src;
+  uint32_t rposb = h.rposb;
+  uint2 pre = h.pre;
   uint32_t haveb = 4 * kChunk, nc = 2;
-  uint32_t st = t0 < t1 ? a.states[(uint64_t)t0 * 64 + lane] : kStateL;
+  uint32_t st = h.st;
 
   for (uint32_t t = t0; t < t1; ++t) {
     uint32_t x = st;
@@ -521,7 +612,9 @@ __device__ __forceinline__ uint32_t small_int_bits(int q) {
 // (INT).  B: batch capacity (1 or 4).  MAT: decode-only test hook.  XBF: the dot path
 // multiplies bf16 activations (else fp16).
 // Block = W waves on consecutive slices of one row group; wave w owns R consecutive
-// tiles, decoded one after the other as one word stream.
+// tiles, decoded one after the other as one word stream or, for the fused GEMV of
+// INT (one or two codes per symbol) and FP8 payloads with R >= 2, as two streams
+// (first and second half) in lockstep.
 // LDS, from address 0 (the kernel declares no static LDS): [pair side table]
 // [decode table] [activations] [rings].
 // Register budget: batch-1 kernels are held to 64 VGPRs so 8 waves fit per SIMD (two
@@ -536,23 +629,24 @@ k_decode(const KArgs ka) {
   (void)smem;
   constexpr bool DOT = kDot<PAY, KW> && !MAT;
   constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT;
-  const uint32_t W = blockDim.x >> 6;
+  const uint32_t W = ka.waves;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Hardware block b runs on XCD b % 8.  Give each XCD a contiguous range of logical
-  // blocks (the slice groups of one row group are adjacent).  gridDim.x is a
-  // multiple of 8; surplus blocks exit at once.
-  const uint32_t per = gridDim.x >> 3;
+  // blocks (the slice groups of one row group are adjacent).  The grid (ka.grid) is
+  // a multiple of 8; surplus blocks exit at once.
+  const uint32_t per = ka.grid >> 3;
   const uint32_t gl = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (gl >= ka.n_blocks) return;
   // tensor of a grouped launch: blocks are numbered tensor by tensor
   uint32_t ti = 0;
-  for (uint32_t i = 1; i < ka.nt; ++i)
-    if (gl >= ka.t[i].block_begin) ti = i;
+#pragma unroll
+  for (uint32_t i = 1; i < kMaxGroup; ++i)
+    if (i < ka.nt && gl >= ka.block_begin[i]) ti = i;
   const TArgs& a = ka.t[ti];
-  const uint32_t lb = gl - a.block_begin;
+  const uint32_t lb = gl - ka.block_begin[ti];
   const uint32_t rg = lb / a.n_sg, sg = lb - rg * a.n_sg;
   const uint32_t R = a.tiles_per_wave;
   const uint32_t sl_blk = sg * W * R;
@@ -567,20 +661,85 @@ k_decode(const KArgs ka) {
   const uint32_t xs = lut + lut_bytes;
   const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * (DOT ? 2 : 4) + 15) & ~15u);
   const uint32_t rings = xs + xs_bytes;
-  // wave-uniform LDS address, pinned to a scalar register (the compiler otherwise
-  // may carry it in a VGPR and pay a vector add per ring read)
-  const uint32_t ring = __builtin_amdgcn_readfirstlane(rings + wid * (2 * kRingStride));
+  // two streams per wave when a wave owns two or more tiles (fused GEMV, INT / FP8)
+  constexpr bool kTwoCapable = !MAT && ((PAY == 1 && KW <= 2) || PAY == 3);
+  const uint32_t NSr = (kTwoCapable && R >= 2) ? 2u : 1u;
+  // wave-uniform LDS addresses, pinned to scalar registers (the compiler otherwise
+  // may carry them in VGPRs and pay a vector add per ring read)
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(rings + wid * NSr * (2 * kRingStride));
+  const uint32_t ringB = __builtin_amdgcn_readfirstlane(ring + 2 * kRingStride);
 
-  // ---- A2: stage the decode table (two 16-byte loads in flight per thread); E8
-  // tables are packed to 4-byte entries on the way
+  // this wave's tiles; their offsets and start states are requested before the
+  // staging loads so both latencies overlap
+  const uint32_t w_sl0 = min(sl_blk + wid * R, sl_blk_end);
+  const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
+  const uint32_t w_mid = NSr == 1 ? w_sl1 : w_sl0 + (w_sl1 - w_sl0 + 1) / 2;
+  const uint32_t tb = rg * a.n_sl;
+  StreamHead hA, hB;
+  head_begin(a, tb + w_sl0, tb + w_mid, lane, hA);
+  if (kTwoCapable && NSr == 2) head_begin(a, tb + w_mid, tb + w_sl1, lane, hB);
+
+  // ---- A2 / A3 prologue.  Every global load is issued before the first wait: the
+  // first round of the decode table (up to 4 x 16 bytes per thread) and of the
+  // activations (16 bytes per thread) go out together with the stream heads; the
+  // first word chunks follow as soon as the tile offsets (scalar loads) arrive; the
+  // LDS writes come last.  Larger tables / activation slices than one round take a
+  // second pass.
+  const uint32_t bd = W * 64;
+  constexpr int KL = 4;
+  const uint32_t nl16 = E8 ? 0 : a.lut_entries / 2;              // table, 16-byte units
+  const uint4* lsrc = reinterpret_cast<const uint4*>(a.lut);
+  uint4 lv[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    const uint32_t idx = tid + (uint32_t)i * bd;
+    if (idx < nl16) lv[i] = lsrc[idx];
+  }
+  const uint32_t nvec = MAT ? 0 : a.xs_cols / 8;                 // activations, 8 columns per unit
+  const uint32_t nxv = nvec * B;
+  auto x_load = [&](uint32_t v) {
+    const uint32_t b = v / nvec, c8 = v - b * nvec, col = c_lo + 8 * c8;
+    uint4 raw = {0u, 0u, 0u, 0u};
+    if (col < c_hi && b < a.nb)
+      raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (uint64_t)b * a.cols + col);
+    return raw;
+  };
+  auto x_store = [&](uint32_t v, const uint4 raw) {
+    const uint32_t b = v / nvec, c8 = v - b * nvec;
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (DOT) {
+      if constexpr (B == 1) {
+        lds_store4(xs + c8 * 16, raw);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *lds_ptr<uint32_t>(xs + ((4 * c8 + i) * B + b) * 4) = w4[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t h = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
+        const float f = a.x_is_bf16 ? __uint_as_float((uint32_t)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+        *lds_ptr<float>(xs + ((8 * c8 + i) * B + b) * 4) = f;
+      }
+    }
+  };
+  uint4 xv0 = {0u, 0u, 0u, 0u};
+  if constexpr (!MAT) {
+    if (tid < nxv) xv0 = x_load(tid);
+  }
+  // first word chunks of the stream(s): in flight across the LDS writes and barrier
+  head_chunks(a, lane, hA);
+  if (kTwoCapable && NSr == 2) head_chunks(a, lane, hB);
+
   if constexpr (E8) {
+    // E8 tables are packed to 4-byte entries on the way
     const uint2* src = a.lut;
-    for (uint32_t i = tid; i < a.lut_entries; i += blockDim.x) {
+    for (uint32_t i = tid; i < a.lut_entries; i += bd) {
       const uint2 e = src[i];
       *lds_ptr<uint32_t>(lut + i * 4) = (e.x & 0xFFFu) | ((e.y & 0x7FFu) << 12) | (e.x & 0xFF000000u);
     }
     if constexpr (E8F8) {
-      for (uint32_t i = tid; i < 256; i += blockDim.x) {
+      for (uint32_t i = tid; i < 256; i += bd) {
         const int w2 = (int)i - 128;                 // doubled coordinate
         const uint32_t mag = e4m3_of_half_int((uint32_t)(w2 < 0 ? -w2 : w2));
         const uint32_t b = mag | (w2 < 0 ? 0x80u : 0u);
@@ -588,20 +747,21 @@ k_decode(const KArgs ka) {
       }
     }
   } else {
-    const uint4* src = reinterpret_cast<const uint4*>(a.lut);
-    const uint32_t n = a.lut_entries / 2, bd = blockDim.x;
-    for (uint32_t i = tid; i < n; i += 2 * bd) {
-      const uint32_t i2 = i + bd;
-      const uint4 v0 = src[i];
-      const uint4 v1 = src[i2 < n ? i2 : i];
-      lds_store4(lut + i * 16, v0);
-      if (i2 < n) lds_store4(lut + i2 * 16, v1);
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const uint32_t idx = tid + (uint32_t)i * bd;
+      if (idx < nl16) lds_store4(lut + idx * 16, lv[i]);
     }
+    for (uint32_t idx = tid + KL * bd; idx < nl16; idx += bd) lds_store4(lut + idx * 16, lsrc[idx]);
+  }
+  if constexpr (!MAT) {
+    if (tid < nxv) x_store(tid, xv0);
+    for (uint32_t v = tid + bd; v < nxv; v += bd) x_store(v, x_load(v));
   }
   if constexpr (PTAB) {
     // symbol -> its codes as 16-bit floats, packed two per word (digits low first)
     // (blocks may have fewer than 256 threads)
-    for (uint32_t sy = tid; sy < 256; sy += blockDim.x) {
+    for (uint32_t sy = tid; sy < 256; sy += bd) {
       constexpr int half = 1 << (CB - 1);
       constexpr uint32_t dmask = (1u << CB) - 1;
       uint32_t w[KW / 2];
@@ -615,38 +775,8 @@ k_decode(const KArgs ka) {
         lds_store2(sy * 8, make_uint2(w[0], w[1]));
     }
   }
-  // ---- A3: stage the block's activation columns, 8 columns (16 bytes) per load:
-  // as fp32 [col][b], or for the dot path as the packed 16-bit pairs [col / 2][b]
-  if constexpr (!MAT) {
-    const uint32_t nvec = a.xs_cols / 8;
-    for (uint32_t v = tid; v < nvec * B; v += blockDim.x) {
-      const uint32_t b = v / nvec, c8 = v - b * nvec, col = c_lo + 8 * c8;
-      uint4 raw = {0u, 0u, 0u, 0u};
-      if (col < c_hi && b < a.nb)
-        raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (uint64_t)b * a.cols + col);
-      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-      if constexpr (DOT) {
-        if constexpr (B == 1) {
-          lds_store4(xs + c8 * 16, raw);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) *lds_ptr<uint32_t>(xs + ((4 * c8 + i) * B + b) * 4) = w4[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint16_t h = (uint16_t)(w4[i >> 1] >> (16 * (i & 1)));
-          const float f = a.x_is_bf16 ? __uint_as_float((uint32_t)h << 16) : (float)__builtin_bit_cast(_Float16, h);
-          *lds_ptr<float>(xs + ((8 * c8 + i) * B + b) * 4) = f;
-        }
-      }
-    }
-  }
   __syncthreads();
 
-  const uint32_t w_sl0 = min(sl_blk + wid * R, sl_blk_end);
-  const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
-  const uint32_t tb = rg * a.n_sl;
   const uint32_t row = rg * 64 + lane;
   const bool active = row < a.rows;
   const bool ragged = (rg + 1) * 64 > a.rows;     // wave-uniform
@@ -656,15 +786,26 @@ k_decode(const KArgs ka) {
   if (w_sl0 < w_sl1) {
     if constexpr (E8) {
       if (ragged)
-        wave_body_e8<B, MAT, true, E8F8>(a, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active, acc);
+        wave_body_e8<B, MAT, true, E8F8>(a, hA, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
+                                         acc);
       else
-        wave_body_e8<B, MAT, false, E8F8>(a, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active, acc);
+        wave_body_e8<B, MAT, false, E8F8>(a, hA, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
+                                          acc);
+    } else if (kTwoCapable && NSr == 2) {
+      if constexpr (kTwoCapable) {
+        if (ragged)
+          wave_body_two<PAY, CB, KW, B, true, XBF>(a, hA, hB, lut, xs, ring, ringB, rg, tb + w_sl0, tb + w_mid,
+                                                   tb + w_mid, tb + w_sl1, c_lo, lane, active, acc);
+        else
+          wave_body_two<PAY, CB, KW, B, false, XBF>(a, hA, hB, lut, xs, ring, ringB, rg, tb + w_sl0, tb + w_mid,
+                                                    tb + w_mid, tb + w_sl1, c_lo, lane, active, acc);
+      }
     } else {
       if (ragged)
-        wave_body<PAY, CB, KW, B, MAT, true, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
-                                                  acc);
+        wave_body<PAY, CB, KW, B, MAT, true, XBF>(a, hA, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane,
+                                                  active, acc);
       else
-        wave_body<PAY, CB, KW, B, MAT, false, XBF>(a, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane,
+        wave_body<PAY, CB, KW, B, MAT, false, XBF>(a, hA, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane,
                                                    active, acc);
     }
   }
@@ -673,11 +814,11 @@ k_decode(const KArgs ka) {
 #pragma unroll
     for (int b = 0; b < B; ++b) *lds_ptr<float>(ring + (b * 64 + lane) * 4) = acc[b];
     __syncthreads();
-    for (uint32_t i = tid; i < 64u * B; i += blockDim.x) {
+    for (uint32_t i = tid; i < 64u * B; i += W * 64) {
       const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
       float s = 0.f;
       for (uint32_t w = 0; w < W; ++w)
-        s += *lds_ptr<const float>(rings + w * (2 * kRingStride) + (b * 64 + l) * 4);
+        s += *lds_ptr<const float>(rings + w * NSr * (2 * kRingStride) + (b * 64 + l) * 4);
       if (a.n_sg == 1) {
         if (r < a.rows && b < a.nb) {
           float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
@@ -706,7 +847,7 @@ struct RArgs {
 
 template <int B>
 __global__ void __launch_bounds__(256) k_reduce(const RArgs ra) {
-  const uint32_t gi = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t gi = blockIdx.x * 256u + threadIdx.x;      // launched with 256 threads
   if (gi >= ra.total_rows) return;
   uint32_t ti = 0;
   for (uint32_t i = 1; i < ra.nt; ++i)
@@ -783,8 +924,10 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
-  (void)R;
-  return pair + lut * 8 + xs + (uint64_t)W * kRingStride * 2;
+  const bool two = !mat && R >= 2 &&
+                   ((t->coding.payload == ECW_P_INT_CODES && t->coding.weights_per_symbol <= 2) ||
+                    t->coding.payload == ECW_P_FP8_E4M3);
+  return pair + lut * 8 + xs + (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
 }
 
 uint64_t launch_lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, int B, bool mat, bool xbf) {
@@ -919,7 +1062,7 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
     a.tiles_per_wave = t->tiles_per_wave;
     a.n_sg = slice_groups(t);
     a.n_blocks = a.n_rg * a.n_sg;
-    a.block_begin = blocks;
+    ka.block_begin[ka.nt] = blocks;
     a.xs_cols = W * t->tiles_per_wave * t->coding.tile_cols;
     blocks += a.n_blocks;
     lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false, x_dtype == ECW_DT_BF16));
@@ -938,11 +1081,13 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
   }
   if (ka.nt == 0) return ECW_OK;
   ka.n_blocks = blocks;
+  ka.waves = W;
   KernelFn fn = pick_gemv_kernel(ts[0]->coding, B, x_dtype == ECW_DT_BF16);
   if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
   if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "launch shape needs more than 160 KiB of LDS");
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   const uint32_t grid = (blocks + 7) / 8 * 8;
+  ka.grid = grid;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
@@ -1095,12 +1240,15 @@ extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, ui
   a.xs_cols = 0;
   ka.nt = 1;
   ka.n_blocks = a.n_blocks;
+  ka.waves = W;
+  ka.block_begin[0] = 0;
   KernelFn fn = pick_kernel<1, true, false>(t->coding);
   if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
   const uint64_t lds = lds_bytes(t, W, 1, 0, 1, true, false);
   if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "decode table needs more than 160 KiB of LDS");
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   const uint32_t grid = (ka.n_blocks + 7) / 8 * 8;
+  ka.grid = grid;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));

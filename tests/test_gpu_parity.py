@@ -214,3 +214,20 @@ def test_e8_gemv_within_bound(case, batch):
     wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
     ok, worst = gemv.check(y.cpu().numpy(), wv, xv)
     assert ok, f"worst error / bound = {worst}"
+
+
+@pytest.mark.parametrize("shape", [(4, 2), (2, 3), (2, 4), (8, 2)])
+@pytest.mark.parametrize("name", ["pair_m11_ragged", "single_int2", "quad_int2", "fp8_m12", "pair_bf16_x"])
+def test_two_streams_per_wave_within_bound(name, shape):
+    # a wave owning R >= 2 tiles decodes two streams in lockstep (INT and FP8 payloads)
+    W, R = shape
+    print(f"[gpu] two streams {name} W={W} R={R}", flush=True)
+    case = [c for c in cases.small_cases() if c.name == name][0]
+    ct = ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
+                              waves_per_block=W, tiles_per_wave=R)
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    for batch in (1, 4):
+        xd, xv = _x(case, batch)
+        y = ct.gemv(xd).cpu().numpy()
+        ok, worst = gemv.check(y, wv, xv)
+        assert ok, worst
