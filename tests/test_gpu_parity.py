@@ -231,3 +231,23 @@ def test_two_streams_per_wave_within_bound(name, shape):
         y = ct.gemv(xd).cpu().numpy()
         ok, worst = gemv.check(y, wv, xv)
         assert ok, worst
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_cross_block_reduction_is_stable(batch):
+    # row groups split over 16 blocks of one wave: the last block of each row group
+    # adds the published partial sums; 20 back-to-back calls must agree bit for bit
+    # and stay within the bound
+    print(f"[gpu] cross-block reduction batch={batch}", flush=True)
+    case = cases._int("split", 320, 2048, 2, 4, 11, 128, seed=31)
+    ct = ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
+                              waves_per_block=1, tiles_per_wave=1)
+    xd, xv = _x(case, batch)
+    y0 = ct.gemv(xd).clone()
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    ok, worst = gemv.check(y0.cpu().numpy(), wv, xv)
+    assert ok, worst
+    ys = [ct.gemv(xd) for _ in range(20)]
+    torch.cuda.synchronize()
+    for y in ys:
+        assert torch.equal(y, y0)
