@@ -375,6 +375,19 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(launch_bytes[dom]), "avg_launch_us": round(avg_us[dom], 3)},
     }
+    # roofline probes on this device: achievable streaming-read rate (2 GiB buffer)
+    # and dependent LDS table lookups (the decode's table reads), all CUs busy
+    big = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    achievable = ecw.probe_stream_read(big)
+    del big
+    lut_rate = {f"m{m}_{eb}B": round(ecw.probe_lds_lookup(m, eb) / 1e9, 1) for m in (11, 12) for eb in (4, 8)}
+    out["probes"] = {"hbm_read_gbs": round(achievable, 1),
+                     "hbm_read_frac_of_peak": round(achievable / HBM_PEAK_GBS, 4),
+                     "dominant_launch_frac_of_achievable": round(achieved / achievable, 4),
+                     "lds_lookups_g_per_s": lut_rate,
+                     "decode_table_lookups_g_per_s": round(sum(layer[n]["tensor"].codes.size
+                                                               // layer[n]["coding"].weights_per_symbol
+                                                               for n in ORDER) / (us_layer * 1e-6) / 1e9, 1)}
     if args.calibrate_copy:
         src = torch.ones(64 << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -101,9 +101,11 @@ def lib():
                                   P(ctypes.c_float)]
     L.dec_time_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz, i32,
                                  P(ctypes.c_float)]
+    L.ecw_probe_stream_read.argtypes = [vp, vp, sz, vp, u32]
+    L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
     for f in ("enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
               "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize",
-              "dec_tune_launch", "dec_time_group"):
+              "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []
     L.ecw_last_error.restype = ctypes.c_char_p
@@ -246,6 +248,45 @@ def materialize_raw(t: Tensor, symbols, w_out, status, stream=None):
                                  symbols.data_ptr() if symbols is not None else None,
                                  w_out.data_ptr() if w_out is not None else None,
                                  status.data_ptr() if status is not None else None), "dec_materialize")
+
+
+# ------------------------------------------------------------------ roofline probes
+def probe_stream_read(buf: torch.Tensor, blocks: int = 2048, reps: int = 5) -> float:
+    """Achievable streaming-read GB/s over the device buffer `buf` (median of reps)."""
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        _check(lib().ecw_probe_stream_read(_stream(None), buf.data_ptr(), nbytes, sink.data_ptr(), blocks),
+               "ecw_probe_stream_read")
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    t = sorted(times[1:])[len(times[1:]) // 2]
+    return nbytes / (t * 1e-3) / 1e9
+
+
+def probe_lds_lookup(log2_m: int, entry_bytes: int, steps: int = 4096, blocks: int = 512,
+                     waves: int = 16) -> float:
+    """Dependent LDS table lookups per second over the whole device (median of 3)."""
+    sink = torch.empty(blocks * waves * 64, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(4):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        _check(lib().ecw_probe_lds_lookup(_stream(None), log2_m, entry_bytes, steps, blocks, waves,
+                                          sink.data_ptr()), "ecw_probe_lds_lookup")
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    t = sorted(times[1:])[1]
+    return blocks * waves * 64 * steps / (t * 1e-3)
 
 
 # ------------------------------------------------------------------ device tensor

@@ -34,12 +34,14 @@ def build(verbose: bool = False) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     host_o = os.path.join(bdir, "ecw_host.o")
-    kern_o = os.path.join(bdir, "ecw_kernels.o")
     _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "ecw_host.cpp"), "-o", host_o], verbose)
-    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "ecw_kernels.hip"), "-o", kern_o], verbose)
+    objs = [host_o]
+    for src in ("ecw_kernels.hip", "ecw_probes.hip"):
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, host_o, kern_o,
-          "-lpthread"], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

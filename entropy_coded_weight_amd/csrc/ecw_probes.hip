@@ -1,0 +1,89 @@
+// Roofline probes for the fused decode: the achievable HBM streaming-read rate and
+// the LDS random-lookup rate of the decode tables, measured on the device the
+// library runs on (the ceilings the decode kernel is compared against).
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "ecw_internal.h"
+
+namespace ecw {
+
+// Streaming read: every thread reads 16-byte vectors in a grid-stride loop, four
+// loads in flight, and folds them into one word so the loads cannot be dropped.
+__global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p, uint64_t n16, uint32_t* out) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// LDS random lookups shaped like the decode: a table of 2^m entries of 4 or 8 bytes,
+// and per lane a dependent chain idx -> entry -> next idx (the state update of the
+// decode is a multiply-add on the entry).  Every wave of the chip runs `steps` steps.
+template <int EB>
+__global__ void __launch_bounds__(1024) k_lds_lookup(uint32_t log2m, uint32_t steps, uint32_t* out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const uint32_t n = 1u << log2m, mask = n - 1u;
+  for (uint32_t i = threadIdx.x; i < n * (EB / 4); i += blockDim.x)
+    reinterpret_cast<uint32_t*>(smem)[i] = i * 2654435761u;
+  __syncthreads();
+  uint32_t x = (blockIdx.x * blockDim.x + threadIdx.x) * 2246822519u + 1u;
+  for (uint32_t s = 0; s < steps; ++s) {
+    const uint32_t slot = x & mask;
+    if constexpr (EB == 8) {
+      const uint2 e = reinterpret_cast<const uint2*>(smem)[slot];
+      x = __umul24(x >> log2m, e.x | 1u) + (e.y >> 16) + 0x9E37u;
+    } else {
+      const uint32_t e = reinterpret_cast<const uint32_t*>(smem)[slot];
+      x = __umul24(x >> log2m, e | 1u) + (e >> 20) + 0x9E37u;
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
+static ecw_status launch_error(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ECW_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ECW_OK;
+}
+
+}  // namespace ecw
+
+using namespace ecw;
+
+extern "C" ecw_status ecw_probe_stream_read(ecw_stream stream, const void* buf, size_t bytes, uint32_t* sink,
+                                            uint32_t blocks) {
+  clear_error();
+  if (!buf || !sink || blocks == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(ECW_E_INVALID_ARG, "stream probe: bad buffer, sink or block count");
+  hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint4*>(buf), (uint64_t)(bytes / 16), sink);
+  return launch_error("stream probe launch failed");
+}
+
+extern "C" ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t entry_bytes,
+                                           uint32_t steps, uint32_t blocks, uint32_t waves_per_block,
+                                           uint32_t* sink) {
+  clear_error();
+  if (!sink || log2_m < 8 || log2_m > 13 || (entry_bytes != 4 && entry_bytes != 8) || blocks == 0 ||
+      waves_per_block == 0 || waves_per_block > 16)
+    return fail(ECW_E_INVALID_ARG, "lookup probe: bad arguments");
+  const size_t lds = ((size_t)entry_bytes) << log2_m;
+  auto fn = entry_bytes == 8 ? k_lds_lookup<8> : k_lds_lookup<4>;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          160 * 1024) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
+  }
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(waves_per_block * 64), lds, (hipStream_t)stream, log2_m, steps, sink);
+  return launch_error("lookup probe launch failed");
+}

@@ -182,6 +182,21 @@ ecw_status dec_time_group(ecw_stream stream, const ecw_tensor* const* t, int n, 
                           float* const* y, int batch, void* workspace, size_t workspace_bytes, int reps,
                           float* us_out);
 
+/* Roofline probes (measurement hooks; asynchronous on `stream`, time them with events).
+ * ecw_probe_stream_read: reads `bytes` (multiple of 16, 16-byte aligned) of device
+ *   memory `buf` once with `blocks` blocks of 256 threads (grid-stride, 16-byte loads)
+ *   and writes one word per thread to `sink` (device, blocks x 256 u32): the
+ *   achievable HBM streaming-read rate the decode is compared against.
+ * ecw_probe_lds_lookup: every lane of `blocks` blocks of `waves_per_block` waves runs
+ *   `steps` dependent lookups into an LDS table of 2^log2_m entries of entry_bytes
+ *   (4 or 8) bytes, the access pattern of the decode's table reads; writes one word
+ *   per thread to `sink` (device, blocks x waves x 64 u32).
+ * Errors: INVALID_ARG, HIP. */
+ecw_status ecw_probe_stream_read(ecw_stream stream, const void* buf, size_t bytes, uint32_t* sink,
+                                 uint32_t blocks);
+ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t entry_bytes, uint32_t steps,
+                                uint32_t blocks, uint32_t waves_per_block, uint32_t* sink);
+
 /* Test hook: the same decode core, writing what dec_gemv keeps in registers.
  *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices);
  *   w_out: nullable device [rows][cols] in the logical dtype (INT int8 codes, BF16

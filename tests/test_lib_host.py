@@ -301,3 +301,10 @@ def test_group_rejects_mismatched_tensors_without_launching():
     assert L.dec_gemv_group(None, arr, 9, 256, 1, ys, 1, None, 0) == 1
     n = ctypes.c_size_t()
     assert L.dec_gemv_group_workspace_size(arr, 2, 1, ctypes.byref(n)) == 0
+
+
+def test_probe_entry_points_reject_bad_arguments():
+    L = ecw.lib()
+    assert L.ecw_probe_stream_read(None, None, 16, None, 1) == 1
+    assert L.ecw_probe_lds_lookup(None, 14, 8, 10, 1, 1, None) == 1
+    assert L.ecw_probe_lds_lookup(None, 11, 6, 10, 1, 1, ctypes.c_void_p(16)) == 1
