@@ -29,12 +29,14 @@ ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
 # launches of one decode step, in data-flow order; tensors of a launch share x
 LAUNCHES = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
 
-# per-tensor coding: (k, log2_m, tile_cols, waves_per_block, tiles_per_wave).  Used
+# per-tensor coding: (k, log2_m, tile_cols, waves_per_block, tiles_per_wave,
+# streams_per_wave, row_groups_per_block).  Used
 # when no tune file exists; `--tune` measures every candidate on the device and
 # writes TUNE_FILE, which later runs load.
-DEFAULT_CODING = {"q": (2, 12, 128, 16, 1), "k": (2, 12, 128, 16, 1), "v": (2, 12, 128, 16, 1),
-                  "o": (2, 12, 128, 16, 1), "gate": (2, 12, 256, 16, 1), "up": (2, 12, 256, 16, 1),
-                  "down": (2, 12, 256, 16, 1)}
+DEFAULT_CODING = {"q": (2, 12, 128, 16, 1, 1, 1), "k": (2, 12, 128, 16, 1, 1, 1),
+                  "v": (2, 12, 128, 16, 1, 1, 1), "o": (2, 12, 128, 16, 1, 1, 1),
+                  "gate": (2, 12, 256, 16, 1, 1, 1), "up": (2, 12, 256, 16, 1, 1, 1),
+                  "down": (2, 12, 256, 16, 1, 1, 1)}
 TUNE_FILE = os.path.join(ROOT, "entropy_coded_weight_amd", "tuned", "llama8b_int4_laplace_batch1.json")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_llama8b_int4_gate_up_traffic.txt")
 
@@ -46,7 +48,8 @@ def load_coding(path: str):
         d = json.load(f)
     coding = dict(DEFAULT_CODING)
     for n, p in d["picks"].items():
-        coding[n] = (p["k"], p["log2_m"], p["tile_cols"], p["waves_per_block"], p["tiles_per_wave"])
+        coding[n] = (p["k"], p["log2_m"], p["tile_cols"], p["waves_per_block"], p["tiles_per_wave"],
+                     p.get("streams_per_wave", 1), p.get("row_groups_per_block", 1))
     return coding, os.path.relpath(path, ROOT)
 
 
@@ -69,7 +72,7 @@ def run_tuner(path: str, batch: int):
         g = A.tune_group({n: specs[n] for n in names}, {n: cands[n] for n in names}, xs[names[0]], log=log)
         picks.update(g)
     table = {n: [dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, stored_bytes=c.stored_bytes,
-                      shapes={f"{w}x{r}": round(us, 3) for (w, r), us in c.shape_us.items()})
+                      shapes={f"{w}x{r}x{ns}x{p}": round(us, 3) for (w, r, ns, p), us in c.shape_us.items()})
                  for c in cands[n]] for n in ORDER}
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
@@ -89,11 +92,11 @@ def build_layer(batch: int, coding: dict):
     layer = {}
     for name in ORDER:
         t = E.config2_tensor(name, layer=0, batch=batch)
-        kk, m, tc, W, R = coding[name]
+        kk, m, tc, W, R, NS, RPB = coding[name]
         n, k = t.codes.shape
         c = ecw.Coding(ecw.INT_CODES, n, k, kk, 4, m, tc)
         blob = ecw.encode(c, t.codes, t.scales)
-        layer[name] = dict(tensor=t, coding=c, blob=blob, launch=(W, R))
+        layer[name] = dict(tensor=t, coding=c, blob=blob, launch=(W, R, NS, RPB))
     return layer
 
 
@@ -362,7 +365,9 @@ def main():
                                        log2_m=layer[n]["coding"].log2_m,
                                        tile_cols=layer[n]["coding"].tile_cols,
                                        waves_per_block=layer[n]["launch"][0],
-                                       tiles_per_wave=layer[n]["launch"][1]) for n in ORDER}},
+                                       tiles_per_wave=layer[n]["launch"][1],
+                                       streams_per_wave=layer[n]["launch"][2],
+                                       row_groups_per_block=layer[n]["launch"][3]) for n in ORDER}},
         "stored_bytes_per_layer": int(layer_bytes),
         "stored_bits_per_weight": round(layer_bytes * 8 / n_weights, 4),
         "gbps_compressed": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

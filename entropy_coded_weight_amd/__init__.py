@@ -55,7 +55,8 @@ class Tables(ctypes.Structure):
 class Tensor(ctypes.Structure):
     _fields_ = [("coding", Coding)] + [(n, ctypes.c_uint32) for n in (
         "n_tables", "n_row_groups", "n_slices", "n_tiles", "steps_full", "steps_last",
-        "lut_entry_bytes", "waves_per_block", "tiles_per_wave", "reserved")] + [
+        "lut_entry_bytes", "waves_per_block", "tiles_per_wave", "streams_per_wave",
+                                         "row_groups_per_block")] + [
         ("blob_bytes", ctypes.c_uint64), ("bytes_words", ctypes.c_uint64),
         ("bytes_raw", ctypes.c_uint64), ("bytes_tile_meta", ctypes.c_uint64),
         ("bytes_tables", ctypes.c_uint64), ("bytes_scales", ctypes.c_uint64),
@@ -293,7 +294,8 @@ def probe_lds_lookup(log2_m: int, entry_bytes: int, steps: int = 4096, blocks: i
 class CompressedTensor:
     """A blob resident in device memory plus its validated descriptor."""
 
-    def __init__(self, blob: np.ndarray, device: str = "cuda", waves_per_block=None, tiles_per_wave=None):
+    def __init__(self, blob: np.ndarray, device: str = "cuda", waves_per_block=None, tiles_per_wave=None,
+                 streams_per_wave=None, row_groups_per_block=None):
         blob = np.ascontiguousarray(blob, dtype=np.uint8)
         self.host_blob = blob
         self.dev = torch.from_numpy(blob).to(device)
@@ -304,6 +306,10 @@ class CompressedTensor:
             self.t.waves_per_block = waves_per_block
         if tiles_per_wave is not None:
             self.t.tiles_per_wave = tiles_per_wave
+        if streams_per_wave is not None:
+            self.t.streams_per_wave = streams_per_wave
+        if row_groups_per_block is not None:
+            self.t.row_groups_per_block = row_groups_per_block
         self._ws = {}
 
     @property
@@ -314,9 +320,12 @@ class CompressedTensor:
     def cols(self):
         return self.t.coding.cols
 
-    def set_launch(self, waves_per_block: int, tiles_per_wave: int):
+    def set_launch(self, waves_per_block: int, tiles_per_wave: int, streams_per_wave: int = 1,
+                   row_groups_per_block: int = 1):
         self.t.waves_per_block = waves_per_block
         self.t.tiles_per_wave = tiles_per_wave
+        self.t.streams_per_wave = streams_per_wave
+        self.t.row_groups_per_block = row_groups_per_block
 
     def stored_bytes(self) -> int:
         t = self.t

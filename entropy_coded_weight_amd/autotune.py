@@ -25,7 +25,9 @@ from . import (INT_CODES, BF16_EXP, FP8_E4M3, Coding, CompressedTensor, EcwError
 
 DEFAULT_LOG2_M = (10, 11, 12)
 DEFAULT_TILE_COLS = (64, 128, 256, 512)
-DEFAULT_SHAPES = tuple((w, r) for w in (4, 8, 16) for r in (1, 2, 4))
+# (waves per block, tiles per wave, streams per wave, row groups per block)
+DEFAULT_SHAPES = tuple((w, r, 1, p) for w in (4, 8, 16) for r in (1, 2) for p in (1, 2, 4)) + \
+    tuple((w, 4, 1, 1) for w in (4, 8, 16)) + tuple((w, r, 2, 1) for w in (4, 8, 16) for r in (2, 4))
 
 
 @dataclass
@@ -34,7 +36,7 @@ class Candidate:
     log2_m: int
     tile_cols: int
     stored_bytes: int
-    shape_us: dict = field(default_factory=dict)     # (W, R) -> us per call (launchable shapes)
+    shape_us: dict = field(default_factory=dict)     # (W, R, S, P) -> us per call (launchable shapes)
 
     def best(self, waves=None):
         items = [(us, s) for s, us in self.shape_us.items() if waves is None or s[0] == waves]
@@ -62,12 +64,12 @@ def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT
 def _tune_launch(ct: CompressedTensor, x: torch.Tensor, shapes, reps: int, stream: torch.cuda.Stream):
     batch = x.shape[0]
     ws_need = 0
-    for w, r in shapes:
-        ct.set_launch(w, r)
+    for w, r, ns, rpb in shapes:
+        ct.set_launch(w, r, ns, rpb)
         ws_need = max(ws_need, workspace_size(ct.t, batch))
     ws = torch.zeros(max(ws_need, 1), dtype=torch.uint8, device=x.device)
     y = torch.empty((batch, ct.rows), dtype=torch.float32, device=x.device)
-    flat = (ctypes.c_uint32 * (2 * len(shapes)))(*[v for s in shapes for v in s])
+    flat = (ctypes.c_uint32 * (4 * len(shapes)))(*[v for s in shapes for v in s])
     us = (ctypes.c_float * len(shapes))()
     xd = DT_F16 if x.dtype == torch.float16 else DT_BF16
     _check(lib().dec_tune_launch(ctypes.c_void_p(stream.cuda_stream), ctypes.byref(ct.t), x.data_ptr(), xd,
@@ -115,7 +117,7 @@ def pick(cands, waves=None, tie: float = 0.02):
     near.sort(key=lambda v: (v[0], v[1]))
     _, us, s, c = near[0]
     return dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
-                us=us, stored_bytes=c.stored_bytes)
+                streams_per_wave=s[2], row_groups_per_block=s[3], us=us, stored_bytes=c.stored_bytes)
 
 
 def time_group(cts, x: torch.Tensor, reps: int = 20, stream: torch.cuda.Stream | None = None) -> float:
@@ -182,7 +184,8 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
             coding = Coding(payload, w.shape[0], w.shape[1], c.k, cb if payload == INT_CODES else 0,
                             c.log2_m, c.tile_cols)
             blobs[key] = encode(coding, w, scales)
-        return CompressedTensor(blobs[key], waves_per_block=shape[0], tiles_per_wave=shape[1])
+        return CompressedTensor(blobs[key], waves_per_block=shape[0], tiles_per_wave=shape[1],
+                                streams_per_wave=shape[2], row_groups_per_block=shape[3])
 
     results = []
     for w in waves:
@@ -195,7 +198,7 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
             nbytes = sum(c.stored_bytes for c, _ in combo)
             results.append((us, nbytes, combo))
             if log:
-                log(f"  group W={w}: " + ", ".join(f"{n}:m={c.log2_m},tc={c.tile_cols},R={s[1]}"
+                log(f"  group W={w}: " + ", ".join(f"{n}:m={c.log2_m},tc={c.tile_cols},R={s[1]},S={s[2]},P={s[3]}"
                                                    for n, (c, s) in zip(names, combo)) + f" -> {us:.2f} us")
             del cts
     if not results:
@@ -204,4 +207,6 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
     near = sorted([r for r in results if r[0] <= t_min * (1 + tie)], key=lambda r: (r[1], r[0]))
     us, _, combo = near[0]
     return {n: dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
-                    us=round(us, 3), stored_bytes=c.stored_bytes) for n, (c, s) in zip(names, combo)}
+                    streams_per_wave=s[2], row_groups_per_block=s[3], us=round(us, 3),
+                    stored_bytes=c.stored_bytes)
+            for n, (c, s) in zip(names, combo)}

@@ -564,6 +564,8 @@ namespace ecw {
 void default_launch(ecw_tensor* t) {
   const uint32_t n_sl = t->n_slices;
   t->tiles_per_wave = 1;
+  t->streams_per_wave = 1;
+  t->row_groups_per_block = 1;
   uint32_t W = std::max(1u, std::min(16u, n_sl));
   while (W > 1 && launch_lds_bytes(t, W, 1, 4, false, true) > 160u * 1024u) W /= 2;
   t->waves_per_block = W;

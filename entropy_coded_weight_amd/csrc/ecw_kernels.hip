@@ -95,7 +95,7 @@ struct TArgs {
   uint32_t* status_out;
   uint32_t rows, cols, n_rg, n_sl, s_full, s_last, log2m, tile_cols;
   uint32_t tiles_per_wave, n_sg, n_blocks, syms_per_row;
-  uint32_t x_is_bf16, nb, lut_entries, xs_cols;
+  uint32_t x_is_bf16, nb, lut_entries, xs_cols, ns, rpb;
   uint32_t raw_full_bytes, raw_rg_bytes;
   const uint8_t* tables;   // TABLES section (E8 decode-only hook: value offsets)
 };
@@ -647,7 +647,10 @@ k_decode(const KArgs ka) {
     if (i < ka.nt && gl >= ka.block_begin[i]) ti = i;
   const TArgs& a = ka.t[ti];
   const uint32_t lb = gl - ka.block_begin[ti];
-  const uint32_t rg = lb / a.n_sg, sg = lb - rg * a.n_sg;
+  // the block's slice group and its run of row groups [r_lo, r_hi)
+  const uint32_t rgi = lb / a.n_sg, sg = lb - rgi * a.n_sg;
+  const uint32_t r_lo = rgi * a.rpb, r_hi = min(r_lo + a.rpb, a.n_rg);
+  uint32_t rg = r_lo;
   const uint32_t R = a.tiles_per_wave;
   const uint32_t sl_blk = sg * W * R;
   const uint32_t sl_blk_end = min(sl_blk + W * R, a.n_sl);
@@ -663,7 +666,7 @@ k_decode(const KArgs ka) {
   const uint32_t rings = xs + xs_bytes;
   // two streams per wave when a wave owns two or more tiles (fused GEMV, INT / FP8)
   constexpr bool kTwoCapable = !MAT && ((PAY == 1 && KW <= 2) || PAY == 3);
-  const uint32_t NSr = (kTwoCapable && R >= 2) ? 2u : 1u;
+  const uint32_t NSr = (kTwoCapable && R >= 2 && a.ns == 2) ? 2u : 1u;
   // wave-uniform LDS addresses, pinned to scalar registers (the compiler otherwise
   // may carry them in VGPRs and pay a vector add per ring read)
   const uint32_t ring = __builtin_amdgcn_readfirstlane(rings + wid * NSr * (2 * kRingStride));
@@ -674,7 +677,7 @@ k_decode(const KArgs ka) {
   const uint32_t w_sl0 = min(sl_blk + wid * R, sl_blk_end);
   const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
   const uint32_t w_mid = NSr == 1 ? w_sl1 : w_sl0 + (w_sl1 - w_sl0 + 1) / 2;
-  const uint32_t tb = rg * a.n_sl;
+  uint32_t tb = rg * a.n_sl;
   StreamHead hA, hB;
   head_begin(a, tb + w_sl0, tb + w_mid, lane, hA);
   if (kTwoCapable && NSr == 2) head_begin(a, tb + w_mid, tb + w_sl1, lane, hB);
@@ -777,6 +780,7 @@ k_decode(const KArgs ka) {
   }
   __syncthreads();
 
+  for (;;) {
   const uint32_t row = rg * 64 + lane;
   const bool active = row < a.rows;
   const bool ragged = (rg + 1) * 64 > a.rows;     // wave-uniform
@@ -829,6 +833,16 @@ k_decode(const KArgs ka) {
         a.partials[(((uint64_t)rg * a.n_sg + sg) * B + b) * 64 + l] = s;
       }
     }
+  }
+  // next row group of the block: new stream heads; the barrier keeps the rings
+  // (which held the reduction slots) untouched until every thread has read them
+  if (++rg >= r_hi) break;
+  tb = rg * a.n_sl;
+  head_begin(a, tb + w_sl0, tb + w_mid, lane, hA);
+  if (kTwoCapable && NSr == 2) head_begin(a, tb + w_mid, tb + w_sl1, lane, hB);
+  head_chunks(a, lane, hA);
+  if (kTwoCapable && NSr == 2) head_chunks(a, lane, hB);
+  __syncthreads();
   }
 }
 
@@ -924,7 +938,7 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
-  const bool two = !mat && R >= 2 &&
+  const bool two = !mat && R >= 2 && t->streams_per_wave == 2 &&
                    ((t->coding.payload == ECW_P_INT_CODES && t->coding.weights_per_symbol <= 2) ||
                     t->coding.payload == ECW_P_FP8_E4M3);
   return pair + lut * 8 + xs + (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
@@ -983,7 +997,8 @@ static ecw_status check_tensor(const ecw_tensor* t) {
   if (reinterpret_cast<uintptr_t>(t->device_blob) % 256) return fail(ECW_E_INVALID_ARG, "device blob misaligned");
   if (t->coding.payload == ECW_P_E8_LATTICE && t->coding.log2_m > 11)
     return fail(ECW_E_UNSUPPORTED, "E8 decode stages 4-byte table entries: M must be at most 2^11");
-  if (t->waves_per_block < 1 || t->waves_per_block > 16 || t->tiles_per_wave < 1 || t->tiles_per_wave > 4096)
+  if (t->waves_per_block < 1 || t->waves_per_block > 16 || t->tiles_per_wave < 1 || t->tiles_per_wave > 4096 ||
+      t->streams_per_wave > 2 || t->row_groups_per_block > 65536)
     return fail(ECW_E_INVALID_ARG, "launch shape out of range");
   if (t->coding.payload != ECW_P_E8_LATTICE && (t->steps_full % 16 || t->steps_last % 16))
     return fail(ECW_E_UNSUPPORTED, "steps per tile must be a multiple of 16");
@@ -1060,8 +1075,10 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
     a.x_is_bf16 = x_dtype == ECW_DT_BF16;
     a.nb = (uint32_t)batch;
     a.tiles_per_wave = t->tiles_per_wave;
+    a.ns = t->streams_per_wave;
+    a.rpb = std::max(1u, t->row_groups_per_block);
     a.n_sg = slice_groups(t);
-    a.n_blocks = a.n_rg * a.n_sg;
+    a.n_blocks = (a.n_rg + a.rpb - 1) / a.rpb * a.n_sg;
     ka.block_begin[ka.nt] = blocks;
     a.xs_cols = W * t->tiles_per_wave * t->coding.tile_cols;
     blocks += a.n_blocks;
@@ -1190,14 +1207,17 @@ extern "C" ecw_status dec_tune_launch(ecw_stream stream, ecw_tensor* t, const vo
   if (!t || !shapes || !us_out || n_shapes < 1 || reps < 1 || reps > 1000)
     return fail(ECW_E_INVALID_ARG, "bad tuning arguments");
   if (!stream) return fail(ECW_E_INVALID_ARG, "tuning captures a graph: pass a created stream, not the default one");
-  const uint32_t W0 = t->waves_per_block, R0 = t->tiles_per_wave;
+  const uint32_t W0 = t->waves_per_block, R0 = t->tiles_per_wave, S0 = t->streams_per_wave,
+                 P0 = t->row_groups_per_block;
   float best = -1.f;
-  uint32_t bestW = W0, bestR = R0;
+  uint32_t bestW = W0, bestR = R0, bestS = S0, bestP = P0;
   ecw_status result = ECW_OK;
   for (int i = 0; i < n_shapes; ++i) {
     us_out[i] = -1.f;
-    t->waves_per_block = shapes[2 * i];
-    t->tiles_per_wave = shapes[2 * i + 1];
+    t->waves_per_block = shapes[4 * i];
+    t->tiles_per_wave = shapes[4 * i + 1];
+    t->streams_per_wave = shapes[4 * i + 2];
+    t->row_groups_per_block = shapes[4 * i + 3];
     float us = 0.f;
     const ecw_status st = time_group(stream, &t, 1, x, x_dtype, &y, batch, workspace, ws_bytes, reps, &us);
     if (st == ECW_E_HIP) {
@@ -1210,10 +1230,14 @@ extern "C" ecw_status dec_tune_launch(ecw_stream stream, ecw_tensor* t, const vo
       best = us;
       bestW = t->waves_per_block;
       bestR = t->tiles_per_wave;
+      bestS = t->streams_per_wave;
+      bestP = t->row_groups_per_block;
     }
   }
   t->waves_per_block = bestW;
   t->tiles_per_wave = bestR;
+  t->streams_per_wave = bestS;
+  t->row_groups_per_block = bestP;
   if (result != ECW_OK) return result;
   if (best < 0.f) return fail(ECW_E_INVALID_ARG, "no launchable candidate shape");
   clear_error();
@@ -1234,6 +1258,8 @@ extern "C" ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, ui
   a.status_out = tile_status;
   a.nb = 1;
   a.tiles_per_wave = 1;   // every tile restarts its stream: per-tile status is exact
+  a.ns = 1;
+  a.rpb = 1;
   const uint32_t W = std::min<uint32_t>(8, t->n_slices);
   a.n_sg = (t->n_slices + W - 1) / W;
   a.n_blocks = a.n_rg * a.n_sg;

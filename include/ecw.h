@@ -88,7 +88,12 @@ typedef struct {
   uint32_t lut_entry_bytes;
   uint32_t waves_per_block;          /* launch shape; dec_prepare sets a default and */
   uint32_t tiles_per_wave;           /* the caller may change it (autotuning)        */
-  uint32_t reserved;
+  uint32_t streams_per_wave;         /* 1, or 2: a wave owning >= 2 tiles decodes its
+                                        two halves as two streams in lockstep (INT
+                                        with <= 2 codes per symbol, FP8); else 1 */
+  uint32_t row_groups_per_block;     /* >= 1: a block decodes this many row groups
+                                        one after the other, staging the decode table
+                                        and activations once */
   uint64_t blob_bytes;
   /* byte ledger of the stored representation */
   uint64_t bytes_words, bytes_raw, bytes_tile_meta, bytes_tables, bytes_scales;
@@ -161,8 +166,8 @@ ecw_status dec_gemv_group(ecw_stream stream, const ecw_tensor* const* t, int n, 
 
 /* Launch-shape autotuning for one tensor (MINE page, Section 4.2: per-tensor
  * tuning of the kernel configuration by measured time).  For each candidate shape
- * shapes[2i] = waves_per_block, shapes[2i+1] = tiles_per_wave, the fused GEMV is
- * captured `reps` times into a HIP graph on `stream` and replayed; us_out[i] receives
+ * shapes[4i..4i+3] = (waves_per_block, tiles_per_wave, streams_per_wave,
+ * row_groups_per_block), the fused GEMV is captured `reps` times into a HIP graph on `stream` and replayed; us_out[i] receives
  * the mean microseconds per call, or -1 when the shape is not launchable (e.g. it
  * needs more than 160 KiB of LDS).  x, y, batch as for dec_gemv; the workspace must
  * hold the largest dec_gemv_workspace_size over the candidates.  On return t's

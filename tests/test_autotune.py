@@ -31,9 +31,9 @@ def _cand(k, m, tc, nbytes, shapes):
 
 
 def test_pick_prefers_speed_then_size_within_tie():
-    a = _cand(2, 12, 128, 1000, {(16, 1): 10.0, (8, 1): 12.0})
-    b = _cand(2, 11, 128, 900, {(16, 1): 10.1})          # within 2%, smaller: wins
-    c = _cand(2, 10, 128, 500, {(16, 1): 11.0})          # 10% slower: loses despite size
+    a = _cand(2, 12, 128, 1000, {(16, 1, 1, 1): 10.0, (8, 1, 1, 1): 12.0})
+    b = _cand(2, 11, 128, 900, {(16, 1, 1, 1): 10.1})          # within 2%, smaller: wins
+    c = _cand(2, 10, 128, 500, {(16, 1, 1, 1): 11.0})          # 10% slower: loses despite size
     p = A.pick([a, b, c])
     assert (p["log2_m"], p["waves_per_block"], p["stored_bytes"]) == (11, 16, 900)
     p8 = A.pick([a, b, c], waves=8)
@@ -42,10 +42,10 @@ def test_pick_prefers_speed_then_size_within_tie():
 
 
 def test_ranked_takes_the_fastest_shapes_per_candidate():
-    a = _cand(2, 12, 128, 1, {(16, 1): 10.0, (16, 2): 9.0, (8, 1): 11.0})
-    b = _cand(2, 11, 128, 1, {(16, 1): 9.5})
+    a = _cand(2, 12, 128, 1, {(16, 1, 1, 1): 10.0, (16, 2, 1, 1): 9.0, (8, 1, 1, 1): 11.0})
+    b = _cand(2, 11, 128, 1, {(16, 1, 1, 1): 9.5})
     r = A._ranked([a, b], 16, 2)
-    assert [(c.log2_m, s) for c, s in r] == [(12, (16, 2)), (11, (16, 1))]
+    assert [(c.log2_m, s) for c, s in r] == [(12, (16, 2, 1, 1)), (11, (16, 1, 1, 1))]
     assert A._ranked([a, b], 4, 2) == []
 
 
@@ -53,7 +53,7 @@ def test_tune_rejects_null_stream_without_launching():
     case = cases.small_cases()[1]
     ct = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
     us = (ctypes.c_float * 1)()
-    shapes = (ctypes.c_uint32 * 2)(4, 1)
+    shapes = (ctypes.c_uint32 * 4)(4, 1, 1, 1)
     st = ecw.lib().dec_tune_launch(None, ctypes.byref(ct), None, ecw.DT_F16, None, 1, None, 0, shapes, 1, 5, us)
     assert st == 1   # ECW_E_INVALID_ARG
 
@@ -68,7 +68,7 @@ def test_device_tuning_picks_a_shape_that_stays_correct():
     xh = rng.standard_normal((1, case.cols)).astype(np.float16)
     x = torch.from_numpy(xh).cuda()
     cands = A.tune_tensor(ecw.INT_CODES, case.logical, case.scales, x, code_bits=4, ks=(2,),
-                          log2_ms=(11, 12), tile_cols=(128, 256), shapes=((4, 1), (8, 1), (16, 2)), reps=5)
+                          log2_ms=(11, 12), tile_cols=(128, 256), shapes=((4, 1, 1, 1), (8, 1, 1, 2), (16, 2, 2, 1)), reps=5)
     assert len(cands) == 4 and all(c.shape_us for c in cands)
     # a two-member group of the same tensor shares one waves-per-block value
     g = A.tune_group({"a": (ecw.INT_CODES, case.logical, case.scales, 4),
@@ -77,8 +77,9 @@ def test_device_tuning_picks_a_shape_that_stays_correct():
     assert g["a"]["waves_per_block"] == g["b"]["waves_per_block"]
     p = A.pick(cands)
     c = ecw.Coding(ecw.INT_CODES, case.rows, case.cols, p["k"], 4, p["log2_m"], p["tile_cols"])
-    ct = ecw.CompressedTensor(ecw.encode(c, case.logical, case.scales),
-                              waves_per_block=p["waves_per_block"], tiles_per_wave=p["tiles_per_wave"])
+    ct = ecw.CompressedTensor(ecw.encode(c, case.logical, case.scales), waves_per_block=p["waves_per_block"],
+                              tiles_per_wave=p["tiles_per_wave"], streams_per_wave=p["streams_per_wave"],
+                              row_groups_per_block=p["row_groups_per_block"])
     y = ct.gemv(x).cpu().numpy()
     wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
     ok, worst = gemv.check(y, wv, gemv.x_values(xh, "f16"))

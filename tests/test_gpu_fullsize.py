@@ -61,7 +61,9 @@ def test_config2_layer_set_at_the_benchmarked_launches():
             p = tune[n]
             c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"])
             cts.append(ecw.CompressedTensor(ecw.encode(c, t.codes, t.scales), waves_per_block=p["waves_per_block"],
-                                            tiles_per_wave=p["tiles_per_wave"]))
+                                            tiles_per_wave=p["tiles_per_wave"],
+                                            streams_per_wave=p.get("streams_per_wave", 1),
+                                            row_groups_per_block=p.get("row_groups_per_block", 1)))
             ts.append(t)
         x = torch.from_numpy(ts[0].x).cuda()
         ys = ecw.GemvGroup(cts).gemv(x)

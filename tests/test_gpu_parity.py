@@ -224,7 +224,7 @@ def test_two_streams_per_wave_within_bound(name, shape):
     print(f"[gpu] two streams {name} W={W} R={R}", flush=True)
     case = [c for c in cases.small_cases() if c.name == name][0]
     ct = ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
-                              waves_per_block=W, tiles_per_wave=R)
+                              waves_per_block=W, tiles_per_wave=R, streams_per_wave=2)
     wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
     for batch in (1, 4):
         xd, xv = _x(case, batch)
@@ -251,3 +251,25 @@ def test_cross_block_reduction_is_stable(batch):
     torch.cuda.synchronize()
     for y in ys:
         assert torch.equal(y, y0)
+
+
+@pytest.mark.parametrize("shape", [(4, 1, 2), (2, 2, 3), (8, 1, 5), (1, 1, 4)])
+@pytest.mark.parametrize("name", ["pair_m11_ragged", "cfg1_gauss_k1_m12", "fp8_m12", "bf16_m12"])
+def test_row_groups_per_block_match_one_per_block(name, shape):
+    # a block decoding several row groups in sequence (staging once) gives the same
+    # bits as one row group per block: same wave order, same block order
+    W, R, P_ = shape
+    print(f"[gpu] row groups per block {name} W={W} R={R} P={P_}", flush=True)
+    case = [c for c in cases.small_cases() if c.name == name][0]
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    one = ecw.CompressedTensor(blob, waves_per_block=W, tiles_per_wave=R, row_groups_per_block=1)
+    many = ecw.CompressedTensor(blob, waves_per_block=W, tiles_per_wave=R, row_groups_per_block=P_)
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    for batch in (1, 4):
+        xd, xv = _x(case, batch)
+        y1 = one.gemv(xd)
+        yp = many.gemv(xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, yp)
+        ok, worst = gemv.check(yp.cpu().numpy(), wv, xv)
+        assert ok, worst
