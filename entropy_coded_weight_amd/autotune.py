@@ -26,8 +26,7 @@ from . import (INT_CODES, BF16_EXP, FP8_E4M3, Coding, CompressedTensor, EcwError
 DEFAULT_LOG2_M = (10, 11, 12)
 DEFAULT_TILE_COLS = (64, 128, 256, 512)
 # (waves per block, tiles per wave, streams per wave, row groups per block)
-DEFAULT_SHAPES = tuple((w, r, 1, p) for w in (4, 8, 16) for r in (1, 2) for p in (1, 2, 4)) + \
-    tuple((w, 4, 1, 1) for w in (4, 8, 16)) + tuple((w, r, 2, 1) for w in (4, 8, 16) for r in (2, 4))
+DEFAULT_SHAPES = tuple((w, r, ns, p) for w in (4, 8, 16) for r in (1, 2, 4) for ns in (1, 2) for p in (1, 2))
 
 
 @dataclass

@@ -576,11 +576,19 @@ uint32_t slice_groups(const ecw_tensor* t) {
   return per ? (t->n_slices + per - 1) / per : 0;
 }
 
-uint64_t workspace_bytes(const ecw_tensor* t, int batch) {
+uint64_t partial_bytes(const ecw_tensor* t, int batch) {
   const uint32_t nsg = slice_groups(t);
   if (nsg <= 1) return 0;
   const uint64_t B = batch > 1 ? 4 : 1;   // kernels are built for batch capacity 1 or 4
   return align_up((uint64_t)t->n_row_groups * nsg * B * 64 * 4, 256);
+}
+
+uint64_t ticket_bytes(const ecw_tensor* t) { return align_up((uint64_t)t->n_row_groups * 4, 256); }
+
+// one u32 arrival ticket per row group, then the partial sums
+uint64_t workspace_bytes(const ecw_tensor* t, int batch) {
+  const uint64_t p = partial_bytes(t, batch);
+  return p ? ticket_bytes(t) + p : 0;
 }
 
 }  // namespace ecw

@@ -29,5 +29,8 @@ void default_launch(ecw_tensor* t);
 uint64_t launch_lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, int B, bool mat, bool xbf);
 uint32_t slice_groups(const ecw_tensor* t);
 uint64_t workspace_bytes(const ecw_tensor* t, int batch);
+// a tensor's workspace: arrival tickets (one per row group), then per-block partial sums
+uint64_t ticket_bytes(const ecw_tensor* t);
+uint64_t partial_bytes(const ecw_tensor* t, int batch);
 
 }  // namespace ecw

@@ -20,9 +20,10 @@
 // weights live in registers between decode and FMA.
 //
 // Cross-wave reduction: the waves of a block cover consecutive column slices of
-// the same 64 rows and are summed in LDS in wave order; when a row group spans
-// several blocks each block writes a partial and a second small kernel sums them in
-// block order.  Both orders are fixed, so results do not depend on scheduling.
+// the same 64 rows and are summed in LDS in wave order.  When a row group spans
+// several blocks, each block publishes its partial sums and takes a ticket; the
+// block that arrives last adds all partials in block order.  Both orders are fixed,
+// so results do not depend on scheduling.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -89,7 +90,8 @@ struct TArgs {
   const uint16_t* scales;
   const void* x;
   float* y;
-  float* partials;
+  float* partials;          // [n_rg][n_sg][B][64] per-block sums (row groups over several blocks)
+  uint32_t* tickets;        // [n_rg] arrival counters, zero between calls
   uint16_t* sym_out;
   void* w_out;
   uint32_t* status_out;
@@ -149,6 +151,15 @@ __device__ __forceinline__ uint32_t shift_in(uint64_t mask, uint32_t x, uint32_t
   return x;
 }
 
+// Pins a value at this point of the instruction stream: the multiply-adds of a step
+// are then issued with the step instead of being sunk to the end of the unrolled
+// loop, which would keep every step's table entry live (and spill).
+template <int B>
+__device__ __forceinline__ void pin(float* acc) {
+#pragma unroll
+  for (int b = 0; b < B; ++b) asm volatile("" : "+v"(acc[b]));
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -183,18 +194,56 @@ __device__ __forceinline__ void renorm_step(uint32_t& x, uint32_t& rposb, uint32
   asm("s_lshl1_add_u32 %0, %1, %0" : "+s"(rposb) : "s"(cnt) : "scc");
 }
 
+// The same step split in two halves, so that two streams issue both ring reads
+// before either waits (the exec-masked shift is an asm block, which the compiler
+// does not move loads across).
+struct RenormRead {
+  uint64_t mask;
+  uint32_t w;
+};
+
+template <bool RAGGED>
+__device__ __forceinline__ RenormRead renorm_read(uint32_t x, uint32_t rposb, uint32_t ring, bool active) {
+  RenormRead r;
+  if constexpr (RAGGED)
+    r.mask = __ballot(active && (x < kStateL));
+  else
+    r.mask = __builtin_amdgcn_ballot_w64(x < kStateL);
+  const uint32_t base = ring + (rposb & (2 * kRing - 2));
+  r.w = *lds_ptr<const uint16_t>(base + (lanes_below(r.mask) << 1));
+  return r;
+}
+
+// Both streams' shifts in one asm block: its inputs are both ring words, so the
+// two ring reads are issued before the first wait.
+__device__ __forceinline__ void renorm_apply2(const RenormRead& ra, uint32_t& xa, uint32_t& rposa,
+                                              const RenormRead& rb, uint32_t& xb, uint32_t& rposb) {
+  uint64_t save;
+  asm("s_and_saveexec_b64 %2, %3\n\tv_lshl_or_b32 %0, %0, 16, %4\n\ts_mov_b64 exec, %2\n\t"
+      "s_and_saveexec_b64 %2, %5\n\tv_lshl_or_b32 %1, %1, 16, %6\n\ts_mov_b64 exec, %2"
+      : "+v"(xa), "+v"(xb), "=&s"(save) : "s"(ra.mask), "v"(ra.w), "s"(rb.mask), "v"(rb.w) : "scc");
+  const uint32_t ca = (uint32_t)__popcll(ra.mask), cb = (uint32_t)__popcll(rb.mask);
+  asm("s_lshl1_add_u32 %0, %2, %0\n\ts_lshl1_add_u32 %1, %3, %1" : "+s"(rposa), "+s"(rposb) : "s"(ca), "s"(cb)
+      : "scc");
+}
+
 // Keep the next four steps' reads inside committed ring data: commit the chunk held
 // in `pre` when fewer than 256 words are ahead of the read position, and load the
-// next one into `pre` (one chunk of prefetch distance).
-__device__ __forceinline__ void refill(uint32_t rposb, uint32_t& haveb, uint32_t& nc, uint2& pre, uint32_t ring,
+// next one into `pre` (one chunk of prefetch distance).  wl: this lane's byte
+// address in the stream's ring (ring + 8 * lane); src: the stream's first chunk
+// (wave-uniform).
+__device__ __forceinline__ void refill(uint32_t rposb, uint32_t& haveb, uint32_t& nc, uint2& pre, uint32_t wl,
                                        const uint2* src, uint32_t nch, uint32_t lane) {
   if (rposb + 8 * 64 > haveb) {      // wave-uniform
-    const uint32_t slot = nc & 1u;
-    lds_store2(ring + slot * (2 * kChunk) + lane * 8, pre);
-    if (slot == 0 && lane < 16) lds_store2(ring + 2 * kRing + lane * 8, pre);
+    if (nc & 1u) {
+      lds_store2(wl + 2 * kChunk, pre);
+    } else {
+      lds_store2(wl, pre);
+      if (lane < 16) lds_store2(wl + 2 * kRing, pre);
+    }
     haveb += 2 * kChunk;
     ++nc;
-    if (nc < nch) pre = src[(uint64_t)nc * 64];
+    if (nc < nch) pre = src[(uint64_t)nc * 64 + lane];
   }
 }
 
@@ -275,18 +324,19 @@ __device__ __forceinline__ void head_chunks(const TArgs& a, uint32_t lane, Strea
   h.gb = wb & ~(kChunk - 1);
   h.nch = (we - h.gb + kChunk - 1) / kChunk;
   h.rposb = (wb - h.gb) * 2;
-  h.src = reinterpret_cast<const uint2*>(a.words + h.gb) + lane;
+  h.src = reinterpret_cast<const uint2*>(a.words + h.gb);
   const uint2 zero2 = {0u, 0u};
-  h.c0 = h.nch > 0 ? h.src[0] : zero2;
-  h.c1 = h.nch > 1 ? h.src[64] : zero2;
-  h.pre = h.nch > 2 ? h.src[128] : zero2;
+  h.c0 = h.nch > 0 ? h.src[lane] : zero2;
+  h.c1 = h.nch > 1 ? h.src[64 + lane] : zero2;
+  h.pre = h.nch > 2 ? h.src[128 + lane] : zero2;
 }
 
 // First two chunks into the ring (and the head mirror); after the block barrier.
-__device__ __forceinline__ void head_ring(const StreamHead& h, uint32_t ring, uint32_t lane) {
-  lds_store2(ring + lane * 8, h.c0);
-  if (lane < 16) lds_store2(ring + 2 * kRing + lane * 8, h.c0);
-  lds_store2(ring + 2 * kChunk + lane * 8, h.c1);
+// wl: ring + 8 * lane.
+__device__ __forceinline__ void head_ring(const StreamHead& h, uint32_t wl, uint32_t lane) {
+  lds_store2(wl, h.c0);
+  if (lane < 16) lds_store2(wl + 2 * kRing, h.c0);
+  lds_store2(wl + 2 * kChunk, h.c1);
 }
 
 // The wave body: the wave's tiles [t0, t1) (consecutive slices of one row group)
@@ -306,7 +356,8 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
   const uint32_t sl0 = rg * a.n_sl;
   const uint4 zero4 = {0u, 0u, 0u, 0u};
 
-  head_ring(h, ring, lane);
+  const uint32_t wl = ring + lane * 8;
+  head_ring(h, wl, lane);
   const uint32_t gb = h.gb, nch = h.nch;
   const uint2* src = h.src;
   uint32_t rposb = h.rposb;
@@ -329,7 +380,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
       const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
-        refill(rposb, haveb, nc, pre, ring, src, nch, lane);
+        refill(rposb, haveb, nc, pre, wl, src, nch, lane);
         uint4 xq[MAT ? 1 : XW];
         if constexpr (!MAT) {
 #pragma unroll
@@ -343,6 +394,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
           if constexpr (!MAT) {
             mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW,
                                      PAY == 2 ? raw_byte(rgp, u) : 0u, acc);
+            pin<B>(acc);
           } else if (!RAGGED || active) {
             const uint32_t aux = e.x >> 24;
             uint32_t symbol = aux;
@@ -384,24 +436,30 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
   }
 }
 
-// Two word streams per wave (fused GEMV only): tiles [tA0, tA1) and [tB0, tB1) of
-// the same row group are decoded in lockstep, two independent dependency chains per
-// wave, each with its own ring.  B's tiles follow A's, so only B can hold the short
-// last slice (SB <= SA).
+// Two word streams per wave (fused GEMV only): the tiles of row groups rg and rg + 1
+// at the same slices [sl0, sl1) are decoded in lockstep.  The two dependency chains
+// (table read -> state update -> ballot / prefix -> ring read) interleave, and both
+// streams multiply the same activation columns, so every activation read is shared.
+// Both tiles of a slice have the same number of steps: the loop has no per-step
+// branch.  Only stream B (the higher row group) can be ragged.  Each lane sums its
+// own row in step order, exactly as a one-stream wave does, so the results are the
+// same bits.
 template <int PAY, int CB, int KW, int B, bool RAGGED, bool XBF>
-__device__ __forceinline__ void wave_body_two(const TArgs& a, const StreamHead& hA, const StreamHead& hB,
-                                              uint32_t lut, uint32_t xs, uint32_t ringA, uint32_t ringB,
-                                              uint32_t rg, uint32_t tA0, uint32_t tA1, uint32_t tB0, uint32_t tB1,
-                                              uint32_t c_lo, uint32_t lane, bool active, float* acc) {
+__device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead& hA, const StreamHead& hB,
+                                                uint32_t lut, uint32_t xs, uint32_t ringA, uint32_t ringB,
+                                                uint32_t rg, uint32_t sl0, uint32_t sl1, uint32_t c_lo,
+                                                uint32_t lane, bool activeB, float* accA, float* accB) {
   constexpr int U = 16;
   constexpr bool DOT = kDot<PAY, KW>;
   constexpr bool CLEAN = kCleanBias<PAY, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
-  const uint32_t sl0 = rg * a.n_sl;
+  const uint4 zero4 = {0u, 0u, 0u, 0u};
 
-  head_ring(hA, ringA, lane);
-  head_ring(hB, ringB, lane);
+  // ring B sits at a fixed distance after ring A: one lane address serves both
+  const uint32_t wl = ringA + lane * 8;
+  head_ring(hA, wl, lane);
+  head_ring(hB, wl + 2 * kRingStride, lane);
   const uint32_t nchA = hA.nch, nchB = hB.nch;
   const uint2* srcA = hA.src;
   const uint2* srcB = hB.src;
@@ -409,50 +467,48 @@ __device__ __forceinline__ void wave_body_two(const TArgs& a, const StreamHead& 
   uint2 preA = hA.pre, preB = hB.pre;
   uint32_t haveA = 4 * kChunk, ncA = 2, haveB = 4 * kChunk, ncB = 2;
   uint32_t stA = hA.st, stB = hB.st;
+  const uint32_t tA0 = rg * a.n_sl, tB0 = tA0 + a.n_sl;
 
-  uint32_t tB = tB0;
-  for (uint32_t tA = tA0; tA < tA1; ++tA) {
-    const bool pairB = tB < tB1;                          // wave-uniform
+  for (uint32_t sl = sl0; sl < sl1; ++sl) {
     uint32_t xA = stA, xB = stB;
-    if (tA + 1 < tA1) stA = a.states[(uint64_t)(tA + 1) * 64 + lane];
-    if (pairB && tB + 1 < tB1) stB = a.states[(uint64_t)(tB + 1) * 64 + lane];
-    const uint32_t slA = tA - sl0, slB = tB - sl0;
-    const uint32_t SA = (slA + 1 == a.n_sl) ? a.s_last : a.s_full;
-    const uint32_t SB = pairB ? ((slB + 1 == a.n_sl) ? a.s_last : a.s_full) : 0;
-    const uint32_t xgA0 = xs + ((slA * a.tile_cols - c_lo) * B / (DOT ? 2 : 1)) * 4;
-    const uint32_t xgB0 = xs + ((slB * a.tile_cols - c_lo) * B / (DOT ? 2 : 1)) * 4;
-    for (uint32_t j = 0; j < SA; j += U) {
-      const bool dualB = j < SB;                            // wave-uniform
-      const uint32_t xgA = xgA0 + ((KW * j) * B / (DOT ? 2 : 1)) * 4;
-      const uint32_t xgB = xgB0 + ((KW * j) * B / (DOT ? 2 : 1)) * 4;
+    if (sl + 1 < sl1) {
+      stA = a.states[(uint64_t)(tA0 + sl + 1) * 64 + lane];
+      stB = a.states[(uint64_t)(tB0 + sl + 1) * 64 + lane];
+    }
+    const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
+    const uint32_t col = sl * a.tile_cols - c_lo;
+    const uint8_t* rawA = raw_tile(a, rg, sl, lane);
+    const uint8_t* rawB = raw_tile(a, rg + 1, sl, lane);
+    for (uint32_t j = 0; j < S; j += U) {
+      uint4 rgA = zero4, rgB = zero4;
+      if constexpr (PAY == 2) {
+        rgA = *reinterpret_cast<const uint4*>(rawA + (uint64_t)(j / U) * 1024);
+        rgB = *reinterpret_cast<const uint4*>(rawB + (uint64_t)(j / U) * 1024);
+      }
+      const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
-        refill(rposA, haveA, ncA, preA, ringA, srcA, nchA, lane);
-        if (dualB) refill(rposB, haveB, ncB, preB, ringB, srcB, nchB, lane);
-        uint4 xqA[XW], xqB[XW];
+        refill(rposA, haveA, ncA, preA, wl, srcA, nchA, lane);
+        refill(rposB, haveB, ncB, preB, wl + 2 * kRingStride, srcB, nchB, lane);
+        uint4 xq[XW];
 #pragma unroll
-        for (int i = 0; i < XW; ++i) xqA[i] = lds_load4(xgA + (qtr * XW + i) * 16);
-        if (dualB) {
-#pragma unroll
-          for (int i = 0; i < XW; ++i) xqB[i] = lds_load4(xgB + (qtr * XW + i) * 16);
-        }
+        for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
+          const int u = qtr * 4 + u4;
           const uint2 eA = decode_step<CLEAN>(xA, lut, m, mmask);
-          if (dualB) {
-            const uint2 eB = decode_step<CLEAN>(xB, lut, m, mmask);
-            mac<PAY, CB, KW, B, XBF>(eA, reinterpret_cast<const uint32_t*>(xqA) + u4 * XW, 0u, acc);
-            mac<PAY, CB, KW, B, XBF>(eB, reinterpret_cast<const uint32_t*>(xqB) + u4 * XW, 0u, acc);
-            renorm_step<RAGGED>(xA, rposA, ringA, active);
-            renorm_step<RAGGED>(xB, rposB, ringB, active);
-          } else {
-            mac<PAY, CB, KW, B, XBF>(eA, reinterpret_cast<const uint32_t*>(xqA) + u4 * XW, 0u, acc);
-            renorm_step<RAGGED>(xA, rposA, ringA, active);
-          }
+          const uint2 eB = decode_step<CLEAN>(xB, lut, m, mmask);
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(xq) + u4 * XW;
+          mac<PAY, CB, KW, B, XBF>(eA, xw, PAY == 2 ? raw_byte(rgA, u) : 0u, accA);
+          mac<PAY, CB, KW, B, XBF>(eB, xw, PAY == 2 ? raw_byte(rgB, u) : 0u, accB);
+          pin<B>(accA);
+          pin<B>(accB);
+          const RenormRead rA = renorm_read<false>(xA, rposA, ringA, true);
+          const RenormRead rB = renorm_read<RAGGED>(xB, rposB, ringB, activeB);
+          renorm_apply2(rA, xA, rposA, rB, xB, rposB);
         }
       }
     }
-    if (pairB) ++tB;
   }
 }
 
@@ -483,7 +539,8 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
   const uint32_t row = rg * 64 + lane;
   const uint32_t sl0 = rg * a.n_sl;
 
-  head_ring(h, ring, lane);
+  const uint32_t wl = ring + lane * 8;
+  head_ring(h, wl, lane);
   const uint32_t gb = h.gb, nch = h.nch;
   const uint2* src = h.src;
   uint32_t rposb = h.rposb;
@@ -511,7 +568,7 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
           xv[4 * i + 3] = __uint_as_float(q.w);
         }
       }
-      refill(rposb, haveb, nc, pre, ring, src, nch, lane);
+      refill(rposb, haveb, nc, pre, wl, src, nch, lane);
       const int c = e8_decode<MAT>(x, lut + ((x & mmask) << 2), m) & 1;    // coset, table 0
       if constexpr (MAT) {
         if ((!RAGGED || active) && a.sym_out) {
@@ -524,7 +581,7 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
       int zsum = 0;
 #pragma unroll
       for (int j = 1; j <= 8; ++j) {
-        if (j == 4 || j == 8) refill(rposb, haveb, nc, pre, ring, src, nch, lane);
+        if (j == 4 || j == 8) refill(rposb, haveb, nc, pre, wl, src, nch, lane);
         const int v = e8_decode<MAT>(x, tb + (uint32_t)(j - 1) * tbytes + ((x & mmask) << 2), m);
         int z;
         if (j < 8) {
@@ -647,16 +704,22 @@ k_decode(const KArgs ka) {
     if (i < ka.nt && gl >= ka.block_begin[i]) ti = i;
   const TArgs& a = ka.t[ti];
   const uint32_t lb = gl - ka.block_begin[ti];
-  // the block's slice group and its run of row groups [r_lo, r_hi)
+  constexpr bool E8 = PAY == 4;
+  // streams per wave: 2 = the tiles of two adjacent row groups in lockstep (fused
+  // GEMV of INT, BF16 and FP8 payloads)
+  constexpr bool kTwoCapable = !MAT && !E8;
+  const uint32_t NSr = (kTwoCapable && a.ns == 2) ? 2u : 1u;
+  // the block's slice group and its run of row-group units [u_lo, u_hi); a unit is
+  // NSr adjacent row groups, decoded by the waves' streams
   const uint32_t rgi = lb / a.n_sg, sg = lb - rgi * a.n_sg;
-  const uint32_t r_lo = rgi * a.rpb, r_hi = min(r_lo + a.rpb, a.n_rg);
-  uint32_t rg = r_lo;
+  const uint32_t n_units = (a.n_rg + NSr - 1) / NSr;
+  const uint32_t u_lo = rgi * a.rpb, u_hi = min(u_lo + a.rpb, n_units);
+  uint32_t rg = u_lo * NSr;
   const uint32_t R = a.tiles_per_wave;
   const uint32_t sl_blk = sg * W * R;
   const uint32_t sl_blk_end = min(sl_blk + W * R, a.n_sl);
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
-  constexpr bool E8 = PAY == 4;
   constexpr bool E8F8 = E8 && CB == 1;            // E8: CB selects the FP8 reconstruction
   const uint32_t pair_bytes = PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
   const uint32_t lut = pair_bytes;
@@ -664,9 +727,6 @@ k_decode(const KArgs ka) {
   const uint32_t xs = lut + lut_bytes;
   const uint32_t xs_bytes = MAT ? 0 : ((a.xs_cols * B * (DOT ? 2 : 4) + 15) & ~15u);
   const uint32_t rings = xs + xs_bytes;
-  // two streams per wave when a wave owns two or more tiles (fused GEMV, INT / FP8)
-  constexpr bool kTwoCapable = !MAT && ((PAY == 1 && KW <= 2) || PAY == 3);
-  const uint32_t NSr = (kTwoCapable && R >= 2 && a.ns == 2) ? 2u : 1u;
   // wave-uniform LDS addresses, pinned to scalar registers (the compiler otherwise
   // may carry them in VGPRs and pay a vector add per ring read)
   const uint32_t ring = __builtin_amdgcn_readfirstlane(rings + wid * NSr * (2 * kRingStride));
@@ -676,11 +736,11 @@ k_decode(const KArgs ka) {
   // staging loads so both latencies overlap
   const uint32_t w_sl0 = min(sl_blk + wid * R, sl_blk_end);
   const uint32_t w_sl1 = min(w_sl0 + R, sl_blk_end);
-  const uint32_t w_mid = NSr == 1 ? w_sl1 : w_sl0 + (w_sl1 - w_sl0 + 1) / 2;
   uint32_t tb = rg * a.n_sl;
   StreamHead hA, hB;
-  head_begin(a, tb + w_sl0, tb + w_mid, lane, hA);
-  if (kTwoCapable && NSr == 2) head_begin(a, tb + w_mid, tb + w_sl1, lane, hB);
+  bool hasB = NSr == 2 && rg + 1 < a.n_rg;        // wave-uniform
+  head_begin(a, tb + w_sl0, tb + w_sl1, lane, hA);
+  if (kTwoCapable && hasB) head_begin(a, tb + a.n_sl + w_sl0, tb + a.n_sl + w_sl1, lane, hB);
 
   // ---- A2 / A3 prologue.  Every global load is issued before the first wait: the
   // first round of the decode table (up to 4 x 16 bytes per thread) and of the
@@ -732,7 +792,7 @@ k_decode(const KArgs ka) {
   }
   // first word chunks of the stream(s): in flight across the LDS writes and barrier
   head_chunks(a, lane, hA);
-  if (kTwoCapable && NSr == 2) head_chunks(a, lane, hB);
+  if (kTwoCapable && hasB) head_chunks(a, lane, hB);
 
   if constexpr (E8) {
     // E8 tables are packed to 4-byte entries on the way
@@ -784,105 +844,118 @@ k_decode(const KArgs ka) {
   const uint32_t row = rg * 64 + lane;
   const bool active = row < a.rows;
   const bool ragged = (rg + 1) * 64 > a.rows;     // wave-uniform
-  float acc[B];
+  float acc[2][B];
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.f;
+  for (int b = 0; b < B; ++b) acc[0][b] = acc[1][b] = 0.f;
   if (w_sl0 < w_sl1) {
     if constexpr (E8) {
       if (ragged)
         wave_body_e8<B, MAT, true, E8F8>(a, hA, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
-                                         acc);
+                                         acc[0]);
       else
         wave_body_e8<B, MAT, false, E8F8>(a, hA, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
-                                          acc);
-    } else if (kTwoCapable && NSr == 2) {
+                                          acc[0]);
+    } else if (kTwoCapable && hasB) {
       if constexpr (kTwoCapable) {
-        if (ragged)
-          wave_body_two<PAY, CB, KW, B, true, XBF>(a, hA, hB, lut, xs, ring, ringB, rg, tb + w_sl0, tb + w_mid,
-                                                   tb + w_mid, tb + w_sl1, c_lo, lane, active, acc);
+        const bool activeB = row + 64 < a.rows;
+        if ((rg + 2) * 64 > a.rows)
+          wave_body_rows2<PAY, CB, KW, B, true, XBF>(a, hA, hB, lut, xs, ring, ringB, rg, w_sl0, w_sl1, c_lo,
+                                                     lane, activeB, acc[0], acc[1]);
         else
-          wave_body_two<PAY, CB, KW, B, false, XBF>(a, hA, hB, lut, xs, ring, ringB, rg, tb + w_sl0, tb + w_mid,
-                                                    tb + w_mid, tb + w_sl1, c_lo, lane, active, acc);
+          wave_body_rows2<PAY, CB, KW, B, false, XBF>(a, hA, hB, lut, xs, ring, ringB, rg, w_sl0, w_sl1, c_lo,
+                                                      lane, activeB, acc[0], acc[1]);
       }
     } else {
       if (ragged)
         wave_body<PAY, CB, KW, B, MAT, true, XBF>(a, hA, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane,
-                                                  active, acc);
+                                                  active, acc[0]);
       else
         wave_body<PAY, CB, KW, B, MAT, false, XBF>(a, hA, lut, xs, ring, rg, tb + w_sl0, tb + w_sl1, c_lo, lane,
-                                                   active, acc);
+                                                   active, acc[0]);
     }
   }
   if constexpr (!MAT) {
-    // ---- A8: epilogue.  Reuse this wave's first ring as its reduction slot.
+    // ---- A8: epilogue.  Reuse each stream's ring as its reduction slot.
 #pragma unroll
-    for (int b = 0; b < B; ++b) *lds_ptr<float>(ring + (b * 64 + lane) * 4) = acc[b];
+    for (int b = 0; b < B; ++b) {
+      *lds_ptr<float>(ring + (b * 64 + lane) * 4) = acc[0][b];
+      if (NSr == 2) *lds_ptr<float>(ringB + (b * 64 + lane) * 4) = acc[1][b];
+    }
     __syncthreads();
-    for (uint32_t i = tid; i < 64u * B; i += W * 64) {
-      const uint32_t b = i >> 6, l = i & 63, r = rg * 64 + l;
-      float s = 0.f;
+    const uint32_t nrg = hasB ? 2u : 1u;
+    const float unit_scale = (E8 && !E8F8) ? 0.5f : 1.f;     // INT8 route: weights are 2v
+    for (uint32_t i = tid; i < 64u * B * nrg; i += W * 64) {
+      const uint32_t s = i / (64u * B), bi = i - s * (64u * B);
+      const uint32_t b = bi >> 6, l = bi & 63, rgs = rg + s, r = rgs * 64 + l;
+      float sum = 0.f;
       for (uint32_t w = 0; w < W; ++w)
-        s += *lds_ptr<const float>(rings + w * NSr * (2 * kRingStride) + (b * 64 + l) * 4);
+        sum += *lds_ptr<const float>(rings + (w * NSr + s) * (2 * kRingStride) + (b * 64 + l) * 4);
       if (a.n_sg == 1) {
         if (r < a.rows && b < a.nb) {
-          float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]);
-          if constexpr (E8 && !E8F8) sc *= 0.5f;    // INT8 route: weights are 2v
-          a.y[(uint64_t)b * a.rows + r] = s * sc;
+          const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]) * unit_scale;
+          a.y[(uint64_t)b * a.rows + r] = sum * sc;
         }
       } else {
-        a.partials[(((uint64_t)rg * a.n_sg + sg) * B + b) * 64 + l] = s;
+        // agent-scope stores: they reach the level every block's agent-scope loads
+        // read, with no cache write-back of the whole L2
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.partials) + (((uint64_t)rgs * a.n_sg + sg) * B + b) * 64 + l,
+                           __float_as_uint(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (a.n_sg > 1) {
+      // The row group spans several blocks.  Each thread waits until its partial
+      // stores are complete, then one thread takes the unit's ticket; the block that
+      // draws the last ticket adds every block's partials in block order and resets
+      // the ticket for the next call.  Partials and tickets are only touched by
+      // agent-scope atomic operations, so the completed stores are what the last
+      // block reads.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const uint32_t flag = rings;                // LDS word; the reduction slots are read
+      if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(a.tickets + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *lds_ptr<uint32_t>(flag) = old + 1 == a.n_sg ? 1u : 0u;
+      }
+      __syncthreads();
+      if (*lds_ptr<const uint32_t>(flag)) {
+        for (uint32_t i = tid; i < 64u * B * nrg; i += W * 64) {
+          const uint32_t s = i / (64u * B), bi = i - s * (64u * B);
+          const uint32_t b = bi >> 6, l = bi & 63, rgs = rg + s, r = rgs * 64 + l;
+          const uint32_t* p = reinterpret_cast<const uint32_t*>(a.partials) + ((uint64_t)rgs * a.n_sg * B + b) * 64 + l;
+          float sum = 0.f;
+          for (uint32_t g0 = 0; g0 < a.n_sg; g0 += 8) {
+            // up to 8 loads in flight, summed in block order
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              v[k] = g0 + k < a.n_sg
+                         ? __uint_as_float(__hip_atomic_load(p + (uint64_t)(g0 + k) * B * 64, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT))
+                         : 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (g0 + k < a.n_sg) sum += v[k];
+          }
+          if (r < a.rows && b < a.nb) {
+            const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]) * unit_scale;
+            a.y[(uint64_t)b * a.rows + r] = sum * sc;
+          }
+        }
+        if (tid == 0) __hip_atomic_store(a.tickets + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  // next row group of the block: new stream heads; the barrier keeps the rings
-  // (which held the reduction slots) untouched until every thread has read them
-  if (++rg >= r_hi) break;
+  // next unit of the block: new stream heads; the barrier keeps the rings (which
+  // held the reduction slots) untouched until every thread has read them
+  rg += NSr;
+  if (rg >= u_hi * NSr || rg >= a.n_rg) break;
   tb = rg * a.n_sl;
-  head_begin(a, tb + w_sl0, tb + w_mid, lane, hA);
-  if (kTwoCapable && NSr == 2) head_begin(a, tb + w_mid, tb + w_sl1, lane, hB);
+  hasB = NSr == 2 && rg + 1 < a.n_rg;
+  head_begin(a, tb + w_sl0, tb + w_sl1, lane, hA);
+  if (kTwoCapable && hasB) head_begin(a, tb + a.n_sl + w_sl0, tb + a.n_sl + w_sl1, lane, hB);
   head_chunks(a, lane, hA);
-  if (kTwoCapable && NSr == 2) head_chunks(a, lane, hB);
+  if (kTwoCapable && hasB) head_chunks(a, lane, hB);
   __syncthreads();
-  }
-}
-
-// Fixed-order sum of the per-block partials of each row (row groups that span
-// several blocks), times the row scale.  A separate launch: the kernel boundary
-// makes the partials visible without device-wide cache flushes.  One launch covers
-// every tensor of a group that needs it.
-struct RArgs {
-  const float* partials[kMaxGroup];
-  const uint16_t* scales[kMaxGroup];
-  float* y[kMaxGroup];
-  uint32_t rows[kMaxGroup], n_sg[kMaxGroup], row_begin[kMaxGroup];
-  uint32_t nt, nb, unit_scale, total_rows;
-  float scale_mul;       // 0.5 for the E8 INT8 route (weights are 2v), else 1
-};
-
-template <int B>
-__global__ void __launch_bounds__(256) k_reduce(const RArgs ra) {
-  const uint32_t gi = blockIdx.x * 256u + threadIdx.x;      // launched with 256 threads
-  if (gi >= ra.total_rows) return;
-  uint32_t ti = 0;
-  for (uint32_t i = 1; i < ra.nt; ++i)
-    if (gi >= ra.row_begin[i]) ti = i;
-  const uint32_t r = gi - ra.row_begin[ti], rg = r >> 6, l = r & 63, n_sg = ra.n_sg[ti];
-  const float sc = ra.unit_scale ? 1.f : (float)__builtin_bit_cast(_Float16, ra.scales[ti][r]) * ra.scale_mul;
-  const float* p = ra.partials[ti] + (uint64_t)rg * n_sg * B * 64 + l;
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    if ((uint32_t)b >= ra.nb) break;
-    // loads of up to 8 partials are issued together, then summed in block order
-    float s = 0.f;
-    for (uint32_t g0 = 0; g0 < n_sg; g0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (g0 + i < n_sg) ? p[((uint64_t)(g0 + i) * B + b) * 64] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (g0 + i < n_sg) s += v[i];
-    }
-    ra.y[ti][(uint64_t)b * ra.rows[ti] + r] = s * sc;
   }
 }
 
@@ -938,9 +1011,8 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
-  const bool two = !mat && R >= 2 && t->streams_per_wave == 2 &&
-                   ((t->coding.payload == ECW_P_INT_CODES && t->coding.weights_per_symbol <= 2) ||
-                    t->coding.payload == ECW_P_FP8_E4M3);
+  const bool two = !mat && !e8 && t->streams_per_wave == 2;
+  (void)R;
   return pair + lut * 8 + xs + (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
 }
 
@@ -1008,7 +1080,7 @@ static ecw_status check_tensor(const ecw_tensor* t) {
 static uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace layout of a group: each tensor whose row groups span several blocks
-// gets its partials, in tensor order, 256-byte aligned.
+// gets its tickets and then its partials, in tensor order, 256-byte aligned.
 static uint64_t group_workspace(const ecw_tensor* const* ts, int n, int batch, uint64_t* off) {
   uint64_t pos = 0;
   for (int i = 0; i < n; ++i) {
@@ -1040,9 +1112,7 @@ static ecw_status check_group(const ecw_tensor* const* ts, int n, int batch, int
   return ECW_OK;
 }
 
-// Fused decode + GEMV of a group of tensors that read the same x (one launch),
-// then one launch that adds the cross-block partials where a row group spans
-// several blocks.
+// Fused decode + GEMV of a group of tensors that read the same x: one launch.
 static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, int n, const void* x,
                                int x_dtype, float* const* ys, int batch, void* workspace, size_t ws_bytes) {
   ecw_status st = check_group(ts, n, batch, x_dtype, x, ys);
@@ -1054,9 +1124,8 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
   const int B = batch > 1 ? 4 : 1;
   const uint32_t W = ts[0]->waves_per_block;
   KArgs ka{};
-  RArgs ra{};
   uint64_t lds = 0;
-  uint32_t blocks = 0, red_rows = 0;
+  uint32_t blocks = 0;
   for (int i = 0; i < n; ++i) {
     const ecw_tensor* t = ts[i];
     if (t->coding.rows == 0) continue;
@@ -1078,21 +1147,18 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
     a.ns = t->streams_per_wave;
     a.rpb = std::max(1u, t->row_groups_per_block);
     a.n_sg = slice_groups(t);
-    a.n_blocks = (a.n_rg + a.rpb - 1) / a.rpb * a.n_sg;
+    const uint32_t ns = (t->streams_per_wave == 2 && t->coding.payload != ECW_P_E8_LATTICE) ? 2u : 1u;
+    const uint32_t units = (a.n_rg + ns - 1) / ns;
+    a.n_blocks = (units + a.rpb - 1) / a.rpb * a.n_sg;
     ka.block_begin[ka.nt] = blocks;
     a.xs_cols = W * t->tiles_per_wave * t->coding.tile_cols;
     blocks += a.n_blocks;
     lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false, x_dtype == ECW_DT_BF16));
     if (a.n_sg > 1) {
-      a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + woff[i]);
-      const uint32_t j = ra.nt++;
-      ra.partials[j] = a.partials;
-      ra.scales[j] = a.scales;
-      ra.y[j] = ys[i];
-      ra.rows[j] = a.rows;
-      ra.n_sg[j] = a.n_sg;
-      ra.row_begin[j] = red_rows;
-      red_rows += a.rows;
+      // tickets first: for one tensor they sit at the same place for every launch shape
+      uint8_t* base = static_cast<uint8_t*>(workspace) + woff[i];
+      a.tickets = reinterpret_cast<uint32_t*>(base);
+      a.partials = reinterpret_cast<float*>(base + ticket_bytes(t));
     }
     ++ka.nt;
   }
@@ -1108,19 +1174,6 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
   hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
-  if (ra.nt) {
-    ra.nb = (uint32_t)batch;
-    ra.unit_scale = ts[0]->coding.payload == ECW_P_BF16_EXP;
-    ra.scale_mul = (ts[0]->coding.payload == ECW_P_E8_LATTICE && ts[0]->coding.recon_dtype == ECW_DT_I8) ? 0.5f : 1.f;
-    ra.total_rows = red_rows;
-    const dim3 rgrid((red_rows + 255) / 256);
-    if (B == 1)
-      hipLaunchKernelGGL(k_reduce<1>, rgrid, dim3(256), 0, (hipStream_t)stream, ra);
-    else
-      hipLaunchKernelGGL(k_reduce<4>, rgrid, dim3(256), 0, (hipStream_t)stream, ra);
-    err = hipGetLastError();
-    if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
-  }
   return ECW_OK;
 }
 

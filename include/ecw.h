@@ -88,12 +88,15 @@ typedef struct {
   uint32_t lut_entry_bytes;
   uint32_t waves_per_block;          /* launch shape; dec_prepare sets a default and */
   uint32_t tiles_per_wave;           /* the caller may change it (autotuning)        */
-  uint32_t streams_per_wave;         /* 1, or 2: a wave owning >= 2 tiles decodes its
-                                        two halves as two streams in lockstep (INT
-                                        with <= 2 codes per symbol, FP8); else 1 */
-  uint32_t row_groups_per_block;     /* >= 1: a block decodes this many row groups
-                                        one after the other, staging the decode table
-                                        and activations once */
+  uint32_t streams_per_wave;         /* 1, or 2: each wave decodes the tiles of two
+                                        adjacent row groups at the same slices in
+                                        lockstep, sharing the activation reads
+                                        (fused GEMV of INT, BF16 and FP8 payloads;
+                                        E8 and the decode-only hook use 1) */
+  uint32_t row_groups_per_block;     /* >= 1: a block decodes this many row-group
+                                        units (streams_per_wave adjacent row groups
+                                        each) one after the other, staging the decode
+                                        table and activations once */
   uint64_t blob_bytes;
   /* byte ledger of the stored representation */
   uint64_t bytes_words, bytes_raw, bytes_tile_meta, bytes_tables, bytes_scales;
@@ -135,8 +138,15 @@ ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, const void* dev
 
 /* Bytes of device workspace dec_gemv needs for this tensor, launch shape and batch
  * (0 when each row group fits one block).  The workspace holds the per-block
- * partial sums of row groups that span several blocks; dec_gemv then enqueues a
- * second small kernel that adds them in block order.  No initialisation needed. */
+ * partial sums of row groups that span several blocks and one arrival ticket per
+ * row group: the block that arrives last adds the partials in block order, inside
+ * the same kernel.  The workspace must be zero-filled before its first use; every
+ * call that completes leaves its tickets at zero again, so later calls and graph
+ * replays need no re-initialisation.  One tensor's tickets sit at the start of its
+ * workspace for every launch shape; in a group (dec_gemv_group) they move with the
+ * other members' launch shapes, so a group workspace is zero-filled again when a
+ * member's launch shape changes.  Calls that overlap in time must not share a
+ * workspace. */
 ecw_status dec_gemv_workspace_size(const ecw_tensor* t, int batch, size_t* bytes);
 
 /* Fused decode + matrix-vector product: y[b][r] = sum_c W[r][c] * x[b][c].
@@ -194,7 +204,8 @@ ecw_status dec_time_group(ecw_stream stream, const ecw_tensor* const* t, int n, 
  *   achievable HBM streaming-read rate the decode is compared against.
  * ecw_probe_lds_lookup: every lane of `blocks` blocks of `waves_per_block` waves runs
  *   `steps` dependent lookups into an LDS table of 2^log2_m entries of entry_bytes
- *   (4 or 8) bytes, the access pattern of the decode's table reads; writes one word
+ *   (4, 8 or 16; at most 160 KiB) bytes, the access pattern of the decode's table
+ *   reads; writes one word
  *   per thread to `sink` (device, blocks x waves x 64 u32).
  * Errors: INVALID_ARG, HIP. */
 ecw_status ecw_probe_stream_read(ecw_stream stream, const void* buf, size_t bytes, uint32_t* sink,
