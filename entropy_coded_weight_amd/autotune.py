@@ -162,8 +162,10 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
                tie: float = 0.02, log=None):
     """Tensors sharing one launch (same activations) must share waves per block.  For
     each common waves-per-block value, every combination of each member's `top`
-    fastest single-tensor candidates at that value is timed as the real grouped
-    launch; the fastest group wins (ties within `tie`: fewer stored bytes).
+    fastest single-tensor candidates at that value, and every launch shape all
+    members can take (each with its fastest coding at that shape), is timed as the
+    real grouped launch; the fastest group wins (ties within `tie`: fewer stored
+    bytes).
     specs[name] = (payload, w, scales, code_bits) re-encodes a candidate.  By default
     `top` keeps the number of timed combinations near 16 per waves-per-block value."""
     import itertools
@@ -191,7 +193,23 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
         ranked = [_ranked(cands_by_name[n], w, top) for n in names]
         if any(not r for r in ranked):
             continue
-        for combo in itertools.product(*ranked):
+        combos = list(itertools.product(*ranked))
+        # A group holds more tiles than any member alone, so its best shape may be one
+        # no member ranks high alone (e.g. more tiles per wave, to keep every wave of
+        # the launch resident at once): also try each shape common to all members,
+        # each member with its fastest coding at that shape.
+        shapes = set.intersection(*[{s for c in cands_by_name[n] for s in c.shape_us if s[0] == w}
+                                    for n in names])
+        for shape in sorted(shapes):
+            combo = []
+            for n in names:
+                best = min(((c.shape_us[shape], c.stored_bytes, id(c), c) for c in cands_by_name[n]
+                            if shape in c.shape_us), default=None)
+                combo.append((best[3], shape))
+            combo = tuple(combo)
+            if combo not in combos:
+                combos.append(combo)
+        for combo in combos:
             cts = [tensor_for(n, c, s) for n, (c, s) in zip(names, combo)]
             us = time_group(cts, x, reps, stream)
             nbytes = sum(c.stored_bytes for c, _ in combo)

@@ -29,7 +29,10 @@
 //                     |q| <= 8 has a zero low byte, so the two high bytes are the
 //                     whole values)
 //   INT, k = 4:       a8 = symbol, h16 = 0
-//   BF16:             a8 = exponent byte, h16 = 0
+//   BF16:             a8 = exponent byte rotated right by one bit (bit 0 in bit 7),
+//                     h16 = 0.  With the raw byte (sign << 7 | mantissa) the bf16
+//                     value's high byte is then sign | a8[6:0] and its low byte
+//                     a8[7] | mantissa: whole bytes, joined with byte permutes
 //   FP8 E4M3:         a8 = code byte, h16 = fp16(e4m3 value) (NaN codes: 0x7E00)
 //   E8:               a8 = field value (int8), h16 = 0
 #pragma once
@@ -140,6 +143,10 @@ inline void entry_payload(uint32_t payload, uint32_t code_bits, uint32_t k, int3
       }
       return;
     }
+    case 2:
+      *a8 = ((s >> 1) | (s << 7)) & 0xFF;
+      *h16 = 0;
+      return;
     case 3:
       *a8 = s & 0xFF;
       *h16 = fp16_of_e4m3((uint8_t)s);

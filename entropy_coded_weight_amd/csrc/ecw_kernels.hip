@@ -52,6 +52,10 @@ template <int PAY, int KW>
 constexpr bool kDot = PAY == 1 && KW >= 2;
 template <int PAY, int KW, bool XBF>
 constexpr bool kPairTable = PAY == 1 && (KW == 4 || (KW == 2 && XBF));
+// BF16 weights with bf16 activations: two steps' weights are joined into one packed
+// bf16 pair and multiplied with one bf16 dot product.
+template <int PAY, bool XBF>
+constexpr bool kBfPair = PAY == 2 && XBF;
 // Table entries whose high word is the bias alone (no payload bits beside it).
 template <int PAY, int KW>
 constexpr bool kCleanBias = (PAY == 1 && KW == 4) || PAY == 2 || PAY == 4;
@@ -247,11 +251,50 @@ __device__ __forceinline__ void refill(uint32_t rposb, uint32_t& haveb, uint32_t
   }
 }
 
+// BF16 join from whole bytes (DFloat11 page, Algorithm 1: the decoded exponent
+// joined with the stored sign and mantissa).  The table byte a8 holds the exponent
+// rotated right by one bit; the raw byte r is sign << 7 | mantissa.  The bf16 high
+// byte is sign | a8[6:0] and its low byte a8[7] | mantissa, so two byte permutes and
+// one bit-field select build it.  Selector bytes index {src0: bytes 4-7, src1: 0-3};
+// 0x0C yields zero.
+//   bf16_in_f32: one weight as fp32 bits (bf16 in the high half); e.x holds a8 in
+//   byte 3, rdw holds r in byte q.
+__device__ __forceinline__ uint32_t bf16_in_f32(uint32_t ex, uint32_t rdw, int q) {
+  const uint32_t p1 = __builtin_amdgcn_perm(ex, rdw, 0x07000C0Cu | ((uint32_t)q << 16));   // [0, 0, r, a8]
+  const uint32_t p2 = __builtin_amdgcn_perm(ex, rdw, 0x00070C0Cu | ((uint32_t)q << 24));   // [0, 0, a8, r]
+  return (p2 & 0x80800000u) | (p1 & 0x7F7F7F7Fu);
+}
+//   bf16_pair: the weights of two consecutive steps (first in the low half); their
+//   raw bytes are bytes q and q + 1 of rdw.
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t ex0, uint32_t ex1, uint32_t rdw, int q) {
+  const uint32_t a = __builtin_amdgcn_perm(ex1, ex0, 0x0C0C0703u);                           // [a8_0, a8_1, 0, 0]
+  const uint32_t qq = (uint32_t)q;
+  const uint32_t p1 = __builtin_amdgcn_perm(a, rdw, qq | (4u << 8) | ((qq + 1) << 16) | (5u << 24));
+  const uint32_t p2 = __builtin_amdgcn_perm(a, rdw, 4u | (qq << 8) | (5u << 16) | ((qq + 1) << 24));
+  return (p2 & 0x80808080u) | (p1 & 0x7F7F7F7Fu);
+}
+
+// Activations of four bf16-pair steps: two pair words per batch row, staged as
+// [pair word][B].
+template <int B>
+__device__ __forceinline__ void bf16_pair_x(uint32_t addr, uint32_t* xp) {
+  if constexpr (B == 1) {
+    const uint2 v = lds_load2(addr);
+    xp[0] = v.x;
+    xp[1] = v.y;
+  } else {
+    const uint4 v0 = lds_load4(addr), v1 = lds_load4(addr + 16);
+    xp[0] = v0.x; xp[1] = v0.y; xp[2] = v0.z; xp[3] = v0.w;
+    xp[4] = v1.x; xp[5] = v1.y; xp[6] = v1.z; xp[7] = v1.w;
+  }
+}
+
 // A6 + A7: rebuild the weight(s) of one symbol in registers and accumulate.
 // xw: this symbol's activations as 32-bit words (fp32 [KW][B], or for the dot path
-// packed 16-bit pairs [KW/2][B]).  r: BF16 raw byte.
+// packed 16-bit pairs [KW/2][B]).  BF16: rdw is the raw dword holding this step's
+// byte, at byte q.
 template <int PAY, int CB, int KW, int B, bool XBF>
-__device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t r, float* acc) {
+__device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t rdw, int q, float* acc) {
   if constexpr (kDot<PAY, KW> && !kPairTable<PAY, KW, XBF>) {
     // fp16 (q0, q1) = bytes (0, hi8 q0, 0, hi8 q1) from the entry's high half
     const uint32_t wp = __builtin_amdgcn_perm(e.y, e.y, 0x030C020Cu);
@@ -276,9 +319,7 @@ __device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t 
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, __uint_as_float(xw[b]), acc[b]);   // q0
   } else if constexpr (PAY == 2) {
-    // bf16 bits = sign << 15 | exponent << 7 | mantissa, as fp32 bits << 16
-    const uint32_t bits = ((r << 24) & 0x80000000u) | ((e.x >> 1) & 0x7F800000u) | ((r << 16) & 0x007F0000u);
-    const float w = __uint_as_float(bits);
+    const float w = __uint_as_float(bf16_in_f32(e.x, rdw, q));
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = fmaf(w, __uint_as_float(xw[b]), acc[b]);
   } else {
@@ -287,9 +328,11 @@ __device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t 
   }
 }
 
+__device__ __forceinline__ uint32_t raw_dword(const uint4& g, int u) {
+  return (u < 4) ? g.x : (u < 8) ? g.y : (u < 12) ? g.z : g.w;
+}
 __device__ __forceinline__ uint32_t raw_byte(const uint4& g, int u) {
-  const uint32_t dw = (u < 4) ? g.x : (u < 8) ? g.y : (u < 12) ? g.z : g.w;
-  return (dw >> (8 * (u & 3))) & 0xFFu;
+  return (raw_dword(g, u) >> (8 * (u & 3))) & 0xFFu;
 }
 
 __device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, uint32_t sl, uint32_t lane) {
@@ -349,6 +392,8 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
                                           uint32_t lane, bool active, float* acc) {
   constexpr int U = 16;
   constexpr bool DOT = kDot<PAY, KW>;
+  constexpr bool BFP = kBfPair<PAY, XBF> && !MAT;   // bf16 weight pairs, two steps per dot
+  constexpr bool PK = DOT || BFP;                   // activations staged as 16-bit pairs
   constexpr bool CLEAN = kCleanBias<PAY, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;   // 32-bit activation words per step
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
@@ -364,6 +409,10 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
   uint2 pre = h.pre;
   uint32_t haveb = 4 * kChunk, nc = 2;
   uint32_t st = h.st;
+  // BF16 raw bytes: each 16-step group is loaded one group ahead of its use
+  const uint8_t* rawp = raw_tile(a, rg, t0 - sl0, lane);
+  uint4 rnext = zero4;
+  if constexpr (PAY == 2) rnext = *reinterpret_cast<const uint4*>(rawp);
 
   for (uint32_t t = t0; t < t1; ++t) {
     uint32_t x = st;
@@ -371,32 +420,51 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
     const uint32_t sl = t - sl0;
     const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
     const uint32_t col = sl * a.tile_cols - c_lo;
-    const uint8_t* rawp = raw_tile(a, rg, sl, lane);
 
     for (uint32_t j = 0; j < S; j += U) {
       uint4 rgp = zero4;
-      if constexpr (PAY == 2) rgp = *reinterpret_cast<const uint4*>(rawp + (uint64_t)(j / U) * 1024);
+      if constexpr (PAY == 2) {
+        rgp = rnext;
+        // the next group: of this tile, else the first of the wave's next tile
+        const bool more = j + U < S || t + 1 < t1;          // wave-uniform
+        rawp = j + U < S ? rawp + 1024 : raw_tile(a, rg, sl + 1, lane);
+        if (more) rnext = *reinterpret_cast<const uint4*>(rawp);
+      }
       // activation words of step j: fp32 [col][B], or packed pairs [col / 2][B]
-      const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
+      const uint32_t xg = xs + ((col + KW * j) * B / (PK ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
         refill(rposb, haveb, nc, pre, wl, src, nch, lane);
-        uint4 xq[MAT ? 1 : XW];
-        if constexpr (!MAT) {
+        uint4 xq[MAT || BFP ? 1 : XW];
+        uint32_t xp[BFP ? 2 * B : 1];     // bf16 pairs: two pair words per batch row
+        if constexpr (BFP) {
+          bf16_pair_x<B>(xg + qtr * 8 * B, xp);
+        } else if constexpr (!MAT) {
 #pragma unroll
           for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
         }
+        uint32_t ex0 = 0;                 // bf16 pairs: the first step's table word
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
           const uint32_t step = j + u;
           const uint2 e = decode_step<CLEAN>(x, lut, m, mmask);
-          if constexpr (!MAT) {
-            mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW,
-                                     PAY == 2 ? raw_byte(rgp, u) : 0u, acc);
+          if constexpr (BFP) {
+            if (u4 & 1) {
+              const uint32_t wp = bf16_pair(ex0, e.x, raw_dword(rgp, u), (u - 1) & 3);
+#pragma unroll
+              for (int b = 0; b < B; ++b) acc[b] = dot2<true>(wp, xp[(u4 >> 1) * B + b], acc[b]);
+              pin<B>(acc);
+            } else {
+              ex0 = e.x;
+            }
+          } else if constexpr (!MAT) {
+            mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW, raw_dword(rgp, u), u & 3,
+                                     acc);
             pin<B>(acc);
           } else if (!RAGGED || active) {
-            const uint32_t aux = e.x >> 24;
+            uint32_t aux = e.x >> 24;
+            if constexpr (PAY == 2) aux = ((aux << 1) | (aux >> 7)) & 0xFFu;   // table byte: rotated exponent
             uint32_t symbol = aux;
             int q[KW > 0 ? KW : 1];
             if constexpr (PAY == 1) {
@@ -451,6 +519,8 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
                                                 uint32_t lane, bool activeB, float* accA, float* accB) {
   constexpr int U = 16;
   constexpr bool DOT = kDot<PAY, KW>;
+  constexpr bool BFP = kBfPair<PAY, XBF>;
+  constexpr bool PK = DOT || BFP;
   constexpr bool CLEAN = kCleanBias<PAY, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
@@ -469,6 +539,15 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
   uint32_t stA = hA.st, stB = hB.st;
   const uint32_t tA0 = rg * a.n_sl, tB0 = tA0 + a.n_sl;
 
+  // BF16 raw bytes: each 16-step group is loaded one group ahead of its use
+  const uint8_t* rawA = raw_tile(a, rg, sl0, lane);
+  const uint8_t* rawB = raw_tile(a, rg + 1, sl0, lane);
+  uint4 nextA = zero4, nextB = zero4;
+  if constexpr (PAY == 2) {
+    nextA = *reinterpret_cast<const uint4*>(rawA);
+    nextB = *reinterpret_cast<const uint4*>(rawB);
+  }
+
   for (uint32_t sl = sl0; sl < sl1; ++sl) {
     uint32_t xA = stA, xB = stB;
     if (sl + 1 < sl1) {
@@ -477,30 +556,56 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
     }
     const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
     const uint32_t col = sl * a.tile_cols - c_lo;
-    const uint8_t* rawA = raw_tile(a, rg, sl, lane);
-    const uint8_t* rawB = raw_tile(a, rg + 1, sl, lane);
     for (uint32_t j = 0; j < S; j += U) {
       uint4 rgA = zero4, rgB = zero4;
       if constexpr (PAY == 2) {
-        rgA = *reinterpret_cast<const uint4*>(rawA + (uint64_t)(j / U) * 1024);
-        rgB = *reinterpret_cast<const uint4*>(rawB + (uint64_t)(j / U) * 1024);
+        rgA = nextA;
+        rgB = nextB;
+        const bool more = j + U < S || sl + 1 < sl1;        // wave-uniform
+        rawA = j + U < S ? rawA + 1024 : raw_tile(a, rg, sl + 1, lane);
+        rawB = j + U < S ? rawB + 1024 : raw_tile(a, rg + 1, sl + 1, lane);
+        if (more) {
+          nextA = *reinterpret_cast<const uint4*>(rawA);
+          nextB = *reinterpret_cast<const uint4*>(rawB);
+        }
       }
-      const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
+      const uint32_t xg = xs + ((col + KW * j) * B / (PK ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
         refill(rposA, haveA, ncA, preA, wl, srcA, nchA, lane);
         refill(rposB, haveB, ncB, preB, wl + 2 * kRingStride, srcB, nchB, lane);
-        uint4 xq[XW];
+        uint4 xq[BFP ? 1 : XW];
+        uint32_t xp[BFP ? 2 * B : 1];
+        if constexpr (BFP) {
+          bf16_pair_x<B>(xg + qtr * 8 * B, xp);
+        } else {
 #pragma unroll
-        for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
+          for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
+        }
+        uint32_t exA0 = 0, exB0 = 0;
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
           const uint2 eA = decode_step<CLEAN>(xA, lut, m, mmask);
           const uint2 eB = decode_step<CLEAN>(xB, lut, m, mmask);
-          const uint32_t* xw = reinterpret_cast<const uint32_t*>(xq) + u4 * XW;
-          mac<PAY, CB, KW, B, XBF>(eA, xw, PAY == 2 ? raw_byte(rgA, u) : 0u, accA);
-          mac<PAY, CB, KW, B, XBF>(eB, xw, PAY == 2 ? raw_byte(rgB, u) : 0u, accB);
+          if constexpr (BFP) {
+            if (u4 & 1) {
+              const uint32_t wA = bf16_pair(exA0, eA.x, raw_dword(rgA, u), (u - 1) & 3);
+              const uint32_t wB = bf16_pair(exB0, eB.x, raw_dword(rgB, u), (u - 1) & 3);
+#pragma unroll
+              for (int b = 0; b < B; ++b) {
+                accA[b] = dot2<true>(wA, xp[(u4 >> 1) * B + b], accA[b]);
+                accB[b] = dot2<true>(wB, xp[(u4 >> 1) * B + b], accB[b]);
+              }
+            } else {
+              exA0 = eA.x;
+              exB0 = eB.x;
+            }
+          } else {
+            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xq) + u4 * XW;
+            mac<PAY, CB, KW, B, XBF>(eA, xw, raw_dword(rgA, u), u & 3, accA);
+            mac<PAY, CB, KW, B, XBF>(eB, xw, raw_dword(rgB, u), u & 3, accB);
+          }
           pin<B>(accA);
           pin<B>(accB);
           const RenormRead rA = renorm_read<false>(xA, rposA, ringA, true);
@@ -684,7 +789,8 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kWave
 k_decode(const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
   (void)smem;
-  constexpr bool DOT = kDot<PAY, KW> && !MAT;
+  // activations staged as packed 16-bit pairs (dot-product paths), else as fp32
+  constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, XBF>) && !MAT;
   constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT;
   const uint32_t W = ka.waves;
   const uint32_t tid = threadIdx.x;
@@ -981,7 +1087,7 @@ static KernelFn pick_kernel(const ecw_coding& c) {
         case 2 * 16 + 4: return k_decode<1, 2, 4, B, MAT, XBF>;
       }
       return nullptr;
-    case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT, false>;
+    case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT, XBF>;
     case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT, false>;
     case ECW_P_E8_LATTICE:
       return c.recon_dtype == ECW_DT_FP8_E4M3 ? k_decode<4, 1, 8, B, MAT, false> : k_decode<4, 0, 8, B, MAT, false>;
@@ -994,8 +1100,10 @@ static KernelFn pick_gemv_kernel(const ecw_coding& c, int B, bool xbf) {
   return xbf ? pick_kernel<4, false, true>(c) : pick_kernel<4, false, false>(c);
 }
 
-static bool dot_path(const ecw_coding& c) {
-  return c.payload == ECW_P_INT_CODES && c.weights_per_symbol >= 2;
+// activations staged as packed 16-bit pairs: INT with several codes per symbol, and
+// BF16 weights with bf16 activations
+static bool dot_path(const ecw_coding& c, bool xbf) {
+  return (c.payload == ECW_P_INT_CODES && c.weights_per_symbol >= 2) || (c.payload == ECW_P_BF16_EXP && xbf);
 }
 static bool pair_table(const ecw_coding& c, bool xbf) {
   return c.payload == ECW_P_INT_CODES && (c.weights_per_symbol == 4 || (c.weights_per_symbol == 2 && xbf));
@@ -1005,7 +1113,7 @@ static bool pair_table(const ecw_coding& c, bool xbf) {
 // word rings.  Mirrors the layout k_decode computes.
 static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat,
                           bool xbf) {
-  const bool dot = !mat && dot_path(t->coding);
+  const bool dot = !mat && dot_path(t->coding, xbf);
   const bool e8 = t->coding.payload == ECW_P_E8_LATTICE;
   uint64_t pair = (!mat && pair_table(t->coding, xbf)) ? kPairTableBytes : 0;
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;

@@ -26,7 +26,7 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p
   out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
-// LDS random lookups shaped like the decode: a table of 2^m entries of 4, 8 or 16 bytes,
+// LDS random lookups shaped like the decode: a table of 2^m entries of 4, 8, 12 or 16 bytes,
 // and per lane a dependent chain idx -> entry -> next idx (the state update of the
 // decode is a multiply-add on the entry).  Every wave of the chip runs `steps` steps.
 template <int EB>
@@ -39,7 +39,11 @@ __global__ void __launch_bounds__(1024) k_lds_lookup(uint32_t log2m, uint32_t st
   uint32_t x = (blockIdx.x * blockDim.x + threadIdx.x) * 2246822519u + 1u;
   for (uint32_t s = 0; s < steps; ++s) {
     const uint32_t slot = x & mask;
-    if constexpr (EB == 16) {
+    if constexpr (EB == 12) {
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 e = *reinterpret_cast<const u32x3*>(smem + slot * 12);
+      x = __umul24(x >> log2m, e.x | 1u) + ((e.y ^ e.z) >> 16) + 0x9E37u;
+    } else if constexpr (EB == 16) {
       const uint4 e = reinterpret_cast<const uint4*>(smem)[slot];
       x = __umul24(x >> log2m, e.x | 1u) + ((e.y ^ e.z ^ e.w) >> 16) + 0x9E37u;
     } else if constexpr (EB == 8) {
@@ -77,12 +81,15 @@ extern "C" ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, u
                                            uint32_t steps, uint32_t blocks, uint32_t waves_per_block,
                                            uint32_t* sink) {
   clear_error();
-  if (!sink || log2_m < 8 || log2_m > 13 || (entry_bytes != 4 && entry_bytes != 8 && entry_bytes != 16) ||
+  if (!sink || log2_m < 8 || log2_m > 13 ||
+      (entry_bytes != 4 && entry_bytes != 8 && entry_bytes != 12 && entry_bytes != 16) ||
       (entry_bytes << log2_m) > 160u * 1024u || blocks == 0 ||
       waves_per_block == 0 || waves_per_block > 16)
     return fail(ECW_E_INVALID_ARG, "lookup probe: bad arguments");
   const size_t lds = ((size_t)entry_bytes) << log2_m;
-  auto fn = entry_bytes == 16 ? k_lds_lookup<16> : entry_bytes == 8 ? k_lds_lookup<8> : k_lds_lookup<4>;
+  auto fn = entry_bytes == 16 ? k_lds_lookup<16>
+             : entry_bytes == 12 ? k_lds_lookup<12>
+             : entry_bytes == 8 ? k_lds_lookup<8> : k_lds_lookup<4>;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                           160 * 1024) != hipSuccess) {
     (void)hipGetLastError();

@@ -204,7 +204,7 @@ ecw_status dec_time_group(ecw_stream stream, const ecw_tensor* const* t, int n, 
  *   achievable HBM streaming-read rate the decode is compared against.
  * ecw_probe_lds_lookup: every lane of `blocks` blocks of `waves_per_block` waves runs
  *   `steps` dependent lookups into an LDS table of 2^log2_m entries of entry_bytes
- *   (4, 8 or 16; at most 160 KiB) bytes, the access pattern of the decode's table
+ *   (4, 8, 12 or 16; at most 160 KiB) bytes, the access pattern of the decode's table
  *   reads; writes one word
  *   per thread to `sink` (device, blocks x waves x 64 u32).
  * Errors: INVALID_ARG, HIP. */

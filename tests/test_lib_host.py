@@ -116,6 +116,27 @@ def test_fp8_entry_payload_is_the_code_value():
     assert np.array_equal(lut[:, 0] >> 24, sym)
 
 
+def test_bf16_entry_payload_is_the_rotated_exponent():
+    # a8 = the exponent rotated right by one bit, so that together with the raw byte
+    # (sign << 7 | mantissa) the bf16 value is sign | a8[6:0] : a8[7] | mantissa, whole
+    # bytes; h16 = 0 and the high word is the bias alone
+    case = [c for c in cases.small_cases() if c.name == "bf16_m12"][0]
+    bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    _, _, freq = blobfmt.tables(bl)
+    lut = blobfmt.lut(bl)[0]
+    cum = np.concatenate([[0], np.cumsum(freq[0])[:-1]])
+    sym = np.repeat(np.arange(256), freq[0])
+    a8 = lut[:, 0] >> 24
+    assert np.array_equal(a8, ((sym >> 1) | (sym << 7)) & 0xFF)
+    assert np.array_equal(lut[:, 1], np.arange(lut.shape[0]) - cum[sym])
+    # the byte join rebuilds every bf16 bit pattern with this exponent
+    for e in np.unique(sym):
+        r = np.arange(256)
+        rot = ((e >> 1) | (e << 7)) & 0xFF
+        joined = (((r & 0x80) | (rot & 0x7F)) << 8) | ((rot & 0x80) | (r & 0x7F))
+        assert np.array_equal(joined, ((r & 0x80) << 8) | (e << 7) | (r & 0x7F))
+
+
 def test_prepare_ledger_and_defaults():
     case = cases.small_cases()[0]
     blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
