@@ -207,6 +207,63 @@ def _rows(n, k=256, seed=1):
     return np.sort(np.random.default_rng(seed).choice(n, min(k, n), replace=False))
 
 
+def _plugin_bits(counts: np.ndarray) -> float:
+    p = counts[counts > 0] / counts.sum()
+    return float(-(p * np.log2(p)).sum())
+
+
+def e8_bits_per_weight(v2: np.ndarray) -> float:
+    """Plug-in entropy per weight of the lattice fields of doubled-coordinate blocks
+    v2 [n, 8]: the coset, then the eight fields (z1..z7, m = floor(z8 / 2)) given the
+    coset, each with its own histogram (the 17 coset-indexed tables)."""
+    v2 = np.asarray(v2, dtype=np.int64).reshape(-1, 8)
+    c = v2[:, 0] & 1
+    z = (v2 - c[:, None]) // 2
+    f = np.concatenate([z[:, :7], np.floor_divide(z[:, 7:8], 2)], axis=1)
+    total = _plugin_bits(np.bincount(c, minlength=2)) * len(c)
+    for cc in (0, 1):
+        sel = f[c == cc]
+        for j in range(8):
+            if len(sel):
+                total += _plugin_bits(np.bincount(sel[:, j] - sel[:, j].min())) * len(sel)
+    return total / (8 * len(c))
+
+
+def config5_inputs():
+    """The lattice workload, generated with the library's E8 quantiser: w = N(0, 0.02^2)
+    [3072, 12288]; rows divided by their RMS; the lattice step from 12 steps of
+    geometric bisection on [1e-3, 8] so that the plug-in entropy of the block fields on
+    2^18 sampled blocks is 4.0 bits per weight; v = nearest E8 point of u / s; fp16
+    row scale = least-squares refit <w_r, v_r> / <v_r, v_r>.  Returns (2v int8
+    [N, K], fp16 scales, fp16 x [1, K], step, bits per weight)."""
+    import math
+    import ecw_inputs as E
+    import entropy_coded_weight_amd as ecw
+    n, k = 3072, 12288
+    rng = E.rng_for(5, 0, 0)
+    w = E.normal_matrix((n, k), rng)
+    x = rng.standard_normal((1, k)).astype(np.float16)
+    rms = np.sqrt((w * w).mean(axis=1))
+    u = (w / rms[:, None]).reshape(-1, 8)
+    srng = np.random.default_rng([0, 5, n, k])
+    sample = u[srng.choice(u.shape[0], 1 << 18, replace=False)]
+    lo, hi = 1e-3, 8.0
+    for _ in range(12):
+        mid = math.sqrt(lo * hi)
+        if e8_bits_per_weight(ecw.e8_nearest(sample / mid)) > 4.0:
+            lo = mid
+        else:
+            hi = mid
+    step = math.sqrt(lo * hi)
+    v2 = np.empty(u.shape, np.int8)
+    for b0 in range(0, u.shape[0], 1 << 18):
+        v2[b0:b0 + (1 << 18)] = ecw.e8_nearest(u[b0:b0 + (1 << 18)] / step)
+    v2 = v2.reshape(n, k)
+    v = v2.astype(np.float64) / 2.0
+    scales = ((w * v).sum(axis=1) / np.maximum((v * v).sum(axis=1), 1e-30)).astype(np.float16)
+    return v2, scales, x, step, e8_bits_per_weight(ecw.e8_nearest(sample / step))
+
+
 def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
     """Per-workload measurements besides the layer set: coding and launch shape
     picked by the autotuner on this device (warm), then timed cold; sampled rows
@@ -280,6 +337,47 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
                            {"workload": "BF16 N(0, 0.02^2) weights at 14336x4096 and 4096x14336, exponent "
                                         "byte rANS-coded, sign+mantissa byte raw, bf16 x, batch 1; "
                                         "two launches"})
+
+    if "5" in which:
+        log("config 5: E8 lattice fields, 3072x12288, INT8 and FP8 reconstruction")
+        v2, scales, xh, step, bpw = config5_inputs()
+        x = torch.from_numpy(xh).to(dev)
+        n, K = v2.shape
+        rows = _rows(n)
+        vv = v2[rows].astype(np.float64) / 2.0
+        for recon, tag in ((ecw.DT_I8, "int8"), (ecw.DT_FP8_E4M3, "fp8")):
+            # table size and tile width tuned like the other payloads: the 17 tables
+            # take 4 bytes per slot in LDS, so M = 2^9 leaves room for two blocks per CU
+            cand = []
+            for m in (9, 10, 11):
+                for tc in (64, 128, 256):
+                    c = ecw.Coding(ecw.E8_LATTICE, n, K, 8, 0, m, tc, recon)
+                    blob = ecw.encode(c, v2, scales)
+                    ct = ecw.CompressedTensor(blob)
+                    stream = torch.cuda.Stream()
+                    with torch.cuda.stream(stream):
+                        su = A._tune_launch(ct, x, [s for s in A.DEFAULT_SHAPES if s[2] == 1], 10, stream)
+                    stream.synchronize()
+                    us, shape = min((u, s) for s, u in su.items())
+                    cand.append((us, stored(blob), m, tc, shape, blob))
+            t_min = min(c_[0] for c_ in cand)
+            _, _, m, tc, shape, blob = min((c_ for c_ in cand if c_[0] <= 1.02 * t_min), key=lambda c_: c_[1])
+            us, ys = time_cold([("w", [(blob, shape)], x)], 1, steps, cold_bytes)
+            if recon == ecw.DT_I8:
+                wv = vv * scales[rows].astype(np.float64)[:, None]
+            else:
+                e4 = torch.from_numpy(vv.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+                wv = e4 * scales[rows].astype(np.float64)[:, None]
+            worst = check_rows(ys["w"][0][:, rows], wv, xh.astype(np.float64))
+            res[f"5_{tag}"] = summary(us, stored(blob), v2.size, v2.size + n * 2, worst,
+                                      {"w": dict(k=8, log2_m=m, tile_cols=tc, waves_per_block=shape[0],
+                                                 tiles_per_wave=shape[1], streams_per_wave=shape[2],
+                                                 row_groups_per_block=shape[3])},
+                                      {"workload": "3072x12288 N(0, 0.02^2) weights, row-RMS normalised, E8 "
+                                                   f"lattice step {step:.4f} ({bpw:.3f} bits/weight plug-in "
+                                                   "entropy), 9 fields per 8-weight block coded with 17 "
+                                                   f"coset-indexed tables (M tuned), {tag} reconstruction, "
+                                                   "fp16 row scales, fp16 x, batch 1"})
 
     if "4" in which:
         names = ["q", "k", "v", "o", "gate", "up", "down"] + (["lm_head"] if lm_head else [])
@@ -415,9 +513,10 @@ def main():
     ap.add_argument("--tune-file", default=TUNE_FILE)
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print per-launch averages of rocprofv3 CSV output under DIR and exit")
-    ap.add_argument("--configs", default="1,3,4",
+    ap.add_argument("--configs", default="1,3,4,5",
                     help="secondary workloads measured after the layer set (1: Gaussian codes, "
-                         "3: BF16 exponent coding, 4: FP8 layer at batch 1 and 4); '' for none")
+                         "3: BF16 exponent coding, 4: FP8 layer at batch 1 and 4, 5: E8 lattice "
+                         "fields, INT8 and FP8 reconstruction); '' for none")
     ap.add_argument("--lm-head", action="store_true",
                     help="include the 128256x4096 LM head in workload 4 (its generation takes minutes)")
     ap.add_argument("--tensors", default=",".join(ORDER),

@@ -92,6 +92,7 @@ def lib():
     P = ctypes.POINTER
     L.enc_build_tables.argtypes = [P(Coding), vp, P(Tables)]
     L.enc_encode.argtypes = [P(Coding), P(Tables), vp, vp, vp, P(sz)]
+    L.enc_e8_nearest.argtypes = [vp, sz, vp]
     L.dec_prepare.argtypes = [vp, sz, vp, P(Tensor)]
     L.dec_gemv_workspace_size.argtypes = [P(Tensor), i32, P(sz)]
     L.dec_gemv.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz]
@@ -104,7 +105,7 @@ def lib():
                                  P(ctypes.c_float)]
     L.ecw_probe_stream_read.argtypes = [vp, vp, sz, vp, u32]
     L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
-    for f in ("enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
+    for f in ("enc_build_tables", "enc_encode", "enc_e8_nearest", "dec_prepare", "dec_gemv_workspace_size",
               "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize",
               "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup"):
         getattr(L, f).restype = ctypes.c_int
@@ -156,6 +157,15 @@ def encode(coding: Coding, w: np.ndarray, scales=None, tables: Tables | None = N
     _check(L.enc_encode(ctypes.byref(coding), ctypes.byref(tables), _ptr(w),
                         _ptr(sc) if sc is not None else None, _ptr(buf), ctypes.byref(n)), "enc_encode")
     return buf[: n.value].copy()
+
+
+def e8_nearest(u: np.ndarray) -> np.ndarray:
+    """Nearest E8 lattice point of each block of eight values (enc_e8_nearest):
+    u float64 [n, 8] -> doubled coordinates 2v int8 [n, 8]."""
+    u = np.ascontiguousarray(u, dtype=np.float64).reshape(-1, 8)
+    out = np.empty(u.shape, dtype=np.int8)
+    _check(lib().enc_e8_nearest(_ptr(u), u.shape[0], _ptr(out)), "enc_e8_nearest")
+    return out
 
 
 def prepare(blob: np.ndarray, device_ptr: int | None = None) -> Tensor:

@@ -230,6 +230,64 @@ using namespace ecw;
 extern "C" uint32_t ecw_abi_version(void) { return ECW_ABI_VERSION; }
 extern "C" const char* ecw_last_error(void) { return g_last_error.c_str(); }
 
+// ------------------------------------------------------------------ enc_e8_nearest
+namespace ecw {
+
+// Nearest point of D8 (integer vectors with an even sum) to y: round each
+// coordinate half to even; if the sum is odd, round the coordinate with the largest
+// rounding error (lowest index on ties) the other way.
+static void nearest_d8(const double* y, double* z) {
+  double sum = 0.0;
+  int worst = 0;
+  double worst_err = -1.0;
+  for (int i = 0; i < 8; ++i) {
+    z[i] = std::nearbyint(y[i]);
+    sum += z[i];
+    const double e = std::fabs(y[i] - z[i]);
+    if (e > worst_err) {
+      worst_err = e;
+      worst = i;
+    }
+  }
+  if (std::fmod(sum, 2.0) != 0.0) z[worst] += (y[worst] - z[worst] >= 0.0) ? 1.0 : -1.0;
+}
+
+// Squared distance, summed as pairs of pairs (((d0+d1)+(d2+d3))+((d4+d5)+(d6+d7))).
+static double dist2(const double* y, const double* p, double shift) {
+  double d[8];
+  for (int i = 0; i < 8; ++i) {
+    const double t = y[i] - (p[i] + shift);
+    d[i] = t * t;
+  }
+  return ((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7]));
+}
+
+}  // namespace ecw
+
+extern "C" ecw_status enc_e8_nearest(const double* u, size_t n_blocks, int8_t* v2) {
+  clear_error();
+  if (n_blocks && (!u || !v2)) return fail(ECW_E_INVALID_ARG, "NULL input or output");
+  std::vector<int8_t> out(n_blocks * 8);
+  for (size_t b = 0; b < n_blocks; ++b) {
+    const double* y = u + b * 8;
+    double z0[8], z1[8], ym[8];
+    for (int i = 0; i < 8; ++i) {
+      if (!std::isfinite(y[i])) return fail(ECW_E_INVALID_ARG, "non-finite input");
+      ym[i] = y[i] - 0.5;
+    }
+    nearest_d8(y, z0);
+    nearest_d8(ym, z1);
+    const bool half = dist2(y, z1, 0.5) < dist2(y, z0, 0.0);
+    for (int i = 0; i < 8; ++i) {
+      const double d = half ? 2.0 * z1[i] + 1.0 : 2.0 * z0[i];
+      if (d < -127.0 || d > 127.0) return fail(ECW_E_UNSUPPORTED, "doubled coordinate outside int8");
+      out[b * 8 + i] = (int8_t)d;
+    }
+  }
+  if (n_blocks) std::memcpy(v2, out.data(), out.size());
+  return ECW_OK;
+}
+
 // ------------------------------------------------------------------ enc_build_tables
 extern "C" ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_tables* out) {
   clear_error();

@@ -125,6 +125,19 @@ ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_tables* out)
 ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const void* w,
                       const uint16_t* row_scales, void* blob, size_t* blob_bytes);
 
+/* Lattice quantisation for the E8 payload (EntroPack page, Section 3.2: blocks of
+ * eight row-normalised weights are quantised to E8 lattice points).  For each of
+ * n_blocks blocks of 8 doubles in u (host, [n_blocks][8]) writes the nearest point
+ * of E8 = D8 u (D8 + 1/2) as doubled coordinates 2v (host int8 [n_blocks][8]), the
+ * logical tensor enc_encode takes for ECW_P_E8_LATTICE.  The nearest point follows
+ * Conway and Sloane's decoder: each coordinate rounded half to even; for D8, when
+ * the rounded sum is odd, the coordinate with the largest rounding error (lowest
+ * index among equals) is rounded the other way; D8 + 1/2 the same on u - 1/2; the
+ * closer of the two by squared distance, the integer coset on a tie.
+ * Errors: INVALID_ARG (NULL with n_blocks > 0, non-finite input), UNSUPPORTED (a
+ * doubled coordinate outside [-127, 127]); nothing is written on error. */
+ecw_status enc_e8_nearest(const double* u, size_t n_blocks, int8_t* v2);
+
 /* Validate a blob and describe it.
  *   host_blob / blob_bytes: the blob in host memory (read only during the call).
  *   device_blob: the same bytes already copied to device memory, 256-byte aligned

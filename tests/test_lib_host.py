@@ -137,6 +137,29 @@ def test_bf16_entry_payload_is_the_rotated_exponent():
         assert np.array_equal(joined, ((r & 0x80) << 8) | (e << 7) | (r & 0x7F))
 
 
+def test_e8_nearest_matches_the_oracle():
+    # the library's lattice quantiser (the product path's E8 generator step) against
+    # the oracle's Conway-Sloane decoder, itself pinned by brute force: random blocks
+    # at several scales, exact half-integers (rounding ties), and blocks equidistant
+    # from both cosets
+    from oracle import e8
+    rng = np.random.default_rng([0, 77])
+    blocks = [rng.normal(0, s, (20000, 8)) for s in (0.3, 1.0, 4.0, 11.0)]
+    blocks.append(rng.integers(-20, 20, (4000, 8)) + 0.5)
+    blocks.append(rng.integers(-20, 20, (4000, 8)).astype(np.float64))
+    blocks.append(np.full((1, 8), 0.25))                   # equidistant: coset 0 wins
+    blocks.append(np.full((1, 8), -0.25))
+    blocks.append(rng.integers(-8, 8, (4000, 8)) + 0.25)
+    u = np.concatenate(blocks)
+    got = ecw.e8_nearest(u).astype(np.int64)
+    c, z = e8.nearest_e8(u)
+    assert np.array_equal(got, e8.doubled_coords(c, z))
+    with pytest.raises(ecw.EcwError):
+        ecw.e8_nearest(np.full((1, 8), 100.0))               # 2v = 200 does not fit int8
+    with pytest.raises(ecw.EcwError):
+        ecw.e8_nearest(np.full((1, 8), np.nan))
+
+
 def test_prepare_ledger_and_defaults():
     case = cases.small_cases()[0]
     blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
@@ -329,3 +352,16 @@ def test_probe_entry_points_reject_bad_arguments():
     assert L.ecw_probe_stream_read(None, None, 16, None, 1) == 1
     assert L.ecw_probe_lds_lookup(None, 14, 8, 10, 1, 1, None) == 1
     assert L.ecw_probe_lds_lookup(None, 11, 6, 10, 1, 1, ctypes.c_void_p(16)) == 1
+
+
+def test_bench_lattice_inputs_match_the_test_recipe():
+    # bench.py generates the lattice workload with the library's quantiser (the
+    # benchmark may not call the oracle); the tests generate it with the oracle's.
+    # Both must give the same tensor, scales and activations.
+    import bench
+    v2, scales, x, step, bpw = bench.config5_inputs()
+    v2o, so, xo = cases.config5()
+    assert np.array_equal(v2, v2o)
+    assert np.array_equal(scales.view(np.uint16), so.view(np.uint16))
+    assert np.array_equal(x, xo)
+    assert abs(bpw - 4.0) < 0.01
