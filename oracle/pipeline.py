@@ -6,8 +6,10 @@ independent 64-row tiles and rANS-encode each (``rans``; EntroPack page Sections
 3.6 and C.3).  Decoding reverses these steps and rebuilds the weights (EntroPack
 page Section 3.7; DFloat11 page Algorithm 1's bit join; MINE page Section 4.1).
 
-Payload kinds: 1 integer codes, 2 BF16 exponent + raw sign/mantissa byte,
-3 FP8 E4M3 bytes, 4 E8 lattice fields (doubled coordinates as logical tensor).
+Payload kinds: 1 integer codes, 2 BF16 exponent + raw sign/mantissa byte (one
+exponent per symbol, or with k = 2 a pair of exponent digits plus the correction
+stream of escaped weights: MINE page Section 4.1 "Escapes"), 3 FP8 E4M3 bytes,
+4 E8 lattice fields (doubled coordinates as logical tensor).
 Reconstruction dtypes for E8: 4 = INT8 (2v), 5 = FP8 E4M3 (nearest to v).
 """
 from __future__ import annotations
@@ -16,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import coding, e8, rans, symbols
+from . import coding, corrections, e8, rans, symbols
 
 INT_CODES, BF16_EXP, FP8_E4M3, E8_LATTICE = 1, 2, 3, 4
 DT_I8, DT_FP8 = 4, 5
@@ -51,6 +53,7 @@ class Components:
     raw: np.ndarray | None     # uint8, BF16 raw plane in tile order
     scales: np.ndarray | None  # float16 [N]
     counts: np.ndarray = field(default=None)   # histogram [n_tables, 256]
+    pair_values: np.ndarray | None = None      # BF16 pairs: exponent of each digit
 
 
 def syms_per_slice(c: Coding) -> int:
@@ -58,7 +61,13 @@ def syms_per_slice(c: Coding) -> int:
         return c.tile_cols // c.k
     if c.payload == E8_LATTICE:
         return 9 * c.tile_cols // 8
+    if c.payload == BF16_EXP:
+        return c.tile_cols // c.k
     return c.tile_cols
+
+
+def _bf16_pairs(c: Coding) -> bool:
+    return c.payload == BF16_EXP and c.k == 2
 
 
 # ---------------------------------------------------------------- logical -> symbols
@@ -84,7 +93,14 @@ def _row_symbols(c: Coding, logical: np.ndarray):
 
 
 def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
-    vals, tbl, raw = _row_symbols(c, logical)
+    pair_values = esc = None
+    if _bf16_pairs(c):
+        ex, _ = symbols.bf16_split(logical)
+        pair_values = symbols.bf16_pair_values(coding.histogram(ex, 256))
+        vals, raw, esc = symbols.bf16_pair_split(logical, pair_values)
+        tbl = np.zeros_like(vals)
+    else:
+        vals, tbl, raw = _row_symbols(c, logical)
     n_tables = e8.N_TABLES if c.payload == E8_LATTICE else 1
     value_offset = np.zeros(n_tables, dtype=np.int64)
     alphabet = np.zeros(n_tables, dtype=np.int64)
@@ -112,13 +128,21 @@ def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
     raw_tiles = [None] * T
     g_sym = symbols.rows_to_tiles(sym, sps)
     g_tbl = symbols.rows_to_tiles(tbl, sps)
-    g_raw = symbols.rows_to_tiles(raw, sps) if raw is not None else [None] * len(g_sym)
-    for (ids, sdat, act), (_, tdat, _), rg in zip(g_sym, g_tbl, g_raw):
+    # raw bytes and escapes are per weight: tiles of tile_cols columns
+    g_raw = symbols.rows_to_tiles(raw, c.tile_cols) if raw is not None else [None] * len(g_sym)
+    g_esc = [None] * len(g_sym)
+    if esc is not None:
+        g_esc = list(zip(symbols.rows_to_tiles(esc, c.tile_cols),
+                         symbols.rows_to_tiles(np.asarray(logical, np.uint16), c.tile_cols)))
+    for (ids, sdat, act), (_, tdat, _), rg, eg in zip(g_sym, g_tbl, g_raw, g_esc):
         st, words, cnt = rans.encode_tiles(sdat, tdat, freq, c.log2_m, act)
         states[ids] = st
         offs = rans.offsets_from_counts(cnt)
         for i, t in enumerate(ids):
             per_tile_words[t] = words[offs[i]:offs[i + 1]]
+            if eg is not None:
+                recs = corrections.tile_records(eg[1][1][i], eg[0][1][i], act[i])
+                per_tile_words[t] = np.concatenate([per_tile_words[t], corrections.stream_words(recs)])
         if rg is not None:
             plane = symbols.raw_plane_bytes(rg[1], act)
             for i, t in enumerate(ids):
@@ -129,15 +153,25 @@ def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
         np.zeros(0, np.uint8) if raw is not None else None)
     sc = None if scales is None else np.asarray(scales, dtype=np.float16)
     return Components(c, n_tables, alphabet, value_offset, freq, n_rg, n_sl, s_full, s_last,
-                      states, rans.offsets_from_counts(counts_t), words_all, raw_all, sc, counts)
+                      states, rans.offsets_from_counts(counts_t), words_all, raw_all, sc, counts,
+                      pair_values)
 
 
 # ---------------------------------------------------------------- symbols -> logical
 def decode_symbols(comp: Components):
     """-> (row symbol values int64 [N, n_sym], tile ok flags bool [T])."""
+    sym, ok, _ = _decode_all(comp)
+    return sym, ok
+
+
+def _decode_all(comp: Components):
+    """-> (row symbols, tile ok flags, {tile: per-lane [(column, bits)]} of the
+    correction streams (BF16 pairs; empty otherwise))."""
     c = comp.coding
     sps = syms_per_slice(c)
-    n_sym = {INT_CODES: c.cols // max(c.k, 1), BF16_EXP: c.cols, FP8_E4M3: c.cols,
+    pairs = _bf16_pairs(c)
+    corr = {}
+    n_sym = {INT_CODES: c.cols // max(c.k, 1), BF16_EXP: c.cols // c.k, FP8_E4M3: c.cols,
              E8_LATTICE: 9 * c.cols // 8}[c.payload]
     T = comp.n_rg * comp.n_sl
     ok = np.zeros(T, dtype=bool)
@@ -158,27 +192,45 @@ def decode_symbols(comp: Components):
                     return np.zeros(out.shape[:2], np.int64)
                 cos = out[:, :, j - jj] + comp.value_offset[0]
                 return 1 + 8 * cos + (jj - 1)
-        syms, okg = _decode_group(comp, comp.states[ids], offsets, S, act, tos)
+        if pairs:
+            syms, okg, ptr = _decode_group(comp, comp.states[ids], offsets, S, act, tos, trailing=True)
+            for i, t in enumerate(ids):
+                b, e = int(comp.offsets[t]), int(comp.offsets[t + 1])
+                recs, okc = corrections.parse(comp.words[b + int(ptr[i]):e], 2 * S, act[i])
+                okg[i] &= okc
+                corr[int(t)] = recs
+        else:
+            syms, okg = _decode_group(comp, comp.states[ids], offsets, S, act, tos)
         ok[ids] = okg
         dec_groups.append((ids, syms, act))
     sym = symbols.tiles_to_rows(c.rows, n_sym, sps, dec_groups)
-    return sym, ok
+    return sym, ok, corr
 
 
-def _decode_group(comp, states, offsets, S, act, tos):
+def _decode_group(comp, states, offsets, S, act, tos, trailing=False):
     # rans.decode_tiles expects offsets as a [T+1] prefix; tiles here may not be
     # contiguous, so decode with explicit (begin, end) pairs gathered into a copy.
     T = states.shape[0]
     lens = offsets[:, 1] - offsets[:, 0]
     words = np.concatenate([comp.words[b:e] for b, e in offsets]) if T else np.zeros(0, np.uint16)
     offs = rans.offsets_from_counts(lens)
-    return rans.decode_tiles(states, words, offs, S, comp.freq, comp.coding.log2_m, act, tos)
+    return rans.decode_tiles(states, words, offs, S, comp.freq, comp.coding.log2_m, act, tos,
+                             trailing=trailing)
 
 
 def decode(comp: Components) -> np.ndarray:
     """Bit-exact logical tensor."""
     c = comp.coding
-    sym, _ = decode_symbols(comp)
+    sym, _, corr = _decode_all(comp)
+    if _bf16_pairs(c):
+        w = symbols.bf16_pair_join(sym, raw_rows(comp), comp.pair_values)
+        for t, per_lane in corr.items():
+            g, sl = divmod(t, comp.n_sl)
+            for lane, recs in enumerate(per_lane):
+                for col, bits in recs:
+                    if g * 64 + lane < c.rows:
+                        w[g * 64 + lane, sl * c.tile_cols + col] = bits
+        return w
     if c.payload == INT_CODES:
         return symbols.symbols_to_int_codes(sym, c.code_bits, c.k)
     if c.payload == FP8_E4M3:
@@ -203,16 +255,15 @@ def decode(comp: Components) -> np.ndarray:
 def raw_rows(comp: Components) -> np.ndarray:
     """Inverse of the raw-plane layout -> uint8 [N, K]."""
     c = comp.coding
-    sps = syms_per_slice(c)
     out = np.zeros((comp.n_rg * 64, c.cols), dtype=np.uint8)
     pos = 0
     for t in range(comp.n_rg * comp.n_sl):
         g, sl = divmod(t, comp.n_sl)
-        S = comp.s_last if sl == comp.n_sl - 1 else comp.s_full
+        S = (comp.s_last if sl == comp.n_sl - 1 else comp.s_full) * c.k     # weights per lane
         G = -(-S // 16)
         blk = comp.raw[pos:pos + G * 1024].reshape(G, 64, 16).transpose(1, 0, 2).reshape(64, G * 16)
         pos += G * 1024
-        out[g * 64:(g + 1) * 64, sl * sps:sl * sps + S] = blk[:, :S]
+        out[g * 64:(g + 1) * 64, sl * c.tile_cols:sl * c.tile_cols + S] = blk[:, :S]
     return out[:c.rows]
 
 

@@ -78,7 +78,8 @@ def encode_tiles(sym: np.ndarray, tbl: np.ndarray, freq: np.ndarray, log2_m: int
 
 
 def decode_tiles(states: np.ndarray, words: np.ndarray, offsets: np.ndarray, S: int,
-                 freq: np.ndarray, log2_m: int, active: np.ndarray, table_of_step=None):
+                 freq: np.ndarray, log2_m: int, active: np.ndarray, table_of_step=None,
+                 trailing: bool = False):
     """Decode tiles; the reference for the GPU decoder.
 
     states uint32 [T, 64]; words uint16 (all tiles); offsets int [T + 1] word offsets
@@ -86,6 +87,9 @@ def decode_tiles(states: np.ndarray, words: np.ndarray, offsets: np.ndarray, S: 
     symbols decoded so far (default: table 0).
     Returns (symbols int64 [T, 64, S], ok bool [T]) where ok is the end-of-tile
     invariant: every active state back at L and exactly all of the tile's words read.
+    trailing: the tile's words may go on after the ANS words (a correction stream);
+    then ok leaves out the last condition and the words read per tile are returned
+    as a third value.
     """
     states = np.asarray(states, dtype=np.uint64)
     T = states.shape[0]
@@ -125,8 +129,10 @@ def decode_tiles(states: np.ndarray, words: np.ndarray, offsets: np.ndarray, S: 
         w = words64[idx] if words64.size else np.zeros_like(x)
         x = np.where(need, (x << np.uint64(WORD_BITS)) | w, x)
         ptr += need.sum(axis=1)
-    ok = (~overrun) & (ptr == count) & np.all(np.where(act, x == L, True), axis=1)
-    return out, ok
+    ok = (~overrun) & np.all(np.where(act, x == L, True), axis=1)
+    if trailing:
+        return out, ok, ptr
+    return out, ok & (ptr == count)
 
 
 def offsets_from_counts(counts: np.ndarray) -> np.ndarray:

@@ -11,6 +11,15 @@
   byte is sign << 7 | mantissa, and the weight is rebuilt with the bit join of the
   DFloat11 page's Algorithm 1: (sign << 8) | (exponent << 7) | mantissa, with the
   sign taken from bit 7 of the raw byte.
+* BF16 exponent pairs: two consecutive columns per symbol, each exponent as a
+  4-bit digit into the table's t = 16 stored exponents (MINE page, Section 4.1
+  "Escapes": a table restricted to the t most frequent values admits pairs when
+  t^2 <= M; Section 4.2 "Tuning t": keep the t most frequent codes and always 0,
+  which escaped values are coded as).  Readings taken: with at most 256 pair
+  symbols per table, t = 16; the stored exponents are 0 and the 15 most frequent
+  other exponents (ties to the smaller exponent), ascending, so digit 0 is
+  exponent 0; an escaped weight is coded as digit 0 with raw byte 0, i.e. as +0.0,
+  and its bf16 bits go to the correction stream (``corrections``).
 * FP8 E4M3: the byte itself is the symbol (MINE page Section 4.1; OCP E4M3 with
   bias 7, no infinities, S.1111.111 = NaN).
 * Tiling: rows in groups of 64 (lane l = row r0 + l, the MINE page's lane-per-row
@@ -76,6 +85,56 @@ def bf16_value(bits: np.ndarray) -> np.ndarray:
     mag = np.where(e == 0, m / 128.0 * 2.0 ** -126, (1.0 + m / 128.0) * np.exp2(e - 127.0))
     mag = np.where(e == 255, np.where(m == 0, np.inf, np.nan), mag)
     return np.where(s == 1, -mag, mag)
+
+
+PAIR_DIGITS = 16
+
+
+def bf16_pair_values(exponent_counts: np.ndarray) -> np.ndarray:
+    """The 16 exponents of a pair table: 0, then the 15 most frequent nonzero
+    exponents (more occurrences first, the smaller exponent on ties), in ascending
+    order.  Digits beyond the occurring exponents hold 0 and are never used."""
+    c = np.asarray(exponent_counts, dtype=np.int64)
+    others = [e for e in range(1, 256) if c[e] > 0]
+    others.sort(key=lambda e: (-int(c[e]), e))
+    keep = sorted(others[:PAIR_DIGITS - 1])
+    v = np.zeros(PAIR_DIGITS, dtype=np.int64)
+    v[1:1 + len(keep)] = keep
+    return v
+
+
+def bf16_pair_split(bits: np.ndarray, values: np.ndarray):
+    """bf16 bits [N, K] (K even) -> (pair symbols int64 [N, K/2], raw bytes uint8
+    [N, K], escaped bool [N, K]).  Exponent e has digit d >= 1 if values[d] == e (the
+    first such d); exponent 0 has digit 0; any other exponent is escaped: digit 0 and
+    raw byte 0.  The even column's digit is the low nibble."""
+    ex, raw = bf16_split(bits)
+    if ex.shape[1] % 2:
+        raise ValueError("pair mode needs an even column count")
+    digit = np.zeros(256, dtype=np.int64)
+    known = np.zeros(256, dtype=bool)
+    known[0] = True
+    for d in range(PAIR_DIGITS - 1, 0, -1):     # descending, so the first match wins
+        v = int(values[d])
+        if v != 0:
+            digit[v] = d
+            known[v] = True
+    esc = ~known[ex]
+    dg = np.where(esc, 0, digit[ex])
+    raw = np.where(esc, 0, raw).astype(np.uint8)
+    sym = dg[:, 0::2] | (dg[:, 1::2] << 4)
+    return sym, raw, esc
+
+
+def bf16_pair_join(sym: np.ndarray, raw: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """Pair symbols [N, K/2] + raw bytes [N, K] -> bf16 bits [N, K] (escapes not yet
+    applied: they read as +0.0)."""
+    s = np.asarray(sym, dtype=np.int64)
+    v = np.asarray(values, dtype=np.int64)
+    ex = np.empty((s.shape[0], 2 * s.shape[1]), dtype=np.int64)
+    ex[:, 0::2] = v[s & 15]
+    ex[:, 1::2] = v[s >> 4]
+    return bf16_join(ex, raw)
 
 
 # ---------------------------------------------------------------- FP8 E4M3

@@ -345,3 +345,116 @@ def test_weight_values_definitions():
     w = P.weight_values(c, np.array([[0x38, 0xB8]], np.uint8), np.array([2.0], np.float16))
     assert np.array_equal(w, [[2.0, -2.0]])        # 0x38 = 1.0 in E4M3
     assert gemv.x_values(np.array([0x3F80], np.uint16), "bf16")[0] == 1.0
+
+
+# ------------------------------------------------------------------ BF16 exponent pairs
+def test_bf16_pair_values_keep_zero_and_the_fifteen_most_frequent():
+    # MINE page, Section 4.2 "Tuning t": the t most frequent codes, and always 0.
+    counts = np.zeros(256, np.int64)
+    counts[100:120] = np.arange(1, 21)          # exponent 100 + i occurs i + 1 times
+    v = symbols.bf16_pair_values(counts)
+    assert list(v) == [0] + list(range(105, 120))
+    counts[104] = counts[105]                   # a tie for the last place: smaller exponent
+    assert list(symbols.bf16_pair_values(counts)) == [0, 104] + list(range(106, 120))
+    counts[:] = 0
+    counts[0], counts[127], counts[126] = 500, 3, 1  # exponent 0 never takes a slot of its own
+    assert list(symbols.bf16_pair_values(counts)) == [0, 126, 127] + [0] * 13
+
+
+def test_bf16_pair_stream_worked_example():
+    # One 64 x 64 tile of 1.0 (exponent 127) with 14 more exponents (110..123) twice
+    # each in row 20 and three rare exponents (90, 91, 92) once each: those three are
+    # the escapes.  Expected words written out by hand from the record layout:
+    # weight bits | column << 16 | last << 27, a lane mask first, rounds of lanes.
+    bits = np.full((64, 64), 0x3F80, np.uint16)
+    for i, e in enumerate(range(110, 124)):
+        bits[20, 2 * i] = bits[20, 2 * i + 1] = e << 7
+    bits[3, 5] = 0x8000 | (90 << 7) | 0x15      # 0xAD15
+    bits[3, 40] = (91 << 7) | 0x7F              # 0x2DFF
+    bits[9, 0] = (92 << 7) | 0x01               # 0x2E01
+    c = P.Coding(P.BF16_EXP, 64, 64, k=2, log2_m=10, tile_cols=64)
+    comp = P.encode(c, bits)
+    assert list(comp.pair_values) == [0] + list(range(110, 124)) + [127]
+    tail = [0x0208, 0, 0, 0,                    # lanes 3 and 9 hold records
+            0xAD15, 0x0005,                     # round 0, lane 3: column 5
+            0x2E01, 0x0800,                     # round 0, lane 9: column 0, last
+            0x2DFF, 0x0828]                     # round 1, lane 3: column 40, last
+    assert [int(w) for w in comp.words[-10:]] == tail
+    sym, ok = P.decode_symbols(comp)
+    assert ok.all()
+    assert sym[3, 2] == 15 | (0 << 4)           # 1.0 is digit 15; the escape is digit 0
+    raw = P.raw_rows(comp)
+    assert raw[3, 5] == 0 and raw[3, 40] == 0 and raw[9, 0] == 0
+    assert np.array_equal(P.decode(comp), bits)
+
+
+def _bf16_mixed(rows, cols, seed):
+    """Gaussian bf16 weights plus zeros, negative zeros, subnormals, huge values and
+    infinities, so that many exponents are escaped."""
+    rng = np.random.default_rng([0, 310, seed])
+    b = E.bf16_weights((rows, cols), rng).bits.copy()
+    n = b.size
+    flat = b.reshape(-1)
+    idx = rng.choice(n, n // 50, replace=False)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F7F, 0x7F80, 0xFF80, 0x4000, 0x3F80], np.uint16)
+    flat[idx] = rng.choice(special, idx.size)
+    idx = rng.choice(n, n // 100, replace=False)
+    flat[idx] = rng.integers(0, 1 << 16, idx.size).astype(np.uint16)
+    return b
+
+
+@pytest.mark.parametrize("rows,cols,tc,m", [(70, 288, 128, 12), (64, 64, 64, 8), (130, 512, 256, 10)])
+def test_bf16_pairs_roundtrip_with_escapes(rows, cols, tc, m):
+    b = _bf16_mixed(rows, cols, rows + cols)
+    c = P.Coding(P.BF16_EXP, rows, cols, k=2, log2_m=m, tile_cols=tc)
+    comp = P.encode(c, b)
+    _, ok = P.decode_symbols(comp)
+    assert ok.all()
+    assert np.array_equal(P.decode(comp), b)
+
+
+def test_bf16_pairs_escape_count_and_stream_length():
+    # every weight whose exponent is neither 0 nor stored is one record (two words);
+    # each tile adds its 4-word mask
+    b = _bf16_mixed(96, 256, 7)
+    c = P.Coding(P.BF16_EXP, 96, 256, k=2, log2_m=12, tile_cols=128)
+    comp = P.encode(c, b)
+    ex = ((b.astype(np.int64) >> 7) & 0xFF)
+    kept = set(int(v) for v in comp.pair_values) | {0}
+    n_esc = int(sum(np.count_nonzero(ex == e) for e in range(256) if e not in kept))
+    assert n_esc > 0
+    _, _, corr = P._decode_all(comp)
+    assert sum(len(r) for lanes in corr.values() for r in lanes) == n_esc
+    T = comp.n_rg * comp.n_sl
+    offs = comp.offsets
+    # the ANS part of each tile is what a rANS decode of that tile reads
+    ans = sum(int(offs[t + 1] - offs[t]) for t in range(T)) - 4 * T - 2 * n_esc
+    assert ans >= 0
+    assert 16 * ans <= 1.01 * coding.cross_entropy_total_bits(comp.counts[0], comp.freq[0], 12) + 16 * 64 * T
+
+
+def test_bf16_pairs_size_matches_single_exponent_coding():
+    # Gaussian weights: 29 or so exponents, the 15 most frequent cover all but ~1e-4
+    # of the weights, so pairs code the exponent in about the single-symbol size
+    b = E.bf16_weights((256, 2048), np.random.default_rng([0, 3, 10])).bits
+    one = P.encode(P.Coding(P.BF16_EXP, 256, 2048, k=1, log2_m=12, tile_cols=512), b)
+    two = P.encode(P.Coding(P.BF16_EXP, 256, 2048, k=2, log2_m=12, tile_cols=512), b)
+    assert np.array_equal(P.decode(two), b)
+    assert two.words.size < 1.01 * one.words.size
+    h1 = coding.entropy_bits(one.counts[0])
+    assert 16 * two.words.size <= 1.02 * b.size * h1
+
+
+def test_bf16_pairs_corrupt_correction_stream_is_detected():
+    bits = np.full((64, 64), 0x3F80, np.uint16)
+    for i, e in enumerate(range(100, 116)):
+        bits[i, 3] = e << 7                     # 16 rare exponents: one is escaped
+    c = P.Coding(P.BF16_EXP, 64, 64, k=2, log2_m=10, tile_cols=64)
+    comp = P.encode(c, bits)
+    assert P.decode_symbols(comp)[1].all()
+    bad = P.Components(**{**comp.__dict__, "words": comp.words.copy()})
+    bad.words[-1] ^= 0x0800                     # clear the last flag
+    assert not P.decode_symbols(bad)[1].any()
+    bad = P.Components(**{**comp.__dict__, "words": comp.words.copy()})
+    bad.words[-1] = (bad.words[-1] & 0xF800) | 64   # column outside the slice
+    assert not P.decode_symbols(bad)[1].any()
