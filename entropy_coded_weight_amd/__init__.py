@@ -23,6 +23,7 @@ INT_CODES, BF16_EXP, FP8_E4M3, E8_LATTICE = 1, 2, 3, 4
 DT_F16, DT_BF16, DT_F32, DT_I8, DT_FP8_E4M3 = 1, 2, 3, 4, 5
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "CORRUPT", 4: "BUFFER_TOO_SMALL", 5: "HIP"}
 
+ABI_VERSION = 2          # layout of the structs below
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libecw.so")
 
@@ -43,7 +44,9 @@ class Tables(ctypes.Structure):
                 ("alphabet", ctypes.c_uint32 * 17),
                 ("value_offset", ctypes.c_int32 * 17),
                 ("freq", (ctypes.c_uint16 * 256) * 17),
-                ("count", (ctypes.c_uint64 * 256) * 17)]
+                ("count", (ctypes.c_uint64 * 256) * 17),
+                ("pair_values", ctypes.c_uint8 * 16),
+                ("escapes", ctypes.c_uint64)]
 
     def freq_array(self) -> np.ndarray:
         return np.ctypeslib.as_array(self.freq)[: self.n_tables].astype(np.int64)
@@ -113,6 +116,9 @@ def lib():
     L.ecw_last_error.restype = ctypes.c_char_p
     L.ecw_abi_version.argtypes = []
     L.ecw_abi_version.restype = u32
+    if L.ecw_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {L.ecw_abi_version()}, the binding expects "
+                          f"{ABI_VERSION}: rebuild the library")
     _lib = L
     return L
 
@@ -362,7 +368,7 @@ class CompressedTensor:
 
     def materialize(self, want_symbols=True, want_weights=True, stream=None):
         c = self.t.coding
-        n_sym = {INT_CODES: c.cols // max(c.weights_per_symbol, 1), BF16_EXP: c.cols,
+        n_sym = {INT_CODES: c.cols // max(c.weights_per_symbol, 1), BF16_EXP: c.cols // max(c.weights_per_symbol, 1),
                  FP8_E4M3: c.cols, E8_LATTICE: c.cols // 8 * 9}[c.payload]
         dev = self.dev.device
         sym = torch.zeros((c.rows, n_sym), dtype=torch.int16, device=dev) if want_symbols else None

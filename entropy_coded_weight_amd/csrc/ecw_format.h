@@ -4,18 +4,29 @@
 //   [0, 256)        BlobHeader
 //   sections, each starting on a 256-byte boundary, in this order:
 //   TABLES   n_tables x TableRecord                        (alphabet, offset, freq)
+//            BF16 pairs: then 16 bytes, the exponent of each digit
 //   LUT      n_tables x M x 8 B decode entries             (derived from freq)
 //   STATES   n_tiles x 64 x u32 decoder start states       (inactive lanes: 2^16)
 //   OFFSETS  (n_tiles + 1) x u32 word offsets into WORDS   (last = total words)
 //   WORDS    u16 payload words of all tiles in tile order, then >= kWordPad bytes of
 //            zero padding (the decoder's chunked loads may read past a tile's end)
-//   RAW      BF16 only: per tile G = ceil(S/16) groups of [64 lanes][16 bytes]
+//   RAW      BF16 only: per tile G = ceil(weights per row slice / 16) groups of
+//            [64 lanes][16 bytes] (byte i of a lane's group g: column 16 g + i)
 //   SCALES   rows x fp16 row scales (absent for BF16)
 //
 // Tile t = row_group * n_slices + slice covers rows [64 g, 64 g + 64) and the
 // symbols of columns [slice * tile_cols, ...).  Inside a tile, words are in decoder
 // order: step-major, lanes ascending (EntroPack page, Sections 3.6 and C.3: one
 // wave per independent tile, 32-bit states, 16-bit words).
+//
+// BF16 pairs (k = 2): a symbol is two exponent digits d0 | d1 << 4 (even column
+// low) into the 16 stored exponents; digit 0 is exponent 0.  A weight whose
+// exponent is not stored is coded as digit 0 with raw byte 0 (+0.0) and escaped:
+// after the tile's last ANS word comes its correction stream (MINE page, Section
+// 4.1 "Escapes"): a 64-bit lane mask (4 words, low first; bit l = lane l has
+// records), then records in rounds (round r: the r-th record of each lane with more
+// than r, lanes ascending), each record two words, low half first:
+//   bits 0..15 bf16 weight, 16..26 column in the slice, 27 last of its row, 28..31 0
 //
 // Decode entry of slot i (table t), symbol s, as two u32 (MINE page, Section 4.1:
 // one table read yields both the state-update operands and the payload):
@@ -33,6 +44,8 @@
 //                     h16 = 0.  With the raw byte (sign << 7 | mantissa) the bf16
 //                     value's high byte is then sign | a8[6:0] and its low byte
 //                     a8[7] | mantissa: whole bytes, joined with byte permutes
+//   BF16, k = 2:      a8 = symbol, h16 = rot(e0) | rot(e1) << 8 with e0, e1 the
+//                     digits' exponents and rot the rotation above
 //   FP8 E4M3:         a8 = code byte, h16 = fp16(e4m3 value) (NaN codes: 0x7E00)
 //   E8:               a8 = field value (int8), h16 = 0
 #pragma once
@@ -49,6 +62,9 @@ constexpr uint32_t kSectionAlign = 256;
 constexpr uint32_t kWordPad = 4096;        // zero bytes after the last word
 constexpr uint32_t kMinLog2M = 8;
 constexpr uint32_t kMaxLog2M = 13;
+constexpr uint32_t kPairDigits = 16;        // BF16 pairs: stored exponents
+constexpr uint32_t kEscLast = 1u << 27;     // correction record: last of its row
+constexpr uint32_t kEscMaskWords = 4;       // correction stream: lane mask words
 
 enum Section : uint32_t {
   kSecTables = 0, kSecLut, kSecStates, kSecOffsets, kSecWords, kSecRaw, kSecScales, kNumSections
@@ -84,16 +100,18 @@ struct TableRecord {          // 520 bytes
 static_assert(sizeof(TableRecord) == 520, "table record size");
 
 inline uint32_t symbols_per_row_slice(uint32_t payload, uint32_t k, uint32_t tile_cols) {
-  if (payload == 1) return tile_cols / k;
+  if (payload == 1 || payload == 2) return tile_cols / k;
   if (payload == 4) return tile_cols / 8 * 9;
   return tile_cols;
 }
 inline uint32_t symbols_per_row(uint32_t payload, uint32_t k, uint32_t cols) {
-  if (payload == 1) return cols / k;
+  if (payload == 1 || payload == 2) return cols / k;
   if (payload == 4) return cols / 8 * 9;
   return cols;
 }
-inline uint64_t raw_group_count(uint32_t steps) { return (steps + 15) / 16; }
+// BF16 raw plane: 16-byte groups per lane for `weights` columns of a tile
+inline uint64_t raw_group_count(uint32_t weights) { return (weights + 15) / 16; }
+inline uint32_t rot_exponent(uint32_t e) { return ((e >> 1) | (e << 7)) & 0xFF; }
 
 // fp16 bit pattern of a small integer |v| <= 2048 (exact).
 inline uint16_t fp16_of_int(int v) {
@@ -121,9 +139,10 @@ inline uint16_t fp16_of_e4m3(uint8_t b) {
   return (uint16_t)(sign | ((e - 7 + 15) << 10) | (m << 7));
 }
 
-// Table entry payload of symbol s (see the layout above).
+// Table entry payload of symbol s (see the layout above).  pair_values: the BF16 pair
+// stored exponents (else unused).
 inline void entry_payload(uint32_t payload, uint32_t code_bits, uint32_t k, int32_t value_offset,
-                          uint32_t s, uint32_t* a8, uint32_t* h16) {
+                          const uint8_t* pair_values, uint32_t s, uint32_t* a8, uint32_t* h16) {
   switch (payload) {
     case 1: {
       const int half = 1 << (code_bits - 1);
@@ -144,8 +163,13 @@ inline void entry_payload(uint32_t payload, uint32_t code_bits, uint32_t k, int3
       return;
     }
     case 2:
-      *a8 = ((s >> 1) | (s << 7)) & 0xFF;
-      *h16 = 0;
+      if (k == 2) {
+        *a8 = s & 0xFF;
+        *h16 = rot_exponent(pair_values[s & 15]) | (rot_exponent(pair_values[(s >> 4) & 15]) << 8);
+      } else {
+        *a8 = rot_exponent(s);
+        *h16 = 0;
+      }
       return;
     case 3:
       *a8 = s & 0xFF;

@@ -58,9 +58,19 @@ ecw_status check_coding(const ecw_coding* c) {
       break;
     }
     case ECW_P_BF16_EXP:
+      if (c->weights_per_symbol == 2) {
+        // exponent pairs with escapes; a record's column field has 11 bits
+        if (c->cols % 32) return fail(ECW_E_UNSUPPORTED, "BF16 pairs: cols must be a multiple of 32");
+        if (c->tile_cols > 2048) return fail(ECW_E_UNSUPPORTED, "BF16 pairs: tile_cols must be at most 2048");
+      } else if (c->weights_per_symbol != 1) {
+        return fail(ECW_E_UNSUPPORTED, "BF16 symbols carry one exponent or a pair");
+      } else if (c->cols % 16) {
+        return fail(ECW_E_UNSUPPORTED, "cols must be a multiple of 16");
+      }
+      if (c->recon_dtype != 0) return fail(ECW_E_INVALID_ARG, "recon_dtype is E8-only");
+      break;
     case ECW_P_FP8_E4M3:
-      if (c->weights_per_symbol != 1)
-        return fail(ECW_E_UNSUPPORTED, "BF16/FP8 symbols carry one weight (pairs need escapes)");
+      if (c->weights_per_symbol != 1) return fail(ECW_E_UNSUPPORTED, "FP8 symbols carry one weight");
       if (c->cols % 16) return fail(ECW_E_UNSUPPORTED, "cols must be a multiple of 16");
       if (c->recon_dtype != 0) return fail(ECW_E_INVALID_ARG, "recon_dtype is E8-only");
       break;
@@ -93,14 +103,31 @@ Geometry geometry_of(const ecw_coding& c) {
 // ------------------------------------------------------------------ symbol access
 // Per row, the symbol stream in column order and (E8) its table index; BF16 also
 // yields a raw byte per symbol.
+struct Escape {
+  uint32_t lane, col;     // col: column inside the tile's slice
+  uint16_t bits;
+};
+
 struct SymbolSource {
   const ecw_coding& c;
   const void* w;
   const ecw_tables* t;   // value offsets (E8); may be null while building tables
+  int8_t digit[256];     // BF16 pairs: digit of each exponent, -1 = escaped
+
+  // BF16 pairs: exponent 0 has digit 0; e != 0 the first d >= 1 with pv[d] == e.
+  void set_digits(const uint8_t* pv) {
+    for (int e = 0; e < 256; ++e) digit[e] = -1;
+    for (int d = (int)kPairDigits - 1; d >= 1; --d)
+      if (pv[d]) digit[pv[d]] = (int8_t)d;
+    digit[0] = 0;
+  }
 
   // Writes n symbols of row r starting at symbol index s0.  Returns false on an
-  // invalid logical value.  tbl/raw may be null.
-  bool row(uint32_t r, uint32_t s0, uint32_t n, int32_t* val, uint8_t* tbl, uint8_t* raw) const {
+  // invalid logical value.  tbl/raw may be null; raw gets one byte per weight.
+  // BF16 pairs: escaped weights get raw byte 0 and, if esc is given, an Escape
+  // (lane `lane`, column relative to symbol s0's first column).
+  bool row(uint32_t r, uint32_t s0, uint32_t n, int32_t* val, uint8_t* tbl, uint8_t* raw,
+           std::vector<Escape>* esc = nullptr, uint32_t lane = 0) const {
     const uint64_t K = c.cols;
     switch (c.payload) {
       case ECW_P_INT_CODES: {
@@ -121,6 +148,27 @@ struct SymbolSource {
       }
       case ECW_P_BF16_EXP: {
         const uint16_t* p = static_cast<const uint16_t*>(w) + r * K;
+        if (c.weights_per_symbol == 2) {
+          for (uint32_t i = 0; i < n; ++i) {
+            uint32_t s = 0;
+            for (uint32_t u = 0; u < 2; ++u) {
+              const uint32_t col = 2 * (s0 + i) + u;
+              const uint16_t bits = p[col];
+              int d = digit[(bits >> 7) & 0xFF];
+              uint8_t rb = (uint8_t)(((bits >> 8) & 0x80) | (bits & 0x7F));
+              if (d < 0) {
+                d = 0;
+                rb = 0;
+                if (esc) esc->push_back({lane, 2 * i + u, bits});
+              }
+              s |= (uint32_t)d << (4 * u);
+              if (raw) raw[2 * i + u] = rb;
+            }
+            val[i] = (int32_t)s;
+            if (tbl) tbl[i] = 0;
+          }
+          return true;
+        }
         for (uint32_t i = 0; i < n; ++i) {
           uint32_t bits = p[s0 + i];
           val[i] = (int32_t)((bits >> 7) & 0xFF);
@@ -302,7 +350,30 @@ extern "C" ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_t
   std::vector<std::vector<uint64_t>> hist(nth, std::vector<uint64_t>(17 * 512, 0));
   std::vector<int32_t> vmin(nth * 17, INT32_MAX), vmax(nth * 17, INT32_MIN);
   std::atomic<bool> bad{false};
-  SymbolSource src{*c, w, nullptr};
+  SymbolSource src{*c, w, nullptr, {}};
+  if (c->payload == ECW_P_BF16_EXP && c->weights_per_symbol == 2) {
+    // BF16 pairs: the stored exponents are 0 and the 15 most frequent others, the
+    // smaller exponent first on ties, ascending (MINE page, Section 4.2 "Tuning t")
+    std::vector<std::vector<uint64_t>> eh(nth, std::vector<uint64_t>(256, 0));
+    parallel_for(c->rows, [&](uint64_t r, unsigned tid) {
+      const uint16_t* p = static_cast<const uint16_t*>(w) + r * (uint64_t)c->cols;
+      uint64_t* h = eh[tid].data();
+      for (uint32_t i = 0; i < c->cols; ++i) h[(p[i] >> 7) & 0xFF] += 1;
+    });
+    uint64_t ec[256] = {0};
+    for (uint32_t k = 0; k < nth; ++k)
+      for (int e = 0; e < 256; ++e) ec[e] += eh[k][e];
+    std::vector<uint32_t> order;
+    for (uint32_t e = 1; e < 256; ++e)
+      if (ec[e]) order.push_back(e);
+    std::sort(order.begin(), order.end(), [&](uint32_t a, uint32_t b) { return ec[a] != ec[b] ? ec[a] > ec[b] : a < b; });
+    order.resize(std::min<size_t>(order.size(), kPairDigits - 1));
+    std::sort(order.begin(), order.end());
+    for (size_t i = 0; i < order.size(); ++i) out->pair_values[1 + i] = (uint8_t)order[i];
+    src.set_digits(out->pair_values);
+    for (int e = 0; e < 256; ++e)
+      if (src.digit[e] < 0) out->escapes += ec[e];
+  }
   // E8 values are offset by 256 inside the scratch histogram so negatives index it
   parallel_for(c->rows, [&](uint64_t r, unsigned tid) {
     std::vector<int32_t> val(g.syms_per_row);
@@ -392,6 +463,8 @@ static ecw_status check_tables_for(const ecw_coding* c, const ecw_tables* t, con
     if (sum != M && !(sum == 0 && g.n_tiles == 0) && !(sum == 0 && c->payload == ECW_P_E8_LATTICE))
       return fail(ECW_E_INVALID_ARG, "table frequencies do not sum to M");
   }
+  if (c->payload == ECW_P_BF16_EXP && c->weights_per_symbol == 2 && t->pair_values[0] != 0)
+    return fail(ECW_E_INVALID_ARG, "BF16 pairs: digit 0 must be exponent 0 (escaped weights are coded as 0)");
   return ECW_OK;
 }
 
@@ -410,9 +483,13 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
   const uint32_t M = 1u << c->log2_m;
   const uint32_t m = c->log2_m;
   const bool bf16 = c->payload == ECW_P_BF16_EXP;
+  const bool pairs = bf16 && c->weights_per_symbol == 2;
+  const uint32_t kw = bf16 ? c->weights_per_symbol : 1;     // raw bytes per symbol
+  SymbolSource src0{*c, w, t, {}};
+  if (pairs) src0.set_digits(t->pair_values);
 
   // Section sizes that do not depend on the coded words
-  const uint64_t tables_b = (uint64_t)g.n_tables * sizeof(TableRecord);
+  const uint64_t tables_b = (uint64_t)g.n_tables * sizeof(TableRecord) + (pairs ? kPairDigits : 0);
   const uint64_t lut_b = (uint64_t)g.n_tables * M * 8;
   const uint64_t states_b = (uint64_t)g.n_tiles * 64 * 4;
   const uint64_t offsets_b = ((uint64_t)g.n_tiles + 1) * 4;
@@ -420,11 +497,23 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
   if (bf16) {
     for (uint32_t sl = 0; sl < g.n_sl; ++sl) {
       uint32_t S = (sl + 1 == g.n_sl) ? g.s_last : g.s_full;
-      raw_b += raw_group_count(S) * 1024ull * g.n_rg;
+      raw_b += raw_group_count(S * kw) * 1024ull * g.n_rg;
     }
   }
   const uint64_t scales_b = has_scales ? (uint64_t)c->rows * 2 : 0;
-  const uint64_t max_words = (uint64_t)g.n_rg * 64 * g.syms_per_row;   // <= 1 word per symbol
+  uint64_t max_words = (uint64_t)g.n_rg * 64 * g.syms_per_row;   // <= 1 word per symbol
+  if (pairs) {
+    // correction streams: a 4-word mask per tile and 2 words per escaped weight
+    std::atomic<uint64_t> n_esc{0};
+    if (w)
+      parallel_for(c->rows, [&](uint64_t r, unsigned) {
+        const uint16_t* p = static_cast<const uint16_t*>(w) + r * (uint64_t)c->cols;
+        uint64_t n = 0;
+        for (uint32_t i = 0; i < c->cols; ++i) n += src0.digit[(p[i] >> 7) & 0xFF] < 0;
+        n_esc += n;
+      });
+    max_words += (uint64_t)g.n_tiles * kEscMaskWords + 2 * n_esc.load();
+  }
   auto layout = [&](uint64_t n_words, SectionRef* sec) {
     uint64_t pos = kHeaderBytes;
     const uint64_t sizes[kNumSections] = {tables_b, lut_b, states_b, offsets_b,
@@ -464,13 +553,14 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     const uint32_t s0 = sl * g.s_full;
     std::vector<int32_t> val((size_t)64 * S);
     std::vector<uint8_t> tbl((size_t)64 * S);
+    std::vector<Escape> esc;   // BF16 pairs, lanes ascending, columns ascending
     bool active[64];
-    SymbolSource src{*c, w, t};
+    const SymbolSource& src = src0;
     for (uint32_t l = 0; l < 64; ++l) {
       uint32_t r = rg * 64 + l;
       active[l] = r < c->rows;
       if (!active[l]) continue;
-      if (!src.row(r, s0, S, &val[(size_t)l * S], &tbl[(size_t)l * S], nullptr)) {
+      if (!src.row(r, s0, S, &val[(size_t)l * S], &tbl[(size_t)l * S], nullptr, pairs ? &esc : nullptr, l)) {
         bad_value = true;
         return;
       }
@@ -512,6 +602,27 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     }
     o.words.assign(pushed.rbegin(), pushed.rend());
     for (int l = 0; l < 64; ++l) o.states[l] = (uint32_t)x[l];
+    if (pairs) {
+      // correction stream after the ANS words: lane mask, then rounds of records
+      uint32_t cnt[64] = {0}, first[64] = {0}, rounds = 0;
+      uint64_t mask = 0;
+      for (const Escape& e : esc) ++cnt[e.lane];
+      for (uint32_t l = 0, a = 0; l < 64; ++l) {
+        first[l] = a;
+        a += cnt[l];
+        if (cnt[l]) mask |= 1ull << l;
+        rounds = std::max(rounds, cnt[l]);
+      }
+      for (uint32_t i = 0; i < kEscMaskWords; ++i) o.words.push_back((uint16_t)(mask >> (16 * i)));
+      for (uint32_t rd = 0; rd < rounds; ++rd)
+        for (uint32_t l = 0; l < 64; ++l) {
+          if (cnt[l] <= rd) continue;
+          const Escape& e = esc[first[l] + rd];
+          const uint32_t rec = e.bits | (e.col << 16) | (rd + 1 == cnt[l] ? kEscLast : 0u);
+          o.words.push_back((uint16_t)rec);
+          o.words.push_back((uint16_t)(rec >> 16));
+        }
+    }
   });
   if (bad_value) return fail(ECW_E_INVALID_ARG, "logical tensor holds a value outside the tables");
   if (bad_freq) return fail(ECW_E_INVALID_ARG, "a symbol of the tensor has zero frequency");
@@ -519,20 +630,21 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
   // BF16 raw plane (row-group-major tile order), written serially per tile
   if (bf16) {
     uint64_t pos = 0;
-    SymbolSource src{*c, w, t};
+    const SymbolSource& src = src0;
     std::vector<int32_t> val;
     std::vector<uint8_t> raw;
     for (uint32_t ti = 0; ti < g.n_tiles; ++ti) {
       const uint32_t rg = ti / g.n_sl, sl = ti % g.n_sl;
       const uint32_t S = (sl + 1 == g.n_sl) ? g.s_last : g.s_full;
-      const uint64_t G = raw_group_count(S);
+      const uint32_t nw = S * kw;             // weights per lane
+      const uint64_t G = raw_group_count(nw);
       val.resize(S);
-      raw.resize(S);
+      raw.resize(nw);
       for (uint32_t l = 0; l < 64; ++l) {
         uint32_t r = rg * 64 + l;
         if (r >= c->rows) continue;
         src.row(r, sl * g.s_full, S, val.data(), nullptr, raw.data());
-        for (uint32_t j = 0; j < S; ++j) raw_plane[pos + (j / 16) * 1024 + l * 16 + (j % 16)] = raw[j];
+        for (uint32_t j = 0; j < nw; ++j) raw_plane[pos + (j / 16) * 1024 + l * 16 + (j % 16)] = raw[j];
       }
       pos += G * 1024;
     }
@@ -586,13 +698,15 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     for (uint32_t s = 0; s < 256; ++s) {
       const uint32_t f = t->freq[k][s];
       uint32_t a8, h16;
-      entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], s, &a8, &h16);
+      entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], t->pair_values, s, &a8,
+                    &h16);
       for (uint32_t i = 0; i < f; ++i, ++slot) {
         lut[2 * slot] = f | (a8 << 24);
         lut[2 * slot + 1] = i | (h16 << 16);   // bias = slot - cum[s]
       }
     }
   }
+  if (pairs) std::memcpy(out + sec[kSecTables].offset + g.n_tables * sizeof(TableRecord), t->pair_values, kPairDigits);
   // STATES, OFFSETS, WORDS
   uint32_t* states = reinterpret_cast<uint32_t*>(out + sec[kSecStates].offset);
   uint32_t* offs = reinterpret_cast<uint32_t*>(out + sec[kSecOffsets].offset);
@@ -683,13 +797,15 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     return fail(ECW_E_CORRUPT, "tile geometry does not match the coding");
   const uint32_t M = 1u << c.log2_m;
   const bool bf16 = c.payload == ECW_P_BF16_EXP;
+  const bool pairs = bf16 && c.weights_per_symbol == 2;
+  const uint32_t kw = bf16 ? c.weights_per_symbol : 1;
   // sections: aligned, in bounds, in order, non-overlapping, exact sizes
   uint64_t raw_b = 0;
   if (bf16)
     for (uint32_t sl = 0; sl < g.n_sl; ++sl)
-      raw_b += raw_group_count(sl + 1 == g.n_sl ? g.s_last : g.s_full) * 1024ull * g.n_rg;
+      raw_b += raw_group_count((sl + 1 == g.n_sl ? g.s_last : g.s_full) * kw) * 1024ull * g.n_rg;
   const uint64_t want[kNumSections] = {
-      (uint64_t)g.n_tables * sizeof(TableRecord), (uint64_t)g.n_tables * M * 8,
+      (uint64_t)g.n_tables * sizeof(TableRecord) + (pairs ? kPairDigits : 0), (uint64_t)g.n_tables * M * 8,
       (uint64_t)g.n_tiles * 256, ((uint64_t)g.n_tiles + 1) * 4, 0, raw_b,
       bf16 ? 0 : (uint64_t)c.rows * 2};
   uint64_t prev_end = kHeaderBytes;
@@ -704,6 +820,11 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     prev_end = end;
   }
   // tables
+  uint8_t pair_values[kPairDigits] = {0};
+  if (pairs) {
+    std::memcpy(pair_values, b + h.sec[kSecTables].offset + g.n_tables * sizeof(TableRecord), kPairDigits);
+    if (pair_values[0] != 0) return fail(ECW_E_CORRUPT, "BF16 pairs: digit 0 is not exponent 0");
+  }
   std::vector<uint32_t> cum((size_t)g.n_tables * 256);
   std::vector<TableRecord> recs(g.n_tables);
   for (uint32_t k = 0; k < g.n_tables; ++k) {
@@ -724,7 +845,7 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
       uint32_t slot = 0;
       for (uint32_t s = 0; s < 256; ++s) {
         uint32_t a8, h16;
-        entry_payload(c.payload, c.code_bits, c.weights_per_symbol, rec.value_offset, s, &a8, &h16);
+        entry_payload(c.payload, c.code_bits, c.weights_per_symbol, rec.value_offset, pair_values, s, &a8, &h16);
         for (uint32_t i = 0; i < rec.freq[s]; ++i, ++slot)
           if (lut[2 * slot] != (rec.freq[s] | (a8 << 24)) || lut[2 * slot + 1] != (i | (h16 << 16)))
             return fail(ECW_E_CORRUPT, "decode table does not match the frequencies");
@@ -740,8 +861,12 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     const uint32_t rg = ti / g.n_sl, sl = ti % g.n_sl;
     const uint32_t S = (sl + 1 == g.n_sl) ? g.s_last : g.s_full;
     const uint32_t act = std::min<uint32_t>(64, c.rows - rg * 64);
-    if ((uint64_t)offs[ti + 1] - offs[ti] > (uint64_t)act * S)
-      return fail(ECW_E_CORRUPT, "tile holds more words than symbols");
+    const uint64_t nwt = (uint64_t)offs[ti + 1] - offs[ti];
+    // at most one ANS word per symbol (BF16 pairs: plus the lane mask and two words
+    // per escaped weight)
+    const uint64_t cap = (uint64_t)act * S + (pairs ? kEscMaskWords + 2ull * act * S * 2 : 0);
+    if (nwt > cap) return fail(ECW_E_CORRUPT, "tile holds more words than symbols");
+    if (pairs && nwt < kEscMaskWords) return fail(ECW_E_CORRUPT, "tile has no correction stream");
     for (uint32_t l = 0; l < 64; ++l) {
       const uint32_t x = states[(size_t)ti * 64 + l];
       if (l < act ? x < kStateL : x != kStateL)

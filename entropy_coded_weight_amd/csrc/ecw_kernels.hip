@@ -1164,9 +1164,10 @@ static void fill_tensor(const ecw_tensor* t, TArgs& a) {
   a.tile_cols = t->coding.tile_cols;
   a.syms_per_row = symbols_per_row(t->coding.payload, t->coding.weights_per_symbol, t->coding.cols);
   a.lut_entries = t->n_tables << t->coding.log2_m;
-  a.raw_full_bytes = (uint32_t)(raw_group_count(t->steps_full) * 1024);
-  a.raw_rg_bytes = t->n_slices ? (uint32_t)((t->n_slices - 1) * raw_group_count(t->steps_full) * 1024 +
-                                            raw_group_count(t->steps_last) * 1024) : 0;
+  const uint32_t kw = t->coding.payload == ECW_P_BF16_EXP ? t->coding.weights_per_symbol : 1;   // raw bytes per step
+  a.raw_full_bytes = (uint32_t)(raw_group_count(t->steps_full * kw) * 1024);
+  a.raw_rg_bytes = t->n_slices ? (uint32_t)((t->n_slices - 1) * raw_group_count(t->steps_full * kw) * 1024 +
+                                            raw_group_count(t->steps_last * kw) * 1024) : 0;
 }
 
 static ecw_status check_tensor(const ecw_tensor* t) {

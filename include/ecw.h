@@ -31,7 +31,8 @@
 extern "C" {
 #endif
 
-#define ECW_ABI_VERSION 1u
+#define ECW_ABI_VERSION 2u
+#define ECW_PAIR_DIGITS 16
 #define ECW_MAX_TABLES 17
 #define ECW_MAX_ALPHABET 256
 
@@ -61,7 +62,9 @@ typedef enum {
 typedef struct {
   uint32_t payload;            /* ecw_payload */
   uint32_t rows, cols;         /* N (outputs) x K (inputs); W is row-major [N][K] */
-  uint32_t weights_per_symbol; /* k: INT 1|2|4 with code_bits*k <= 8; BF16/FP8 1; E8 8 */
+  uint32_t weights_per_symbol; /* k: INT 1|2|4 with code_bits*k <= 8; BF16 1|2; FP8 1;
+                                  E8 8 (BF16 k = 2: cols a multiple of 32, tile_cols
+                                  at most 2048) */
   uint32_t code_bits;          /* INT only: 2, 3 or 4; else 0 */
   uint32_t log2_m;             /* table size M = 2^log2_m, 8..13 */
   uint32_t tile_rows;          /* must be 64 (one wave64 lane per row) */
@@ -71,13 +74,22 @@ typedef struct {
 
 /* Frequency tables of a coding (host POD).  Table 0 serves every payload except
  * E8, where table 0 codes the coset and table 1 + 8c + j codes field j (z1..z7, then
- * m = floor(z8/2)) given coset c (EntroPack page, Sections 3.3 and A.3). */
+ * m = floor(z8/2)) given coset c (EntroPack page, Sections 3.3 and A.3).
+ * BF16 pairs (k = 2; MINE page, Section 4.1 "Escapes" and Section 4.2 "Tuning t"):
+ * a symbol is two 4-bit digits (even column low) into pair_values, the 16 exponents
+ * the table codes.  enc_build_tables stores 0 and the 15 most frequent nonzero
+ * exponents (ties to the smaller), ascending; pair_values[0] must be 0.  An exponent
+ * e != 0 has the first digit d >= 1 with pair_values[d] == e; a weight whose
+ * exponent has no digit is escaped: coded as digit 0 with raw byte 0 (+0.0), its
+ * bits kept in the tile's correction stream (one 4-byte record). */
 typedef struct {
   uint32_t n_tables;
   uint32_t alphabet[ECW_MAX_TABLES];          /* symbols in use per table (<= 256)   */
   int32_t value_offset[ECW_MAX_TABLES];       /* field value = symbol + value_offset */
   uint16_t freq[ECW_MAX_TABLES][ECW_MAX_ALPHABET];   /* f > 0 iff count > 0; sum = M */
   uint64_t count[ECW_MAX_TABLES][ECW_MAX_ALPHABET];  /* histogram the freqs come from */
+  uint8_t pair_values[ECW_PAIR_DIGITS];        /* BF16 pairs: exponent of each digit */
+  uint64_t escapes;                            /* BF16 pairs: weights escaped (output) */
 } ecw_tables;
 
 /* Validated, device-ready view of one blob (host POD, filled by dec_prepare). */

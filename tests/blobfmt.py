@@ -40,11 +40,20 @@ def parse(blob: np.ndarray) -> Blob:
 def tables(bl: Blob):
     t = bl.section("tables")
     n = bl.h["n_tables"]
-    rec = t.reshape(n, 520)
+    rec = t[: 520 * n].reshape(n, 520)
     alphabet = rec[:, 0:4].copy().view(np.uint32).ravel().astype(np.int64)
     value_offset = rec[:, 4:8].copy().view(np.int32).ravel().astype(np.int64)
     freq = rec[:, 8:].copy().view(np.uint16).astype(np.int64)
     return alphabet, value_offset, freq
+
+
+def pair_values(bl: Blob):
+    """BF16 pairs: the 16 stored exponents after the table records (else None)."""
+    if bl.h["payload"] != 2 or bl.h["weights_per_symbol"] != 2:
+        return None
+    t = bl.section("tables")
+    n = bl.h["n_tables"]
+    return t[520 * n: 520 * n + 16].astype(np.int64)
 
 
 def states(bl: Blob) -> np.ndarray:

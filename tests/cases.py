@@ -82,11 +82,39 @@ def small_cases():
     cases.append(Case("bf16_m12", BF16, 130, 512, 1, 0, 12, 256, b.bits, None, "bf16"))
     b = E.bf16_weights((64, 1536), np.random.default_rng([0, 300, 2]))
     cases.append(Case("bf16_m10_ragged_k", BF16, 64, 1536, 1, 0, 10, 1024, b.bits, None, "bf16"))
+    # BF16 exponent pairs: few escapes (Gaussian), many escapes over several rounds
+    # with fp16 activations and a ragged row group, the widest slice the record's
+    # 11-bit column allows, and the smallest table
+    b = E.bf16_weights((130, 512), np.random.default_rng([0, 300, 3]))
+    cases.append(Case("bf16_pairs_m12", BF16, 130, 512, 2, 0, 12, 256, b.bits, None, "bf16"))
+    cases.append(Case("bf16_pairs_mixed_ragged", BF16, 70, 288, 2, 0, 12, 128, bf16_mixed(70, 288, 1), None, "f16"))
+    cases.append(Case("bf16_pairs_mixed_bf16x", BF16, 96, 640, 2, 0, 11, 128, bf16_mixed(96, 640, 2), None, "bf16"))
+    cases.append(Case("bf16_pairs_tc2048_m8", BF16, 64, 4096, 2, 0, 8, 2048, bf16_mixed(64, 4096, 3, 0.002), None,
+                      "bf16"))
     f = E.fp8_weights((96, 768), np.random.default_rng([0, 400, 1]))
     cases.append(Case("fp8_m12", FP8, 96, 768, 1, 0, 12, 256, f.codes, f.scales, "bf16"))
     f = E.fp8_weights((64, 512), np.random.default_rng([0, 400, 2]))
     cases.append(Case("fp8_m9", FP8, 64, 512, 1, 0, 9, 64, f.codes, f.scales, "bf16"))
     return cases
+
+
+def bf16_mixed(rows, cols, seed, frac=0.02):
+    """Gaussian bf16 weights with a fraction of special values (zeros of both signs,
+    subnormals, very large and very small normals) and of random bit patterns with
+    exponents up to 190, so many exponents fall outside the 16 a pair table stores
+    while every product and row sum stays finite in fp32."""
+    rng = np.random.default_rng([0, 320, seed])
+    b = E.bf16_weights((rows, cols), rng).bits.copy()
+    flat = b.reshape(-1)
+    n = flat.size
+    idx = rng.choice(n, int(n * frac), replace=False)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x5F00, 0xDF12, 0x2000, 0x4000], np.uint16)
+    flat[idx] = rng.choice(special, idx.size)
+    idx = rng.choice(n, int(n * frac / 2), replace=False)
+    sign = rng.integers(0, 2, idx.size) << 15
+    expo = rng.integers(0, 191, idx.size) << 7
+    flat[idx] = (sign | expo | rng.integers(0, 128, idx.size)).astype(np.uint16)
+    return b
 
 
 def e8_case(recon_dtype=4, rows=96, cols=192, m=11, tc=64, sigma=3.0, seed=1):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = ecw.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert L.ecw_abi_version() == 1
+    assert L.ecw_abi_version() == 2
 
 
 def test_tile_metadata_bytes_match_page_formula():
@@ -62,7 +62,9 @@ def test_byte_parity_with_oracle_and_oracle_decodes_library_blob(case):
     comp2 = P.Components(comp.coding, comp.n_tables, alphabet, voff, freq, comp.n_rg, comp.n_sl,
                          comp.s_full, comp.s_last, blobfmt.states(bl), blobfmt.offsets(bl),
                          blobfmt.words(bl), bl.section("raw") if comp.raw is not None else None,
-                         blobfmt.scales(bl))
+                         blobfmt.scales(bl), pair_values=blobfmt.pair_values(bl))
+    if comp.pair_values is not None:
+        assert np.array_equal(comp2.pair_values, comp.pair_values)
     _, ok = P.decode_symbols(comp2)
     assert ok.all()
     assert np.array_equal(P.decode(comp2), case.logical)
@@ -365,3 +367,96 @@ def test_bench_lattice_inputs_match_the_test_recipe():
     assert np.array_equal(scales.view(np.uint16), so.view(np.uint16))
     assert np.array_equal(x, xo)
     assert abs(bpw - 4.0) < 0.01
+
+
+# ------------------------------------------------------------------ BF16 exponent pairs
+def _pair_case(name):
+    return [c for c in cases.small_cases() if c.name == name][0]
+
+
+def test_bf16_pair_tables_match_oracle():
+    from oracle import symbols
+    for name in ("bf16_pairs_m12", "bf16_pairs_mixed_ragged"):
+        case = _pair_case(name)
+        t = ecw.build_tables(case.lib_coding(), case.logical)
+        comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+        assert np.array_equal(np.array(list(t.pair_values)), comp.pair_values)
+        _, _, esc = symbols.bf16_pair_split(case.logical, comp.pair_values)
+        assert t.escapes == int(esc.sum()) > 0
+        assert np.array_equal(t.count_array(), comp.counts)
+        assert np.array_equal(t.freq_array(), comp.freq)
+
+
+def test_bf16_pair_entry_payload_holds_both_rotated_exponents():
+    # a8 = the symbol; h16 = rot(e0) | rot(e1) << 8 for the digits' exponents, so one
+    # pair of byte permutes with the two raw bytes rebuilds both bf16 values
+    case = _pair_case("bf16_pairs_m12")
+    bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    _, _, freq = blobfmt.tables(bl)
+    pv = blobfmt.pair_values(bl)
+    lut = blobfmt.lut(bl)[0]
+    sym = np.repeat(np.arange(256), freq[0])
+    assert np.array_equal(lut[:, 0] >> 24, sym)
+    rot = lambda e: ((e >> 1) | (e << 7)) & 0xFF
+    h = lut[:, 1] >> 16
+    assert np.array_equal(h & 0xFF, rot(pv[sym & 15]))
+    assert np.array_equal(h >> 8, rot(pv[sym >> 4]))
+
+
+def test_bf16_pair_coding_limits_and_validation():
+    L = ecw.lib()
+    case = _pair_case("bf16_pairs_m12")
+    # cols must be a multiple of 32; the record's 11-bit column caps the slice width
+    for c in (ecw.Coding(ecw.BF16_EXP, 64, 48, 2, 0, 12, 64), ecw.Coding(ecw.BF16_EXP, 64, 4096, 2, 0, 12, 4096),
+              ecw.Coding(ecw.BF16_EXP, 64, 64, 4, 0, 12, 64)):
+        t = ecw.Tables()
+        w = np.zeros((c.rows, c.cols), np.uint16)
+        assert L.enc_build_tables(ctypes.byref(c), w.ctypes.data_as(ctypes.c_void_p), ctypes.byref(t)) == 2
+    # digit 0 must stay exponent 0 (escaped weights are coded as +0.0)
+    t = ecw.build_tables(case.lib_coding(), case.logical)
+    t.pair_values[0] = 5
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(case.lib_coding(), case.logical, None, t)
+    base = ecw.encode(case.lib_coding(), case.logical, None)
+    assert _prep_status(base) == 0
+    bl = blobfmt.parse(base)
+    off_t, n_t = bl.sec["tables"]
+    assert n_t == 520 + 16
+    b = base.copy()
+    b[off_t + 520] = 7
+    assert _prep_status(b) == 3
+    # a tile too short to hold its correction stream's lane mask
+    off_o, _ = bl.sec["offsets"]
+    b = base.copy()
+    offs = b[off_o: off_o + 8].view(np.uint32)
+    offs[1] = offs[0] + 3
+    assert _prep_status(b) == 3
+
+
+def test_bf16_pairs_with_fewer_digits_escape_more():
+    # tables may store fewer than 16 exponents (unused digits hold 0): every other
+    # exponent is escaped, and the oracle still decodes the library's blob exactly
+    case = _pair_case("bf16_pairs_m12")
+    c = case.lib_coding()
+    t = ecw.build_tables(c, case.logical)
+    keep = [v for v in t.pair_values][:6]
+    for d in range(6, 16):
+        t.pair_values[d] = 0
+    w = case.logical
+    ex = (w.astype(np.int64) >> 7) & 0xFF
+    # frequencies for the pair symbols the shortened table produces
+    from oracle import coding, symbols
+    sym, _, esc = symbols.bf16_pair_split(w, np.array(keep + [0] * 10))
+    counts = coding.histogram(sym, 256)
+    f = coding.normalise(counts, c.log2_m)
+    for s_ in range(256):
+        t.freq[0][s_] = int(f[s_])
+    blob = ecw.encode(c, w, None, t)
+    bl = blobfmt.parse(blob)
+    comp = P.Components(case.oracle_coding(), 1, np.array([256]), np.array([0]), f[None, :],
+                        bl.h["n_row_groups"], bl.h["n_slices"], bl.h["steps_full"], bl.h["steps_last"],
+                        blobfmt.states(bl), blobfmt.offsets(bl), blobfmt.words(bl), bl.section("raw"), None,
+                        pair_values=blobfmt.pair_values(bl))
+    assert esc.sum() > 1000 and not np.isin(ex, keep).all()
+    assert P.decode_symbols(comp)[1].all()
+    assert np.array_equal(P.decode(comp), w)
