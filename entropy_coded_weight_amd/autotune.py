@@ -43,9 +43,12 @@ class Candidate:
 
 
 def legal_ks(payload: int, code_bits: int, ks=None):
-    if payload != INT_CODES:
-        return (1,)
-    out = [k for k in (1, 2, 4) if code_bits * k <= 8]
+    if payload == INT_CODES:
+        out = [k for k in (1, 2, 4) if code_bits * k <= 8]
+    elif payload == BF16_EXP:
+        out = [1, 2]          # exponent pairs, with escapes outside the 16 stored exponents
+    else:
+        out = [1]
     return tuple(k for k in out if ks is None or k in ks)
 
 
@@ -56,6 +59,8 @@ def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT
         for m in log2_ms:
             for tc in tile_cols:
                 if tc % 64 or tc % (8 * k) or tc > max(64, ((cols + 63) // 64) * 64):
+                    continue
+                if payload == BF16_EXP and k == 2 and (cols % 32 or tc > 2048):
                     continue
                 yield k, m, tc
 

@@ -54,11 +54,16 @@ template <int PAY, int KW, bool XBF>
 constexpr bool kPairTable = PAY == 1 && (KW == 4 || (KW == 2 && XBF));
 // BF16 weights with bf16 activations: two steps' weights are joined into one packed
 // bf16 pair and multiplied with one bf16 dot product.
-template <int PAY, bool XBF>
-constexpr bool kBfPair = PAY == 2 && XBF;
+template <int PAY, int KW, bool XBF>
+constexpr bool kBfPair = PAY == 2 && KW == 1 && XBF;
+// BF16 exponent pairs: one symbol carries the exponents of two adjacent weights (the
+// entry's high half holds both, rotated); escaped weights come from the tile's
+// correction stream.
+template <int PAY, int KW>
+constexpr bool kBfSym2 = PAY == 2 && KW == 2;
 // Table entries whose high word is the bias alone (no payload bits beside it).
 template <int PAY, int KW>
-constexpr bool kCleanBias = (PAY == 1 && KW == 4) || PAY == 2 || PAY == 4;
+constexpr bool kCleanBias = (PAY == 1 && KW == 4) || (PAY == 2 && KW == 1) || PAY == 4;
 
 #define ECW_LDS __attribute__((address_space(3)))
 template <typename T>
@@ -251,6 +256,62 @@ __device__ __forceinline__ void refill(uint32_t rposb, uint32_t& haveb, uint32_t
   }
 }
 
+// Correction stream of a BF16 exponent-pair tile (MINE page, Section 4.1 "Escapes":
+// escaped weights were coded as 0; their records follow the tile's ANS words).
+// After the tile's last symbol: every lane reads its bit of the 64-bit lane mask,
+// then the lanes that still hold records read one each per round, at their prefix
+// offset among those lanes (the renormalisation's coordination), and add weight *
+// activation (or, decode-only, store the weight).  Rounds end when every lane has
+// read its row's last record, or after `width` rounds (a row has at most `width`
+// escapes) so that a damaged stream still ends.  Records are read as two 16-bit
+// halves, each wrapped into the ring.  col: staged column of the tile's first
+// weight; width: weights per row in the tile; wrow: w_out index of this row's first
+// weight in the tile.
+template <int B, bool MAT, bool XBF>
+__device__ __forceinline__ void tile_corrections(const TArgs& a, uint32_t& rposb, uint32_t& haveb, uint32_t& nc,
+                                              uint2& pre, uint32_t wl, const uint2* src, uint32_t nch,
+                                              uint32_t lane, uint32_t ring, uint32_t xs, uint32_t col,
+                                              uint32_t width, bool active, uint64_t wrow, float* acc) {
+  constexpr uint32_t kWrap = 2 * kRing - 2;
+  refill(rposb, haveb, nc, pre, wl, src, nch, lane);
+  const uint32_t mw = *lds_ptr<const uint16_t>(ring + ((rposb + 2 * (lane >> 4)) & kWrap));
+  bool has = active && ((mw >> (lane & 15)) & 1u);
+  rposb += 2 * kEscMaskWords;
+  uint64_t act = __ballot(has);
+  for (uint32_t round = 0; act != 0 && round < width; ++round) {
+    refill(rposb, haveb, nc, pre, wl, src, nch, lane);
+    const uint32_t pos = rposb + 4 * lanes_below(act);
+    const uint32_t lo = *lds_ptr<const uint16_t>(ring + (pos & kWrap));
+    const uint32_t hi = *lds_ptr<const uint16_t>(ring + ((pos + 2) & kWrap));
+    rposb += 4 * (uint32_t)__popcll(act);
+    if (has) {
+      const uint32_t rec = lo | (hi << 16);
+      const uint32_t c = (rec >> 16) & 0x7FFu;
+      if (c < width) {
+        if constexpr (MAT) {
+          if (a.w_out) static_cast<uint16_t*>(a.w_out)[wrow + c] = (uint16_t)rec;
+        } else {
+          const float w = __uint_as_float(rec << 16);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            float xv;
+            if constexpr (XBF) {
+              // packed pairs [column / 2][B]; the tile starts on an even column
+              const uint32_t xw = *lds_ptr<const uint32_t>(xs + (((col + c) >> 1) * B + b) * 4);
+              xv = __uint_as_float((c & 1u) ? (xw & 0xFFFF0000u) : (xw << 16));
+            } else {
+              xv = *lds_ptr<const float>(xs + ((col + c) * B + b) * 4);
+            }
+            acc[b] = fmaf(w, xv, acc[b]);
+          }
+        }
+      }
+      if (rec & kEscLast) has = false;
+    }
+    act = __ballot(has);
+  }
+}
+
 // BF16 join from whole bytes (DFloat11 page, Algorithm 1: the decoded exponent
 // joined with the stored sign and mantissa).  The table byte a8 holds the exponent
 // rotated right by one bit; the raw byte r is sign << 7 | mantissa.  The bf16 high
@@ -271,6 +332,16 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t ex0, uint32_t ex1, uint32
   const uint32_t qq = (uint32_t)q;
   const uint32_t p1 = __builtin_amdgcn_perm(a, rdw, qq | (4u << 8) | ((qq + 1) << 16) | (5u << 24));
   const uint32_t p2 = __builtin_amdgcn_perm(a, rdw, 4u | (qq << 8) | (5u << 16) | ((qq + 1) << 24));
+  return (p2 & 0x80808080u) | (p1 & 0x7F7F7F7Fu);
+}
+
+//   bf16_sym2: both weights of a BF16 exponent-pair symbol (first in the low half)
+//   from the entry's high word (bias | rot e0 << 16 | rot e1 << 24) and their raw
+//   bytes, bytes q and q + 1 of rdw.
+__device__ __forceinline__ uint32_t bf16_sym2(uint32_t ey, uint32_t rdw, int q) {
+  const uint32_t qq = (uint32_t)q;
+  const uint32_t p1 = __builtin_amdgcn_perm(ey, rdw, qq | (6u << 8) | ((qq + 1) << 16) | (7u << 24));
+  const uint32_t p2 = __builtin_amdgcn_perm(ey, rdw, 6u | (qq << 8) | (7u << 16) | ((qq + 1) << 24));
   return (p2 & 0x80808080u) | (p1 & 0x7F7F7F7Fu);
 }
 
@@ -318,6 +389,19 @@ __device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t 
   } else if constexpr (PAY == 1) {
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = fma_mix_hi(e.y, __uint_as_float(xw[b]), acc[b]);   // q0
+  } else if constexpr (kBfSym2<PAY, KW>) {
+    const uint32_t wp = bf16_sym2(e.y, rdw, q);
+    if constexpr (XBF) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[b] = dot2<true>(wp, xw[b], acc[b]);
+    } else {
+      const float w0 = __uint_as_float(wp << 16), w1 = __uint_as_float(wp & 0xFFFF0000u);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        acc[b] = fmaf(w0, __uint_as_float(xw[b]), acc[b]);
+        acc[b] = fmaf(w1, __uint_as_float(xw[B + b]), acc[b]);
+      }
+    }
   } else if constexpr (PAY == 2) {
     const float w = __uint_as_float(bf16_in_f32(e.x, rdw, q));
 #pragma unroll
@@ -391,8 +475,10 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
                                           uint32_t ring, uint32_t rg, uint32_t t0, uint32_t t1, uint32_t c_lo,
                                           uint32_t lane, bool active, float* acc) {
   constexpr int U = 16;
-  constexpr bool DOT = kDot<PAY, KW>;
-  constexpr bool BFP = kBfPair<PAY, XBF> && !MAT;   // bf16 weight pairs, two steps per dot
+  constexpr bool BF2 = kBfSym2<PAY, KW>;               // bf16 exponent-pair symbols
+  constexpr bool DOT = kDot<PAY, KW> || (BF2 && XBF);
+  constexpr bool BFP = kBfPair<PAY, KW, XBF> && !MAT;   // bf16 weight pairs, two steps per dot
+  constexpr int RG = BF2 ? 2 : 1;                      // raw 16-byte groups per U steps
   constexpr bool PK = DOT || BFP;                   // activations staged as 16-bit pairs
   constexpr bool CLEAN = kCleanBias<PAY, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;   // 32-bit activation words per step
@@ -409,10 +495,15 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
   uint2 pre = h.pre;
   uint32_t haveb = 4 * kChunk, nc = 2;
   uint32_t st = h.st;
-  // BF16 raw bytes: each 16-step group is loaded one group ahead of its use
+  // BF16 raw bytes: the groups of each U steps are loaded one U-step block ahead
   const uint8_t* rawp = raw_tile(a, rg, t0 - sl0, lane);
-  uint4 rnext = zero4;
-  if constexpr (PAY == 2) rnext = *reinterpret_cast<const uint4*>(rawp);
+  uint4 rnext[RG];
+#pragma unroll
+  for (int i = 0; i < RG; ++i) rnext[i] = zero4;
+  if constexpr (PAY == 2) {
+#pragma unroll
+    for (int i = 0; i < RG; ++i) rnext[i] = *reinterpret_cast<const uint4*>(rawp + 1024 * i);
+  }
 
   for (uint32_t t = t0; t < t1; ++t) {
     uint32_t x = st;
@@ -422,13 +513,19 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
     const uint32_t col = sl * a.tile_cols - c_lo;
 
     for (uint32_t j = 0; j < S; j += U) {
-      uint4 rgp = zero4;
+      uint4 rgp[RG];
+#pragma unroll
+      for (int i = 0; i < RG; ++i) rgp[i] = zero4;
       if constexpr (PAY == 2) {
-        rgp = rnext;
-        // the next group: of this tile, else the first of the wave's next tile
+#pragma unroll
+        for (int i = 0; i < RG; ++i) rgp[i] = rnext[i];
+        // the next groups: of this tile, else the first of the wave's next tile
         const bool more = j + U < S || t + 1 < t1;          // wave-uniform
-        rawp = j + U < S ? rawp + 1024 : raw_tile(a, rg, sl + 1, lane);
-        if (more) rnext = *reinterpret_cast<const uint4*>(rawp);
+        rawp = j + U < S ? rawp + 1024 * RG : raw_tile(a, rg, sl + 1, lane);
+        if (more) {
+#pragma unroll
+          for (int i = 0; i < RG; ++i) rnext[i] = *reinterpret_cast<const uint4*>(rawp + 1024 * i);
+        }
       }
       // activation words of step j: fp32 [col][B], or packed pairs [col / 2][B]
       const uint32_t xg = xs + ((col + KW * j) * B / (PK ? 2 : 1)) * 4;
@@ -449,9 +546,19 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
           const int u = qtr * 4 + u4;
           const uint32_t step = j + u;
           const uint2 e = decode_step<CLEAN>(x, lut, m, mmask);
+          // BF16: the dword of raw bytes holding this step's (first) weight, at byte q
+          uint32_t rdw;
+          int q;
+          if constexpr (BF2) {
+            rdw = raw_dword(rgp[u >> 3], (2 * u) & 15);
+            q = (u & 1) * 2;
+          } else {
+            rdw = raw_dword(rgp[0], u);
+            q = u & 3;
+          }
           if constexpr (BFP) {
             if (u4 & 1) {
-              const uint32_t wp = bf16_pair(ex0, e.x, raw_dword(rgp, u), (u - 1) & 3);
+              const uint32_t wp = bf16_pair(ex0, e.x, rdw, (u - 1) & 3);
 #pragma unroll
               for (int b = 0; b < B; ++b) acc[b] = dot2<true>(wp, xp[(u4 >> 1) * B + b], acc[b]);
               pin<B>(acc);
@@ -459,12 +566,11 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
               ex0 = e.x;
             }
           } else if constexpr (!MAT) {
-            mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW, raw_dword(rgp, u), u & 3,
-                                     acc);
+            mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW, rdw, q, acc);
             pin<B>(acc);
           } else if (!RAGGED || active) {
             uint32_t aux = e.x >> 24;
-            if constexpr (PAY == 2) aux = ((aux << 1) | (aux >> 7)) & 0xFFu;   // table byte: rotated exponent
+            if constexpr (PAY == 2 && !BF2) aux = ((aux << 1) | (aux >> 7)) & 0xFFu;   // rotated exponent
             uint32_t symbol = aux;
             int q[KW > 0 ? KW : 1];
             if constexpr (PAY == 1) {
@@ -483,8 +589,19 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
               if constexpr (PAY == 1) {
 #pragma unroll
                 for (int i = 0; i < KW; ++i) static_cast<int8_t*>(a.w_out)[wi + i] = (int8_t)q[i];
+              } else if constexpr (BF2) {
+                // escaped weights are written here as +0.0 and overwritten by the
+                // tile's correction stream
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                  const int byte = 2 * u + i;
+                  const uint32_t r = raw_byte(rgp[byte >> 4], byte & 15);
+                  const uint32_t ar = (e.y >> (16 + 8 * i)) & 0xFFu;
+                  const uint32_t ex = ((ar << 1) | (ar >> 7)) & 0xFFu;
+                  static_cast<uint16_t*>(a.w_out)[wi + i] = (uint16_t)(((r & 0x80u) << 8) | (ex << 7) | (r & 0x7Fu));
+                }
               } else if constexpr (PAY == 2) {
-                const uint32_t r = raw_byte(rgp, u);
+                const uint32_t r = raw_byte(rgp[0], u);
                 static_cast<uint16_t*>(a.w_out)[wi] = (uint16_t)(((r & 0x80u) << 8) | (aux << 7) | (r & 0x7Fu));
               } else {
                 static_cast<uint8_t*>(a.w_out)[wi] = (uint8_t)aux;
@@ -495,6 +612,9 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
         }
       }
     }
+    if constexpr (BF2)
+      tile_corrections<B, MAT, XBF>(a, rposb, haveb, nc, pre, wl, src, nch, lane, ring, xs, col, 2 * S, active,
+                                    (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols, acc);
     if constexpr (MAT) {
       const bool ok_lane = !active || x == kStateL;
       const uint64_t bad = __ballot(!ok_lane);
@@ -519,7 +639,7 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
                                                 uint32_t lane, bool activeB, float* accA, float* accB) {
   constexpr int U = 16;
   constexpr bool DOT = kDot<PAY, KW>;
-  constexpr bool BFP = kBfPair<PAY, XBF>;
+  constexpr bool BFP = kBfPair<PAY, KW, XBF>;
   constexpr bool PK = DOT || BFP;
   constexpr bool CLEAN = kCleanBias<PAY, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;
@@ -790,7 +910,7 @@ k_decode(const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
   (void)smem;
   // activations staged as packed 16-bit pairs (dot-product paths), else as fp32
-  constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, XBF>) && !MAT;
+  constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, KW, XBF> || (kBfSym2<PAY, KW> && XBF)) && !MAT;
   constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT;
   const uint32_t W = ka.waves;
   const uint32_t tid = threadIdx.x;
@@ -813,7 +933,7 @@ k_decode(const KArgs ka) {
   constexpr bool E8 = PAY == 4;
   // streams per wave: 2 = the tiles of two adjacent row groups in lockstep (fused
   // GEMV of INT, BF16 and FP8 payloads)
-  constexpr bool kTwoCapable = !MAT && !E8;
+  constexpr bool kTwoCapable = !MAT && !E8 && !kBfSym2<PAY, KW>;
   const uint32_t NSr = (kTwoCapable && a.ns == 2) ? 2u : 1u;
   // the block's slice group and its run of row-group units [u_lo, u_hi); a unit is
   // NSr adjacent row groups, decoded by the waves' streams
@@ -1087,7 +1207,8 @@ static KernelFn pick_kernel(const ecw_coding& c) {
         case 2 * 16 + 4: return k_decode<1, 2, 4, B, MAT, XBF>;
       }
       return nullptr;
-    case ECW_P_BF16_EXP: return k_decode<2, 0, 1, B, MAT, XBF>;
+    case ECW_P_BF16_EXP:
+      return c.weights_per_symbol == 2 ? k_decode<2, 0, 2, B, MAT, XBF> : k_decode<2, 0, 1, B, MAT, XBF>;
     case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT, false>;
     case ECW_P_E8_LATTICE:
       return c.recon_dtype == ECW_DT_FP8_E4M3 ? k_decode<4, 1, 8, B, MAT, false> : k_decode<4, 0, 8, B, MAT, false>;
@@ -1109,6 +1230,14 @@ static bool pair_table(const ecw_coding& c, bool xbf) {
   return c.payload == ECW_P_INT_CODES && (c.weights_per_symbol == 4 || (c.weights_per_symbol == 2 && xbf));
 }
 
+// Two row-group streams per wave: asked for, and built for the payload (E8 and BF16
+// exponent pairs decode one stream per wave).
+static bool two_streams(const ecw_tensor* t) {
+  const ecw_coding& c = t->coding;
+  return t->streams_per_wave == 2 && c.payload != ECW_P_E8_LATTICE &&
+         !(c.payload == ECW_P_BF16_EXP && c.weights_per_symbol == 2);
+}
+
 // Dynamic LDS of one block: pair side table, decode table, staged activations,
 // word rings.  Mirrors the layout k_decode computes.
 static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t xs_cols, int B, bool mat,
@@ -1119,7 +1248,7 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
-  const bool two = !mat && !e8 && t->streams_per_wave == 2;
+  const bool two = !mat && two_streams(t);
   (void)R;
   return pair + lut * 8 + xs + (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
 }
@@ -1256,7 +1385,7 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
     a.ns = t->streams_per_wave;
     a.rpb = std::max(1u, t->row_groups_per_block);
     a.n_sg = slice_groups(t);
-    const uint32_t ns = (t->streams_per_wave == 2 && t->coding.payload != ECW_P_E8_LATTICE) ? 2u : 1u;
+    const uint32_t ns = two_streams(t) ? 2u : 1u;
     const uint32_t units = (a.n_rg + ns - 1) / ns;
     a.n_blocks = (units + a.rpb - 1) / a.rpb * a.n_sg;
     ka.block_begin[ka.nt] = blocks;

@@ -21,7 +21,11 @@ def test_candidates_respect_the_format():
     assert {k for k, _, _ in got2} == {1, 2, 4}
     # tiles wider than the (64-rounded) row are pointless
     assert all(tc <= 256 for _, _, tc in got2)
-    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256)]
+    # BF16: one exponent per symbol, or a pair (cols a multiple of 32, slices up to 2048)
+    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256),
+                                                                                                (2, 12, 256)]
+    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 528, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256)]
+    assert list(A.coding_candidates(ecw.FP8_E4M3, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256)]
 
 
 def _cand(k, m, tc, nbytes, shapes):
