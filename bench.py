@@ -72,11 +72,15 @@ def run_tuner(path: str, batch: int):
         specs[name] = (INT_CODES, t.codes, t.scales, 4)
         log(f"tuning {name} {t.codes.shape}")
         cands[name] = A.tune_tensor(INT_CODES, t.codes, t.scales, xs[name], code_bits=4, ks=(1, 2), log=log)
-    picks = {}
+    picks, fronts = {}, {}
     for ln, names in LAUNCHES:
         log(f"tuning launch {ln}")
-        g = A.tune_group({n: specs[n] for n in names}, {n: cands[n] for n in names}, xs[names[0]], log=log)
+        pts = []
+        g = A.tune_group({n: specs[n] for n in names}, {n: cands[n] for n in names}, xs[names[0]], log=log,
+                         points=pts)
         picks.update(g)
+        # the launch's speed-size Pareto front over every timed grouping (MINE page, Section 4.2)
+        fronts[ln] = [[round(u, 3), int(b), ch] for u, b, ch in A.pareto_front(pts)]
     table = {n: [dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, stored_bytes=c.stored_bytes,
                       shapes={f"{w}x{r}x{ns}x{p}": round(us, 3) for (w, r, ns, p), us in c.shape_us.items()})
                  for c in cands[n]] for n in ORDER}
@@ -84,7 +88,8 @@ def run_tuner(path: str, batch: int):
     with open(path, "w") as f:
         json.dump({"workload": "Llama-3.1-8B-shaped layer set, 16-level Laplacian codes (H=2.2 bits), "
                                f"fp16 row scales, fp16 x, batch {batch}",
-                   "device": torch.cuda.get_device_name(0), "picks": picks, "candidates": table}, f, indent=1)
+                   "device": torch.cuda.get_device_name(0), "picks": picks, "fronts": fronts,
+                   "candidates": table}, f, indent=1)
     log(f"wrote {path}")
 
 
@@ -379,6 +384,9 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
                                                    f"coset-indexed tables (M tuned), {tag} reconstruction, "
                                                    "fp16 row scales, fp16 x, batch 1"})
 
+    if "p" in which:
+        res["budget"] = budget_points(steps, cold_bytes)
+
     if "4" in which:
         names = ["q", "k", "v", "o", "gate", "up", "down"] + (["lm_head"] if lm_head else [])
         groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
@@ -447,6 +455,70 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
     return res
 
 
+def budget_points(steps: int, cold_bytes: float):
+    """The layer set under byte budgets: from the tune file's per-launch speed-size
+    Pareto fronts, the fastest choice of one grouping per launch whose stored bytes fit
+    the budget (exact multiple-choice knapsack), for the smallest feasible budget, the
+    fastest choice's size and one midway; each choice is encoded, timed cold and
+    checked like the headline, and its payload words are set against the
+    cross-entropy lower bound of its tables (MINE page, Section 4.2)."""
+    import torch
+    import ecw_inputs as E
+    import entropy_coded_weight_amd as ecw
+    from entropy_coded_weight_amd import autotune as A
+    tf = json.load(open(TUNE_FILE))
+    if "fronts" not in tf:
+        return None
+    fr = {ln: [(u, b, ch) for u, b, ch in pts] for ln, pts in tf["fronts"].items()}
+    lo = sum(min(b for _, b, _ in pts) for pts in fr.values())
+    fastest = A.choose_under_budget(fr, 1 << 62)
+    tensors = {}
+    out = []
+    for label, budget in (("smallest", lo), ("midway", (lo + fastest[1]) // 2), ("fastest", fastest[1])):
+        u_pred, b_sel, choice = A.choose_under_budget(fr, budget)
+        log(f"budget {label}: {budget / 1e6:.3f} MB -> predicted {u_pred:.2f} us, {b_sel / 1e6:.3f} MB")
+        launches, words, bound, stored_b = [], 0, 0.0, 0
+        checks, xhost = [], {}
+        for ln, ch in choice.items():
+            members = []
+            for n, p in ch.items():
+                if n not in tensors:
+                    tensors[n] = E.config2_tensor(n)
+                t = tensors[n]
+                c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"])
+                tab = ecw.build_tables(c, t.codes)
+                blob = ecw.encode(c, t.codes, t.scales, tab)
+                tt = ecw.prepare(blob)
+                words += tt.bytes_words
+                stored_b += tt.bytes_words + tt.bytes_raw + tt.bytes_tile_meta + tt.bytes_tables + tt.bytes_scales
+                bound += A.size_lower_bound_bytes(tab)
+                members.append((blob, (p["waves_per_block"], p["tiles_per_wave"], p["streams_per_wave"],
+                                       p["row_groups_per_block"])))
+                checks.append((ln, len(members) - 1, n))
+            xh = tensors[next(iter(ch))].x          # the launch's activations: its first member's
+            launches.append((ln, members, torch.from_numpy(xh).cuda()))
+            xhost[ln] = xh
+        us, ys = time_cold(launches, 1, steps, cold_bytes)
+        worst = 0.0
+        for ln, i, n in checks:
+            t = tensors[n]
+            rows = _rows(t.codes.shape[0])
+            wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
+            worst = max(worst, check_rows(ys[ln][i][:, rows], wv, xhost[ln].astype(np.float64)))
+        out.append({"label": label, "budget_bytes": int(budget), "stored_bytes": int(stored_b),
+                    "predicted_us_warm": round(u_pred, 3), "measured_us_cold": round(sum(us.values()), 3),
+                    "per_launch_us": {k: round(v, 3) for k, v in us.items()},
+                    "payload_words_bytes": int(words), "payload_lower_bound_bytes": int(bound),
+                    "words_over_bound": round(words / bound, 5), "parity_worst_err_over_bound": worst,
+                    "codings": {n: {k: p[k] for k in ("k", "log2_m", "tile_cols", "waves_per_block",
+                                                      "tiles_per_wave", "streams_per_wave",
+                                                      "row_groups_per_block")}
+                                for ch in choice.values() for n, p in ch.items()}})
+        log(f"  measured {out[-1]['measured_us_cold']:.2f} us cold, words/bound {out[-1]['words_over_bound']:.4f}")
+    return {"workload": "the INT4 layer set under byte budgets (one grouping per launch from the tune file's "
+                        "Pareto fronts)", "front_points": {ln: len(p) for ln, p in fr.items()}, "points": out}
+
+
 def summarize_rocprof(directory: str):
     """Print per-(kernel, grid size) averages from rocprofv3 CSV output under
     `directory`: kernel durations from *_kernel_trace.csv and counter values from
@@ -513,10 +585,11 @@ def main():
     ap.add_argument("--tune-file", default=TUNE_FILE)
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print per-launch averages of rocprofv3 CSV output under DIR and exit")
-    ap.add_argument("--configs", default="1,3,4,5",
+    ap.add_argument("--configs", default="1,3,4,5,p",
                     help="secondary workloads measured after the layer set (1: Gaussian codes, "
                          "3: BF16 exponent coding, 4: FP8 layer at batch 1 and 4, 5: E8 lattice "
-                         "fields, INT8 and FP8 reconstruction); '' for none")
+                         "fields, INT8 and FP8 reconstruction, p: the layer set under byte budgets "
+                         "from the tune file's Pareto fronts); '' for none")
     ap.add_argument("--lm-head", action="store_true",
                     help="include the 128256x4096 LM head in workload 4 (its generation takes minutes)")
     ap.add_argument("--tensors", default=",".join(ORDER),

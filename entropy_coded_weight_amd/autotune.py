@@ -164,7 +164,7 @@ def _ranked(cands, waves, top):
 
 
 def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | None = None, reps: int = 20,
-               tie: float = 0.02, log=None):
+               tie: float = 0.02, log=None, points: list | None = None):
     """Tensors sharing one launch (same activations) must share waves per block.  For
     each common waves-per-block value, every combination of each member's `top`
     fastest single-tensor candidates at that value, and every launch shape all
@@ -172,12 +172,16 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
     real grouped launch; the fastest group wins (ties within `tie`: fewer stored
     bytes).
     specs[name] = (payload, w, scales, code_bits) re-encodes a candidate.  By default
-    `top` keeps the number of timed combinations near 16 per waves-per-block value."""
+    `top` keeps the number of timed combinations near 16 per waves-per-block value.
+    points: if given, every timed group is appended as (us, stored bytes, picks), the
+    material of the group's speed-size Pareto front."""
     import itertools
     names = list(cands_by_name)
     if top is None:
         top = {1: 16, 2: 4, 3: 2}.get(len(names), 1)
     if len(names) == 1:
+        if points is not None:
+            points.extend((us, nbytes, {names[0]: p}) for us, nbytes, p in tensor_points(cands_by_name[names[0]]))
         return {names[0]: pick(cands_by_name[names[0]], tie=tie)}
     waves = sorted({s[0] for n in names for c in cands_by_name[n] for s in c.shape_us})
     stream = torch.cuda.Stream()
@@ -219,6 +223,8 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
             us = time_group(cts, x, reps, stream)
             nbytes = sum(c.stored_bytes for c, _ in combo)
             results.append((us, nbytes, combo))
+            if points is not None:
+                points.append((us, nbytes, {n: _pick_dict(c, s, us) for n, (c, s) in zip(names, combo)}))
             if log:
                 log(f"  group W={w}: " + ", ".join(f"{n}:m={c.log2_m},tc={c.tile_cols},R={s[1]},S={s[2]},P={s[3]}"
                                                    for n, (c, s) in zip(names, combo)) + f" -> {us:.2f} us")
@@ -228,7 +234,63 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
     t_min = min(r[0] for r in results)
     near = sorted([r for r in results if r[0] <= t_min * (1 + tie)], key=lambda r: (r[1], r[0]))
     us, _, combo = near[0]
-    return {n: dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
-                    streams_per_wave=s[2], row_groups_per_block=s[3], us=round(us, 3),
-                    stored_bytes=c.stored_bytes)
-            for n, (c, s) in zip(names, combo)}
+    return {n: _pick_dict(c, s, us) for n, (c, s) in zip(names, combo)}
+
+
+def _pick_dict(c: Candidate, s, us: float) -> dict:
+    return dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
+                streams_per_wave=s[2], row_groups_per_block=s[3], us=round(us, 3), stored_bytes=c.stored_bytes)
+
+
+# ------------------------------------------------------------------ speed-size trade-off
+# MINE page, Section 4.2: the tuner keeps the speed-size Pareto front of every
+# section's codings, so that the fastest coding under a memory constraint can be
+# chosen later (smaller codings may decode more slowly), and the cross-entropy of a
+# table against the histogram is a lower bound on the coded size.
+
+def pareto_front(points):
+    """The points (us, bytes, payload) that no other point dominates (no slower and no
+    larger, and better in one), sorted by bytes ascending (so us descending).  Of
+    equal points the first is kept."""
+    out = []
+    for p in sorted(points, key=lambda p: (p[1], p[0])):
+        if not out or p[0] < out[-1][0]:
+            out.append(p)
+    return out
+
+
+def tensor_points(cands):
+    """(us, bytes, pick) of every timed (coding, launch shape) of one tensor."""
+    return [(us, c.stored_bytes, _pick_dict(c, s, us)) for c in cands for s, us in c.shape_us.items()]
+
+
+def choose_under_budget(fronts: dict, budget: int):
+    """One point per item (fronts[name] = [(us, bytes, payload)]) minimising the summed
+    time with summed bytes <= budget: the multiple-choice knapsack, solved exactly by
+    merging the items' fronts one at a time and keeping only the Pareto front of the
+    partial sums (a dominated partial choice is never part of an optimum that its
+    dominator cannot match).  Returns (us, bytes, {name: payload}) or None if no
+    choice fits."""
+    partial = [(0.0, 0, {})]
+    for name, pts in fronts.items():
+        merged = [(u + pu, b + pb, {**ch, name: pp}) for u, b, ch in partial for pu, pb, pp in pts
+                  if b + pb <= budget]
+        partial = pareto_front(merged)
+        if not partial:
+            return None
+    return min(partial, key=lambda p: (p[0], p[1]))
+
+
+def size_lower_bound_bytes(tables) -> float:
+    """Cross-entropy bound of a coding's payload words: sum over symbols of
+    count * log2(M / f) bits, from the histogram and frequencies of its tables."""
+    import math
+    total = 0.0
+    M = sum(int(f) for f in tables.freq[0])
+    for t in range(tables.n_tables):
+        m_t = sum(int(f) for f in tables.freq[t]) or M
+        for s in range(256):
+            n = int(tables.count[t][s])
+            if n:
+                total += n * (math.log2(m_t) - math.log2(int(tables.freq[t][s])))
+    return total / 8.0

@@ -88,3 +88,56 @@ def test_device_tuning_picks_a_shape_that_stays_correct():
     wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
     ok, worst = gemv.check(y, wv, gemv.x_values(xh, "f16"))
     assert ok, worst
+
+
+# ------------------------------------------------------------------ speed-size trade-off
+def _dominated(p, q):
+    return q[0] <= p[0] and q[1] <= p[1] and (q[0] < p[0] or q[1] < p[1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pareto_front_is_the_set_of_undominated_points(seed):
+    rng = np.random.default_rng([0, 77, seed])
+    pts = [(float(rng.integers(1, 20)), int(rng.integers(1, 20)), i) for i in range(40)]
+    front = A.pareto_front(pts)
+    undominated = {(u, b) for u, b, _ in pts if not any(_dominated((u, b), (qu, qb)) for qu, qb, _ in pts)}
+    assert {(u, b) for u, b, _ in front} == undominated
+    assert len(front) == len(undominated)                     # one point per (us, bytes)
+    assert all(front[i][1] < front[i + 1][1] and front[i][0] > front[i + 1][0] for i in range(len(front) - 1))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_budget_choice_is_the_exact_knapsack_optimum(seed):
+    import itertools
+    rng = np.random.default_rng([0, 78, seed])
+    fronts = {f"t{i}": [(float(rng.uniform(1, 10)), int(rng.integers(1, 30)), j) for j in range(int(rng.integers(1, 6)))]
+              for i in range(4)}
+    lo = sum(min(b for _, b, _ in pts) for pts in fronts.values())
+    hi = sum(max(b for _, b, _ in pts) for pts in fronts.values())
+    for budget in (lo - 1, lo, (lo + hi) // 2, hi):
+        best = None
+        for combo in itertools.product(*fronts.values()):
+            b = sum(p[1] for p in combo)
+            u = sum(p[0] for p in combo)
+            if b <= budget and (best is None or u < best):
+                best = u
+        got = A.choose_under_budget(fronts, budget)
+        if best is None:
+            assert got is None
+        else:
+            assert got[0] == pytest.approx(best, abs=1e-9) and got[1] <= budget
+            assert sum(fronts[n][[p[2] for p in fronts[n]].index(ch)][1] for n, ch in got[2].items()) == got[1]
+
+
+def test_size_lower_bound_is_the_tables_cross_entropy():
+    from oracle import coding as OC, pipeline as P
+    for case in cases.small_cases()[:3] + [c for c in cases.small_cases() if c.name == "bf16_pairs_m12"]:
+        t = ecw.build_tables(case.lib_coding(), case.logical)
+        lb = A.size_lower_bound_bytes(t)
+        comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+        assert lb == pytest.approx(OC.cross_entropy_total_bits(comp.counts[0], comp.freq[0], case.log2_m) / 8,
+                                   rel=1e-12)
+        # the final states carry the last bits of information: the bound holds for the
+        # words plus the tile metadata
+        tt = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales, t))
+        assert lb <= tt.bytes_words + tt.bytes_tile_meta

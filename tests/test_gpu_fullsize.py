@@ -76,12 +76,15 @@ def test_config2_layer_set_at_the_benchmarked_launches():
             _materialize_equal(ct, t.codes)
 
 
-@pytest.mark.parametrize("name", ["gate", "down"])
-def test_config3_bf16_full(name):
-    print(f"[gpu] config 3 {name}", flush=True)
+# (weights per symbol, log2 M, tile width, waves per block): one exponent per symbol,
+# and exponent pairs in the codings and launch shapes the autotuner picked on MI355X
+@pytest.mark.parametrize("name,k,m,tc,W", [("gate", 1, 12, 256, None), ("down", 1, 12, 256, None),
+                                           ("gate", 2, 11, 128, 4), ("down", 2, 12, 128, 16)])
+def test_config3_bf16_full(name, k, m, tc, W):
+    print(f"[gpu] config 3 {name} k={k} m={m} tc={tc} W={W}", flush=True)
     t = E.config3_tensor(name)
-    c = ecw.Coding(ecw.BF16_EXP, *t.bits.shape, 1, 0, 12, 256)
-    ct = ecw.CompressedTensor(ecw.encode(c, t.bits))
+    c = ecw.Coding(ecw.BF16_EXP, *t.bits.shape, k, 0, m, tc)
+    ct = ecw.CompressedTensor(ecw.encode(c, t.bits), waves_per_block=W, tiles_per_wave=1 if W else None)
     x = torch.from_numpy(t.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
     y = ct.gemv(x).cpu().numpy()
     rows = _rows(t.bits.shape[0])
