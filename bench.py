@@ -387,6 +387,9 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
     if "p" in which:
         res["budget"] = budget_points(steps, cold_bytes)
 
+    if "d" in which:
+        res["dequant"] = dequant_gemm(steps, cold_bytes)
+
     if "4" in which:
         names = ["q", "k", "v", "o", "gate", "up", "down"] + (["lm_head"] if lm_head else [])
         groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
@@ -519,6 +522,82 @@ def budget_points(steps: int, cold_bytes: float):
                         "Pareto fronts)", "front_points": {ln: len(p) for ln, p in fr.items()}, "points": out}
 
 
+def dequant_gemm(steps: int, cold_bytes: float):
+    """Products with more than four activation rows: the dequantising decode writes the
+    dense fp16 / bf16 weights (HBM: the stored bytes read, 2 bytes per weight
+    written), then the library GEMM (hipBLASLt through torch.mm, fp32 output) reads
+    them.  Timed cold (copies rotated over >= cold_bytes), per call, for the INT4 gate
+    tensor in its tune-file coding and the BF16 gate tensor as exponent pairs; the
+    dense GEMM alone on resident weights is timed beside it.  Sampled rows of the
+    dense weights are checked bit for bit against float64 values rounded in numpy /
+    torch."""
+    import torch
+    import ecw_inputs as E
+    import entropy_coded_weight_amd as ecw
+    coding, _ = load_coding(TUNE_FILE)
+    out = {}
+    t_int = E.config2_tensor("gate")
+    t_bf = E.config3_tensor("gate")
+    kk, m, tc, *_ = coding["gate"]
+    specs = [("int4_gate", ecw.Coding(ecw.INT_CODES, *t_int.codes.shape, kk, 4, m, tc), t_int.codes, t_int.scales,
+              torch.float16),
+             ("bf16_gate", ecw.Coding(ecw.BF16_EXP, *t_bf.bits.shape, 2, 0, 11, 128), t_bf.bits, None, torch.bfloat16)]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                fn(r)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (3 * reps)
+
+    for label, c, w, sc, tdt in specs:
+        blob = ecw.encode(c, w, sc)
+        t = ecw.prepare(blob)
+        stored = t.bytes_words + t.bytes_raw + t.bytes_tile_meta + t.bytes_tables + t.bytes_scales
+        n, k = w.shape
+        copies = max(2, int(np.ceil(cold_bytes / (stored + 2 * n * k))))
+        cts = [ecw.CompressedTensor(blob) for _ in range(copies)]
+        dense = [torch.empty((n, k), dtype=tdt, device="cuda") for _ in range(copies)]
+        us_deq = timed(lambda r: cts[r % copies].dequantize(tdt, out=dense[r % copies]), max(copies, steps // 4))
+        rows = _rows(n)
+        got = dense[0][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        if label.startswith("int4"):
+            want = (w[rows].astype(np.float64) * sc[rows].astype(np.float64)[:, None]).astype(np.float16) \
+                .view(np.uint16)
+        else:
+            want = w[rows]
+        exact = bool(np.array_equal(got, want))
+        d = {"dequant_us": round(us_deq, 3), "stored_bytes": int(stored), "dense_bytes": int(2 * n * k),
+             "dequant_gbps": round((stored + 2 * n * k) / (us_deq * 1e-6) / 1e9, 1),
+             "dequant_hbm_frac": round((stored + 2 * n * k) / (us_deq * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+             "dense_bits_exact_on_sampled_rows": exact, "gemm": {}}
+        for batch in (16, 256):
+            x = torch.randn((batch, k), dtype=tdt, device="cuda")
+            us_mm = timed(lambda r: torch.mm(x, dense[r % copies].t(), out_dtype=torch.float32),
+                          max(copies, steps // 4))
+            us_all = timed(lambda r: cts[r % copies].gemm(x, w_buf=dense[r % copies]), max(copies, steps // 4))
+            d["gemm"][f"batch{batch}"] = {"dequant_plus_gemm_us": round(us_all, 3), "gemm_only_us": round(us_mm, 3)}
+        log(f"dequant {label}: {us_deq:.2f} us ({d['dequant_gbps']:.0f} GB/s, {100 * d['dequant_hbm_frac']:.1f}% "
+            f"of HBM), exact={exact}; " + ", ".join(f"{b}: {v['dequant_plus_gemm_us']:.1f} us (GEMM alone "
+                                                    f"{v['gemm_only_us']:.1f})" for b, v in d["gemm"].items()))
+        out[label] = d
+        del cts, dense
+    out["workload"] = ("gate 14336x4096: INT4 Laplacian codes (tune-file coding) to fp16, BF16 exponent pairs "
+                       "(M = 2^11, 128-wide tiles) to bf16; GEMM batch 16 and 256, fp32 output")
+    return out
+
+
 def summarize_rocprof(directory: str):
     """Print per-(kernel, grid size) averages from rocprofv3 CSV output under
     `directory`: kernel durations from *_kernel_trace.csv and counter values from
@@ -585,11 +664,12 @@ def main():
     ap.add_argument("--tune-file", default=TUNE_FILE)
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print per-launch averages of rocprofv3 CSV output under DIR and exit")
-    ap.add_argument("--configs", default="1,3,4,5,p",
+    ap.add_argument("--configs", default="1,3,4,5,p,d",
                     help="secondary workloads measured after the layer set (1: Gaussian codes, "
                          "3: BF16 exponent coding, 4: FP8 layer at batch 1 and 4, 5: E8 lattice "
                          "fields, INT8 and FP8 reconstruction, p: the layer set under byte budgets "
-                         "from the tune file's Pareto fronts); '' for none")
+                         "from the tune file's Pareto fronts, d: dequantising decode + GEMM for "
+                         "batches above 4); '' for none")
     ap.add_argument("--lm-head", action="store_true",
                     help="include the 128256x4096 LM head in workload 4 (its generation takes minutes)")
     ap.add_argument("--tensors", default=",".join(ORDER),
@@ -787,6 +867,19 @@ def main():
         torch.cuda.synchronize()
     if args.configs and args.tensors == ",".join(["q", "k", "v", "o", "gate", "up", "down"]):
         out["configs"] = secondary_configs(args.configs, args.steps, args.cold_bytes, args.lm_head)
+        budget = out["configs"].pop("budget", None)
+        deq = out["configs"].pop("dequant", None)
+        if deq:
+            out["dequant"] = deq
+            if not all(v["dense_bits_exact_on_sampled_rows"] for k, v in deq.items() if k != "workload"):
+                log("PARITY FAILURE in the dequantising decode")
+                sys.exit(1)
+        if budget:
+            out["budget"] = budget
+            for pt in budget["points"]:
+                if not pt["parity_worst_err_over_bound"] <= 1.0:
+                    log(f"PARITY FAILURE in budget point {pt['label']}")
+                    sys.exit(1)
         for k, v in out["configs"].items():
             log(f"config {k}: {v['us']:.2f} us, {v['gbps_compressed']:.0f} GB/s ({100 * v['hbm_frac']:.1f}% of HBM), "
                 f"{v['stored_bits_per_weight']:.3f} bits/weight, parity {v['parity_worst_err_over_bound']:.3g}")

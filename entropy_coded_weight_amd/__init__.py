@@ -70,7 +70,7 @@ class Tensor(ctypes.Structure):
 
 EXPORTS = ["enc_build_tables", "enc_encode", "dec_prepare", "dec_gemv_workspace_size",
            "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize",
-           "ecw_last_error", "ecw_abi_version"]
+           "dec_dequantize", "ecw_last_error", "ecw_abi_version"]
 
 _lib = None
 
@@ -100,6 +100,7 @@ def lib():
     L.dec_gemv_workspace_size.argtypes = [P(Tensor), i32, P(sz)]
     L.dec_gemv.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz]
     L.dec_materialize.argtypes = [vp, P(Tensor), vp, vp, vp]
+    L.dec_dequantize.argtypes = [vp, P(Tensor), vp, i32]
     L.dec_gemv_group_workspace_size.argtypes = [P(P(Tensor)), i32, i32, P(sz)]
     L.dec_gemv_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz]
     L.dec_tune_launch.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz, P(u32), i32, i32,
@@ -109,7 +110,7 @@ def lib():
     L.ecw_probe_stream_read.argtypes = [vp, vp, sz, vp, u32]
     L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
     for f in ("enc_build_tables", "enc_encode", "enc_e8_nearest", "dec_prepare", "dec_gemv_workspace_size",
-              "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize",
+              "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize", "dec_dequantize",
               "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []
@@ -267,6 +268,14 @@ def materialize_raw(t: Tensor, symbols, w_out, status, stream=None):
                                  status.data_ptr() if status is not None else None), "dec_materialize")
 
 
+def dequantize_raw(t: Tensor, w_out: torch.Tensor, stream=None):
+    """dec_dequantize into a caller-provided device tensor [rows, cols] of fp16/bf16."""
+    dt = DT_F16 if w_out.dtype == torch.float16 else DT_BF16 if w_out.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise ValueError("w_out must be float16 or bfloat16")
+    _check(lib().dec_dequantize(_stream(stream), ctypes.byref(t), w_out.data_ptr(), dt), "dec_dequantize")
+
+
 # ------------------------------------------------------------------ roofline probes
 def probe_stream_read(buf: torch.Tensor, blocks: int = 2048, reps: int = 5) -> float:
     """Achievable streaming-read GB/s over the device buffer `buf` (median of reps)."""
@@ -365,6 +374,26 @@ class CompressedTensor:
             y = torch.empty((x.shape[0], self.rows), dtype=torch.float32, device=x.device)
         gemv_raw(self.t, x, y, self.workspace(x.shape[0]), stream)
         return y
+
+    def dequantize(self, dtype=torch.float16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """The real weight values as a dense [rows, cols] fp16/bf16 matrix (dec_dequantize)."""
+        if out is None:
+            out = torch.empty((self.rows, self.t.coding.cols), dtype=dtype, device=self.dev.device)
+        dequantize_raw(self.t, out, stream)
+        return out
+
+    def gemm(self, x: torch.Tensor, w_buf: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """y = x W^T in fp32 for any batch: up to 4 rows of x the fused decode-GEMV;
+        more rows decode W once into a dense matrix (w_buf, if given, is reused) and
+        multiply with the library GEMM (hipBLASLt through torch), fp32 output."""
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if x.shape[0] <= 4:
+            return self.gemv(x, stream=stream)
+        w = self.dequantize(x.dtype, w_buf, stream)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            return torch.mm(x, w.t(), out_dtype=torch.float32)
 
     def materialize(self, want_symbols=True, want_weights=True, stream=None):
         c = self.t.coding

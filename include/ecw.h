@@ -103,8 +103,8 @@ typedef struct {
   uint32_t streams_per_wave;         /* 1, or 2: each wave decodes the tiles of two
                                         adjacent row groups at the same slices in
                                         lockstep, sharing the activation reads
-                                        (fused GEMV of INT, BF16 and FP8 payloads;
-                                        E8 and the decode-only hook use 1) */
+                                        (fused GEMV of INT and FP8 payloads; BF16,
+                                        E8 and the decode-only calls use 1) */
   uint32_t row_groups_per_block;     /* >= 1: a block decodes this many row-group
                                         units (streams_per_wave adjacent row groups
                                         each) one after the other, staging the decode
@@ -247,6 +247,19 @@ ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t ent
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, uint16_t* symbols,
                            void* w_out, uint32_t* tile_status);
+
+/* Dequantising decode for products with more than four activation rows (prefill):
+ * the weights are decoded once into a dense matrix that a library GEMM then reads
+ * (MINE page, Section 4.2: the dequant kernel that materialises a layer; EntroPack
+ * page, Section 3.7).  Writes the real weight values W_val [rows][cols], row-major,
+ * rounded to nearest even into out_dtype (ECW_DT_F16 or ECW_DT_BF16): INT code *
+ * row scale, BF16 the bf16 value (escaped weights included), FP8 the E4M3 value *
+ * row scale; every such value is exact in fp32 before the rounding.
+ *   w_out: device, rows x cols x 2 bytes, 16-byte aligned (caller-owned).
+ * Asynchronous on `stream`, stores are row-contiguous 64-byte segments.
+ * Errors: INVALID_ARG (bad tensor, dtype or buffer), UNSUPPORTED (E8 fields, cols
+ * not a multiple of 16, table too large for LDS), HIP. */
+ecw_status dec_dequantize(ecw_stream stream, const ecw_tensor* t, void* w_out, int out_dtype);
 
 const char* ecw_last_error(void);
 uint32_t ecw_abi_version(void);

@@ -284,6 +284,24 @@ def weight_values(c: Coding, logical: np.ndarray, scales=None) -> np.ndarray:
     raise ValueError("payload")
 
 
+def dequantized(c: Coding, logical: np.ndarray, scales=None, dtype: str = "f16") -> np.ndarray:
+    """The real weight values rounded to nearest even into fp16 or bf16, as uint16
+    bits [N, K]: what a dequantising decode hands to a dense GEMM (MINE page, Section
+    4.2, the dequant kernel).  Every value of these payloads is exact in fp32 (a
+    code or E4M3 significand of at most 4 bits times an 11-bit fp16 scale, or a bf16
+    value), so rounding once from float64 and once from float32 agree."""
+    import torch
+    wv = weight_values(c, logical, scales)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return wv.astype(np.float16).view(np.uint16)
+    f32 = wv.astype(np.float32)
+    fin = np.isfinite(wv)
+    if not np.array_equal(f32.astype(np.float64)[fin], wv[fin]):
+        raise ValueError("weight value not exact in fp32")
+    return torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def reconstructed_dtype_tensor(c: Coding, logical: np.ndarray) -> np.ndarray:
     """The weights in their reconstruction dtype, bit patterns (what a decoder emits)."""
     if c.payload == E8_LATTICE:

@@ -458,3 +458,19 @@ def test_bf16_pairs_corrupt_correction_stream_is_detected():
     bad = P.Components(**{**comp.__dict__, "words": comp.words.copy()})
     bad.words[-1] = (bad.words[-1] & 0xF800) | 64   # column outside the slice
     assert not P.decode_symbols(bad)[1].any()
+
+
+def test_dequantized_rounds_to_nearest_even():
+    # hand-rounded values.  fp16, scale 1 + 2^-10: 3 * scale = 3 + 1.5 * 2^-9 lies
+    # half-way between 3 + 2^-9 (odd significand) and 3 + 2^-8 (even): 3 + 2^-8 =
+    # 0x4202.  -7 * scale = -(7 + 1.75 * 2^-8) rounds to -(7 + 2^-7) = 0xC702.
+    c = P.Coding(P.INT_CODES, 1, 2, k=1, code_bits=4)
+    sc = np.array([1.0 + 2.0 ** -10], np.float16)
+    assert list(P.dequantized(c, np.array([[3, -7]], np.int8), sc, "f16").ravel()) == [0x4202, 0xC702]
+    # bf16, scale 1 + 2^-8: 1 * scale ties between 1 and 1 + 2^-7 -> 1.0 = 0x3F80;
+    # 3 * scale = 3 + 0.75 * 2^-6 -> 3 + 2^-6 = 0x4041
+    sc = np.array([1.0 + 2.0 ** -8], np.float16)
+    assert list(P.dequantized(c, np.array([[1, 3]], np.int8), sc, "bf16").ravel()) == [0x3F80, 0x4041]
+    # bf16 weights pass through unchanged
+    b = P.dequantized(P.Coding(P.BF16_EXP, 1, 2), np.array([[0x3F81, 0xC2F7]], np.uint16), None, "bf16")
+    assert list(b.ravel()) == [0x3F81, 0xC2F7]
