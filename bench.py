@@ -852,6 +852,18 @@ def main():
     achievable = ecw.probe_stream_read(big)
     del big
     lut_rate = {f"m{m}_{eb}B": round(ecw.probe_lds_lookup(m, eb) / 1e9, 1) for m in (11, 12) for eb in (4, 8)}
+    # the decode loop is bound by instruction issue, not HBM: the same launch against
+    # the chip's VALU issue rate (256 CUs x 4 SIMDs, one wave64 VALU instruction per
+    # SIMD every 4 clocks at 2.4 GHz), from the VALU instruction count rocprofv3
+    # measured for this kernel and these codings
+    if rec and rec.get("valu_instructions") and rec.get("launch") == dom:
+        valu = float(rec["valu_instructions"])
+        peak_g = 256 * 4 * 2.4e9 / 4 / 1e9
+        out["issue_roofline"] = {"bound": "alu", "kernel": dom_label,
+                                 "achieved": round(valu / (avg_us[dom] * 1e-6) / 1e9, 1), "peak": peak_g,
+                                 "unit": "G wave64 VALU instructions/s",
+                                 "frac": round(valu / (avg_us[dom] * 1e-6) / 1e9 / peak_g, 4),
+                                 "valu_instructions_per_launch": int(valu)}
     out["probes"] = {"hbm_read_gbs": round(achievable, 1),
                      "hbm_read_frac_of_peak": round(achievable / HBM_PEAK_GBS, 4),
                      "dominant_launch_frac_of_achievable": round(achieved / achievable, 4),
