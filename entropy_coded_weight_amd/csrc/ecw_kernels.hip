@@ -889,10 +889,43 @@ __device__ __forceinline__ int e8_decode(uint32_t& x, uint32_t addr, uint32_t m)
   return (int)e >> 24;
 }
 
-template <int B, bool MAT, bool RAGGED, bool F8>
+// Dequantising decode of lattice fields (DQ = 1: fp16, 2: bf16; decode-only): each
+// weight is v * row scale (INT8 route: 2v / 2) or e4m3(v) * row scale (FP8 route),
+// exact in fp32 and rounded once.  Segments of four blocks (32 weights, 64 B) are
+// stored row-contiguous through the wave's LDS tile, a quarter of the rows at a time
+// (16 rows x kStagePitch; the 17 tables leave little LDS); a tile whose last slice
+// ends on a partial segment stores its remaining blocks' chunks only.
+template <int DQ>
+__device__ __forceinline__ void e8_store_segment(const TArgs& a, const uint32_t* pk, uint32_t nck, uint32_t stage,
+                                                 uint32_t rg, uint64_t c0, uint32_t lane) {
+  uint16_t* out = static_cast<uint16_t*>(a.deq_out);
+  const uint32_t rr = lane >> 2, part = lane & 3;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    if ((lane >> 4) == (uint32_t)qq) {
+      const uint32_t sb = stage + (lane & 15) * kStagePitch;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((uint32_t)c < nck)
+          lds_store4(sb + 16 * c, make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]));
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t orow = rg * 64 + (uint32_t)qq * 16 + rr;
+    if (part < nck && orow < a.rows) {
+      const uint4 val = lds_load4(stage + rr * kStagePitch + part * 16);
+      __builtin_nontemporal_store(ecw_u32x4{val.x, val.y, val.z, val.w},
+                                  reinterpret_cast<ecw_u32x4*>(out + (uint64_t)orow * a.cols + c0 + part * 8));
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int B, bool MAT, bool RAGGED, bool F8, int DQ = 0>
 __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h, uint32_t lut, uint32_t xs,
                                              uint32_t ring, uint32_t f8tab, uint32_t rg, uint32_t t0, uint32_t t1,
-                                             uint32_t c_lo, uint32_t lane, bool active, float* acc) {
+                                             uint32_t c_lo, uint32_t lane, bool active, float* acc,
+                                             uint32_t stage = 0) {
+  static_assert(DQ == 0 || MAT, "dequantising decode is decode-only");
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
   const uint32_t tbytes = 4u << m;                 // bytes per compact table
   const uint32_t row = rg * 64 + lane;
@@ -906,6 +939,9 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
   uint2 pre = h.pre;
   uint32_t haveb = 4 * kChunk, nc = 2;
   uint32_t st = h.st;
+  float scale = 0.f;                      // dequantising decode: the row scale
+  if constexpr (DQ != 0) scale = active ? (float)__builtin_bit_cast(_Float16, a.scales[row]) : 0.f;
+  uint32_t pk[DQ != 0 ? 16 : 1];          // dequantising decode: 4 blocks as packed 16-bit values
 
   for (uint32_t t = t0; t < t1; ++t) {
     uint32_t x = st;
@@ -913,7 +949,8 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
     const uint32_t sl = t - sl0;
     const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
     const uint32_t col0 = sl * a.tile_cols - c_lo;
-    for (uint32_t blk = 0; blk < S / 9; ++blk) {
+    const uint32_t nblk = S / 9;
+    for (uint32_t blk = 0; blk < nblk; ++blk) {
       const uint32_t step0 = blk * 9;
       // activations of the block's 8 columns: fp32 [col][B]
       float xv[MAT ? 1 : 8 * B];
@@ -950,7 +987,27 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
           z = 2 * v + (zsum & 1);                                         // z8 from m and parity
         }
         const int w2 = 2 * z + c;                                         // doubled coordinate
-        if constexpr (!MAT) {
+        if constexpr (DQ != 0) {
+          float val;
+          if constexpr (F8) {
+            const uint32_t hh = *lds_ptr<const uint32_t>(f8tab + ((uint32_t)(w2 + 128) & 255u) * 4) >> 16;
+            val = exact_product((float)__builtin_bit_cast(_Float16, (uint16_t)hh), scale);
+          } else {
+            val = exact_product((float)w2 * 0.5f, scale);
+          }
+          const uint32_t v16 = to16<DQ == 2>(val);
+          // weight j - 1 of block blk % 4 in the segment: word (blk % 4) * 4 + (j - 1) / 2
+          // (blk is a runtime value: select the word among the four candidates)
+          const uint32_t bq = blk & 3u;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int wi = w * 4 + (j - 1) / 2;
+            if (bq == (uint32_t)w) {
+              if ((j - 1) & 1) pk[wi] |= v16 << 16;
+              else pk[wi] = v16;
+            }
+          }
+        } else if constexpr (!MAT) {
           if constexpr (F8) {
             const uint32_t h = *lds_ptr<const uint32_t>(f8tab + ((uint32_t)(w2 + 128) & 255u) * 4);
 #pragma unroll
@@ -978,6 +1035,14 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
         }
         renorm_step<RAGGED>(x, rposb, ring, active);
       }
+      if constexpr (DQ != 0) {
+        if ((blk & 3u) == 3u)
+          e8_store_segment<DQ>(a, pk, 4, stage, rg, (uint64_t)sl * a.tile_cols + 8ull * (blk - 3), lane);
+      }
+    }
+    if constexpr (DQ != 0) {
+      if (nblk & 3u)                      // the last slice's partial segment
+        e8_store_segment<DQ>(a, pk, nblk & 3u, stage, rg, (uint64_t)sl * a.tile_cols + 8ull * (nblk & ~3u), lane);
     }
     if constexpr (MAT) {
       const bool ok_lane = !active || x == kStateL;
@@ -1037,10 +1102,11 @@ __device__ __forceinline__ uint32_t small_int_bits(int q) {
 // 16-wave blocks per CU) and hide the LDS latency of the decode chain.
 template <int B>
 constexpr int kWavesPerEU = B == 1 ? 8 : 4;
-// Decode-only kernels of BF16 payloads hold the raw-byte groups and a 32-weight
-// output segment beside the decode state: they get 128 VGPRs instead of spilling.
+// Decode-only kernels of BF16 payloads (raw-byte groups and a 32-weight output
+// segment beside the decode state) and the dequantising decode of lattice fields get
+// 128 VGPRs instead of spilling.
 template <int PAY, int B, bool MAT, bool XBF>
-constexpr int kKernelWaves = (MAT && PAY == 2) ? 4 : kWavesPerEU<B>;
+constexpr int kKernelWaves = (MAT && (PAY == 2 || (PAY == 4 && XBF))) ? 4 : kWavesPerEU<B>;
 
 // Decode-only kernels (MAT) do not multiply activations, so XBF selects their output
 // instead: false = the test hook's symbols / logical weights / tile status, true =
@@ -1216,7 +1282,15 @@ k_decode(const KArgs ka) {
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[0][b] = acc[1][b] = 0.f;
   if (w_sl0 < w_sl1) {
-    if constexpr (E8) {
+    if constexpr (E8 && DEQ) {
+      // quarter-height LDS tile per wave after the rings (the 17 tables leave little LDS)
+      const uint32_t stage = __builtin_amdgcn_readfirstlane(rings + W * (2 * kRingStride) + wid * 16 * kStagePitch);
+      const uint32_t ta = tb + w_sl0, tz = tb + w_sl1;
+      if (a.deq_bf16)
+        wave_body_e8<B, MAT, true, E8F8, 2>(a, hA, lut, xs, ring, 0, rg, ta, tz, c_lo, lane, active, acc[0], stage);
+      else
+        wave_body_e8<B, MAT, true, E8F8, 1>(a, hA, lut, xs, ring, 0, rg, ta, tz, c_lo, lane, active, acc[0], stage);
+    } else if constexpr (E8) {
       if (ragged)
         wave_body_e8<B, MAT, true, E8F8>(a, hA, lut, xs, ring, 0, rg, tb + w_sl0, tb + w_sl1, c_lo, lane, active,
                                          acc[0]);
@@ -1370,10 +1444,8 @@ static KernelFn pick_kernel(const ecw_coding& c) {
       return c.weights_per_symbol == 2 ? k_decode<2, 0, 2, B, MAT, XBF> : k_decode<2, 0, 1, B, MAT, XBF>;
     case ECW_P_FP8_E4M3: return k_decode<3, 0, 1, B, MAT, MAT && XBF>;
     case ECW_P_E8_LATTICE:
-      if constexpr (MAT && XBF) return nullptr;     // no dequantising decode of lattice fields
-      else
-        return c.recon_dtype == ECW_DT_FP8_E4M3 ? k_decode<4, 1, 8, B, MAT, false>
-                                                : k_decode<4, 0, 8, B, MAT, false>;
+      return c.recon_dtype == ECW_DT_FP8_E4M3 ? k_decode<4, 1, 8, B, MAT, MAT && XBF>
+                                              : k_decode<4, 0, 8, B, MAT, MAT && XBF>;
   }
   return nullptr;
 }
@@ -1413,7 +1485,8 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
   const bool two = !mat && two_streams(t);
   (void)R;
-  const uint64_t stage = (mat && !e8) ? (uint64_t)W * 64 * kStagePitch : 0;   // dequantising decode
+  // dequantising decode: a 64-row tile per wave (lattice fields: 16 rows)
+  const uint64_t stage = mat ? (uint64_t)W * (e8 ? 16 : 64) * kStagePitch : 0;
   return pair + lut * 8 + xs + (uint64_t)W * (two ? 2 : 1) * kRingStride * 2 + stage;
 }
 
@@ -1749,9 +1822,7 @@ extern "C" ecw_status dec_dequantize(ecw_stream stream, const ecw_tensor* t, voi
   if (st != ECW_OK) return st;
   if (out_dtype != ECW_DT_F16 && out_dtype != ECW_DT_BF16)
     return fail(ECW_E_INVALID_ARG, "output dtype must be F16 or BF16");
-  if (t->coding.payload == ECW_P_E8_LATTICE)
-    return fail(ECW_E_UNSUPPORTED, "dequantising decode of E8 fields is not built");
-  if (t->coding.cols % 16) return fail(ECW_E_UNSUPPORTED, "cols must be a multiple of 16");
+  if (t->coding.cols % 8) return fail(ECW_E_UNSUPPORTED, "cols must be a multiple of 8");
   if (t->coding.rows && t->coding.cols && (!w_out || reinterpret_cast<uintptr_t>(w_out) % 16))
     return fail(ECW_E_INVALID_ARG, "w_out must be a 16-byte aligned device pointer");
   if (t->n_tiles == 0) return ECW_OK;

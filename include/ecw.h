@@ -254,11 +254,12 @@ ecw_status dec_materialize(ecw_stream stream, const ecw_tensor* t, uint16_t* sym
  * page, Section 3.7).  Writes the real weight values W_val [rows][cols], row-major,
  * rounded to nearest even into out_dtype (ECW_DT_F16 or ECW_DT_BF16): INT code *
  * row scale, BF16 the bf16 value (escaped weights included), FP8 the E4M3 value *
- * row scale; every such value is exact in fp32 before the rounding.
+ * row scale, E8 v * row scale (INT8 route) or e4m3(v) * row scale (FP8 route); every
+ * such value is exact in fp32 before the rounding.
  *   w_out: device, rows x cols x 2 bytes, 16-byte aligned (caller-owned).
  * Asynchronous on `stream`, stores are row-contiguous 64-byte segments.
- * Errors: INVALID_ARG (bad tensor, dtype or buffer), UNSUPPORTED (E8 fields, cols
- * not a multiple of 16, table too large for LDS), HIP. */
+ * Errors: INVALID_ARG (bad tensor, dtype or buffer), UNSUPPORTED (cols not a
+ * multiple of 8, tables too large for LDS), HIP. */
 ecw_status dec_dequantize(ecw_stream stream, const ecw_tensor* t, void* w_out, int out_dtype);
 
 const char* ecw_last_error(void);
