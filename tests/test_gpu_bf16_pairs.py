@@ -115,3 +115,32 @@ def test_bf16_pairs_grouped_launch(batch):
         wv = P.weight_values(case.oracle_coding(), case.logical)
         ok, worst = gemv.check(y.cpu().numpy(), wv, xv)
         assert ok, worst
+
+
+def test_bf16_pairs_damaged_correction_stream_is_reported():
+    # A cleared last-record flag makes the lane read on past its records; the rounds
+    # stop after as many rounds as the slice has columns, every read stays inside the
+    # wave's ring and every store inside the lane's row, and the tile reports that it
+    # did not end on its word count.  The validator cannot see this (it does not
+    # decode), so the decode must end on its own.
+    bits = np.full((64, 64), 0x3F80, np.uint16)
+    for i, e in enumerate(range(100, 116)):
+        bits[i, 3] = e << 7                     # 16 rare exponents: one is escaped
+    c = ecw.Coding(ecw.BF16_EXP, 64, 64, 2, 0, 10, 64)
+    blob = ecw.encode(c, bits)
+    from tests import blobfmt
+    bl = blobfmt.parse(blob)
+    off_w, _ = bl.sec["words"]
+    n_words = int(blobfmt.offsets(bl)[-1])
+    bad = blob.copy()
+    hi = bad[off_w + 2 * (n_words - 1): off_w + 2 * n_words].view(np.uint16)
+    assert hi[0] & 0x0800                       # the last record's flag
+    hi[0] &= ~np.uint16(0x0800)
+    ct = ecw.CompressedTensor(bad)
+    _, w, st = ct.materialize()
+    torch.cuda.synchronize()
+    assert int(st.cpu().numpy()[0]) != 0
+    ok = ecw.CompressedTensor(blob)
+    _, w0, st0 = ok.materialize()
+    torch.cuda.synchronize()
+    assert int(st0.abs().sum()) == 0 and np.array_equal(w0.cpu().numpy().view(np.uint16), bits)
