@@ -377,8 +377,11 @@ class CompressedTensor:
 
     def dequantize(self, dtype=torch.float16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         """The real weight values as a dense [rows, cols] fp16/bf16 matrix (dec_dequantize)."""
+        shape = (self.rows, self.t.coding.cols)
         if out is None:
-            out = torch.empty((self.rows, self.t.coding.cols), dtype=dtype, device=self.dev.device)
+            out = torch.empty(shape, dtype=dtype, device=self.dev.device)
+        elif tuple(out.shape) != shape or not out.is_contiguous() or out.device != self.dev.device:
+            raise ValueError(f"out must be a contiguous {shape} tensor on {self.dev.device}")
         dequantize_raw(self.t, out, stream)
         return out
 
@@ -388,6 +391,8 @@ class CompressedTensor:
         multiply with the library GEMM (hipBLASLt through torch), fp32 output."""
         if x.dim() == 1:
             x = x.unsqueeze(0)
+        if x.shape[-1] != self.t.coding.cols:
+            raise ValueError(f"x has {x.shape[-1]} columns, the tensor {self.t.coding.cols}")
         if x.shape[0] <= 4:
             return self.gemv(x, stream=stream)
         w = self.dequantize(x.dtype, w_buf, stream)
