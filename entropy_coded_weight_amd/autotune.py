@@ -88,6 +88,10 @@ def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks
     """Search the codings of one logical tensor `w` (host array as enc_encode takes it)
     with activations `x` (device [batch, cols]).  Returns the list of Candidates."""
     rows, cols = w.shape
+    # two row streams per wave exist for INT codes and FP8 only: elsewhere a shape
+    # asking for two runs as one and would only be timed twice
+    if payload not in (INT_CODES, FP8_E4M3):
+        shapes = tuple(s for s in shapes if s[2] == 1)
     stream = torch.cuda.Stream()
     out = []
     for k, m, tc in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols):
