@@ -123,3 +123,39 @@ def test_config5_e8_full(recon):
     want = P.reconstructed_dtype_tensor(P.Coding(P.E8_LATTICE, n, K, k=8, log2_m=11, tile_cols=128,
                                                  recon_dtype=recon), v2)
     _materialize_equal(ct, want)
+
+
+@pytest.mark.parametrize("which", ["int4_gate_f16", "bf16_gate_pairs_bf16"])
+def test_dequantize_full_size_sampled_rows(which):
+    # the dense matrix the GEMM path reads, at full size in the benchmarked codings:
+    # 256 sampled rows bit for bit against the oracle's rounding; the GEMM at 16
+    # activation rows within the bound of the same dense weights
+    print(f"[gpu] dequantize full size {which}", flush=True)
+    if which.startswith("int4"):
+        t = E.config2_tensor("gate")
+        p = json.load(open(os.path.join(ROOT, "entropy_coded_weight_amd", "tuned",
+                                        "llama8b_int4_laplace_batch1.json")))["picks"]["gate"]
+        c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"])
+        logical, scales, tdt, dname = t.codes, t.scales, torch.float16, "f16"
+        oc = P.Coding(P.INT_CODES, *t.codes.shape, k=p["k"], code_bits=4, log2_m=p["log2_m"],
+                      tile_cols=p["tile_cols"])
+    else:
+        t = E.config3_tensor("gate")
+        c = ecw.Coding(ecw.BF16_EXP, *t.bits.shape, 2, 0, 11, 128)
+        logical, scales, tdt, dname = t.bits, None, torch.bfloat16, "bf16"
+        oc = P.Coding(P.BF16_EXP, *t.bits.shape, k=2, log2_m=11, tile_cols=128)
+    ct = ecw.CompressedTensor(ecw.encode(c, logical, scales))
+    w = ct.dequantize(tdt)
+    torch.cuda.synchronize()
+    rows = _rows(logical.shape[0])
+    sc = scales[rows] if scales is not None else None
+    oc_rows = P.Coding(oc.payload, len(rows), oc.cols, k=oc.k, code_bits=oc.code_bits, log2_m=oc.log2_m,
+                       tile_cols=oc.tile_cols)
+    want = P.dequantized(oc_rows, logical[rows], sc, dname)
+    got = w[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    x = torch.randn((16, logical.shape[1]), dtype=tdt, device="cuda")
+    y = ct.gemm(x, w_buf=w)
+    torch.cuda.synchronize()
+    w16 = torch.from_numpy(want.view(np.int16)).view(tdt).double().numpy()
+    _check_sampled(y.cpu().numpy(), w16, x.double().cpu().numpy(), rows)
