@@ -52,7 +52,7 @@ ecw_status check_coding(const ecw_coding* c) {
       if (!(k == 1 || k == 2 || k == 4) || b * k > 8)
         return fail(ECW_E_UNSUPPORTED, "weights_per_symbol must be 1, 2 or 4 with code_bits*k <= 8");
       if ((1u << (b * k)) > (1u << c->log2_m))
-        return fail(ECW_E_UNSUPPORTED, "alphabet^k exceeds M (escapes not built)");
+        return fail(ECW_E_UNSUPPORTED, "alphabet^k exceeds M (integer codes have no escapes)");
       if (c->cols % (16 * k)) return fail(ECW_E_UNSUPPORTED, "cols must be a multiple of 16*k");
       if (c->recon_dtype != 0) return fail(ECW_E_INVALID_ARG, "recon_dtype is E8-only");
       break;
@@ -427,7 +427,7 @@ extern "C" ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_t
       present += out->count[t][s] > 0;
     }
     if (present > (1u << c->log2_m))
-      return fail(ECW_E_UNSUPPORTED, "more distinct symbols than table slots (escapes not built)");
+      return fail(ECW_E_UNSUPPORTED, "more distinct symbols than table slots (only BF16 exponent pairs escape)");
     normalise(out->count[t], c->log2_m, out->freq[t]);
   }
   return ECW_OK;
