@@ -18,8 +18,9 @@ What it computes, and the passage each part follows:
                   Algorithm 1's bit join; MINE page Section 4.1), FP8 E4M3 bytes.
 * ``corrections`` -- the sparse correction stream of escaped weights that lets
                   BF16 exponents be coded in pairs over a table of the 16 most
-                  frequent exponents (MINE page, Section 4.1 "Escapes", Section 4.2
-                  "Tuning t").
+                  frequent exponents, and 4-bit codes in quads over a table of the
+                  most frequent 4-tuples (MINE page, Section 4.1 "Escapes",
+                  Section 4.2 "Tuning t").
 * ``e8``       -- E8 lattice fields with coset-conditioned tables and parity
                   reduction (EntroPack page, Sections 3.2, 3.3 and A.3).
 * ``gemv``     -- y = W x in float64 and the per-row error bound.

@@ -8,7 +8,8 @@ page Section 3.7; DFloat11 page Algorithm 1's bit join; MINE page Section 4.1).
 
 Payload kinds: 1 integer codes, 2 BF16 exponent + raw sign/mantissa byte (one
 exponent per symbol, or with k = 2 a pair of exponent digits plus the correction
-stream of escaped weights: MINE page Section 4.1 "Escapes"), 3 FP8 E4M3 bytes,
+stream of escaped weights: MINE page Section 4.1 "Escapes"; 4-bit codes with k = 4
+likewise over a table of stored 4-tuples), 3 FP8 E4M3 bytes,
 4 E8 lattice fields (doubled coordinates as logical tensor).
 Reconstruction dtypes for E8: 4 = INT8 (2v), 5 = FP8 E4M3 (nearest to v).
 """
@@ -34,6 +35,7 @@ class Coding:
     log2_m: int = 12
     tile_cols: int = 256
     recon_dtype: int = 0       # E8 only
+    stored_tuples: int = 0     # quads of 4-bit codes: t, the tuples the table stores
 
 
 @dataclass
@@ -54,6 +56,7 @@ class Components:
     scales: np.ndarray | None  # float16 [N]
     counts: np.ndarray = field(default=None)   # histogram [n_tables, 256]
     pair_values: np.ndarray | None = None      # BF16 pairs: exponent of each digit
+    stored: np.ndarray | None = None           # code quads: the stored tuples, ascending
 
 
 def syms_per_slice(c: Coding) -> int:
@@ -68,6 +71,15 @@ def syms_per_slice(c: Coding) -> int:
 
 def _bf16_pairs(c: Coding) -> bool:
     return c.payload == BF16_EXP and c.k == 2
+
+
+def _quads(c: Coding) -> bool:
+    """Quads of 4-bit codes over a table of stored tuples, with escapes."""
+    return c.payload == INT_CODES and c.k == 4 and c.code_bits == 4
+
+
+def _escapes(c: Coding) -> bool:
+    return _bf16_pairs(c) or _quads(c)
 
 
 # ---------------------------------------------------------------- logical -> symbols
@@ -93,12 +105,22 @@ def _row_symbols(c: Coding, logical: np.ndarray):
 
 
 def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
-    pair_values = esc = None
+    pair_values = esc = stored = esc_bits = None
     if _bf16_pairs(c):
         ex, _ = symbols.bf16_split(logical)
         pair_values = symbols.bf16_pair_values(coding.histogram(ex, 256))
         vals, raw, esc = symbols.bf16_pair_split(logical, pair_values)
         tbl = np.zeros_like(vals)
+        esc_bits = np.asarray(logical, np.uint16)
+    elif _quads(c):
+        if not 1 <= c.stored_tuples <= (1 << c.log2_m):
+            raise ValueError("stored tuples must be in [1, M]")
+        tu = symbols.quad_tuples(logical)
+        stored = symbols.quad_stored(coding.histogram(tu, 1 << 16), c.stored_tuples)
+        vals, esc = symbols.quad_map(tu, stored)
+        tbl = np.zeros_like(vals)
+        raw = None
+        esc_bits = symbols.small_int_bf16_bits(logical)
     else:
         vals, tbl, raw = _row_symbols(c, logical)
     n_tables = e8.N_TABLES if c.payload == E8_LATTICE else 1
@@ -111,14 +133,18 @@ def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
                 value_offset[t] = sel.min()
                 alphabet[t] = sel.max() - sel.min() + 1
         sym = vals - value_offset[tbl]
+    elif stored is not None:
+        sym = vals
+        alphabet[0] = stored.size
     else:
         sym = vals
         alphabet[0] = {INT_CODES: 1 << (c.code_bits * c.k), BF16_EXP: 256, FP8_E4M3: 256}[c.payload]
-    if np.any(alphabet > 256):
+    width = max(256, int(alphabet.max()))      # only quad tables exceed 256 symbols
+    if width > 256 and stored is None:
         raise ValueError("alphabet larger than 256")
-    counts = np.zeros((n_tables, 256), dtype=np.int64)
+    counts = np.zeros((n_tables, width), dtype=np.int64)
     for t in range(n_tables):
-        counts[t] = coding.histogram(sym[tbl == t], 256)
+        counts[t] = coding.histogram(sym[tbl == t], width)
     freq = np.stack([coding.normalise(counts[t], c.log2_m) for t in range(n_tables)])
     sps = syms_per_slice(c)
     n_rg, n_sl, s_full, s_last = symbols.tile_plan(c.rows, sym.shape[1], sps)
@@ -133,7 +159,7 @@ def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
     g_esc = [None] * len(g_sym)
     if esc is not None:
         g_esc = list(zip(symbols.rows_to_tiles(esc, c.tile_cols),
-                         symbols.rows_to_tiles(np.asarray(logical, np.uint16), c.tile_cols)))
+                         symbols.rows_to_tiles(esc_bits, c.tile_cols)))
     for (ids, sdat, act), (_, tdat, _), rg, eg in zip(g_sym, g_tbl, g_raw, g_esc):
         st, words, cnt = rans.encode_tiles(sdat, tdat, freq, c.log2_m, act)
         states[ids] = st
@@ -154,7 +180,7 @@ def encode(c: Coding, logical: np.ndarray, scales=None) -> Components:
     sc = None if scales is None else np.asarray(scales, dtype=np.float16)
     return Components(c, n_tables, alphabet, value_offset, freq, n_rg, n_sl, s_full, s_last,
                       states, rans.offsets_from_counts(counts_t), words_all, raw_all, sc, counts,
-                      pair_values)
+                      pair_values, stored)
 
 
 # ---------------------------------------------------------------- symbols -> logical
@@ -169,7 +195,7 @@ def _decode_all(comp: Components):
     correction streams (BF16 pairs; empty otherwise))."""
     c = comp.coding
     sps = syms_per_slice(c)
-    pairs = _bf16_pairs(c)
+    pairs = _escapes(c)
     corr = {}
     n_sym = {INT_CODES: c.cols // max(c.k, 1), BF16_EXP: c.cols // c.k, FP8_E4M3: c.cols,
              E8_LATTICE: 9 * c.cols // 8}[c.payload]
@@ -196,7 +222,7 @@ def _decode_all(comp: Components):
             syms, okg, ptr = _decode_group(comp, comp.states[ids], offsets, S, act, tos, trailing=True)
             for i, t in enumerate(ids):
                 b, e = int(comp.offsets[t]), int(comp.offsets[t + 1])
-                recs, okc = corrections.parse(comp.words[b + int(ptr[i]):e], 2 * S, act[i])
+                recs, okc = corrections.parse(comp.words[b + int(ptr[i]):e], c.k * S, act[i])
                 okg[i] &= okc
                 corr[int(t)] = recs
         else:
@@ -231,6 +257,16 @@ def decode(comp: Components) -> np.ndarray:
                     if g * 64 + lane < c.rows:
                         w[g * 64 + lane, sl * c.tile_cols + col] = bits
         return w
+    if _quads(c):
+        q = symbols.quad_join(sym, comp.stored)
+        for t, per_lane in corr.items():
+            g, sl = divmod(t, comp.n_sl)
+            for lane, recs in enumerate(per_lane):
+                for col, bits in recs:
+                    if g * 64 + lane < c.rows:
+                        q[g * 64 + lane, sl * c.tile_cols + col] = int(np.array([bits << 16], np.uint32)
+                                                                       .view(np.float32)[0])
+        return q
     if c.payload == INT_CODES:
         return symbols.symbols_to_int_codes(sym, c.code_bits, c.k)
     if c.payload == FP8_E4M3:

@@ -20,6 +20,16 @@
   other exponents (ties to the smaller exponent), ascending, so digit 0 is
   exponent 0; an escaped weight is coded as digit 0 with raw byte 0, i.e. as +0.0,
   and its bf16 bits go to the correction stream (``corrections``).
+* Quads of 4-bit codes: four consecutive columns per symbol over a table of t
+  stored 4-tuples (MINE page, Section 4.1 "Escapes": restrict the decoding table
+  to the most frequent symbols, code an escaped value as 0 and keep the real value
+  in the correction stream).  The page builds pairs over t single values and
+  limits 4-bit codes to pairs; reading taken here for quads: the table stores the
+  t most frequent whole tuples (ties to the smaller tuple, the zero tuple always
+  kept), and a tuple outside the table is coded as the stored tuple reached by
+  setting the fewest of its codes to 0 (the first such set of positions in
+  (count, mask) order); each nonzero code so set is escaped, its record holding the
+  code's value as a bf16 number.
 * FP8 E4M3: the byte itself is the symbol (MINE page Section 4.1; OCP E4M3 with
   bias 7, no infinities, S.1111.111 = NaN).
 * Tiling: rows in groups of 64 (lane l = row r0 + l, the MINE page's lane-per-row
@@ -135,6 +145,82 @@ def bf16_pair_join(sym: np.ndarray, raw: np.ndarray, values: np.ndarray) -> np.n
     ex[:, 0::2] = v[s & 15]
     ex[:, 1::2] = v[s >> 4]
     return bf16_join(ex, raw)
+
+
+# ---------------------------------------------------------------- 4-bit code quads
+QUAD_ZERO = 0x8888      # the tuple of four zero codes (digit 8 = code 0)
+
+
+def quad_tuples(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes [N, K] (K % 4 == 0) -> tuples int64 [N, K/4], the digit q + 8 of
+    column 4j + i at bits [4i, 4i + 4)."""
+    return int_codes_to_symbols(codes, 4, 4)
+
+
+def quad_stored(tuple_counts: np.ndarray, t: int) -> np.ndarray:
+    """The stored tuples of a quad table: the t most frequent occurring tuples (more
+    occurrences first, the smaller tuple on ties), with the zero tuple taking the
+    place of the last one if it is not among them, in ascending order.  MINE page,
+    Section 4.1 "Escapes" (a table restricted to the most frequent symbols, 0 always
+    kept for the escaped values); read here for whole 4-tuples of codes."""
+    c = np.asarray(tuple_counts, dtype=np.int64)
+    occ = [int(v) for v in np.nonzero(c)[0]]
+    occ.sort(key=lambda v: (-int(c[v]), v))
+    keep = occ[:t]
+    if QUAD_ZERO not in keep:
+        keep = keep[:t - 1] + [QUAD_ZERO]
+    return np.array(sorted(keep), dtype=np.int64)
+
+
+def _zeroed(tup: int, mask: int) -> int:
+    for i in range(4):
+        if (mask >> i) & 1:
+            tup = (tup & ~(15 << (4 * i))) | (8 << (4 * i))
+    return tup
+
+
+# masks over the four codes, fewest codes first, then the smaller mask
+QUAD_MASKS = sorted(range(1, 16), key=lambda m: (bin(m).count("1"), m))
+
+
+def quad_map(tuples: np.ndarray, stored: np.ndarray):
+    """Tuples [N, n] -> (symbol ids int64 [N, n], escaped bool [N, 4n]).  A stored
+    tuple is its own symbol; any other is coded as the stored tuple reached by
+    setting some of its codes to 0, taking the first such set of positions in
+    QUAD_MASKS order; its nonzero codes so set are escaped."""
+    tu = np.asarray(tuples, dtype=np.int64)
+    index = {int(v): i for i, v in enumerate(stored)}
+    ids = np.zeros(tu.shape, dtype=np.int64)
+    esc = np.zeros((tu.shape[0], 4 * tu.shape[1]), dtype=bool)
+    memo = {}
+    for (r, j), v in np.ndenumerate(tu):
+        v = int(v)
+        if v not in memo:
+            if v in index:
+                memo[v] = (index[v], 0)
+            else:
+                for m in QUAD_MASKS:
+                    z = _zeroed(v, m)
+                    if z in index:
+                        memo[v] = (index[z], m)
+                        break
+        i, m = memo[v]
+        ids[r, j] = i
+        for p in range(4):
+            if (m >> p) & 1 and ((v >> (4 * p)) & 15) != 8:
+                esc[r, 4 * j + p] = True
+    return ids, esc
+
+
+def quad_join(ids: np.ndarray, stored: np.ndarray) -> np.ndarray:
+    """Symbol ids [N, n] -> codes int8 [N, 4n] (escaped codes read as 0)."""
+    tu = np.asarray(stored, dtype=np.int64)[np.asarray(ids, dtype=np.int64)]
+    return symbols_to_int_codes(tu, 4, 4).astype(np.int8)
+
+
+def small_int_bf16_bits(q: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of integers |q| <= 256 (exact): the high half of the fp32."""
+    return (np.asarray(q, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 # ---------------------------------------------------------------- FP8 E4M3

@@ -474,3 +474,102 @@ def test_dequantized_rounds_to_nearest_even():
     # bf16 weights pass through unchanged
     b = P.dequantized(P.Coding(P.BF16_EXP, 1, 2), np.array([[0x3F81, 0xC2F7]], np.uint16), None, "bf16")
     assert list(b.ravel()) == [0x3F81, 0xC2F7]
+
+
+# ------------------------------------------------------------------ quads of 4-bit codes
+def test_quad_stored_keeps_the_most_frequent_and_zero():
+    # MINE page, Section 4.1 "Escapes": the table keeps the most frequent symbols and
+    # always the value escapes are coded as (here the tuple of four zero codes)
+    counts = np.zeros(1 << 16, np.int64)
+    counts[0x8888], counts[0x8889], counts[0x88A8], counts[0x1234], counts[0x0001] = 50, 9, 7, 7, 3
+    assert list(symbols.quad_stored(counts, 3)) == [0x1234, 0x8888, 0x8889]     # tie: the smaller tuple
+    assert list(symbols.quad_stored(counts, 9)) == [0x0001, 0x1234, 0x8888, 0x8889, 0x88A8]
+    counts[0x8888] = 0                          # zero takes the last place when missing
+    assert list(symbols.quad_stored(counts, 2)) == [0x8888, 0x8889]
+    assert list(symbols.quad_stored(counts, 1)) == [0x8888]
+
+
+def test_quad_map_is_the_fewest_escapes_by_enumeration():
+    # against every stored tuple: the chosen one agrees with the tuple wherever it is
+    # not a zero code, no stored tuple needs fewer escapes, and ties go to the first
+    # set of zeroed positions in the order (count, mask)
+    rng = np.random.default_rng([0, 4, 4])
+    stored = np.unique(np.concatenate([[0x8888], rng.integers(0, 1 << 16, 40),
+                                       0x8888 ^ (rng.integers(0, 16, 40) << (4 * rng.integers(0, 4, 40)))]))
+    tup = np.concatenate([stored[:10], rng.integers(0, 1 << 16, 300),
+                          0x8888 ^ (rng.integers(0, 16, 100) << (4 * rng.integers(0, 4, 100)))])
+    ids, esc = symbols.quad_map(tup[None, :], stored)
+    dig = lambda v: [(int(v) >> (4 * i)) & 15 for i in range(4)]
+    for j, v in enumerate(tup):
+        d = dig(v)
+        best = None
+        for s in stored:
+            e = dig(s)
+            if all(e[i] == d[i] or e[i] == 8 for i in range(4)):
+                pos = [i for i in range(4) if e[i] != d[i]]
+                key = (len(pos), sum(1 << i for i in pos))
+                if best is None or key < best[0]:
+                    best = (key, int(s), pos)
+        assert stored[ids[0, j]] == best[1]
+        assert [i for i in range(4) if esc[0, 4 * j + i]] == best[2]
+
+
+def test_quad_stream_worked_example():
+    # One 64 x 64 tile of zero codes with three stored tuples (zero, (1,0,0,0) ten
+    # times, (0,2,0,0) five times) and three tuples outside the table.  Records
+    # written out by hand: bf16 of the code | column << 16 | last << 27.
+    q = np.zeros((64, 64), np.int8)
+    q[0:10, 0] = 1                              # tuple 0x8889
+    q[0:5, 5] = 2                               # tuple 0x88A8
+    q[7, 8:10] = (1, 2)                         # 0x88A9: zeroing the 1 gives 0x88A8
+    q[3, 63] = -3                               # 0x5888: only zero is reachable
+    q[3, 12] = 7                                # 0x888F
+    c = P.Coding(P.INT_CODES, 64, 64, k=4, code_bits=4, log2_m=8, tile_cols=64, stored_tuples=3)
+    comp = P.encode(c, q)
+    assert list(comp.stored) == [0x8888, 0x8889, 0x88A8]
+    tail = [0x0088, 0, 0, 0,                    # lanes 3 and 7 hold records
+            0x40E0, 0x000C,                     # round 0, lane 3: 7.0 at column 12
+            0x3F80, 0x0808,                     # round 0, lane 7: 1.0 at column 8, last
+            0xC040, 0x083F]                     # round 1, lane 3: -3.0 at column 63, last
+    assert [int(w) for w in comp.words[-10:]] == tail
+    sym, ok = P.decode_symbols(comp)
+    assert ok.all()
+    assert sym[7, 2] == 2 and sym[3, 15] == 0 and sym[3, 3] == 0 and sym[0, 0] == 1 and sym[0, 1] == 2
+    assert np.array_equal(P.decode(comp), q)
+
+
+@pytest.mark.parametrize("rows,cols,tc,m,t", [(130, 512, 256, 12, 2048), (70, 256, 128, 10, 64),
+                                              (64, 64, 64, 8, 1), (65, 192, 64, 13, 4096)])
+def test_quads_roundtrip_with_escapes(rows, cols, tc, m, t):
+    q = E.laplace_codes((rows, cols), np.random.default_rng([0, 44, rows])).codes
+    c = P.Coding(P.INT_CODES, rows, cols, k=4, code_bits=4, log2_m=m, tile_cols=tc, stored_tuples=t)
+    comp = P.encode(c, q)
+    assert comp.stored.size <= t and 0x8888 in comp.stored
+    _, ok = P.decode_symbols(comp)
+    assert ok.all()
+    assert np.array_equal(P.decode(comp), q)
+
+
+def test_quads_escape_count_and_size():
+    # every code set to 0 by the mapping is one record (two words), each tile adds its
+    # 4-word mask; the ANS part stays within the cross-entropy bound
+    q = E.laplace_codes((128, 1024), np.random.default_rng([0, 45])).codes
+    c = P.Coding(P.INT_CODES, 128, 1024, k=4, code_bits=4, log2_m=12, tile_cols=256, stored_tuples=1024)
+    comp = P.encode(c, q)
+    coded = symbols.quad_join(P.decode_symbols(comp)[0], comp.stored)
+    n_esc = int(np.count_nonzero(coded != q))
+    assert n_esc > 0 and np.all(coded[coded != q] == 0)
+    _, _, corr = P._decode_all(comp)
+    assert sum(len(r) for lanes in corr.values() for r in lanes) == n_esc
+    T = comp.n_rg * comp.n_sl
+    ans = int(comp.offsets[-1]) - 4 * T - 2 * n_esc
+    ce = coding.cross_entropy_total_bits(comp.counts[0], comp.freq[0], 12)
+    assert 16 * ans <= 1.01 * ce + 16 * 64 * T
+    assert ce <= 16 * ans + 32 * 64 * T
+
+
+def test_quads_need_one_to_m_stored_tuples():
+    q = np.zeros((64, 64), np.int8)
+    for t in (0, 257):
+        with pytest.raises(ValueError):
+            P.encode(P.Coding(P.INT_CODES, 64, 64, k=4, code_bits=4, log2_m=8, tile_cols=64, stored_tuples=t), q)
