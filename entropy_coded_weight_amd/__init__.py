@@ -23,7 +23,8 @@ INT_CODES, BF16_EXP, FP8_E4M3, E8_LATTICE = 1, 2, 3, 4
 DT_F16, DT_BF16, DT_F32, DT_I8, DT_FP8_E4M3 = 1, 2, 3, 4, 5
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "CORRUPT", 4: "BUFFER_TOO_SMALL", 5: "HIP"}
 
-ABI_VERSION = 2          # layout of the structs below
+ABI_VERSION = 3          # layout of the structs below
+MAX_TUPLES = 4096
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libecw.so")
 
@@ -31,12 +32,12 @@ LIB_PATH = os.path.join(_HERE, "libecw.so")
 class Coding(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in (
         "payload", "rows", "cols", "weights_per_symbol", "code_bits", "log2_m",
-        "tile_rows", "tile_cols", "recon_dtype")]
+        "tile_rows", "tile_cols", "recon_dtype", "stored_tuples")]
 
     def __init__(self, payload, rows, cols, weights_per_symbol=1, code_bits=0, log2_m=12,
-                 tile_cols=256, recon_dtype=0, tile_rows=64):
+                 tile_cols=256, recon_dtype=0, tile_rows=64, stored_tuples=0):
         super().__init__(payload, rows, cols, weights_per_symbol, code_bits, log2_m,
-                         tile_rows, tile_cols, recon_dtype)
+                         tile_rows, tile_cols, recon_dtype, stored_tuples)
 
 
 class Tables(ctypes.Structure):
@@ -46,7 +47,11 @@ class Tables(ctypes.Structure):
                 ("freq", (ctypes.c_uint16 * 256) * 17),
                 ("count", (ctypes.c_uint64 * 256) * 17),
                 ("pair_values", ctypes.c_uint8 * 16),
-                ("escapes", ctypes.c_uint64)]
+                ("escapes", ctypes.c_uint64),
+                ("n_tuples", ctypes.c_uint32),
+                ("tuples", ctypes.c_uint16 * MAX_TUPLES),
+                ("tuple_freq", ctypes.c_uint16 * MAX_TUPLES),
+                ("tuple_count", ctypes.c_uint64 * MAX_TUPLES)]
 
     def freq_array(self) -> np.ndarray:
         return np.ctypeslib.as_array(self.freq)[: self.n_tables].astype(np.int64)

@@ -5,6 +5,9 @@
 //   sections, each starting on a 256-byte boundary, in this order:
 //   TABLES   n_tables x TableRecord                        (alphabet, offset, freq)
 //            BF16 pairs: then 16 bytes, the exponent of each digit
+//            INT quads: the record's alphabet is n, the number of stored tuples,
+//            and its freq is zero; then stored_tuples u16 tuples (the first n
+//            ascending, the rest 0) and stored_tuples u16 frequencies (likewise)
 //   LUT      n_tables x M x 8 B decode entries             (derived from freq)
 //   STATES   n_tiles x 64 x u32 decoder start states       (inactive lanes: 2^16)
 //   OFFSETS  (n_tiles + 1) x u32 word offsets into WORDS   (last = total words)
@@ -28,6 +31,12 @@
 // than r, lanes ascending), each record two words, low half first:
 //   bits 0..15 bf16 weight, 16..26 column in the slice, 27 last of its row, 28..31 0
 //
+// INT quads (4-bit codes, k = 4): a symbol is the index of a stored 4-tuple of codes
+// (digit q + 8 of column 4j + i at bits 4i..4i+3); a tuple outside the table is
+// coded as the stored tuple reached by setting the fewest of its codes to 0, and
+// each nonzero code so set is escaped into the same correction stream, its record
+// holding the code as a bf16 number.
+//
 // Decode entry of slot i (table t), symbol s, as two u32 (MINE page, Section 4.1:
 // one table read yields both the state-update operands and the payload):
 //   lo = f | a8 << 24     f <= 2^13 sits in the low 24 bits, so the 24-bit multiply
@@ -40,6 +49,8 @@
 //                     |q| <= 8 has a zero low byte, so the two high bytes are the
 //                     whole values)
 //   INT, k = 4:       a8 = symbol, h16 = 0
+//   INT quads:        a8 = 0, h16 = 8 * symbol (the byte offset of the symbol's
+//                     entry in the per-block table of its four codes)
 //   BF16:             a8 = exponent byte rotated right by one bit (bit 0 in bit 7),
 //                     h16 = 0.  With the raw byte (sign << 7 | mantissa) the bf16
 //                     value's high byte is then sign | a8[6:0] and its low byte
@@ -65,6 +76,13 @@ constexpr uint32_t kMaxLog2M = 13;
 constexpr uint32_t kPairDigits = 16;        // BF16 pairs: stored exponents
 constexpr uint32_t kEscLast = 1u << 27;     // correction record: last of its row
 constexpr uint32_t kEscMaskWords = 4;       // correction stream: lane mask words
+constexpr uint32_t kMaxTuples = 4096;       // INT quads: stored tuples at most
+constexpr uint32_t kQuadZero = 0x8888;      // INT quads: the tuple of four zero codes
+
+// INT quads: four 4-bit codes per symbol over a table of stored tuples
+inline bool quad_coding(uint32_t payload, uint32_t code_bits, uint32_t k) {
+  return payload == 1 && code_bits == 4 && k == 4;
+}
 
 enum Section : uint32_t {
   kSecTables = 0, kSecLut, kSecStates, kSecOffsets, kSecWords, kSecRaw, kSecScales, kNumSections
@@ -85,7 +103,8 @@ struct BlobHeader {
       recon_dtype;
   // derived geometry
   uint32_t n_tables, n_row_groups, n_slices, n_tiles, steps_full, steps_last, lut_entry_bytes;
-  uint32_t reserved0, reserved1;
+  uint32_t stored_tuples;   // INT quads (else 0)
+  uint32_t reserved1;
   uint64_t total_bytes;  // byte offset 88
   SectionRef sec[8];
   uint8_t pad[256 - 4 * 4 - 9 * 4 - 9 * 4 - 8 - 8 * 16];  // sections at byte offset 96

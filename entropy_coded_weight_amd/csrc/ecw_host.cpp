@@ -45,14 +45,23 @@ ecw_status check_coding(const ecw_coding* c) {
     return fail(ECW_E_INVALID_ARG, "tile_cols must be a positive multiple of 64");
   if (c->rows > (1u << 30) || c->cols > (1u << 30))
     return fail(ECW_E_INVALID_ARG, "rows/cols too large");
+  const bool quads = quad_coding(c->payload, c->code_bits, c->weights_per_symbol);
+  if (!quads && c->stored_tuples != 0) return fail(ECW_E_INVALID_ARG, "stored_tuples is for INT quads of 4-bit codes");
   switch (c->payload) {
     case ECW_P_INT_CODES: {
       uint32_t b = c->code_bits, k = c->weights_per_symbol;
       if (b < 2 || b > 4) return fail(ECW_E_UNSUPPORTED, "code_bits must be 2, 3 or 4");
-      if (!(k == 1 || k == 2 || k == 4) || b * k > 8)
-        return fail(ECW_E_UNSUPPORTED, "weights_per_symbol must be 1, 2 or 4 with code_bits*k <= 8");
-      if ((1u << (b * k)) > (1u << c->log2_m))
-        return fail(ECW_E_UNSUPPORTED, "alphabet^k exceeds M (integer codes have no escapes)");
+      if (quads) {
+        // a table of stored 4-tuples; a record's column field has 11 bits
+        if (c->stored_tuples < 1 || c->stored_tuples > std::min(kMaxTuples, 1u << c->log2_m))
+          return fail(ECW_E_INVALID_ARG, "INT quads: stored_tuples must be in [1, min(M, 4096)]");
+        if (c->tile_cols > 2048) return fail(ECW_E_UNSUPPORTED, "INT quads: tile_cols must be at most 2048");
+      } else if (!(k == 1 || k == 2 || k == 4) || b * k > 8) {
+        return fail(ECW_E_UNSUPPORTED, "weights_per_symbol must be 1, 2 or 4 with code_bits*k <= 8 "
+                                       "(or 4 with 4-bit codes over stored tuples)");
+      }
+      if (!quads && (1u << (b * k)) > (1u << c->log2_m))
+        return fail(ECW_E_UNSUPPORTED, "alphabet^k exceeds M (integer codes escape in quads of 4-bit codes only)");
       if (c->cols % (16 * k)) return fail(ECW_E_UNSUPPORTED, "cols must be a multiple of 16*k");
       if (c->recon_dtype != 0) return fail(ECW_E_INVALID_ARG, "recon_dtype is E8-only");
       break;
@@ -108,11 +117,60 @@ struct Escape {
   uint16_t bits;
 };
 
+// INT quads: how each of the 65536 tuples is coded.  A stored tuple is its own
+// symbol; any other becomes the stored tuple reached by setting the fewest of its
+// codes to 0 (position sets tried by count, then as a 4-bit mask ascending), and
+// its nonzero codes so set are escaped.
+struct QuadMap {
+  std::vector<int32_t> id;     // symbol (index of the stored tuple), -1 = none
+  std::vector<uint8_t> esc;    // bit i: code i is escaped
+
+  void build(const uint16_t* stored, uint32_t n) {
+    std::vector<int32_t> index(1u << 16, -1);
+    for (uint32_t i = 0; i < n; ++i) index[stored[i]] = (int32_t)i;
+    uint32_t order[15], no = 0;
+    for (uint32_t pc = 1; pc <= 4; ++pc)
+      for (uint32_t m = 1; m < 16; ++m)
+        if ((uint32_t)__builtin_popcount(m) == pc) order[no++] = m;
+    id.assign(1u << 16, -1);
+    esc.assign(1u << 16, 0);
+    for (uint32_t v = 0; v < (1u << 16); ++v) {
+      if (index[v] >= 0) {
+        id[v] = index[v];
+        continue;
+      }
+      for (uint32_t oi = 0; oi < 15; ++oi) {
+        const uint32_t m = order[oi];
+        uint32_t z = v, e = 0;
+        for (uint32_t p = 0; p < 4; ++p)
+          if ((m >> p) & 1) {
+            if (((v >> (4 * p)) & 15) != 8) e |= 1u << p;
+            z = (z & ~(15u << (4 * p))) | (8u << (4 * p));
+          }
+        if (index[z] >= 0) {
+          id[v] = index[z];
+          esc[v] = (uint8_t)e;
+          break;
+        }
+      }
+    }
+  }
+};
+
+// bf16 bits of a small integer (exact)
+static uint16_t bf16_of_int(int q) {
+  const float f = (float)q;
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
 struct SymbolSource {
   const ecw_coding& c;
   const void* w;
   const ecw_tables* t;   // value offsets (E8); may be null while building tables
   int8_t digit[256];     // BF16 pairs: digit of each exponent, -1 = escaped
+  const QuadMap* qm = nullptr;   // INT quads
 
   // BF16 pairs: exponent 0 has digit 0; e != 0 the first d >= 1 with pv[d] == e.
   void set_digits(const uint8_t* pv) {
@@ -125,7 +183,8 @@ struct SymbolSource {
   // Writes n symbols of row r starting at symbol index s0.  Returns false on an
   // invalid logical value.  tbl/raw may be null; raw gets one byte per weight.
   // BF16 pairs: escaped weights get raw byte 0 and, if esc is given, an Escape
-  // (lane `lane`, column relative to symbol s0's first column).
+  // (lane `lane`, column relative to symbol s0's first column); INT quads likewise
+  // (the escaped code reads as 0).
   bool row(uint32_t r, uint32_t s0, uint32_t n, int32_t* val, uint8_t* tbl, uint8_t* raw,
            std::vector<Escape>* esc = nullptr, uint32_t lane = 0) const {
     const uint64_t K = c.cols;
@@ -140,6 +199,15 @@ struct SymbolSource {
             int v = q[(uint64_t)(s0 + i) * k + u];
             if (v < -half || v >= half) return false;
             s |= (uint32_t)(v + half) << (b * u);
+          }
+          if (qm) {
+            const int32_t id = qm->id[s];
+            if (id < 0) return false;
+            if (esc && qm->esc[s])
+              for (uint32_t u = 0; u < 4; ++u)
+                if ((qm->esc[s] >> u) & 1)
+                  esc->push_back({lane, 4 * i + u, bf16_of_int(q[(uint64_t)(s0 + i) * 4 + u])});
+            s = (uint32_t)id;
           }
           val[i] = (int32_t)s;
           if (tbl) tbl[i] = 0;
@@ -242,33 +310,34 @@ static void parallel_for(uint64_t n, F&& f) {
 }
 
 // ------------------------------------------------------------------ normaliser
-static void normalise(const uint64_t* count, uint32_t log2_m, uint16_t* freq) {
+// A symbols (256, or the stored tuples of INT quads); at most M of them occur.
+static void normalise(const uint64_t* count, uint32_t A, uint32_t log2_m, uint16_t* freq) {
   const uint32_t M = 1u << log2_m;
   uint32_t present = 0;
-  for (int s = 0; s < 256; ++s) present += count[s] > 0;
-  for (int s = 0; s < 256; ++s) freq[s] = 0;
+  for (uint32_t s = 0; s < A; ++s) present += count[s] > 0;
+  for (uint32_t s = 0; s < A; ++s) freq[s] = 0;
   if (present == 0) return;
   if (present == 1) {
-    for (int s = 0; s < 256; ++s)
+    for (uint32_t s = 0; s < A; ++s)
       if (count[s]) freq[s] = (uint16_t)M;
     return;
   }
   std::vector<double> d(M + 1, 0.0);
   for (uint32_t f = 1; f <= M; ++f) d[f] = std::log2((double)f + 1.0) - std::log2((double)f);
-  uint32_t f[256];
-  double gain[256];
-  for (int s = 0; s < 256; ++s) {
+  std::vector<uint32_t> f(A);
+  std::vector<double> gain(A);
+  for (uint32_t s = 0; s < A; ++s) {
     f[s] = count[s] ? 1 : 0;
     gain[s] = count[s] ? (double)count[s] * d[1] : -INFINITY;
   }
   for (uint32_t it = 0; it < M - present; ++it) {
-    int best = 0;
-    for (int s = 1; s < 256; ++s)
+    uint32_t best = 0;
+    for (uint32_t s = 1; s < A; ++s)
       if (gain[s] > gain[best]) best = s;        // strict: first maximum wins
     f[best] += 1;
     gain[best] = (double)count[best] * d[f[best]];
   }
-  for (int s = 0; s < 256; ++s) freq[s] = (uint16_t)f[s];
+  for (uint32_t s = 0; s < A; ++s) freq[s] = (uint16_t)f[s];
 }
 
 }  // namespace ecw
@@ -351,6 +420,56 @@ extern "C" ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_t
   std::vector<int32_t> vmin(nth * 17, INT32_MAX), vmax(nth * 17, INT32_MIN);
   std::atomic<bool> bad{false};
   SymbolSource src{*c, w, nullptr, {}};
+  if (quad_coding(c->payload, c->code_bits, c->weights_per_symbol)) {
+    // INT quads: the stored_tuples most frequent 4-tuples (ties to the smaller
+    // tuple, the zero tuple always kept in place of the last), ascending (MINE page,
+    // Section 4.1 "Escapes", Section 4.2 "Tuning t")
+    std::vector<std::vector<uint64_t>> th(nth);
+    parallel_for(c->rows, [&](uint64_t r, unsigned tid) {
+      if (th[tid].empty()) th[tid].assign(1u << 16, 0);
+      const int8_t* q = static_cast<const int8_t*>(w) + r * (uint64_t)c->cols;
+      uint64_t* h = th[tid].data();
+      for (uint32_t j = 0; j < c->cols / 4; ++j) {
+        uint32_t v = 0;
+        for (uint32_t u = 0; u < 4; ++u) {
+          const int x = q[4 * j + u];
+          if (x < -8 || x > 7) {
+            bad = true;
+            return;
+          }
+          v |= (uint32_t)(x + 8) << (4 * u);
+        }
+        h[v] += 1;
+      }
+    });
+    if (bad) return fail(ECW_E_INVALID_ARG, "logical tensor holds a value outside the payload's range");
+    std::vector<uint64_t> cnt(1u << 16, 0);
+    for (auto& h : th)
+      if (!h.empty())
+        for (uint32_t v = 0; v < (1u << 16); ++v) cnt[v] += h[v];
+    std::vector<uint32_t> order;
+    for (uint32_t v = 0; v < (1u << 16); ++v)
+      if (cnt[v]) order.push_back(v);
+    std::sort(order.begin(), order.end(), [&](uint32_t a, uint32_t b) { return cnt[a] != cnt[b] ? cnt[a] > cnt[b] : a < b; });
+    order.resize(std::min<size_t>(order.size(), c->stored_tuples));
+    if (std::find(order.begin(), order.end(), kQuadZero) == order.end()) {
+      if (order.size() == c->stored_tuples) order.pop_back();
+      order.push_back(kQuadZero);
+    }
+    std::sort(order.begin(), order.end());
+    out->n_tuples = (uint32_t)order.size();
+    for (size_t i = 0; i < order.size(); ++i) out->tuples[i] = (uint16_t)order[i];
+    QuadMap qm;
+    qm.build(out->tuples, out->n_tuples);
+    for (uint32_t v = 0; v < (1u << 16); ++v) {
+      if (!cnt[v]) continue;
+      out->tuple_count[qm.id[v]] += cnt[v];
+      out->escapes += cnt[v] * (uint64_t)__builtin_popcount(qm.esc[v]);
+    }
+    out->alphabet[0] = out->n_tuples;
+    normalise(out->tuple_count, out->n_tuples, c->log2_m, out->tuple_freq);
+    return ECW_OK;
+  }
   if (c->payload == ECW_P_BF16_EXP && c->weights_per_symbol == 2) {
     // BF16 pairs: the stored exponents are 0 and the 15 most frequent others, the
     // smaller exponent first on ties, ascending (MINE page, Section 4.2 "Tuning t")
@@ -428,7 +547,7 @@ extern "C" ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_t
     }
     if (present > (1u << c->log2_m))
       return fail(ECW_E_UNSUPPORTED, "more distinct symbols than table slots (only BF16 exponent pairs escape)");
-    normalise(out->count[t], c->log2_m, out->freq[t]);
+    normalise(out->count[t], 256, c->log2_m, out->freq[t]);
   }
   return ECW_OK;
 }
@@ -453,7 +572,8 @@ static ecw_status check_tables_for(const ecw_coding* c, const ecw_tables* t, con
   if (!t) return fail(ECW_E_INVALID_ARG, "tables are NULL");
   if (t->n_tables != g.n_tables) return fail(ECW_E_INVALID_ARG, "table count does not match payload");
   const uint32_t M = 1u << c->log2_m;
-  for (uint32_t k = 0; k < g.n_tables; ++k) {
+  const bool quads = quad_coding(c->payload, c->code_bits, c->weights_per_symbol);
+  for (uint32_t k = 0; k < g.n_tables && !quads; ++k) {
     if (t->alphabet[k] > 256) return fail(ECW_E_INVALID_ARG, "alphabet > 256");
     uint64_t sum = 0;
     for (uint32_t s = 0; s < 256; ++s) {
@@ -465,6 +585,19 @@ static ecw_status check_tables_for(const ecw_coding* c, const ecw_tables* t, con
   }
   if (c->payload == ECW_P_BF16_EXP && c->weights_per_symbol == 2 && t->pair_values[0] != 0)
     return fail(ECW_E_INVALID_ARG, "BF16 pairs: digit 0 must be exponent 0 (escaped weights are coded as 0)");
+  if (quads) {
+    const uint32_t n = t->n_tuples;
+    if (n < 1 || n > c->stored_tuples) return fail(ECW_E_INVALID_ARG, "INT quads: n_tuples must be in [1, stored_tuples]");
+    bool zero = false;
+    uint64_t sum = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+      if (i && t->tuples[i] <= t->tuples[i - 1]) return fail(ECW_E_INVALID_ARG, "INT quads: tuples not ascending");
+      zero |= t->tuples[i] == kQuadZero;
+      sum += t->tuple_freq[i];
+    }
+    if (!zero) return fail(ECW_E_INVALID_ARG, "INT quads: the zero tuple must be stored (escapes are coded as 0)");
+    if (sum != M && !(sum == 0 && g.n_tiles == 0)) return fail(ECW_E_INVALID_ARG, "tuple frequencies do not sum to M");
+  }
   return ECW_OK;
 }
 
@@ -484,12 +617,22 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
   const uint32_t m = c->log2_m;
   const bool bf16 = c->payload == ECW_P_BF16_EXP;
   const bool pairs = bf16 && c->weights_per_symbol == 2;
+  const bool quads = quad_coding(c->payload, c->code_bits, c->weights_per_symbol);
+  const bool escapes = pairs || quads;
   const uint32_t kw = bf16 ? c->weights_per_symbol : 1;     // raw bytes per symbol
   SymbolSource src0{*c, w, t, {}};
   if (pairs) src0.set_digits(t->pair_values);
+  QuadMap qm;
+  if (quads) {
+    qm.build(t->tuples, t->n_tuples);
+    src0.qm = &qm;
+  }
+  // symbols per table: 256, or the stored tuples
+  const uint32_t A = quads ? t->n_tuples : 256;
 
   // Section sizes that do not depend on the coded words
-  const uint64_t tables_b = (uint64_t)g.n_tables * sizeof(TableRecord) + (pairs ? kPairDigits : 0);
+  const uint64_t tables_b = (uint64_t)g.n_tables * sizeof(TableRecord) + (pairs ? kPairDigits : 0) +
+                            (quads ? 4ull * c->stored_tuples : 0);
   const uint64_t lut_b = (uint64_t)g.n_tables * M * 8;
   const uint64_t states_b = (uint64_t)g.n_tiles * 64 * 4;
   const uint64_t offsets_b = ((uint64_t)g.n_tiles + 1) * 4;
@@ -514,6 +657,21 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
       });
     max_words += (uint64_t)g.n_tiles * kEscMaskWords + 2 * n_esc.load();
   }
+  if (quads) {
+    std::atomic<uint64_t> n_esc{0};
+    if (w)
+      parallel_for(c->rows, [&](uint64_t r, unsigned) {
+        const int8_t* q = static_cast<const int8_t*>(w) + r * (uint64_t)c->cols;
+        uint64_t n = 0;
+        for (uint32_t j = 0; j < c->cols / 4; ++j) {
+          uint32_t v = 0;
+          for (uint32_t u = 0; u < 4; ++u) v |= (uint32_t)((q[4 * j + u] + 8) & 15) << (4 * u);
+          n += (uint64_t)__builtin_popcount(qm.esc[v]);
+        }
+        n_esc += n;
+      });
+    max_words += (uint64_t)g.n_tiles * kEscMaskWords + 2 * n_esc.load();
+  }
   auto layout = [&](uint64_t n_words, SectionRef* sec) {
     uint64_t pos = kHeaderBytes;
     const uint64_t sizes[kNumSections] = {tables_b, lut_b, states_b, offsets_b,
@@ -533,13 +691,14 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     return ECW_OK;
   }
 
-  // cumulative frequencies
-  std::vector<uint32_t> cum((size_t)g.n_tables * 256, 0);
+  // frequencies and cumulative frequencies, A per table
+  std::vector<uint32_t> fr((size_t)g.n_tables * A, 0), cum((size_t)g.n_tables * A, 0);
   for (uint32_t k = 0; k < g.n_tables; ++k) {
     uint32_t a = 0;
-    for (uint32_t s = 0; s < 256; ++s) {
-      cum[k * 256 + s] = a;
-      a += t->freq[k][s];
+    for (uint32_t s = 0; s < A; ++s) {
+      fr[k * A + s] = quads ? t->tuple_freq[s] : t->freq[k][s];
+      cum[k * A + s] = a;
+      a += fr[k * A + s];
     }
   }
 
@@ -560,7 +719,7 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
       uint32_t r = rg * 64 + l;
       active[l] = r < c->rows;
       if (!active[l]) continue;
-      if (!src.row(r, s0, S, &val[(size_t)l * S], &tbl[(size_t)l * S], nullptr, pairs ? &esc : nullptr, l)) {
+      if (!src.row(r, s0, S, &val[(size_t)l * S], &tbl[(size_t)l * S], nullptr, escapes ? &esc : nullptr, l)) {
         bad_value = true;
         return;
       }
@@ -570,7 +729,7 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
       if (!active[l]) continue;
       for (uint32_t j = 0; j < S; ++j) {
         int32_t s = val[(size_t)l * S + j] - t->value_offset[tbl[(size_t)l * S + j]];
-        if (s < 0 || s > 255) {
+        if (s < 0 || (uint32_t)s >= A) {
           bad_value = true;
           return;
         }
@@ -587,7 +746,7 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
         if (!active[l]) continue;
         const uint32_t tb = tbl[(size_t)l * S + j];
         const uint32_t s = (uint32_t)val[(size_t)l * S + j];
-        const uint64_t f = t->freq[tb][s];
+        const uint64_t f = fr[tb * A + s];
         if (f == 0) {
           bad_freq = true;
           return;
@@ -597,12 +756,12 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
           pushed.push_back((uint16_t)(x[l] & 0xFFFF));
           x[l] >>= 16;
         }
-        x[l] = (x[l] / f) * M + (x[l] % f) + cum[tb * 256 + s];
+        x[l] = (x[l] / f) * M + (x[l] % f) + cum[tb * A + s];
       }
     }
     o.words.assign(pushed.rbegin(), pushed.rend());
     for (int l = 0; l < 64; ++l) o.states[l] = (uint32_t)x[l];
-    if (pairs) {
+    if (escapes) {
       // correction stream after the ANS words: lane mask, then rounds of records
       uint32_t cnt[64] = {0}, first[64] = {0}, rounds = 0;
       uint64_t mask = 0;
@@ -675,6 +834,7 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
   h.tile_rows = c->tile_rows;
   h.tile_cols = c->tile_cols;
   h.recon_dtype = c->recon_dtype;
+  h.stored_tuples = c->stored_tuples;
   h.n_tables = g.n_tables;
   h.n_row_groups = g.n_rg;
   h.n_slices = g.n_sl;
@@ -689,17 +849,18 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
   // TABLES and LUT
   for (uint32_t k = 0; k < g.n_tables; ++k) {
     TableRecord rec{};
-    rec.alphabet = t->alphabet[k];
+    rec.alphabet = quads ? t->n_tuples : t->alphabet[k];
     rec.value_offset = t->value_offset[k];
-    std::memcpy(rec.freq, t->freq[k], sizeof(rec.freq));
+    if (!quads) std::memcpy(rec.freq, t->freq[k], sizeof(rec.freq));
     std::memcpy(out + sec[kSecTables].offset + k * sizeof(TableRecord), &rec, sizeof(rec));
     uint32_t* lut = reinterpret_cast<uint32_t*>(out + sec[kSecLut].offset) + (size_t)k * M * 2;
     uint32_t slot = 0;
-    for (uint32_t s = 0; s < 256; ++s) {
-      const uint32_t f = t->freq[k][s];
-      uint32_t a8, h16;
-      entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], t->pair_values, s, &a8,
-                    &h16);
+    for (uint32_t s = 0; s < A; ++s) {
+      const uint32_t f = fr[k * A + s];
+      uint32_t a8 = 0, h16 = 8 * s;
+      if (!quads)
+        entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], t->pair_values, s, &a8,
+                      &h16);
       for (uint32_t i = 0; i < f; ++i, ++slot) {
         lut[2 * slot] = f | (a8 << 24);
         lut[2 * slot + 1] = i | (h16 << 16);   // bias = slot - cum[s]
@@ -707,6 +868,11 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     }
   }
   if (pairs) std::memcpy(out + sec[kSecTables].offset + g.n_tables * sizeof(TableRecord), t->pair_values, kPairDigits);
+  if (quads) {
+    uint8_t* q = out + sec[kSecTables].offset + sizeof(TableRecord);
+    std::memcpy(q, t->tuples, 2ull * t->n_tuples);
+    std::memcpy(q + 2ull * c->stored_tuples, t->tuple_freq, 2ull * t->n_tuples);
+  }
   // STATES, OFFSETS, WORDS
   uint32_t* states = reinterpret_cast<uint32_t*>(out + sec[kSecStates].offset);
   uint32_t* offs = reinterpret_cast<uint32_t*>(out + sec[kSecOffsets].offset);
@@ -786,7 +952,7 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     return fail(ECW_E_CORRUPT, "bad header size or section count");
   if (h.total_bytes != blob_bytes) return fail(ECW_E_CORRUPT, "blob size does not match header");
   ecw_coding c{h.payload, h.rows, h.cols, h.weights_per_symbol, h.code_bits,
-               h.log2_m, h.tile_rows, h.tile_cols, h.recon_dtype};
+               h.log2_m, h.tile_rows, h.tile_cols, h.recon_dtype, h.stored_tuples};
   ecw_status st = check_coding(&c);
   if (st != ECW_OK) return fail(st == ECW_E_UNSUPPORTED ? ECW_E_UNSUPPORTED : ECW_E_CORRUPT,
                                 std::string("coding: ") + ecw_last_error());
@@ -798,6 +964,8 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
   const uint32_t M = 1u << c.log2_m;
   const bool bf16 = c.payload == ECW_P_BF16_EXP;
   const bool pairs = bf16 && c.weights_per_symbol == 2;
+  const bool quads = quad_coding(c.payload, c.code_bits, c.weights_per_symbol);
+  const bool escapes = pairs || quads;
   const uint32_t kw = bf16 ? c.weights_per_symbol : 1;
   // sections: aligned, in bounds, in order, non-overlapping, exact sizes
   uint64_t raw_b = 0;
@@ -805,7 +973,8 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     for (uint32_t sl = 0; sl < g.n_sl; ++sl)
       raw_b += raw_group_count((sl + 1 == g.n_sl ? g.s_last : g.s_full) * kw) * 1024ull * g.n_rg;
   const uint64_t want[kNumSections] = {
-      (uint64_t)g.n_tables * sizeof(TableRecord) + (pairs ? kPairDigits : 0), (uint64_t)g.n_tables * M * 8,
+      (uint64_t)g.n_tables * sizeof(TableRecord) + (pairs ? kPairDigits : 0) + (quads ? 4ull * c.stored_tuples : 0),
+      (uint64_t)g.n_tables * M * 8,
       (uint64_t)g.n_tiles * 256, ((uint64_t)g.n_tiles + 1) * 4, 0, raw_b,
       bf16 ? 0 : (uint64_t)c.rows * 2};
   uint64_t prev_end = kHeaderBytes;
@@ -827,7 +996,41 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
   }
   std::vector<uint32_t> cum((size_t)g.n_tables * 256);
   std::vector<TableRecord> recs(g.n_tables);
-  for (uint32_t k = 0; k < g.n_tables; ++k) {
+  if (quads) {
+    // stored tuples: n of them, ascending, the zero tuple among them, the rest of
+    // both arrays zero; frequencies summing to M; decode entries as they define
+    TableRecord rec;
+    std::memcpy(&rec, b + h.sec[kSecTables].offset, sizeof(TableRecord));
+    const uint32_t T = c.stored_tuples, n = rec.alphabet;
+    if (n < 1 || n > T) return fail(ECW_E_CORRUPT, "INT quads: stored tuple count out of range");
+    for (uint32_t s = 0; s < 256; ++s)
+      if (rec.freq[s]) return fail(ECW_E_CORRUPT, "INT quads: the 256-symbol frequencies must be zero");
+    std::vector<uint16_t> tup(T), fq(T);
+    std::memcpy(tup.data(), b + h.sec[kSecTables].offset + sizeof(TableRecord), 2ull * T);
+    std::memcpy(fq.data(), b + h.sec[kSecTables].offset + sizeof(TableRecord) + 2ull * T, 2ull * T);
+    bool zero = false;
+    uint64_t sum = 0;
+    for (uint32_t i = 0; i < T; ++i) {
+      if (i >= n) {
+        if (tup[i] || fq[i]) return fail(ECW_E_CORRUPT, "INT quads: entries past the stored tuples must be zero");
+        continue;
+      }
+      if (i && tup[i] <= tup[i - 1]) return fail(ECW_E_CORRUPT, "INT quads: stored tuples not ascending");
+      zero |= tup[i] == kQuadZero;
+      sum += fq[i];
+    }
+    if (!zero) return fail(ECW_E_CORRUPT, "INT quads: the zero tuple is not stored");
+    if (sum != M && !(sum == 0 && g.n_tiles == 0)) return fail(ECW_E_CORRUPT, "tuple frequencies do not sum to M");
+    const uint32_t* lut = reinterpret_cast<const uint32_t*>(b + h.sec[kSecLut].offset);
+    if (sum == M) {
+      uint32_t slot = 0;
+      for (uint32_t s = 0; s < n; ++s)
+        for (uint32_t i = 0; i < fq[s]; ++i, ++slot)
+          if (lut[2 * slot] != fq[s] || lut[2 * slot + 1] != (i | ((8 * s) << 16)))
+            return fail(ECW_E_CORRUPT, "decode table does not match the frequencies");
+    }
+  }
+  for (uint32_t k = 0; k < g.n_tables && !quads; ++k) {
     std::memcpy(&recs[k], b + h.sec[kSecTables].offset + k * sizeof(TableRecord), sizeof(TableRecord));
     const TableRecord& rec = recs[k];
     if (rec.alphabet > 256) return fail(ECW_E_CORRUPT, "alphabet > 256");
@@ -862,11 +1065,12 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     const uint32_t S = (sl + 1 == g.n_sl) ? g.s_last : g.s_full;
     const uint32_t act = std::min<uint32_t>(64, c.rows - rg * 64);
     const uint64_t nwt = (uint64_t)offs[ti + 1] - offs[ti];
-    // at most one ANS word per symbol (BF16 pairs: plus the lane mask and two words
-    // per escaped weight)
-    const uint64_t cap = (uint64_t)act * S + (pairs ? kEscMaskWords + 2ull * act * S * 2 : 0);
+    // at most one ANS word per symbol (escapes: plus the lane mask and two words per
+    // escaped weight)
+    const uint64_t cap = (uint64_t)act * S +
+                         (escapes ? kEscMaskWords + 2ull * act * S * c.weights_per_symbol : 0);
     if (nwt > cap) return fail(ECW_E_CORRUPT, "tile holds more words than symbols");
-    if (pairs && nwt < kEscMaskWords) return fail(ECW_E_CORRUPT, "tile has no correction stream");
+    if (escapes && nwt < kEscMaskWords) return fail(ECW_E_CORRUPT, "tile has no correction stream");
     for (uint32_t l = 0; l < 64; ++l) {
       const uint32_t x = states[(size_t)ti * 64 + l];
       if (l < act ? x < kStateL : x != kStateL)

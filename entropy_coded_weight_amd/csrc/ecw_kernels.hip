@@ -61,9 +61,15 @@ constexpr bool kBfPair = PAY == 2 && KW == 1 && XBF;
 // correction stream.
 template <int PAY, int KW>
 constexpr bool kBfSym2 = PAY == 2 && KW == 2;
+// Quads of 4-bit codes over a table of stored 4-tuples: the entry's high half is the
+// byte offset of the symbol's four codes in a per-block LDS table (two packed 16-bit
+// pairs of the activations' type); escaped codes come from the tile's correction
+// stream.
+template <int PAY, int CB, int KW>
+constexpr bool kQuad = PAY == 1 && CB == 4 && KW == 4;
 // Table entries whose high word is the bias alone (no payload bits beside it).
-template <int PAY, int KW>
-constexpr bool kCleanBias = (PAY == 1 && KW == 4) || (PAY == 2 && KW == 1) || PAY == 4;
+template <int PAY, int CB, int KW>
+constexpr bool kCleanBias = (PAY == 1 && KW == 4 && CB != 4) || (PAY == 2 && KW == 1) || PAY == 4;
 
 #define ECW_LDS __attribute__((address_space(3)))
 template <typename T>
@@ -110,7 +116,8 @@ struct TArgs {
   uint32_t tiles_per_wave, n_sg, n_blocks, syms_per_row;
   uint32_t x_is_bf16, nb, lut_entries, xs_cols, ns, rpb;
   uint32_t raw_full_bytes, raw_rg_bytes;
-  const uint8_t* tables;   // TABLES section (E8 decode-only hook: value offsets)
+  const uint8_t* tables;   // TABLES section (E8 decode-only hook: value offsets; INT quads: stored tuples)
+  uint32_t quad_t;         // INT quads: stored tuples (entries of the LDS tuple table), else 0
 };
 
 // Launch arguments.  The fields a block needs to find its tensor come first, so one
@@ -258,19 +265,30 @@ __device__ __forceinline__ void refill(uint32_t rposb, uint32_t& haveb, uint32_t
   }
 }
 
-// Correction stream of a BF16 exponent-pair tile (MINE page, Section 4.1 "Escapes":
-// escaped weights were coded as 0; their records follow the tile's ANS words).
+// a * b in fp32, kept a separate multiply: fused with a following conversion to fp16
+// the compiler emits a mixed multiply-add with a +0.0 addend, which turns a product
+// of -0.0 into +0.0
+__device__ __forceinline__ float exact_product(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Correction stream of a BF16 exponent-pair or INT quad tile (MINE page, Section 4.1
+// "Escapes": escaped weights were coded as 0; their records follow the tile's ANS
+// words).
 // After the tile's last symbol: every lane reads its bit of the 64-bit lane mask,
 // then the lanes that still hold records read one each per round, at their prefix
 // offset among those lanes (the renormalisation's coordination), and add weight *
 // activation (OUT = kOutAcc), or store the weight (kOutBits: the bf16 bits into
-// w_out; kOutF16 / kOutBf16: the value into deq_out).  Rounds end when every lane
+// w_out; kOutCode: the int8 code into w_out; kOutF16 / kOutBf16: the value, times
+// the row scale with SC, into deq_out).  Rounds end when every lane
 // has read its row's last record, or after `width` rounds (a row has at most
 // `width` escapes) so that a damaged stream still ends.  Records are read as two
 // 16-bit halves, each wrapped into the ring.  col: staged column of the tile's first
 // weight; width: weights per row in the tile; wrow: output index of this row's first
 // weight in the tile.
-constexpr int kOutAcc = 0, kOutBits = 1, kOutF16 = 2, kOutBf16 = 3;
+constexpr int kOutAcc = 0, kOutBits = 1, kOutF16 = 2, kOutBf16 = 3, kOutCode = 4;
 
 // fp32 -> 16-bit float bits, round to nearest even (bf16: finite inputs)
 template <bool OBF>
@@ -283,11 +301,15 @@ __device__ __forceinline__ uint32_t to16(float v) {
   }
 }
 
-template <int B, int OUT, bool XBF>
+// SC: the dense outputs are the record's value times the row scale (INT quads).
+// PKX: activations staged as packed 16-bit pairs [column / 2][B] of the type XBF
+// selects (else fp32 [column][B]).
+template <int B, int OUT, bool XBF, bool SC = false, bool PKX = XBF>
 __device__ __forceinline__ void tile_corrections(const TArgs& a, uint32_t& rposb, uint32_t& haveb, uint32_t& nc,
                                               uint2& pre, uint32_t wl, const uint2* src, uint32_t nch,
                                               uint32_t lane, uint32_t ring, uint32_t xs, uint32_t col,
-                                              uint32_t width, bool active, uint64_t wrow, float* acc) {
+                                              uint32_t width, bool active, uint64_t wrow, float* acc,
+                                              float scale = 1.f) {
   constexpr uint32_t kWrap = 2 * kRing - 2;
   refill(rposb, haveb, nc, pre, wl, src, nch, lane);
   const uint32_t mw = *lds_ptr<const uint16_t>(ring + ((rposb + 2 * (lane >> 4)) & kWrap));
@@ -306,19 +328,24 @@ __device__ __forceinline__ void tile_corrections(const TArgs& a, uint32_t& rposb
       if (c < width) {
         if constexpr (OUT == kOutBits) {
           if (a.w_out) static_cast<uint16_t*>(a.w_out)[wrow + c] = (uint16_t)rec;
-        } else if constexpr (OUT == kOutBf16) {
+        } else if constexpr (OUT == kOutCode) {
+          if (a.w_out) static_cast<int8_t*>(a.w_out)[wrow + c] = (int8_t)(int)__uint_as_float(rec << 16);
+        } else if constexpr (OUT == kOutBf16 && !SC) {
           static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)rec;
-        } else if constexpr (OUT == kOutF16) {
-          static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)to16<false>(__uint_as_float(rec << 16));
+        } else if constexpr (OUT == kOutBf16 || OUT == kOutF16) {
+          float v = __uint_as_float(rec << 16);
+          if constexpr (SC) v = exact_product(v, scale);
+          static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)to16<OUT == kOutBf16>(v);
         } else {
           const float w = __uint_as_float(rec << 16);
 #pragma unroll
           for (int b = 0; b < B; ++b) {
             float xv;
-            if constexpr (XBF) {
+            if constexpr (PKX) {
               // packed pairs [column / 2][B]; the tile starts on an even column
               const uint32_t xw = *lds_ptr<const uint32_t>(xs + (((col + c) >> 1) * B + b) * 4);
-              xv = __uint_as_float((c & 1u) ? (xw & 0xFFFF0000u) : (xw << 16));
+              const uint32_t h = (c & 1u) ? (xw >> 16) : (xw & 0xFFFFu);
+              xv = XBF ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
             } else {
               xv = *lds_ptr<const float>(xs + ((col + c) * B + b) * 4);
             }
@@ -386,7 +413,15 @@ __device__ __forceinline__ void bf16_pair_x(uint32_t addr, uint32_t* xp) {
 // byte, at byte q.
 template <int PAY, int CB, int KW, int B, bool XBF>
 __device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t rdw, int q, float* acc) {
-  if constexpr (kDot<PAY, KW> && !kPairTable<PAY, KW, XBF>) {
+  if constexpr (kQuad<PAY, CB, KW>) {
+    // the stored tuple's codes as two 16-bit pairs, at the entry's byte offset
+    const uint2 wp = lds_load2(e.y >> 16);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      acc[b] = dot2<XBF>(wp.x, xw[b], acc[b]);
+      acc[b] = dot2<XBF>(wp.y, xw[B + b], acc[b]);
+    }
+  } else if constexpr (kDot<PAY, KW> && !kPairTable<PAY, KW, XBF>) {
     // fp16 (q0, q1) = bytes (0, hi8 q0, 0, hi8 q1) from the entry's high half
     const uint32_t wp = __builtin_amdgcn_perm(e.y, e.y, 0x030C020Cu);
 #pragma unroll
@@ -496,11 +531,12 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
                                           uint32_t lane, bool active, float* acc) {
   constexpr int U = 16;
   constexpr bool BF2 = kBfSym2<PAY, KW>;               // bf16 exponent-pair symbols
+  constexpr bool QD = kQuad<PAY, CB, KW>;              // INT quads over stored tuples
   constexpr bool DOT = kDot<PAY, KW> || (BF2 && XBF);
   constexpr bool BFP = kBfPair<PAY, KW, XBF> && !MAT;   // bf16 weight pairs, two steps per dot
   constexpr int RG = BF2 ? 2 : 1;                      // raw 16-byte groups per U steps
   constexpr bool PK = DOT || BFP;                   // activations staged as 16-bit pairs
-  constexpr bool CLEAN = kCleanBias<PAY, KW>;
+  constexpr bool CLEAN = kCleanBias<PAY, CB, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;   // 32-bit activation words per step
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
   const uint32_t row = rg * 64 + lane;
@@ -592,6 +628,10 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
             uint32_t aux = e.x >> 24;
             if constexpr (PAY == 2 && !BF2) aux = ((aux << 1) | (aux >> 7)) & 0xFFu;   // rotated exponent
             uint32_t symbol = aux;
+            if constexpr (QD) {
+              symbol = e.y >> 19;                                   // index of the stored tuple
+              aux = *lds_ptr<const uint32_t>(e.y >> 16);            // its codes' digits
+            }
             int q[KW > 0 ? KW : 1];
             if constexpr (PAY == 1) {
               constexpr int half = 1 << (CB - 1);
@@ -632,10 +672,10 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
         }
       }
     }
-    if constexpr (BF2)
-      tile_corrections<B, MAT ? kOutBits : kOutAcc, XBF>(a, rposb, haveb, nc, pre, wl, src, nch, lane, ring, xs,
-                                                         col, 2 * S, active,
-                                                         (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols, acc);
+    if constexpr (BF2 || QD)
+      tile_corrections<B, MAT ? (QD ? kOutCode : kOutBits) : kOutAcc, XBF, false, PK>(
+          a, rposb, haveb, nc, pre, wl, src, nch, lane, ring, xs, col, KW * S, active,
+          (uint64_t)row * a.cols + (uint64_t)sl * a.tile_cols, acc);
     if constexpr (MAT) {
       const bool ok_lane = !active || x == kStateL;
       const uint64_t bad = __ballot(!ok_lane);
@@ -659,15 +699,6 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
 // tile's stores.  stage: LDS byte address of the wave's tile.
 constexpr uint32_t kStagePitch = 80;       // 64 B of a row segment + 16 B against bank conflicts
 
-// a * b in fp32, kept a separate multiply: fused with a following conversion to fp16
-// the compiler emits a mixed multiply-add with a +0.0 addend, which turns a product
-// of -0.0 into +0.0
-__device__ __forceinline__ float exact_product(float a, float b) {
-  float p = a * b;
-  asm volatile("" : "+v"(p));
-  return p;
-}
-
 template <int PAY, int CB, int KW>
 constexpr int kFlushSteps = KW == 4 ? 8 : 16;   // 32 weights per flush (16 for KW = 1)
 
@@ -680,7 +711,8 @@ __device__ __forceinline__ void wave_body_deq(const TArgs& a, const StreamHead& 
   constexpr int FW = FS * KW;                  // weights per lane per flush: 16 or 32
   constexpr int CPR = FW / 8;                  // 16-byte chunks per row segment: 2 or 4
   constexpr bool BF2 = kBfSym2<PAY, KW>;
-  constexpr bool CLEAN = kCleanBias<PAY, KW>;
+  constexpr bool QD = kQuad<PAY, CB, KW>;
+  constexpr bool CLEAN = kCleanBias<PAY, CB, KW>;
   constexpr int RG = BF2 ? 2 : 1;
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
   const uint32_t row = rg * 64 + lane;
@@ -738,7 +770,8 @@ __device__ __forceinline__ void wave_body_deq(const TArgs& a, const StreamHead& 
           const uint2 e = decode_step<CLEAN>(x, lut, m, mmask);
           uint32_t v[KW];                                   // this step's weights, 16-bit
           if constexpr (PAY == 1) {
-            const uint32_t aux = e.x >> 24;
+            // INT quads: the stored tuple's digits from the block's tuple table
+            const uint32_t aux = QD ? *lds_ptr<const uint32_t>(e.y >> 16) : e.x >> 24;
             constexpr int half = 1 << (CB - 1);
 #pragma unroll
             for (int i = 0; i < KW; ++i) {
@@ -791,14 +824,14 @@ __device__ __forceinline__ void wave_body_deq(const TArgs& a, const StreamHead& 
         }
       }
     }
-    if constexpr (BF2) {
-      // the escaped weights' +0.0 of this tile are in flight: let the stores land
+    if constexpr (BF2 || QD) {
+      // the escaped weights' zeros of this tile are in flight: let the stores land
       // before their corrections overwrite them (other lanes wrote them)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       float acc_unused[1] = {0.f};
-      tile_corrections<1, OBF ? kOutBf16 : kOutF16, false>(a, rposb, haveb, nc, pre, wl, src, nch, lane, ring, 0,
-                                                          0, 2 * S, active, (uint64_t)row * a.cols + colw,
-                                                          acc_unused);
+      tile_corrections<1, OBF ? kOutBf16 : kOutF16, false, QD>(a, rposb, haveb, nc, pre, wl, src, nch, lane, ring,
+                                                              0, 0, KW * S, active, (uint64_t)row * a.cols + colw,
+                                                              acc_unused, scale);
     }
   }
 }
@@ -819,7 +852,7 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
   static_assert(PAY == 1 || PAY == 3, "two row streams per wave: INT codes and FP8 only");
   constexpr int U = 16;
   constexpr bool DOT = kDot<PAY, KW>;
-  constexpr bool CLEAN = kCleanBias<PAY, KW>;
+  constexpr bool CLEAN = kCleanBias<PAY, CB, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;
   const uint32_t m = a.log2m, mmask = (1u << m) - 1u;
 
@@ -1119,7 +1152,8 @@ k_decode(const KArgs ka) {
   // activations staged as packed 16-bit pairs (dot-product paths), else as fp32
   constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, KW, XBF> || (kBfSym2<PAY, KW> && XBF)) && !MAT;
   constexpr bool DEQ = MAT && XBF;
-  constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT;
+  constexpr bool QD = kQuad<PAY, CB, KW>;
+  constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT && !QD;
   const uint32_t W = ka.waves;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -1141,7 +1175,7 @@ k_decode(const KArgs ka) {
   constexpr bool E8 = PAY == 4;
   // streams per wave: 2 = the tiles of two adjacent row groups in lockstep (fused
   // GEMV of INT and FP8 payloads)
-  constexpr bool kTwoCapable = !MAT && !E8 && PAY != 2;
+  constexpr bool kTwoCapable = !MAT && !E8 && PAY != 2 && !QD;
   const uint32_t NSr = (kTwoCapable && a.ns == 2) ? 2u : 1u;
   // the block's slice group and its run of row-group units [u_lo, u_hi); a unit is
   // NSr adjacent row groups, decoded by the waves' streams
@@ -1155,7 +1189,7 @@ k_decode(const KArgs ka) {
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
   constexpr bool E8F8 = E8 && CB == 1;            // E8: CB selects the FP8 reconstruction
-  const uint32_t pair_bytes = PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
+  const uint32_t pair_bytes = QD ? (a.quad_t * 8 + 15) & ~15u : PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
   const uint32_t lut = pair_bytes;
   const uint32_t lut_bytes = a.lut_entries * (E8 ? 4 : 8);
   const uint32_t xs = lut + lut_bytes;
@@ -1254,6 +1288,20 @@ k_decode(const KArgs ka) {
   if constexpr (!MAT) {
     if (tid < nxv) x_store(tid, xv0);
     for (uint32_t v = tid + bd; v < nxv; v += bd) x_store(v, x_load(v));
+  }
+  if constexpr (QD) {
+    // stored tuple i -> its four codes as two packed 16-bit floats of the
+    // activations' type (decode-only kernels: the tuple's digits), at byte 8 i
+    const uint16_t* tup = reinterpret_cast<const uint16_t*>(a.tables + sizeof(TableRecord));
+    for (uint32_t i = tid; i < a.quad_t; i += bd) {
+      const uint32_t v = tup[i];
+      uint2 e = make_uint2(v, 0u);
+      if constexpr (!MAT) {
+        e.x = small_int_bits<XBF>((int)(v & 15) - 8) | (small_int_bits<XBF>((int)((v >> 4) & 15) - 8) << 16);
+        e.y = small_int_bits<XBF>((int)((v >> 8) & 15) - 8) | (small_int_bits<XBF>((int)(v >> 12) - 8) << 16);
+      }
+      lds_store2(i * 8, e);
+    }
   }
   if constexpr (PTAB) {
     // symbol -> its codes as 16-bit floats, packed two per word (digits low first)
@@ -1438,6 +1486,7 @@ static KernelFn pick_kernel(const ecw_coding& c) {
         case 2 * 16 + 1: return k_decode<1, 2, 1, B, MAT, MAT && XBF>;
         case 2 * 16 + 2: return k_decode<1, 2, 2, B, MAT, XBF>;
         case 2 * 16 + 4: return k_decode<1, 2, 4, B, MAT, XBF>;
+        case 4 * 16 + 4: return k_decode<1, 4, 4, B, MAT, XBF>;
       }
       return nullptr;
     case ECW_P_BF16_EXP:
@@ -1461,16 +1510,18 @@ static bool dot_path(const ecw_coding& c, bool xbf) {
   return (c.payload == ECW_P_INT_CODES && c.weights_per_symbol >= 2) || (c.payload == ECW_P_BF16_EXP && xbf);
 }
 static bool pair_table(const ecw_coding& c, bool xbf) {
+  if (quad_coding(c.payload, c.code_bits, c.weights_per_symbol)) return false;
   return c.payload == ECW_P_INT_CODES && (c.weights_per_symbol == 4 || (c.weights_per_symbol == 2 && xbf));
 }
 
 // Two row-group streams per wave: asked for, and built for the payload (INT codes
 // and FP8; E8 and BF16 decode one stream per wave: the BF16 raw bytes of two streams
-// do not fit the 64-register budget beside the decode state, and exponent pairs
-// would need a correction pass per stream).
+// do not fit the 64-register budget beside the decode state, and exponent pairs and
+// INT quads would need a correction pass per stream).
 static bool two_streams(const ecw_tensor* t) {
   const ecw_coding& c = t->coding;
-  return t->streams_per_wave == 2 && c.payload != ECW_P_E8_LATTICE && c.payload != ECW_P_BF16_EXP;
+  return t->streams_per_wave == 2 && c.payload != ECW_P_E8_LATTICE && c.payload != ECW_P_BF16_EXP &&
+         !quad_coding(c.payload, c.code_bits, c.weights_per_symbol);
 }
 
 // Dynamic LDS of one block: pair side table, decode table, staged activations,
@@ -1481,6 +1532,8 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   const bool e8 = t->coding.payload == ECW_P_E8_LATTICE;
   uint64_t pair = (!mat && pair_table(t->coding, xbf)) ? kPairTableBytes : 0;
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
+  if (quad_coding(t->coding.payload, t->coding.code_bits, t->coding.weights_per_symbol))
+    pair = (8ull * t->coding.stored_tuples + 15) / 16 * 16;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
   const bool two = !mat && two_streams(t);
@@ -1520,6 +1573,8 @@ static void fill_tensor(const ecw_tensor* t, TArgs& a) {
   a.raw = base + t->off_raw;
   a.scales = reinterpret_cast<const uint16_t*>(base + t->off_scales);
   a.tables = base + t->off_tables;
+  a.quad_t = quad_coding(t->coding.payload, t->coding.code_bits, t->coding.weights_per_symbol)
+                 ? t->coding.stored_tuples : 0;
   a.rows = t->coding.rows;
   a.cols = t->coding.cols;
   a.n_rg = t->n_row_groups;

@@ -31,8 +31,9 @@
 extern "C" {
 #endif
 
-#define ECW_ABI_VERSION 2u
+#define ECW_ABI_VERSION 3u
 #define ECW_PAIR_DIGITS 16
+#define ECW_MAX_TUPLES 4096
 #define ECW_MAX_TABLES 17
 #define ECW_MAX_ALPHABET 256
 
@@ -62,14 +63,18 @@ typedef enum {
 typedef struct {
   uint32_t payload;            /* ecw_payload */
   uint32_t rows, cols;         /* N (outputs) x K (inputs); W is row-major [N][K] */
-  uint32_t weights_per_symbol; /* k: INT 1|2|4 with code_bits*k <= 8; BF16 1|2; FP8 1;
-                                  E8 8 (BF16 k = 2: cols a multiple of 32, tile_cols
-                                  at most 2048) */
+  uint32_t weights_per_symbol; /* k: INT 1|2|4 with code_bits*k <= 8, or 4 with
+                                  4-bit codes over stored tuples; BF16 1|2; FP8 1;
+                                  E8 8 (BF16 k = 2 and INT quads of 4-bit codes:
+                                  cols a multiple of 32 (quads: 64), tile_cols at
+                                  most 2048) */
   uint32_t code_bits;          /* INT only: 2, 3 or 4; else 0 */
   uint32_t log2_m;             /* table size M = 2^log2_m, 8..13 */
   uint32_t tile_rows;          /* must be 64 (one wave64 lane per row) */
   uint32_t tile_cols;          /* columns per tile: multiple of 64 (and of 8k) */
   uint32_t recon_dtype;        /* E8 only: ECW_DT_I8 (2v) or ECW_DT_FP8_E4M3 (v); else 0 */
+  uint32_t stored_tuples;      /* INT, code_bits 4, k 4 only: t, the 4-tuples of codes
+                                  the table stores, 1 .. min(M, ECW_MAX_TUPLES); else 0 */
 } ecw_coding;
 
 /* Frequency tables of a coding (host POD).  Table 0 serves every payload except
@@ -81,7 +86,15 @@ typedef struct {
  * exponents (ties to the smaller), ascending; pair_values[0] must be 0.  An exponent
  * e != 0 has the first digit d >= 1 with pair_values[d] == e; a weight whose
  * exponent has no digit is escaped: coded as digit 0 with raw byte 0 (+0.0), its
- * bits kept in the tile's correction stream (one 4-byte record). */
+ * bits kept in the tile's correction stream (one 4-byte record).
+ * INT quads (code_bits 4, k = 4; the same passages): a symbol is one of the stored
+ * 4-tuples of codes (digit q + 8 of column 4j + i at bits 4i..4i+3).
+ * enc_build_tables stores the stored_tuples most frequent tuples (ties to the
+ * smaller, the zero tuple 0x8888 always kept in place of the last), ascending.  A
+ * tuple outside the table is coded as the stored tuple reached by setting the
+ * fewest of its codes to 0 (the first such position set in (count, mask) order);
+ * each nonzero code so set is escaped, its record holding the code as a bf16
+ * number. */
 typedef struct {
   uint32_t n_tables;
   uint32_t alphabet[ECW_MAX_TABLES];          /* symbols in use per table (<= 256)   */
@@ -89,7 +102,13 @@ typedef struct {
   uint16_t freq[ECW_MAX_TABLES][ECW_MAX_ALPHABET];   /* f > 0 iff count > 0; sum = M */
   uint64_t count[ECW_MAX_TABLES][ECW_MAX_ALPHABET];  /* histogram the freqs come from */
   uint8_t pair_values[ECW_PAIR_DIGITS];        /* BF16 pairs: exponent of each digit */
-  uint64_t escapes;                            /* BF16 pairs: weights escaped (output) */
+  uint64_t escapes;                            /* pairs / quads: weights escaped (output) */
+  /* INT quads: the stored tuples (ascending; symbol i = tuples[i]), their
+   * frequencies and the histogram of the tuples they code, n_tuples of each */
+  uint32_t n_tuples;
+  uint16_t tuples[ECW_MAX_TUPLES];
+  uint16_t tuple_freq[ECW_MAX_TUPLES];
+  uint64_t tuple_count[ECW_MAX_TUPLES];
 } ecw_tables;
 
 /* Validated, device-ready view of one blob (host POD, filled by dec_prepare). */

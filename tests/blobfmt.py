@@ -11,7 +11,7 @@ SECTIONS = ["tables", "lut", "states", "offsets", "words", "raw", "scales"]
 HEADER_U32 = ["magic", "version", "header_bytes", "n_sections", "payload", "rows", "cols",
               "weights_per_symbol", "code_bits", "log2_m", "tile_rows", "tile_cols",
               "recon_dtype", "n_tables", "n_row_groups", "n_slices", "n_tiles", "steps_full",
-              "steps_last", "lut_entry_bytes", "reserved0", "reserved1"]
+              "steps_last", "lut_entry_bytes", "stored_tuples", "reserved1"]
 
 
 @dataclass
@@ -54,6 +54,19 @@ def pair_values(bl: Blob):
     t = bl.section("tables")
     n = bl.h["n_tables"]
     return t[520 * n: 520 * n + 16].astype(np.int64)
+
+
+def quad_tables(bl: Blob):
+    """INT quads: (stored tuples, their frequencies), the first n of the stored_tuples
+    slots after the table record, n = the record's alphabet (else None)."""
+    T = bl.h["stored_tuples"]
+    if not T:
+        return None
+    t = bl.section("tables")
+    n = int(t[0:4].copy().view(np.uint32)[0])
+    tup = t[520:520 + 2 * T].copy().view(np.uint16).astype(np.int64)
+    fq = t[520 + 2 * T:520 + 4 * T].copy().view(np.uint16).astype(np.int64)
+    return tup[:n], fq[:n], tup[n:], fq[n:]
 
 
 def states(bl: Blob) -> np.ndarray:

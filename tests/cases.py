@@ -29,17 +29,19 @@ class Case:
     scales: np.ndarray | None
     x_dtype: str = "f16"
     recon_dtype: int = 0
+    stored_tuples: int = 0
 
     def oracle_coding(self):
         from oracle import pipeline as P
         return P.Coding(self.payload, self.rows, self.cols, k=self.k, code_bits=self.code_bits,
-                        log2_m=self.log2_m, tile_cols=self.tile_cols, recon_dtype=self.recon_dtype)
+                        log2_m=self.log2_m, tile_cols=self.tile_cols, recon_dtype=self.recon_dtype,
+                        stored_tuples=self.stored_tuples)
 
     def lib_coding(self):
         import entropy_coded_weight_amd as ecw
         return ecw.Coding(self.payload, self.rows, self.cols, self.k,
                           self.code_bits if self.payload == INT else 0, self.log2_m,
-                          self.tile_cols, self.recon_dtype)
+                          self.tile_cols, self.recon_dtype, stored_tuples=self.stored_tuples)
 
 
 def _int(name, rows, cols, k, bits, m, tc, dist="laplace", seed=0):
@@ -91,11 +93,30 @@ def small_cases():
     cases.append(Case("bf16_pairs_mixed_bf16x", BF16, 96, 640, 2, 0, 11, 128, bf16_mixed(96, 640, 2), None, "bf16"))
     cases.append(Case("bf16_pairs_tc2048_m8", BF16, 64, 4096, 2, 0, 8, 2048, bf16_mixed(64, 4096, 3, 0.002), None,
                       "bf16"))
+    cases += quad_cases()
     f = E.fp8_weights((96, 768), np.random.default_rng([0, 400, 1]))
     cases.append(Case("fp8_m12", FP8, 96, 768, 1, 0, 12, 256, f.codes, f.scales, "bf16"))
     f = E.fp8_weights((64, 512), np.random.default_rng([0, 400, 2]))
     cases.append(Case("fp8_m9", FP8, 64, 512, 1, 0, 9, 64, f.codes, f.scales, "bf16"))
     return cases
+
+
+def quad_cases():
+    """Quads of 4-bit codes over stored tuples: a table as large as the tensor's
+    tuples (few escapes), small tables (many escapes, many rounds per tile), a single
+    stored tuple (every nonzero code escaped), bf16 activations, a ragged row group,
+    one-wave blocks, the widest slice the record's column field allows."""
+    def q(name, rows, cols, m, tc, t, seed, x="f16"):
+        c = _int(name, rows, cols, 4, 4, m, tc, seed=seed)
+        c.stored_tuples = t
+        c.x_dtype = x
+        return c
+    return [q("quads_t2048_m12", 130, 512, 12, 256, 2048, 20),
+            q("quads_t64_m10_ragged", 70, 320, 10, 64, 64, 21),
+            q("quads_t1_m8", 64, 128, 8, 128, 1, 22, "bf16"),
+            q("quads_t512_m11_bf16x", 96, 768, 11, 256, 512, 23, "bf16"),
+            q("quads_one_wave", 100, 128, 11, 128, 256, 24),
+            q("quads_tc2048_m13", 64, 4096, 13, 2048, 4096, 25)]
 
 
 def bf16_mixed(rows, cols, seed, frac=0.02):

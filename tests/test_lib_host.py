@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = ecw.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert L.ecw_abi_version() == 2
+    assert L.ecw_abi_version() == 3
 
 
 def test_tile_metadata_bytes_match_page_formula():
@@ -49,6 +49,14 @@ def test_byte_parity_with_oracle_and_oracle_decodes_library_blob(case):
     assert bl.h["magic"] == 0x31574345 and bl.h["version"] == 1
     assert bl.h["total_bytes"] == blob.size
     alphabet, voff, freq = blobfmt.tables(bl)
+    qt = blobfmt.quad_tables(bl)
+    if qt is not None:
+        assert np.array_equal(qt[0], comp.stored) and not qt[2].any() and not qt[3].any()
+        assert not freq.any()
+        n = qt[0].size                          # the oracle's table is at least 256 wide
+        assert not comp.freq[:, n:].any()
+        freq = np.zeros_like(comp.freq)
+        freq[0, :n] = qt[1]
     assert np.array_equal(freq, comp.freq)
     assert np.array_equal(voff, comp.value_offset)
     assert np.array_equal(blobfmt.states(bl), comp.states)
@@ -62,7 +70,8 @@ def test_byte_parity_with_oracle_and_oracle_decodes_library_blob(case):
     comp2 = P.Components(comp.coding, comp.n_tables, alphabet, voff, freq, comp.n_rg, comp.n_sl,
                          comp.s_full, comp.s_last, blobfmt.states(bl), blobfmt.offsets(bl),
                          blobfmt.words(bl), bl.section("raw") if comp.raw is not None else None,
-                         blobfmt.scales(bl), pair_values=blobfmt.pair_values(bl))
+                         blobfmt.scales(bl), pair_values=blobfmt.pair_values(bl),
+                         stored=qt[0] if qt is not None else None)
     if comp.pair_values is not None:
         assert np.array_equal(comp2.pair_values, comp.pair_values)
     _, ok = P.decode_symbols(comp2)
@@ -460,3 +469,80 @@ def test_bf16_pairs_with_fewer_digits_escape_more():
     assert esc.sum() > 1000 and not np.isin(ex, keep).all()
     assert P.decode_symbols(comp)[1].all()
     assert np.array_equal(P.decode(comp), w)
+
+
+# ------------------------------------------------------------------ INT quads over stored tuples
+def test_quad_tables_match_oracle():
+    from oracle import symbols
+    for case in cases.quad_cases():
+        t = ecw.build_tables(case.lib_coding(), case.logical)
+        comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+        n = t.n_tuples
+        assert n == comp.stored.size and t.alphabet[0] == n
+        assert np.array_equal(np.array(t.tuples[:n]), comp.stored)
+        assert np.array_equal(np.array(t.tuple_count[:n]), comp.counts[0, :n])
+        assert np.array_equal(np.array(t.tuple_freq[:n]), comp.freq[0, :n])
+        _, esc = symbols.quad_map(symbols.quad_tuples(case.logical), comp.stored)
+        assert t.escapes == int(esc.sum())
+        assert (t.escapes > 0) == (case.stored_tuples < 1000)
+
+
+def test_quad_entry_payload_is_the_tuple_table_offset():
+    # a8 = 0; h16 = 8 * symbol, the byte offset of the stored tuple's entry in the
+    # per-block table of its four codes
+    case = [c for c in cases.quad_cases() if c.name == "quads_t64_m10_ragged"][0]
+    bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    tup, fq, _, _ = blobfmt.quad_tables(bl)
+    lut = blobfmt.lut(bl)[0]
+    sym = np.repeat(np.arange(tup.size), fq)
+    cum = np.concatenate([[0], np.cumsum(fq)[:-1]])
+    assert np.array_equal(lut[:, 0], fq[sym])
+    assert np.array_equal(lut[:, 1] & 0xFFFF, np.arange(lut.shape[0]) - cum[sym])
+    assert np.array_equal(lut[:, 1] >> 16, 8 * sym)
+
+
+def test_quad_coding_limits_and_validation():
+    L = ecw.lib()
+    w = np.zeros((64, 128), np.int8)
+    bad = [ecw.Coding(ecw.INT_CODES, 64, 128, 4, 4, 10, 64, stored_tuples=0),       # no table
+           ecw.Coding(ecw.INT_CODES, 64, 128, 4, 4, 10, 64, stored_tuples=1025),    # more than M
+           ecw.Coding(ecw.INT_CODES, 64, 128, 4, 4, 13, 64, stored_tuples=4097),    # more than 4096
+           ecw.Coding(ecw.INT_CODES, 64, 128, 2, 4, 10, 64, stored_tuples=16),      # not a quad coding
+           ecw.Coding(ecw.INT_CODES, 64, 4096, 4, 4, 12, 4096, stored_tuples=16)]   # 11-bit record column
+    for c in bad:
+        t = ecw.Tables()
+        assert L.enc_build_tables(ctypes.byref(c), w.ctypes.data_as(ctypes.c_void_p), ctypes.byref(t)) != 0
+    case = [c for c in cases.quad_cases() if c.name == "quads_t64_m10_ragged"][0]
+    t = ecw.build_tables(case.lib_coding(), case.logical)
+    t2 = ecw.build_tables(case.lib_coding(), case.logical)
+    t2.tuples[1], t2.tuples[2] = t2.tuples[2], t2.tuples[1]          # not ascending
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(case.lib_coding(), case.logical, case.scales, t2)
+    t3 = ecw.build_tables(case.lib_coding(), case.logical)
+    i0 = list(t3.tuples[:t3.n_tuples]).index(0x8888)
+    t3.tuples[i0] = 0x8887 if i0 == 0 or t3.tuples[i0 - 1] < 0x8887 else 0x8889
+    with pytest.raises(ecw.EcwError):
+        ecw.encode(case.lib_coding(), case.logical, case.scales, t3)
+    base = ecw.encode(case.lib_coding(), case.logical, case.scales, t)
+    assert _prep_status(base) == 0
+    bl = blobfmt.parse(base)
+    off_t, n_t = bl.sec["tables"]
+    assert n_t == 520 + 4 * 64
+    n = t.n_tuples
+    for mutate in (lambda b: b[off_t + 520: off_t + 524].view(np.uint16).__setitem__(slice(None), [5, 5]),
+                   lambda b: b[off_t: off_t + 4].view(np.uint32).__setitem__(0, 65),         # n > stored_tuples
+                   lambda b: b[off_t + 520 + 128: off_t + 522 + 128].view(np.uint16).__setitem__(0, 1)):
+        b = base.copy()
+        mutate(b)
+        assert _prep_status(b) == 3
+    # fewer stored tuples than slots: the slots past them must stay zero
+    c8 = ecw.Coding(ecw.INT_CODES, 64, 128, 4, 4, 10, 64, stored_tuples=64)
+    w8 = np.zeros((64, 128), np.int8)
+    w8[0, :4] = 1
+    base = ecw.encode(c8, w8, np.ones(64, np.float16))
+    bl = blobfmt.parse(base)
+    off_t, _ = bl.sec["tables"]
+    assert _prep_status(base) == 0 and int(base[off_t: off_t + 4].view(np.uint32)[0]) == 2
+    b = base.copy()
+    b[off_t + 520 + 2 * 63] = 1
+    assert _prep_status(b) == 3
