@@ -39,10 +39,10 @@ LAUNCHES = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]),
 # streams_per_wave, row_groups_per_block).  Used
 # when no tune file exists; `--tune` measures every candidate on the device and
 # writes TUNE_FILE, which later runs load.
-DEFAULT_CODING = {"q": (2, 12, 128, 16, 1, 1, 1), "k": (2, 12, 128, 16, 1, 1, 1),
-                  "v": (2, 12, 128, 16, 1, 1, 1), "o": (2, 12, 128, 16, 1, 1, 1),
-                  "gate": (2, 12, 256, 16, 1, 1, 1), "up": (2, 12, 256, 16, 1, 1, 1),
-                  "down": (2, 12, 256, 16, 1, 1, 1)}
+DEFAULT_CODING = {"q": (2, 12, 128, 16, 1, 1, 1, 0), "k": (2, 12, 128, 16, 1, 1, 1, 0),
+                  "v": (2, 12, 128, 16, 1, 1, 1, 0), "o": (2, 12, 128, 16, 1, 1, 1, 0),
+                  "gate": (2, 12, 256, 16, 1, 1, 1, 0), "up": (2, 12, 256, 16, 1, 1, 1, 0),
+                  "down": (2, 12, 256, 16, 1, 1, 1, 0)}
 TUNE_FILE = os.path.join(ROOT, "entropy_coded_weight_amd", "tuned", "llama8b_int4_laplace_batch1.json")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_llama8b_int4_gate_up_traffic.txt")
 
@@ -55,13 +55,14 @@ def load_coding(path: str):
     coding = dict(DEFAULT_CODING)
     for n, p in d["picks"].items():
         coding[n] = (p["k"], p["log2_m"], p["tile_cols"], p["waves_per_block"], p["tiles_per_wave"],
-                     p.get("streams_per_wave", 1), p.get("row_groups_per_block", 1))
+                     p.get("streams_per_wave", 1), p.get("row_groups_per_block", 1), p.get("stored_tuples", 0))
     return coding, os.path.relpath(path, ROOT)
 
 
 def run_tuner(path: str, batch: int):
-    """Autotune every tensor of the layer set (k in {1, 2}, M in {2^10, 2^11, 2^12},
-    tile width in {64..512}, waves per block, tiles per wave) and write the picks."""
+    """Autotune every tensor of the layer set (k in {1, 2, 4} with quads over stored
+    tuples, M in {2^10, 2^11, 2^12}, tile width in {64..512}, waves per block, tiles
+    per wave, row streams per wave, row groups per block) and write the picks."""
     import torch
     import ecw_inputs as E
     from entropy_coded_weight_amd import autotune as A, INT_CODES
@@ -71,7 +72,7 @@ def run_tuner(path: str, batch: int):
         xs[name] = torch.from_numpy(t.x).cuda()
         specs[name] = (INT_CODES, t.codes, t.scales, 4)
         log(f"tuning {name} {t.codes.shape}")
-        cands[name] = A.tune_tensor(INT_CODES, t.codes, t.scales, xs[name], code_bits=4, ks=(1, 2), log=log)
+        cands[name] = A.tune_tensor(INT_CODES, t.codes, t.scales, xs[name], code_bits=4, ks=(1, 2, 4), log=log)
     picks, fronts = {}, {}
     for ln, names in LAUNCHES:
         log(f"tuning launch {ln}")
@@ -81,7 +82,8 @@ def run_tuner(path: str, batch: int):
         picks.update(g)
         # the launch's speed-size Pareto front over every timed grouping (MINE page, Section 4.2)
         fronts[ln] = [[round(u, 3), int(b), ch] for u, b, ch in A.pareto_front(pts)]
-    table = {n: [dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, stored_bytes=c.stored_bytes,
+    table = {n: [dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, stored_tuples=c.stored_tuples,
+                      stored_bytes=c.stored_bytes,
                       shapes={f"{w}x{r}x{ns}x{p}": round(us, 3) for (w, r, ns, p), us in c.shape_us.items()})
                  for c in cands[n]] for n in ORDER}
     os.makedirs(os.path.dirname(path), exist_ok=True)
@@ -103,9 +105,9 @@ def build_layer(batch: int, coding: dict):
     layer = {}
     for name in ORDER:
         t = E.config2_tensor(name, layer=0, batch=batch)
-        kk, m, tc, W, R, NS, RPB = coding[name]
+        kk, m, tc, W, R, NS, RPB, T = coding[name]
         n, k = t.codes.shape
-        c = ecw.Coding(ecw.INT_CODES, n, k, kk, 4, m, tc)
+        c = ecw.Coding(ecw.INT_CODES, n, k, kk, 4, m, tc, stored_tuples=T)
         blob = ecw.encode(c, t.codes, t.scales)
         layer[name] = dict(tensor=t, coding=c, blob=blob, launch=(W, R, NS, RPB))
     return layer
@@ -133,7 +135,7 @@ def cpu_baseline(layer, target_s: float = 12.0):
                 c = layer[name]["coding"]
                 kk = c.weights_per_symbol
                 ocd = P.Coding(P.INT_CODES, r1 - r0, K, k=kk, code_bits=4, log2_m=c.log2_m,
-                               tile_cols=c.tile_cols)
+                               tile_cols=c.tile_cols, stored_tuples=c.stored_tuples)
                 comp = P.encode(ocd, t.codes[r0:r1], t.scales[r0:r1])
                 t0 = time.perf_counter()
                 q = P.decode(comp)
@@ -286,7 +288,7 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
                               tile_cols=tile_cols, reps=10)
         p = A.pick(cands)
         c = ecw.Coding(payload, w.shape[0], w.shape[1], p["k"], code_bits if payload == ecw.INT_CODES else 0,
-                       p["log2_m"], p["tile_cols"])
+                       p["log2_m"], p["tile_cols"], stored_tuples=p.get("stored_tuples", 0))
         shape = (p["waves_per_block"], p["tiles_per_wave"], p["streams_per_wave"], p["row_groups_per_block"])
         return ecw.encode(c, w, scales), shape, p
 
@@ -488,7 +490,8 @@ def budget_points(steps: int, cold_bytes: float):
                 if n not in tensors:
                     tensors[n] = E.config2_tensor(n)
                 t = tensors[n]
-                c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"])
+                c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"],
+                               stored_tuples=p.get("stored_tuples", 0))
                 tab = ecw.build_tables(c, t.codes)
                 blob = ecw.encode(c, t.codes, t.scales, tab)
                 tt = ecw.prepare(blob)
@@ -538,9 +541,9 @@ def dequant_gemm(steps: int, cold_bytes: float):
     out = {}
     t_int = E.config2_tensor("gate")
     t_bf = E.config3_tensor("gate")
-    kk, m, tc, *_ = coding["gate"]
-    specs = [("int4_gate", ecw.Coding(ecw.INT_CODES, *t_int.codes.shape, kk, 4, m, tc), t_int.codes, t_int.scales,
-              torch.float16),
+    kk, m, tc, *_, T = coding["gate"]
+    specs = [("int4_gate", ecw.Coding(ecw.INT_CODES, *t_int.codes.shape, kk, 4, m, tc, stored_tuples=T), t_int.codes,
+              t_int.scales, torch.float16),
              ("bf16_gate", ecw.Coding(ecw.BF16_EXP, *t_bf.bits.shape, 2, 0, 11, 128), t_bf.bits, None, torch.bfloat16)]
     stream = torch.cuda.current_stream()
 
@@ -813,7 +816,8 @@ def main():
     traffic = int(rec["traffic_bytes"]) if rec and rec.get("launch") == dom else None
     for n in ORDER:
         c = layer[n]["coding"]
-        log(f"{n:5s} {layer[n]['tensor'].codes.shape} m={c.log2_m} tc={c.tile_cols} "
+        log(f"{n:5s} {layer[n]['tensor'].codes.shape} k={c.weights_per_symbol} t={c.stored_tuples} "
+            f"m={c.log2_m} tc={c.tile_cols} "
             f"launch={layer[n]['launch']} stored={stored[n] / 1e6:.3f} MB")
     for ln, names in LAUNCHES:
         log(f"launch {ln:8s} avg={avg_us[ln]:.2f} us  {launch_bytes[ln] / (avg_us[ln] * 1e-6) / 1e9:.0f} GB/s")
@@ -828,6 +832,7 @@ def main():
                                "(q/k/v, o, gate/up, down)",
                    "batch": args.batch, "copies_rotated": copies, "codings_from": coding_src,
                    "codings": {n: dict(k=layer[n]["coding"].weights_per_symbol,
+                                       stored_tuples=layer[n]["coding"].stored_tuples,
                                        log2_m=layer[n]["coding"].log2_m,
                                        tile_cols=layer[n]["coding"].tile_cols,
                                        waves_per_block=layer[n]["launch"][0],

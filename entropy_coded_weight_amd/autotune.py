@@ -36,6 +36,7 @@ class Candidate:
     tile_cols: int
     stored_bytes: int
     shape_us: dict = field(default_factory=dict)     # (W, R, S, P) -> us per call (launchable shapes)
+    stored_tuples: int = 0                           # INT quads: tuples the table stores
 
     def best(self, waves=None):
         items = [(us, s) for s, us in self.shape_us.items() if waves is None or s[0] == waves]
@@ -44,7 +45,8 @@ class Candidate:
 
 def legal_ks(payload: int, code_bits: int, ks=None):
     if payload == INT_CODES:
-        out = [k for k in (1, 2, 4) if code_bits * k <= 8]
+        # 4-bit codes also come in quads over a table of stored tuples (with escapes)
+        out = [k for k in (1, 2, 4) if code_bits * k <= 8 or (code_bits == 4 and k == 4)]
     elif payload == BF16_EXP:
         out = [1, 2]          # exponent pairs, with escapes outside the 16 stored exponents
     else:
@@ -52,17 +54,28 @@ def legal_ks(payload: int, code_bits: int, ks=None):
     return tuple(k for k in out if ks is None or k in ks)
 
 
+def stored_tuples_for(log2_m: int) -> int:
+    """Tuples an INT quad table stores: half the table slots (at most 4096), so the
+    frequent tuples keep fine-grained frequencies; measured on 2.2-bit Laplacian codes
+    it escapes about 0.5% of the codes at M = 2^12."""
+    return min(4096, (1 << log2_m) // 2)
+
+
 def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT_LOG2_M,
                       tile_cols=DEFAULT_TILE_COLS):
-    """Every (k, m, tile width) the format accepts for this tensor."""
+    """Every (k, m, tile width, stored tuples) the format accepts for this tensor
+    (stored tuples: INT quads of 4-bit codes, else 0)."""
     for k in legal_ks(payload, code_bits, ks):
+        quads = payload == INT_CODES and code_bits == 4 and k == 4
         for m in log2_ms:
             for tc in tile_cols:
                 if tc % 64 or tc % (8 * k) or tc > max(64, ((cols + 63) // 64) * 64):
                     continue
                 if payload == BF16_EXP and k == 2 and (cols % 32 or tc > 2048):
                     continue
-                yield k, m, tc
+                if quads and (cols % 64 or tc > 2048):
+                    continue
+                yield k, m, tc, (stored_tuples_for(m) if quads else 0)
 
 
 def _tune_launch(ct: CompressedTensor, x: torch.Tensor, shapes, reps: int, stream: torch.cuda.Stream):
@@ -88,26 +101,27 @@ def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks
     """Search the codings of one logical tensor `w` (host array as enc_encode takes it)
     with activations `x` (device [batch, cols]).  Returns the list of Candidates."""
     rows, cols = w.shape
-    # two row streams per wave exist for INT codes and FP8 only: elsewhere a shape
-    # asking for two runs as one and would only be timed twice
+    # two row streams per wave exist for INT codes and FP8 only (not INT quads):
+    # elsewhere a shape asking for two runs as one and would only be timed twice
+    one_stream = tuple(s for s in shapes if s[2] == 1)
     if payload not in (INT_CODES, FP8_E4M3):
-        shapes = tuple(s for s in shapes if s[2] == 1)
+        shapes = one_stream
     stream = torch.cuda.Stream()
     out = []
-    for k, m, tc in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols):
-        c = Coding(payload, rows, cols, k, code_bits if payload == INT_CODES else 0, m, tc)
+    for k, m, tc, t in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols):
+        c = Coding(payload, rows, cols, k, code_bits if payload == INT_CODES else 0, m, tc, stored_tuples=t)
         try:
             blob = encode(c, w, scales)
         except EcwError:
             continue          # e.g. more distinct symbols than table slots
         ct = CompressedTensor(blob)
-        cand = Candidate(k, m, tc, ct.stored_bytes())
+        cand = Candidate(k, m, tc, ct.stored_bytes(), stored_tuples=t)
         with torch.cuda.stream(stream):
-            cand.shape_us = _tune_launch(ct, x, shapes, reps, stream)
+            cand.shape_us = _tune_launch(ct, x, one_stream if t else shapes, reps, stream)
         stream.synchronize()
         if log:
             us, s = cand.best()
-            log(f"  k={k} m={m} tc={tc:4d} stored={cand.stored_bytes / 1e6:8.3f} MB best {s} {us:8.2f} us")
+            log(f"  k={k} m={m} tc={tc:4d} t={t:4d} stored={cand.stored_bytes / 1e6:8.3f} MB best {s} {us:8.2f} us")
         out.append(cand)
         del ct
     return out
@@ -125,7 +139,8 @@ def pick(cands, waves=None, tie: float = 0.02):
     near.sort(key=lambda v: (v[0], v[1]))
     _, us, s, c = near[0]
     return dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
-                streams_per_wave=s[2], row_groups_per_block=s[3], us=us, stored_bytes=c.stored_bytes)
+                streams_per_wave=s[2], row_groups_per_block=s[3], us=us, stored_bytes=c.stored_bytes,
+                stored_tuples=c.stored_tuples)
 
 
 def time_group(cts, x: torch.Tensor, reps: int = 20, stream: torch.cuda.Stream | None = None) -> float:
@@ -192,11 +207,11 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
     blobs = {}
 
     def tensor_for(name, c, shape):
-        key = (name, c.k, c.log2_m, c.tile_cols)
+        key = (name, c.k, c.log2_m, c.tile_cols, c.stored_tuples)
         if key not in blobs:
             payload, w, scales, cb = specs[name]
             coding = Coding(payload, w.shape[0], w.shape[1], c.k, cb if payload == INT_CODES else 0,
-                            c.log2_m, c.tile_cols)
+                            c.log2_m, c.tile_cols, stored_tuples=c.stored_tuples)
             blobs[key] = encode(coding, w, scales)
         return CompressedTensor(blobs[key], waves_per_block=shape[0], tiles_per_wave=shape[1],
                                 streams_per_wave=shape[2], row_groups_per_block=shape[3])
@@ -230,7 +245,7 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
             if points is not None:
                 points.append((us, nbytes, {n: _pick_dict(c, s, us) for n, (c, s) in zip(names, combo)}))
             if log:
-                log(f"  group W={w}: " + ", ".join(f"{n}:m={c.log2_m},tc={c.tile_cols},R={s[1]},S={s[2]},P={s[3]}"
+                log(f"  group W={w}: " + ", ".join(f"{n}:k={c.k},m={c.log2_m},tc={c.tile_cols},R={s[1]},S={s[2]},P={s[3]}"
                                                    for n, (c, s) in zip(names, combo)) + f" -> {us:.2f} us")
             del cts
     if not results:
@@ -243,7 +258,8 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
 
 def _pick_dict(c: Candidate, s, us: float) -> dict:
     return dict(k=c.k, log2_m=c.log2_m, tile_cols=c.tile_cols, waves_per_block=s[0], tiles_per_wave=s[1],
-                streams_per_wave=s[2], row_groups_per_block=s[3], us=round(us, 3), stored_bytes=c.stored_bytes)
+                streams_per_wave=s[2], row_groups_per_block=s[3], us=round(us, 3), stored_bytes=c.stored_bytes,
+                stored_tuples=c.stored_tuples)
 
 
 # ------------------------------------------------------------------ speed-size trade-off
@@ -287,9 +303,16 @@ def choose_under_budget(fronts: dict, budget: int):
 
 def size_lower_bound_bytes(tables) -> float:
     """Cross-entropy bound of a coding's payload words: sum over symbols of
-    count * log2(M / f) bits, from the histogram and frequencies of its tables."""
+    count * log2(M / f) bits, from the histogram and frequencies of its tables; with
+    escapes (BF16 pairs, INT quads) plus their 4-byte records (MINE page, Section 4.2
+    "Tuning t")."""
     import math
-    total = 0.0
+    if tables.n_tuples:
+        M = sum(int(f) for f in tables.tuple_freq[:tables.n_tuples])
+        bits = sum(int(n) * (math.log2(M) - math.log2(int(f)))
+                   for n, f in zip(tables.tuple_count[:tables.n_tuples], tables.tuple_freq[:tables.n_tuples]) if n)
+        return bits / 8.0 + 4.0 * tables.escapes
+    total = 4.0 * 8.0 * tables.escapes
     M = sum(int(f) for f in tables.freq[0])
     for t in range(tables.n_tables):
         m_t = sum(int(f) for f in tables.freq[t]) or M

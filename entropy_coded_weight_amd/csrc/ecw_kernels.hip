@@ -597,6 +597,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
           for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
         }
         uint32_t ex0 = 0;                 // bf16 pairs: the first step's table word
+        uint2 qwp = {0u, 0u};             // INT quads: this step's codes
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
@@ -621,6 +622,8 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
             } else {
               ex0 = e.x;
             }
+          } else if constexpr (QD && !MAT) {
+            qwp = lds_load2(e.y >> 16);     // multiplied after the renormalisation's ring read
           } else if constexpr (!MAT) {
             mac<PAY, CB, KW, B, XBF>(e, reinterpret_cast<const uint32_t*>(xq) + u4 * XW, rdw, q, acc);
             pin<B>(acc);
@@ -669,6 +672,17 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
             }
           }
           renorm_step<RAGGED>(x, rposb, ring, active);
+          if constexpr (QD && !MAT) {
+            // the stored tuple's codes (two 16-bit pairs) times this step's activations;
+            // their table read overlapped the ring read
+            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xq) + u4 * XW;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+              acc[b] = dot2<XBF>(qwp.x, xw[b], acc[b]);
+              acc[b] = dot2<XBF>(qwp.y, xw[B + b], acc[b]);
+            }
+            pin<B>(acc);
+          }
         }
       }
     }

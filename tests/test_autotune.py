@@ -12,20 +12,24 @@ from tests import cases
 
 def test_candidates_respect_the_format():
     got = list(A.coding_candidates(ecw.INT_CODES, 256, 1024, code_bits=4))
-    # 16-level codes: k = 4 would need 16-bit symbols; tile widths must be multiples
-    # of 64 and of 8k
-    assert {k for k, _, _ in got} == {1, 2}
-    assert all(tc % 64 == 0 for _, _, tc in got)
-    assert len(got) == 2 * 3 * 4
+    # 16-level codes: one or two per symbol, or quads over a table of stored tuples
+    # (half the table's slots); tile widths must be multiples of 64 and of 8k
+    assert {k for k, _, _, _ in got} == {1, 2, 4}
+    assert all(tc % 64 == 0 for _, _, tc, _ in got)
+    assert all(t == (1 << m) // 2 if k == 4 else t == 0 for k, m, _, t in got)
+    assert len(got) == 3 * 3 * 4
     got2 = list(A.coding_candidates(ecw.INT_CODES, 64, 256, code_bits=2, log2_ms=(10,), tile_cols=(64, 128)))
-    assert {k for k, _, _ in got2} == {1, 2, 4}
+    assert {k for k, _, _, _ in got2} == {1, 2, 4} and all(t == 0 for *_, t in got2)
     # tiles wider than the (64-rounded) row are pointless
-    assert all(tc <= 256 for _, _, tc in got2)
+    assert all(tc <= 256 for _, _, tc, _ in got2)
+    # quads: cols a multiple of 64, slices up to 2048 (the record's column field)
+    assert not [c for c in A.coding_candidates(ecw.INT_CODES, 64, 4096, code_bits=4, ks=(4,), tile_cols=(4096,))]
+    assert A.stored_tuples_for(13) == 4096 and A.stored_tuples_for(12) == 2048
     # BF16: one exponent per symbol, or a pair (cols a multiple of 32, slices up to 2048)
-    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256),
-                                                                                                (2, 12, 256)]
-    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 528, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256)]
-    assert list(A.coding_candidates(ecw.FP8_E4M3, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256)]
+    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256, 0),
+                                                                                                (2, 12, 256, 0)]
+    assert list(A.coding_candidates(ecw.BF16_EXP, 64, 528, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256, 0)]
+    assert list(A.coding_candidates(ecw.FP8_E4M3, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256, 0)]
 
 
 def _cand(k, m, tc, nbytes, shapes):
@@ -131,13 +135,21 @@ def test_budget_choice_is_the_exact_knapsack_optimum(seed):
 
 def test_size_lower_bound_is_the_tables_cross_entropy():
     from oracle import coding as OC, pipeline as P
-    for case in cases.small_cases()[:3] + [c for c in cases.small_cases() if c.name == "bf16_pairs_m12"]:
+    # with escapes (MINE page, Section 4.2 "Tuning t"): plus 4 bytes per record
+    names = ("bf16_pairs_m12", "bf16_pairs_mixed_ragged", "quads_t2048_m12", "quads_t64_m10_ragged")
+    escaped = 0
+    for case in cases.small_cases()[:3] + [c for c in cases.small_cases() if c.name in names]:
         t = ecw.build_tables(case.lib_coding(), case.logical)
         lb = A.size_lower_bound_bytes(t)
         comp = P.encode(case.oracle_coding(), case.logical, case.scales)
-        assert lb == pytest.approx(OC.cross_entropy_total_bits(comp.counts[0], comp.freq[0], case.log2_m) / 8,
-                                   rel=1e-12)
+        _, _, corr = P._decode_all(comp)
+        n_rec = sum(len(r) for lanes in corr.values() for r in lanes)
+        assert n_rec == t.escapes
+        escaped += n_rec
+        assert lb == pytest.approx(OC.cross_entropy_total_bits(comp.counts[0], comp.freq[0], case.log2_m) / 8
+                                   + 4 * n_rec, rel=1e-12)
         # the final states carry the last bits of information: the bound holds for the
         # words plus the tile metadata
         tt = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales, t))
         assert lb <= tt.bytes_words + tt.bytes_tile_meta
+    assert escaped > 0

@@ -59,7 +59,8 @@ def test_config2_layer_set_at_the_benchmarked_launches():
         for n in names:
             t = E.config2_tensor(n)
             p = tune[n]
-            c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"])
+            c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"],
+                           stored_tuples=p.get("stored_tuples", 0))
             cts.append(ecw.CompressedTensor(ecw.encode(c, t.codes, t.scales), waves_per_block=p["waves_per_block"],
                                             tiles_per_wave=p["tiles_per_wave"],
                                             streams_per_wave=p.get("streams_per_wave", 1),
@@ -135,7 +136,8 @@ def test_dequantize_full_size_sampled_rows(which):
         t = E.config2_tensor("gate")
         p = json.load(open(os.path.join(ROOT, "entropy_coded_weight_amd", "tuned",
                                         "llama8b_int4_laplace_batch1.json")))["picks"]["gate"]
-        c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"])
+        c = ecw.Coding(ecw.INT_CODES, *t.codes.shape, p["k"], 4, p["log2_m"], p["tile_cols"],
+                       stored_tuples=p.get("stored_tuples", 0))
         logical, scales, tdt, dname = t.codes, t.scales, torch.float16, "f16"
         oc = P.Coding(P.INT_CODES, *t.codes.shape, k=p["k"], code_bits=4, log2_m=p["log2_m"],
                       tile_cols=p["tile_cols"])
