@@ -184,8 +184,9 @@ def _ranked(cands, waves, top):
 
 def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | None = None, reps: int = 20,
                tie: float = 0.02, log=None, points: list | None = None):
-    """Tensors sharing one launch (same activations) must share waves per block.  For
-    each common waves-per-block value, every combination of each member's `top`
+    """Tensors sharing one launch (same activations) must share waves per block and
+    codes per symbol.  For each common (waves per block, codes per symbol), every
+    combination of each member's `top`
     fastest single-tensor candidates at that value, and every launch shape all
     members can take (each with its fastest coding at that shape), is timed as the
     real grouped launch; the fastest group wins (ties within `tie`: fewer stored
@@ -217,8 +218,11 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
                                 streams_per_wave=shape[2], row_groups_per_block=shape[3])
 
     results = []
-    for w in waves:
-        ranked = [_ranked(cands_by_name[n], w, top) for n in names]
+    # one launch runs one kernel: its members share the codes per symbol
+    ks = sorted(set.intersection(*[{c.k for c in cands_by_name[n]} for n in names]))
+    for w, k in itertools.product(waves, ks):
+        of_k = {n: [c for c in cands_by_name[n] if c.k == k] for n in names}
+        ranked = [_ranked(of_k[n], w, top) for n in names]
         if any(not r for r in ranked):
             continue
         combos = list(itertools.product(*ranked))
@@ -226,12 +230,11 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
         # no member ranks high alone (e.g. more tiles per wave, to keep every wave of
         # the launch resident at once): also try each shape common to all members,
         # each member with its fastest coding at that shape.
-        shapes = set.intersection(*[{s for c in cands_by_name[n] for s in c.shape_us if s[0] == w}
-                                    for n in names])
+        shapes = set.intersection(*[{s for c in of_k[n] for s in c.shape_us if s[0] == w} for n in names])
         for shape in sorted(shapes):
             combo = []
             for n in names:
-                best = min(((c.shape_us[shape], c.stored_bytes, id(c), c) for c in cands_by_name[n]
+                best = min(((c.shape_us[shape], c.stored_bytes, id(c), c) for c in of_k[n]
                             if shape in c.shape_us), default=None)
                 combo.append((best[3], shape))
             combo = tuple(combo)
