@@ -516,7 +516,7 @@ def budget_points(steps: int, cold_bytes: float):
                     "per_launch_us": {k: round(v, 3) for k, v in us.items()},
                     "payload_words_bytes": int(words), "payload_lower_bound_bytes": int(bound),
                     "words_over_bound": round(words / bound, 5), "parity_worst_err_over_bound": worst,
-                    "codings": {n: {k: p[k] for k in ("k", "log2_m", "tile_cols", "waves_per_block",
+                    "codings": {n: {k: p.get(k, 0) for k in ("k", "stored_tuples", "log2_m", "tile_cols", "waves_per_block",
                                                       "tiles_per_wave", "streams_per_wave",
                                                       "row_groups_per_block")}
                                 for ch in choice.values() for n, p in ch.items()}})
