@@ -413,15 +413,8 @@ __device__ __forceinline__ void bf16_pair_x(uint32_t addr, uint32_t* xp) {
 // byte, at byte q.
 template <int PAY, int CB, int KW, int B, bool XBF>
 __device__ __forceinline__ void mac(const uint2 e, const uint32_t* xw, uint32_t rdw, int q, float* acc) {
-  if constexpr (kQuad<PAY, CB, KW>) {
-    // the stored tuple's codes as two 16-bit pairs, at the entry's byte offset
-    const uint2 wp = lds_load2(e.y >> 16);
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      acc[b] = dot2<XBF>(wp.x, xw[b], acc[b]);
-      acc[b] = dot2<XBF>(wp.y, xw[B + b], acc[b]);
-    }
-  } else if constexpr (kDot<PAY, KW> && !kPairTable<PAY, KW, XBF>) {
+  static_assert(!kQuad<PAY, CB, KW>, "INT quads multiply in wave_body, after the renormalisation");
+  if constexpr (kDot<PAY, KW> && !kPairTable<PAY, KW, XBF>) {
     // fp16 (q0, q1) = bytes (0, hi8 q0, 0, hi8 q1) from the entry's high half
     const uint32_t wp = __builtin_amdgcn_perm(e.y, e.y, 0x030C020Cu);
 #pragma unroll
@@ -1645,9 +1638,12 @@ static ecw_status check_group(const ecw_tensor* const* ts, int n, int batch, int
     ecw_status st = check_tensor(ts[i]);
     if (st != ECW_OK) return st;
     const ecw_coding& c = ts[i]->coding, &c0 = ts[0]->coding;
+    // one kernel serves the launch: its template follows payload, code width, codes
+    // per symbol and (lattice fields) the reconstruction route
     if (c.payload != c0.payload || c.code_bits != c0.code_bits || c.weights_per_symbol != c0.weights_per_symbol ||
-        c.cols != c0.cols || ts[i]->waves_per_block != ts[0]->waves_per_block)
-      return fail(ECW_E_INVALID_ARG, "grouped tensors must share payload, code width, cols and waves per block");
+        c.recon_dtype != c0.recon_dtype || c.cols != c0.cols || ts[i]->waves_per_block != ts[0]->waves_per_block)
+      return fail(ECW_E_INVALID_ARG, "grouped tensors must share payload, code width, codes per symbol, "
+                                     "reconstruction, cols and waves per block");
     if (c.rows && (!ys[i] || reinterpret_cast<uintptr_t>(ys[i]) % 16))
       return fail(ECW_E_INVALID_ARG, "y must be a 16-byte aligned device pointer");
   }

@@ -207,9 +207,9 @@ ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const void* x, int x
 /* Grouped launch: several tensors that read the same activations, decoded and
  * multiplied in one kernel launch (MINE page, Section 4.2 "Launch": sections with
  * the same input dimension and quantisation share a launch, e.g. q/k/v and
- * gate/up).  t[0..n): 1 <= n <= 8 tensors with the same payload, code width, cols
- * and waves_per_block (each keeps its own table size, tile width and tiles per
- * wave); y[i]: device fp32 [batch][t[i]->coding.rows].  x, batch, workspace as for
+ * gate/up).  t[0..n): 1 <= n <= 8 tensors with the same payload, code width, codes
+ * per symbol, reconstruction dtype, cols and waves_per_block (each keeps its own
+ * table size, stored tuples, tile width and tiles per wave); y[i]: device fp32 [batch][t[i]->coding.rows].  x, batch, workspace as for
  * dec_gemv; the workspace size comes from dec_gemv_group_workspace_size.  Results
  * are bit-identical to separate dec_gemv calls with the same launch shapes.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
@@ -258,9 +258,12 @@ ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t ent
                                 uint32_t blocks, uint32_t waves_per_block, uint32_t* sink);
 
 /* Test hook: the same decode core, writing what dec_gemv keeps in registers.
- *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices);
+ *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices; INT
+ *          quads: the index of the stored tuple the symbol codes);
  *   w_out: nullable device [rows][cols] in the logical dtype (INT int8 codes, BF16
- *          uint16 bits, FP8 uint8 bytes, E8 int8 2v or uint8 e4m3 per recon_dtype);
+ *          uint16 bits, FP8 uint8 bytes, E8 int8 2v or uint8 e4m3 per recon_dtype),
+ *          escaped weights (BF16 pairs, INT quads) restored from the correction
+ *          streams;
  *   tile_status: nullable device uint32 [n_tiles], 0 when the tile ended with every
  *          active state back at 2^16 and exactly its words read, else nonzero.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */

@@ -356,6 +356,20 @@ def test_group_rejects_mismatched_tensors_without_launching():
     assert L.dec_gemv_group(None, arr, 9, 256, 1, ys, 1, None, 0) == 1
     n = ctypes.c_size_t()
     assert L.dec_gemv_group_workspace_size(arr, 2, 1, ctypes.byref(n)) == 0
+    # one kernel serves a launch: codes per symbol and the lattice reconstruction
+    # route must match too
+    for pair in ((cases.small_cases()[1], _retile(cases.small_cases()[1], k=1)),
+                 (cases.e8_case(4), cases.e8_case(5))):
+        ts = [ecw.prepare(ecw.encode(c.lib_coding(), c.logical, c.scales)) for c in pair]
+        for t in ts:
+            t.device_blob = 256
+        assert L.dec_gemv_group(None, ecw._tensor_array(ts), 2, 256, 1, ys, 1, None, 0) == 1
+        assert "codes per symbol" in L.ecw_last_error().decode()
+
+
+def _retile(case, k):
+    import dataclasses
+    return dataclasses.replace(case, k=k)
 
 
 def test_probe_entry_points_reject_bad_arguments():
