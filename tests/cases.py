@@ -105,7 +105,8 @@ def quad_cases():
     """Quads of 4-bit codes over stored tuples: a table as large as the tensor's
     tuples (few escapes), small tables (many escapes, many rounds per tile), a single
     stored tuple (every nonzero code escaped), bf16 activations, a ragged row group,
-    one-wave blocks, the widest slice the record's column field allows."""
+    one-wave blocks, the widest slice the record's column field allows, and many
+    slices per row group under the largest tables the tuner uses."""
     def q(name, rows, cols, m, tc, t, seed, x="f16"):
         c = _int(name, rows, cols, 4, 4, m, tc, seed=seed)
         c.stored_tuples = t
@@ -116,7 +117,9 @@ def quad_cases():
             q("quads_t1_m8", 64, 128, 8, 128, 1, 22, "bf16"),
             q("quads_t512_m11_bf16x", 96, 768, 11, 256, 512, 23, "bf16"),
             q("quads_one_wave", 100, 128, 11, 128, 256, 24),
-            q("quads_tc2048_m13", 64, 4096, 13, 2048, 4096, 25)]
+            q("quads_tc2048_m13", 64, 4096, 13, 2048, 4096, 25),
+            # 16 slices of a ragged row group, 48 KiB of tables
+            q("quads_16_slices_m12", 70, 1024, 12, 64, 2048, 26)]
 
 
 def bf16_mixed(rows, cols, seed, frac=0.02):
