@@ -187,29 +187,26 @@ def quad_map(tuples: np.ndarray, stored: np.ndarray):
     """Tuples [N, n] -> (symbol ids int64 [N, n], escaped bool [N, 4n]).  A stored
     tuple is its own symbol; any other is coded as the stored tuple reached by
     setting some of its codes to 0, taking the first such set of positions in
-    QUAD_MASKS order; its nonzero codes so set are escaped."""
+    QUAD_MASKS order; its nonzero codes so set are escaped.  (Each distinct tuple is
+    mapped once.)"""
     tu = np.asarray(tuples, dtype=np.int64)
     index = {int(v): i for i, v in enumerate(stored)}
-    ids = np.zeros(tu.shape, dtype=np.int64)
-    esc = np.zeros((tu.shape[0], 4 * tu.shape[1]), dtype=bool)
-    memo = {}
-    for (r, j), v in np.ndenumerate(tu):
-        v = int(v)
-        if v not in memo:
-            if v in index:
-                memo[v] = (index[v], 0)
-            else:
-                for m in QUAD_MASKS:
-                    z = _zeroed(v, m)
-                    if z in index:
-                        memo[v] = (index[z], m)
-                        break
-        i, m = memo[v]
-        ids[r, j] = i
-        for p in range(4):
-            if (m >> p) & 1 and ((v >> (4 * p)) & 15) != 8:
-                esc[r, 4 * j + p] = True
-    return ids, esc
+    uniq, inv = np.unique(tu, return_inverse=True)
+    ids_u = np.zeros(uniq.size, dtype=np.int64)
+    esc_u = np.zeros((uniq.size, 4), dtype=bool)
+    for n, v in enumerate(uniq.tolist()):
+        if v in index:
+            ids_u[n] = index[v]
+            continue
+        for m in QUAD_MASKS:
+            z = _zeroed(v, m)
+            if z in index:
+                ids_u[n] = index[z]
+                for p in range(4):
+                    esc_u[n, p] = bool((m >> p) & 1) and ((v >> (4 * p)) & 15) != 8
+                break
+    inv = inv.reshape(tu.shape)
+    return ids_u[inv], esc_u[inv].reshape(tu.shape[0], 4 * tu.shape[1])
 
 
 def quad_join(ids: np.ndarray, stored: np.ndarray) -> np.ndarray:
