@@ -164,50 +164,9 @@ def check_rows(y: np.ndarray, w_rows: np.ndarray, x: np.ndarray) -> float:
 
 
 def time_cold(launches, batch: int, steps: int, cold_bytes: float):
-    """Device microseconds per launch, cold: every launch is a group of compressed
-    tensors sharing x; blobs are rotated over >= cold_bytes of device copies, and
-    each launch is captured as one graph over all copies and replayed.
-    launches: [(name, [(blob, (W, R, S, P)), ...], x_dev)].  Returns
-    ({name: us}, {name: [y of the last copy per tensor]})."""
-    import torch
-    import entropy_coded_weight_amd as ecw
-    total = sum(ecw.prepare(b).blob_bytes for _, members, _ in launches for b, _ in members)
-    copies = max(2, int(np.ceil(cold_bytes / max(total, 1))))
-    stream = torch.cuda.current_stream()
-    us, outs = {}, {}
-    for name, members, x in launches:
-        groups, wss = [], []
-        for _ in range(copies):
-            cts = []
-            for blob, shape in members:
-                ct = ecw.CompressedTensor(blob)
-                ct.set_launch(*shape)
-                cts.append(ct)
-            g = ecw.GemvGroup(cts)
-            groups.append(g)
-            wss.append(g.workspace(batch))
-        ys = [torch.empty((batch, ct.rows), dtype=torch.float32, device=x.device) for ct in groups[0].tensors]
-        for c in range(copies):
-            ecw.gemv_group_raw([ct.t for ct in groups[c].tensors], x, ys, wss[c])
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in range(copies):
-                ecw.gemv_group_raw([ct.t for ct in groups[c].tensors], x, ys, wss[c])
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(2, steps // copies)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us[name] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-        outs[name] = [y.cpu().numpy() for y in ys]
-        del g, groups, wss
-    return us, outs
+    """Cold device timing of grouped launches (autotune.time_cold)."""
+    from entropy_coded_weight_amd import autotune as A
+    return A.time_cold(launches, batch, steps, cold_bytes)
 
 
 def _rows(n, k=256, seed=1):
@@ -421,7 +380,7 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
                         cands[n] = A.tune_tensor(ecw.FP8_E4M3, t.codes, t.scales, x, log2_ms=(p1["log2_m"],),
                                                  tile_cols=(p1["tile_cols"],), reps=10)
                 specs = {n: (ecw.FP8_E4M3, ts[n].codes, ts[n].scales, 0) for n in ns}
-                g = A.tune_group(specs, {n: cands[n] for n in ns}, x, reps=10)
+                g = A.tune_group(specs, {n: cands[n] for n in ns}, x, cold=False, reps=10)
                 picks.update(g)
             launches, nbytes, nw = [], 0, 0
             for ln, ns in groups:

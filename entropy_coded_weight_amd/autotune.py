@@ -16,6 +16,7 @@ single-tensor candidates at each common value.
 from __future__ import annotations
 
 import ctypes
+import math
 from dataclasses import dataclass, field
 
 import torch
@@ -54,11 +55,13 @@ def legal_ks(payload: int, code_bits: int, ks=None):
     return tuple(k for k in out if ks is None or k in ks)
 
 
-def stored_tuples_for(log2_m: int) -> int:
-    """Tuples an INT quad table stores: half the table slots (at most 4096), so the
-    frequent tuples keep fine-grained frequencies; measured on 2.2-bit Laplacian codes
-    it escapes about 0.5% of the codes at M = 2^12."""
-    return min(4096, (1 << log2_m) // 2)
+def stored_tuples_for(log2_m: int) -> tuple:
+    """Tuple counts t an INT quad table may store (MINE page, Section 4.2 "Tuning t":
+    more stored tuples mean fewer escapes but coarser frequencies): a quarter, half
+    and three quarters of the table slots, at most 4096.  On 2.2-bit Laplacian codes
+    at M = 2^12, half the slots escape about 0.5% of the codes."""
+    M = 1 << log2_m
+    return tuple(sorted({min(4096, M // 4), min(4096, M // 2), min(4096, 3 * M // 4)}))
 
 
 def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT_LOG2_M,
@@ -75,7 +78,8 @@ def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT
                     continue
                 if quads and (cols % 64 or tc > 2048):
                     continue
-                yield k, m, tc, (stored_tuples_for(m) if quads else 0)
+                for t in (stored_tuples_for(m) if quads else (0,)):
+                    yield k, m, tc, t
 
 
 def _tune_launch(ct: CompressedTensor, x: torch.Tensor, shapes, reps: int, stream: torch.cuda.Stream):
@@ -164,6 +168,52 @@ def time_group(cts, x: torch.Tensor, reps: int = 20, stream: torch.cuda.Stream |
     return us.value
 
 
+def time_cold(launches, batch: int, steps: int, cold_bytes: float = 512e6):
+    """Device microseconds per launch, cold: every launch is a group of compressed
+    tensors sharing x; blobs are rotated over >= cold_bytes of device copies, and
+    each launch is captured as one graph over all copies and replayed.
+    launches: [(name, [(blob, (W, R, S, P)), ...], x_dev)].  Returns
+    ({name: us}, {name: [y of the last copy per tensor]})."""
+    from . import CompressedTensor, GemvGroup, gemv_group_raw, prepare
+    total = sum(prepare(b).blob_bytes for _, members, _ in launches for b, _ in members)
+    copies = max(2, int(math.ceil(cold_bytes / max(total, 1))))
+    stream = torch.cuda.current_stream()
+    us, outs = {}, {}
+    for name, members, x in launches:
+        groups, wss = [], []
+        for _ in range(copies):
+            cts = []
+            for blob, shape in members:
+                ct = CompressedTensor(blob)
+                ct.set_launch(*shape)
+                cts.append(ct)
+            g = GemvGroup(cts)
+            groups.append(g)
+            wss.append(g.workspace(batch))
+        ys = [torch.empty((batch, ct.rows), dtype=torch.float32, device=x.device) for ct in groups[0].tensors]
+        for c in range(copies):
+            gemv_group_raw([ct.t for ct in groups[c].tensors], x, ys, wss[c])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(copies):
+                gemv_group_raw([ct.t for ct in groups[c].tensors], x, ys, wss[c])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, steps // copies)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+        outs[name] = [y.cpu().numpy() for y in ys]
+        del g, groups, wss
+    return us, outs
+
+
 def _ranked(cands, waves, top):
     """The `top` fastest (candidate, shape) pairs at a given waves per block."""
     items = []
@@ -182,40 +232,43 @@ def _ranked(cands, waves, top):
     return out
 
 
-def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | None = None, reps: int = 20,
-               tie: float = 0.02, log=None, points: list | None = None):
+def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | None = None,
+               tie: float = 0.02, log=None, points: list | None = None, cold: bool = True,
+               cold_bytes: float = 512e6, cold_steps: int = 200, reps: int = 20):
     """Tensors sharing one launch (same activations) must share waves per block and
     codes per symbol.  For each common (waves per block, codes per symbol), every
-    combination of each member's `top`
-    fastest single-tensor candidates at that value, and every launch shape all
-    members can take (each with its fastest coding at that shape), is timed as the
-    real grouped launch; the fastest group wins (ties within `tie`: fewer stored
-    bytes).
+    combination of each member's `top` fastest single-tensor candidates at that
+    value (timed warm by tune_tensor), and every launch shape all members can take
+    (each with its fastest coding at that shape), is timed as the real grouped launch
+    and cold (time_cold over cold_bytes of rotated copies); the fastest group wins
+    (ties within `tie`: fewer stored bytes).  A launch of one tensor is searched the
+    same way.  cold=False: groups are timed warm (time_group, `reps` graph replays of
+    one copy) and a one-tensor launch takes its fastest warm candidate (a quicker
+    search for secondary workloads).
     specs[name] = (payload, w, scales, code_bits) re-encodes a candidate.  By default
     `top` keeps the number of timed combinations near 16 per waves-per-block value.
     points: if given, every timed group is appended as (us, stored bytes, picks), the
-    material of the group's speed-size Pareto front."""
+    material of the launch's speed-size Pareto front."""
     import itertools
     names = list(cands_by_name)
     if top is None:
         top = {1: 16, 2: 4, 3: 2}.get(len(names), 1)
-    if len(names) == 1:
+    if len(names) == 1 and not cold:
         if points is not None:
             points.extend((us, nbytes, {names[0]: p}) for us, nbytes, p in tensor_points(cands_by_name[names[0]]))
         return {names[0]: pick(cands_by_name[names[0]], tie=tie)}
     waves = sorted({s[0] for n in names for c in cands_by_name[n] for s in c.shape_us})
-    stream = torch.cuda.Stream()
     blobs = {}
+    stream = torch.cuda.Stream()
 
-    def tensor_for(name, c, shape):
+    def blob_for(name, c):
         key = (name, c.k, c.log2_m, c.tile_cols, c.stored_tuples)
         if key not in blobs:
             payload, w, scales, cb = specs[name]
             coding = Coding(payload, w.shape[0], w.shape[1], c.k, cb if payload == INT_CODES else 0,
                             c.log2_m, c.tile_cols, stored_tuples=c.stored_tuples)
             blobs[key] = encode(coding, w, scales)
-        return CompressedTensor(blobs[key], waves_per_block=shape[0], tiles_per_wave=shape[1],
-                                streams_per_wave=shape[2], row_groups_per_block=shape[3])
+        return blobs[key]
 
     results = []
     # one launch runs one kernel: its members share the codes per symbol
@@ -241,8 +294,17 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
             if combo not in combos:
                 combos.append(combo)
         for combo in combos:
-            cts = [tensor_for(n, c, s) for n, (c, s) in zip(names, combo)]
-            us = time_group(cts, x, reps, stream)
+            # timed cold, as the launch runs when serving: the members' blobs rotated
+            # over >= cold_bytes of device copies (MINE page, Section 4.2: cold-cache
+            # measurements, the kernel reproduced until the cache is filled twice)
+            members = [(blob_for(n, c), s) for n, (c, s) in zip(names, combo)]
+            if cold:
+                us = time_cold([("g", members, x)], x.shape[0], cold_steps, cold_bytes)[0]["g"]
+            else:
+                cts = [CompressedTensor(b, waves_per_block=s[0], tiles_per_wave=s[1], streams_per_wave=s[2],
+                                        row_groups_per_block=s[3]) for b, s in members]
+                us = time_group(cts, x, reps, stream)
+                del cts
             nbytes = sum(c.stored_bytes for c, _ in combo)
             results.append((us, nbytes, combo))
             if points is not None:
@@ -250,7 +312,6 @@ def tune_group(specs: dict, cands_by_name: dict, x: torch.Tensor, top: int | Non
             if log:
                 log(f"  group W={w}: " + ", ".join(f"{n}:k={c.k},m={c.log2_m},tc={c.tile_cols},R={s[1]},S={s[2]},P={s[3]}"
                                                    for n, (c, s) in zip(names, combo)) + f" -> {us:.2f} us")
-            del cts
     if not results:
         return None
     t_min = min(r[0] for r in results)

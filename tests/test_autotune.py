@@ -13,18 +13,19 @@ from tests import cases
 def test_candidates_respect_the_format():
     got = list(A.coding_candidates(ecw.INT_CODES, 256, 1024, code_bits=4))
     # 16-level codes: one or two per symbol, or quads over a table of stored tuples
-    # (half the table's slots); tile widths must be multiples of 64 and of 8k
+    # (a quarter, half or three quarters of the table's slots); tile widths must be
+    # multiples of 64 and of 8k
     assert {k for k, _, _, _ in got} == {1, 2, 4}
     assert all(tc % 64 == 0 for _, _, tc, _ in got)
-    assert all(t == (1 << m) // 2 if k == 4 else t == 0 for k, m, _, t in got)
-    assert len(got) == 3 * 3 * 4
+    assert all(t in ((1 << m) // 4, (1 << m) // 2, 3 * (1 << m) // 4) if k == 4 else t == 0 for k, m, _, t in got)
+    assert len(got) == 2 * 3 * 4 + 3 * 3 * 4
     got2 = list(A.coding_candidates(ecw.INT_CODES, 64, 256, code_bits=2, log2_ms=(10,), tile_cols=(64, 128)))
     assert {k for k, _, _, _ in got2} == {1, 2, 4} and all(t == 0 for *_, t in got2)
     # tiles wider than the (64-rounded) row are pointless
     assert all(tc <= 256 for _, _, tc, _ in got2)
     # quads: cols a multiple of 64, slices up to 2048 (the record's column field)
     assert not [c for c in A.coding_candidates(ecw.INT_CODES, 64, 4096, code_bits=4, ks=(4,), tile_cols=(4096,))]
-    assert A.stored_tuples_for(13) == 4096 and A.stored_tuples_for(12) == 2048
+    assert A.stored_tuples_for(13) == (2048, 4096) and A.stored_tuples_for(12) == (1024, 2048, 3072)
     # BF16: one exponent per symbol, or a pair (cols a multiple of 32, slices up to 2048)
     assert list(A.coding_candidates(ecw.BF16_EXP, 64, 512, log2_ms=(12,), tile_cols=(256,))) == [(1, 12, 256, 0),
                                                                                                 (2, 12, 256, 0)]
@@ -81,7 +82,7 @@ def test_device_tuning_picks_a_shape_that_stays_correct():
     # a two-member group of the same tensor shares one waves-per-block value
     g = A.tune_group({"a": (ecw.INT_CODES, case.logical, case.scales, 4),
                       "b": (ecw.INT_CODES, case.logical, case.scales, 4)}, {"a": cands, "b": cands}, x,
-                     top=1, reps=5)
+                     top=1, cold_bytes=32e6, cold_steps=40)
     assert g["a"]["waves_per_block"] == g["b"]["waves_per_block"]
     p = A.pick(cands)
     c = ecw.Coding(ecw.INT_CODES, case.rows, case.cols, p["k"], 4, p["log2_m"], p["tile_cols"])
