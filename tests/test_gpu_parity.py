@@ -137,13 +137,15 @@ def test_degenerate_shapes():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("k", [2, 4])
 @pytest.mark.parametrize("shape", [(16, 1), (4, 1)])
-def test_graph_capture_replays_match_eager(shape):
+def test_graph_capture_replays_match_eager(shape, k):
     # the fused GEMV (when a row group spans blocks, with its in-kernel reduction
-    # and arrival tickets) is captured in a HIP graph and replayed several times with
-    # eager work between
+    # and arrival tickets; INT quads with their correction passes) is captured in a
+    # HIP graph and replayed several times with eager work between
     W, R = shape
-    case = cases._int("graph", 192, 4096, 2, 4, 12, 128, seed=12)
+    case = cases._int("graph", 192, 4096, k, 4, 12, 128, seed=12)
+    case.stored_tuples = 512 if k == 4 else 0
     ct = ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
                               waves_per_block=W, tiles_per_wave=R)
     xd, xv = _x(case, 1)
@@ -267,7 +269,8 @@ def test_cross_block_reduction_is_stable(batch):
 
 
 @pytest.mark.parametrize("shape", [(4, 1, 2), (2, 2, 3), (8, 1, 5), (1, 1, 4)])
-@pytest.mark.parametrize("name", ["pair_m11_ragged", "cfg1_gauss_k1_m12", "fp8_m12", "bf16_m12"])
+@pytest.mark.parametrize("name", ["pair_m11_ragged", "cfg1_gauss_k1_m12", "fp8_m12", "bf16_m12",
+                                  "quads_t64_m10_ragged"])
 def test_row_groups_per_block_match_one_per_block(name, shape):
     # a block decoding several row groups in sequence (staging once) gives the same
     # bits as one row group per block: same wave order, same block order
@@ -289,7 +292,8 @@ def test_row_groups_per_block_match_one_per_block(name, shape):
 
 
 @pytest.mark.parametrize("batch", [1, 4])
-@pytest.mark.parametrize("name", ["pair_m11_ragged", "cfg1_gauss_k1_m12", "bf16_m12", "fp8_m12"])
+@pytest.mark.parametrize("name", ["pair_m11_ragged", "cfg1_gauss_k1_m12", "bf16_m12", "fp8_m12",
+                                  "quads_16_slices_m12"])
 def test_split_row_groups_leave_tickets_at_zero(name, batch):
     # one-wave blocks split every row group over all its slices: the last block of
     # each row group adds the partials; afterwards every arrival ticket is zero again,
