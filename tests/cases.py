@@ -119,7 +119,9 @@ def quad_cases():
             q("quads_one_wave", 100, 128, 11, 128, 256, 24),
             q("quads_tc2048_m13", 64, 4096, 13, 2048, 4096, 25),
             # 16 slices of a ragged row group, 48 KiB of tables
-            q("quads_16_slices_m12", 70, 1024, 12, 64, 2048, 26)]
+            q("quads_16_slices_m12", 70, 1024, 12, 64, 2048, 26),
+            # a last slice narrower than the others (128, 128, 64 columns), bf16 x
+            q("quads_ragged_slice", 130, 320, 11, 128, 256, 27, "bf16")]
 
 
 def bf16_mixed(rows, cols, seed, frac=0.02):
