@@ -549,6 +549,15 @@ def test_quad_coding_limits_and_validation():
         b = base.copy()
         mutate(b)
         assert _prep_status(b) == 3
+    # the header's stored-tuple count: required for quads, forbidden elsewhere
+    b = base.copy()
+    b[80:84] = np.array([0], np.uint32).view(np.uint8)          # header field after lut_entry_bytes
+    assert _prep_status(b) == 3
+    pair = cases.small_cases()[1]
+    pb = ecw.encode(pair.lib_coding(), pair.logical, pair.scales)
+    assert _prep_status(pb) == 0
+    pb[80:84] = np.array([16], np.uint32).view(np.uint8)
+    assert _prep_status(pb) == 3
     # fewer stored tuples than slots: the slots past them must stay zero
     c8 = ecw.Coding(ecw.INT_CODES, 64, 128, 4, 4, 10, 64, stored_tuples=64)
     w8 = np.zeros((64, 128), np.int8)
