@@ -643,7 +643,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              "(the kernel measured here is one GPU's share; sharding over GPUs is not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
