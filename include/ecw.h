@@ -42,7 +42,7 @@ typedef struct ihipStream_t* ecw_stream; /* same type as hipStream_t; NULL = def
 typedef enum {
   ECW_OK = 0,
   ECW_E_INVALID_ARG = 1,     /* null pointer, bad size, misaligned buffer, bad dtype */
-  ECW_E_UNSUPPORTED = 2,     /* legal coding this build does not implement */
+  ECW_E_UNSUPPORTED = 2,     /* legal coding the library does not implement */
   ECW_E_CORRUPT = 3,         /* blob fails validation */
   ECW_E_BUFFER_TOO_SMALL = 4,
   ECW_E_HIP = 5              /* the HIP runtime refused a launch */
