@@ -347,6 +347,36 @@ def test_weight_values_definitions():
     assert gemv.x_values(np.array([0x3F80], np.uint16), "bf16")[0] == 1.0
 
 
+def test_e8_reconstruction_routes_by_hand():
+    # EntroPack page, Sections 3.2 and A.3: the decoder hands out the lattice point
+    # as INT8 or as FP8.  The logical tensor holds doubled coordinates 2v.  Values
+    # below are worked by hand, not by the oracle's own formula.
+    # INT8 route: the stored integer is 2v itself and the row scale applies to v,
+    # so the weight is 2v * scale / 2.
+    c = P.Coding(P.E8_LATTICE, 2, 8, k=8, recon_dtype=P.DT_I8)
+    v2 = np.array([[3, -5, 1, 1, 1, 1, 1, 1],          # coset 1 (all odd)
+                   [0, 2, -2, 4, 0, 0, 0, 0]], np.int8)    # coset 0 (all even)
+    sc = np.array([0.5, 2.0], np.float16)
+    w = P.weight_values(c, v2, sc)
+    assert np.array_equal(w[0], [0.75, -1.25, 0.25, 0.25, 0.25, 0.25, 0.25, 0.25])
+    assert np.array_equal(w[1], [0.0, 2.0, -2.0, 4.0, 0.0, 0.0, 0.0, 0.0])
+    assert np.array_equal(P.reconstructed_dtype_tensor(c, v2), v2)
+    # FP8 route: e4m3 of v, round to nearest with ties to the even significand.
+    # In [8, 16) E4M3 steps by 1, in [16, 32) by 2, in [2, 4) by 0.25.
+    #   v = 8.5  -> 8   (0x50: exponent 10, significand 000)  tie, even wins
+    #   v = 9.5  -> 10  (0x52)                                 tie: 9 = 1.001b odd, 10 = 1.010b even
+    #   v = 17   -> 16  (0x58)                                 tie between 16 and 18
+    #   v = -8.5 -> -8  (0xD0);  v = -11.5 -> -12 (0xD4): 11 = 1.011b odd, 12 = 1.100b even
+    #   v = 23.5 -> 24  (0x5C)                                 not a tie
+    #   v = 0.5  -> 0.5 (0x30);  v = -2.5 -> -2.5 (0xC2)      exact
+    c = P.Coding(P.E8_LATTICE, 1, 16, k=8, recon_dtype=P.DT_FP8)
+    v2 = np.array([[17, 19, 34, -17, -23, 47, 1, -5, 0, 0, 0, 0, 0, 0, 0, 0]], np.int8)
+    want_bytes = [0x50, 0x52, 0x58, 0xD0, 0xD4, 0x5C, 0x30, 0xC2] + [0] * 8
+    assert list(P.reconstructed_dtype_tensor(c, v2)[0]) == want_bytes
+    w = P.weight_values(c, v2, np.array([2.0], np.float16))
+    assert np.array_equal(w[0], [16.0, 20.0, 32.0, -16.0, -24.0, 48.0, 1.0, -5.0] + [0.0] * 8)
+
+
 # ------------------------------------------------------------------ BF16 exponent pairs
 def test_bf16_pair_values_keep_zero_and_the_fifteen_most_frequent():
     # MINE page, Section 4.2 "Tuning t": the t most frequent codes, and always 0.
