@@ -153,7 +153,7 @@ def cpu_baseline(layer, target_s: float = 12.0):
 
 
 def check_rows(y: np.ndarray, w_rows: np.ndarray, x: np.ndarray) -> float:
-    """Worst |y - y_ref| / (1e-3 * sum|w x|) over sampled rows, y_ref in float64.
+    """Worst |y - y_ref| / (1e-3 * sum|w x|) over the given rows, y_ref in float64.
     y [batch, rows], w_rows float64 [rows, K], x float64 [batch, K]."""
     ref = x @ w_rows.T
     bound = 1e-3 * (np.abs(x) @ np.abs(w_rows).T)
@@ -163,14 +163,32 @@ def check_rows(y: np.ndarray, w_rows: np.ndarray, x: np.ndarray) -> float:
     return float(r.max())
 
 
+def check_all(y: np.ndarray, wv_of, x: np.ndarray, chunk: int = 8192) -> float:
+    """check_rows over EVERY row of y [batch, N], in row chunks; wv_of(r0, r1) gives
+    the float64 weight values of rows [r0, r1)."""
+    worst = 0.0
+    for r0 in range(0, y.shape[1], chunk):
+        r1 = min(y.shape[1], r0 + chunk)
+        worst = max(worst, check_rows(y[:, r0:r1], wv_of(r0, r1), x))
+    return worst
+
+
+def fp8_values(t):
+    """Row-chunk weight values of a per-row FP8 E4M3 tensor (E4M3 value * row scale)."""
+    import torch
+    return lambda r0, r1: torch.from_numpy(t.codes[r0:r1]).view(torch.float8_e4m3fn).double().numpy() \
+        * t.scales[r0:r1].astype(np.float64)[:, None]
+
+
+def int_values(t):
+    """Row-chunk weight values of an INT-code tensor (code * fp16 row scale)."""
+    return lambda r0, r1: t.codes[r0:r1].astype(np.float64) * t.scales[r0:r1].astype(np.float64)[:, None]
+
+
 def time_cold(launches, batch: int, steps: int, cold_bytes: float):
     """Cold device timing of grouped launches (autotune.time_cold)."""
     from entropy_coded_weight_amd import autotune as A
     return A.time_cold(launches, batch, steps, cold_bytes)
-
-
-def _rows(n, k=256, seed=1):
-    return np.sort(np.random.default_rng(seed).choice(n, min(k, n), replace=False))
 
 
 def _plugin_bits(counts: np.ndarray) -> float:
@@ -232,7 +250,7 @@ def config5_inputs():
 
 def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
     """Per-workload measurements besides the layer set: coding and launch shape
-    picked by the autotuner on this device (warm), then timed cold; sampled rows
+    picked by the autotuner on this device (warm), then timed cold; every row
     checked against float64."""
     import torch
     import ecw_inputs as E
@@ -274,9 +292,7 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
         blob, shape, p = tuned_blob(ecw.INT_CODES, t.codes, t.scales, x, code_bits=4, ks=(1,), log2_ms=(12,),
                                     tile_cols=(64, 128, 256, 512))
         us, ys = time_cold([("w", [(blob, shape)], x)], 1, steps, cold_bytes)
-        rows = _rows(1024)
-        w = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
-        worst = check_rows(ys["w"][0][:, rows], w, t.x.astype(np.float64))
+        worst = check_all(ys["w"][0], int_values(t), t.x.astype(np.float64))
         n = t.codes.size
         res["1"] = summary(us, stored(blob), n, n * 0.5 + 1024 * 2, worst, {"w": p},
                            {"workload": "one 1024x1024 matrix of 16-level codes from a discretised Gaussian "
@@ -293,12 +309,11 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
             picks[name] = p
             nbytes += stored(blob)
             nw += t.bits.size
-            rows = _rows(t.bits.shape[0])
-            wr = torch.from_numpy(t.bits[rows].view(np.int16)).view(torch.bfloat16).double().numpy()
             xv = torch.from_numpy(t.x_bits.view(np.int16)).view(torch.bfloat16).double().numpy()
-            checks.append((name, rows, wr, xv))
+            checks.append((name, t.bits, xv))
         us, ys = time_cold(launches, 1, steps, cold_bytes)
-        worst = max(check_rows(ys[n][0][:, r], wr, xv) for n, r, wr, xv in checks)
+        worst = max(check_all(ys[n][0], lambda r0, r1, b=b: torch.from_numpy(b[r0:r1].view(np.int16))
+                              .view(torch.bfloat16).double().numpy(), xv) for n, b, xv in checks)
         res["3"] = summary(us, nbytes, nw, nw * 2, worst, picks,
                            {"workload": "BF16 N(0, 0.02^2) weights at 14336x4096 and 4096x14336, exponent "
                                         "byte rANS-coded, sign+mantissa byte raw, bf16 x, batch 1; "
@@ -309,8 +324,6 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
         v2, scales, xh, step, bpw = config5_inputs()
         x = torch.from_numpy(xh).to(dev)
         n, K = v2.shape
-        rows = _rows(n)
-        vv = v2[rows].astype(np.float64) / 2.0
         for recon, tag in ((ecw.DT_I8, "int8"), (ecw.DT_FP8_E4M3, "fp8")):
             # table size and tile width tuned like the other payloads: the 17 tables
             # take 4 bytes per slot in LDS, so M = 2^9 leaves room for two blocks per CU
@@ -329,12 +342,12 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
             t_min = min(c_[0] for c_ in cand)
             _, _, m, tc, shape, blob = min((c_ for c_ in cand if c_[0] <= 1.02 * t_min), key=lambda c_: c_[1])
             us, ys = time_cold([("w", [(blob, shape)], x)], 1, steps, cold_bytes)
-            if recon == ecw.DT_I8:
-                wv = vv * scales[rows].astype(np.float64)[:, None]
-            else:
-                e4 = torch.from_numpy(vv.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
-                wv = e4 * scales[rows].astype(np.float64)[:, None]
-            worst = check_rows(ys["w"][0][:, rows], wv, xh.astype(np.float64))
+            def wv(r0, r1, recon=recon):
+                vv = v2[r0:r1].astype(np.float64) / 2.0
+                if recon != ecw.DT_I8:
+                    vv = torch.from_numpy(vv.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+                return vv * scales[r0:r1].astype(np.float64)[:, None]
+            worst = check_all(ys["w"][0], wv, xh.astype(np.float64))
             res[f"5_{tag}"] = summary(us, stored(blob), v2.size, v2.size + n * 2, worst,
                                       {"w": dict(k=8, log2_m=m, tile_cols=tc, waves_per_block=shape[0],
                                                  tiles_per_wave=shape[1], streams_per_wave=shape[2],
@@ -402,10 +415,7 @@ def secondary_configs(which: str, steps: int, cold_bytes: float, lm_head: bool):
                 xv = x_of(ns[0], batch).double().cpu().numpy()
                 for i, n in enumerate(ns):
                     t = ts[n]
-                    rows = _rows(t.codes.shape[0])
-                    wv = torch.from_numpy(t.codes[rows]).view(torch.float8_e4m3fn).double().numpy() \
-                        * t.scales[rows].astype(np.float64)[:, None]
-                    worst = max(worst, check_rows(ys[ln][i][:, rows], wv, xv))
+                    worst = max(worst, check_all(ys[ln][i], fp8_values(t), xv))
             layer_us = sum(v for k, v in us.items() if k != "lm_head")
             extra = {"workload": "one Llama-3.1-8B-shaped layer (q,k,v,o,gate,up,down) of N(0, 0.02^2) "
                                  "weights quantised per row to FP8 E4M3 (fp16 row scale), byte symbols "
@@ -466,10 +476,7 @@ def budget_points(steps: int, cold_bytes: float):
         us, ys = time_cold(launches, 1, steps, cold_bytes)
         worst = 0.0
         for ln, i, n in checks:
-            t = tensors[n]
-            rows = _rows(t.codes.shape[0])
-            wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
-            worst = max(worst, check_rows(ys[ln][i][:, rows], wv, xhost[ln].astype(np.float64)))
+            worst = max(worst, check_all(ys[ln][i], int_values(tensors[n]), xhost[ln].astype(np.float64)))
         out.append({"label": label, "budget_bytes": int(budget), "stored_bytes": int(stored_b),
                     "predicted_us_warm": round(u_pred, 3), "measured_us_cold": round(sum(us.values()), 3),
                     "per_launch_us": {k: round(v, 3) for k, v in us.items()},
@@ -490,9 +497,8 @@ def dequant_gemm(steps: int, cold_bytes: float):
     written), then the library GEMM (hipBLASLt through torch.mm, fp32 output) reads
     them.  Timed cold (copies rotated over >= cold_bytes), per call, for the INT4 gate
     tensor in its tune-file coding and the BF16 gate tensor as exponent pairs; the
-    dense GEMM alone on resident weights is timed beside it.  Sampled rows of the
-    dense weights are checked bit for bit against float64 values rounded in numpy /
-    torch."""
+    dense GEMM alone on resident weights is timed beside it.  Every dense weight is
+    checked bit for bit against float64 values rounded in numpy."""
     import torch
     import ecw_inputs as E
     import entropy_coded_weight_amd as ecw
@@ -532,18 +538,16 @@ def dequant_gemm(steps: int, cold_bytes: float):
         cts = [ecw.CompressedTensor(blob) for _ in range(copies)]
         dense = [torch.empty((n, k), dtype=tdt, device="cuda") for _ in range(copies)]
         us_deq = timed(lambda r: cts[r % copies].dequantize(tdt, out=dense[r % copies]), max(copies, steps // 4))
-        rows = _rows(n)
-        got = dense[0][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        got = dense[0].view(torch.int16).cpu().numpy().view(np.uint16)
         if label.startswith("int4"):
-            want = (w[rows].astype(np.float64) * sc[rows].astype(np.float64)[:, None]).astype(np.float16) \
-                .view(np.uint16)
+            want = (w.astype(np.float64) * sc.astype(np.float64)[:, None]).astype(np.float16).view(np.uint16)
         else:
-            want = w[rows]
+            want = w
         exact = bool(np.array_equal(got, want))
         d = {"dequant_us": round(us_deq, 3), "stored_bytes": int(stored), "dense_bytes": int(2 * n * k),
              "dequant_gbps": round((stored + 2 * n * k) / (us_deq * 1e-6) / 1e9, 1),
              "dequant_hbm_frac": round((stored + 2 * n * k) / (us_deq * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-             "dense_bits_exact_on_sampled_rows": exact, "gemm": {}}
+             "dense_bits_exact": exact, "gemm": {}}
         for batch in (16, 256):
             x = torch.randn((batch, k), dtype=tdt, device="cuda")
             us_mm = timed(lambda r: torch.mm(x, dense[r % copies].t(), out_dtype=torch.float32),
@@ -740,17 +744,14 @@ def main():
         torch.cuda.synchronize()
         avg_us[ln] = e0.elapsed_time(e1) * 1e3 / (reps * copies)     # us per launch
 
-    # parity on the timed blobs: sampled rows of every tensor against float64, with
-    # the activations its launch used
+    # parity on the timed blobs: every row of every tensor against float64, with the
+    # activations its launch used
     worst = 0.0
     for ln, names in LAUNCHES:
         xv = layer[names[0]]["tensor"].x.astype(np.float64)
         for name in names:
             t = layer[name]["tensor"]
-            y = ys[name].cpu().numpy()
-            rows = np.random.default_rng(1).choice(t.codes.shape[0], 256, replace=False)
-            wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
-            wr = check_rows(y[:, rows], wv, xv)
+            wr = check_all(ys[name].cpu().numpy(), int_values(t), xv)
             worst = max(worst, wr)
             if not wr <= 1.0:
                 log(f"PARITY FAILURE on {name}: worst err/bound {wr}")
@@ -847,7 +848,7 @@ def main():
         deq = out["configs"].pop("dequant", None)
         if deq:
             out["dequant"] = deq
-            if not all(v["dense_bits_exact_on_sampled_rows"] for k, v in deq.items() if k != "workload"):
+            if not all(v["dense_bits_exact"] for k, v in deq.items() if k != "workload"):
                 log("PARITY FAILURE in the dequantising decode")
                 sys.exit(1)
         if budget:

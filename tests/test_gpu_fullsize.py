@@ -5,7 +5,7 @@ For every tensor shape of the five workloads:
   tensor bit for bit (for the lattice FP8 route: its E4M3 rounding), and every tile
   ends on its invariant;
 * operator parity: dec_gemv (grouped as the benchmark groups it, in its launch
-  configuration for the INT4 layer set) on 256 sampled rows against float64,
+  configuration for the INT4 layer set) on EVERY row against a float64 product,
   |y - y_ref| <= 1e-3 * sum|w x| per output.
 """
 import json
@@ -30,13 +30,17 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _rows(n, seed=1, k=256):
-    return np.sort(np.random.default_rng(seed).choice(n, min(k, n), replace=False))
-
-
-def _check_sampled(y, wv_rows, xv, rows):
-    ok, worst = gemv.check(y[:, rows], wv_rows, xv)
-    assert ok, f"worst error / bound = {worst}"
+def _check_all_rows(y, wv_of, xv, n, chunk=8192):
+    """Every output of y [batch, n] against the float64 product, in row chunks;
+    wv_of(r0, r1) gives the float64 weight values of rows [r0, r1)."""
+    assert y.shape[1] == n
+    worst = 0.0
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        ok, w = gemv.check(y[:, r0:r1], wv_of(r0, r1), xv)
+        assert ok, f"rows [{r0}, {r1}): worst error / bound = {w}"
+        worst = max(worst, w)
+    return worst
 
 
 def _materialize_equal(ct, want):
@@ -71,9 +75,9 @@ def test_config2_layer_set_at_the_benchmarked_launches():
         torch.cuda.synchronize()
         xv = gemv.x_values(ts[0].x, "f16")
         for t, ct, y in zip(ts, cts, ys):
-            rows = _rows(t.codes.shape[0])
-            wv = t.codes[rows].astype(np.float64) * t.scales[rows].astype(np.float64)[:, None]
-            _check_sampled(y.cpu().numpy(), wv, xv, rows)
+            _check_all_rows(y.cpu().numpy(),
+                            lambda r0, r1: t.codes[r0:r1].astype(np.float64)
+                            * t.scales[r0:r1].astype(np.float64)[:, None], xv, t.codes.shape[0])
             _materialize_equal(ct, t.codes)
 
 
@@ -88,8 +92,8 @@ def test_config3_bf16_full(name, k, m, tc, W):
     ct = ecw.CompressedTensor(ecw.encode(c, t.bits), waves_per_block=W, tiles_per_wave=1 if W else None)
     x = torch.from_numpy(t.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
     y = ct.gemv(x).cpu().numpy()
-    rows = _rows(t.bits.shape[0])
-    _check_sampled(y, S.bf16_value(t.bits[rows]), gemv.x_values(t.x_bits, "bf16"), rows)
+    _check_all_rows(y, lambda r0, r1: S.bf16_value(t.bits[r0:r1]), gemv.x_values(t.x_bits, "bf16"),
+                    t.bits.shape[0])
     _materialize_equal(ct, t.bits)
 
 
@@ -100,13 +104,15 @@ def test_config4_fp8_full_batch_1_and_4(name):
     n, K = t.codes.shape
     c = ecw.Coding(ecw.FP8_E4M3, n, K, 1, 0, 12, 256)
     ct = ecw.CompressedTensor(ecw.encode(c, t.codes, t.scales))
-    rows = _rows(n)
-    wv = S.e4m3_value(t.codes[rows]) * t.scales[rows].astype(np.float64)[:, None]
+
+    def wv(r0, r1):
+        return S.e4m3_value(t.codes[r0:r1]) * t.scales[r0:r1].astype(np.float64)[:, None]
+
     for batch in (1, 4):
         xb = t.x_bits[:batch]
         x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).cuda().view(torch.bfloat16)
         y = ct.gemv(x).cpu().numpy()
-        _check_sampled(y, wv, gemv.x_values(xb, "bf16"), rows)
+        _check_all_rows(y, wv, gemv.x_values(xb, "bf16"), n)
     _materialize_equal(ct, t.codes)
 
 
@@ -118,19 +124,22 @@ def test_config5_e8_full(recon):
     c = ecw.Coding(ecw.E8_LATTICE, n, K, 8, 0, 11, 128, recon)
     ct = ecw.CompressedTensor(ecw.encode(c, v2, scales))
     y = ct.gemv(torch.from_numpy(xh).cuda()).cpu().numpy()
-    rows = _rows(n)
-    oc = P.Coding(P.E8_LATTICE, len(rows), K, k=8, log2_m=11, tile_cols=128, recon_dtype=recon)
-    _check_sampled(y, P.weight_values(oc, v2[rows], scales[rows]), gemv.x_values(xh, "f16"), rows)
+
+    def wv(r0, r1):
+        oc = P.Coding(P.E8_LATTICE, r1 - r0, K, k=8, log2_m=11, tile_cols=128, recon_dtype=recon)
+        return P.weight_values(oc, v2[r0:r1], scales[r0:r1])
+
+    _check_all_rows(y, wv, gemv.x_values(xh, "f16"), n)
     want = P.reconstructed_dtype_tensor(P.Coding(P.E8_LATTICE, n, K, k=8, log2_m=11, tile_cols=128,
                                                  recon_dtype=recon), v2)
     _materialize_equal(ct, want)
 
 
 @pytest.mark.parametrize("which", ["int4_gate_f16", "bf16_gate_pairs_bf16"])
-def test_dequantize_full_size_sampled_rows(which):
+def test_dequantize_full_size(which):
     # the dense matrix the GEMM path reads, at full size in the benchmarked codings:
-    # 256 sampled rows bit for bit against the oracle's rounding; the GEMM at 16
-    # activation rows within the bound of the same dense weights
+    # every weight bit for bit against the oracle's rounding; the GEMM at 16
+    # activation rows, every output within the bound of the same dense weights
     print(f"[gpu] dequantize full size {which}", flush=True)
     if which.startswith("int4"):
         t = E.config2_tensor("gate")
@@ -149,15 +158,12 @@ def test_dequantize_full_size_sampled_rows(which):
     ct = ecw.CompressedTensor(ecw.encode(c, logical, scales))
     w = ct.dequantize(tdt)
     torch.cuda.synchronize()
-    rows = _rows(logical.shape[0])
-    sc = scales[rows] if scales is not None else None
-    oc_rows = P.Coding(oc.payload, len(rows), oc.cols, k=oc.k, code_bits=oc.code_bits, log2_m=oc.log2_m,
-                       tile_cols=oc.tile_cols)
-    want = P.dequantized(oc_rows, logical[rows], sc, dname)
-    got = w[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    want = P.dequantized(oc, logical, scales, dname)
+    got = w.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, want)
     x = torch.randn((16, logical.shape[1]), dtype=tdt, device="cuda")
     y = ct.gemm(x, w_buf=w)
     torch.cuda.synchronize()
-    w16 = torch.from_numpy(want.view(np.int16)).view(tdt).double().numpy()
-    _check_sampled(y.cpu().numpy(), w16, x.double().cpu().numpy(), rows)
+    w16 = torch.from_numpy(want.view(np.int16)).view(tdt)
+    _check_all_rows(y.cpu().numpy(), lambda r0, r1: w16[r0:r1].double().numpy(), x.double().cpu().numpy(),
+                    logical.shape[0])
