@@ -104,6 +104,7 @@ def lib():
     L.dec_prepare.argtypes = [vp, sz, vp, P(Tensor)]
     L.dec_gemv_workspace_size.argtypes = [P(Tensor), i32, P(sz)]
     L.dec_gemv.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz]
+    L.dec_gemv_noalloc.argtypes = [vp, P(Tensor), vp, i32, vp, i32]
     L.dec_materialize.argtypes = [vp, P(Tensor), vp, vp, vp]
     L.dec_dequantize.argtypes = [vp, P(Tensor), vp, i32]
     L.dec_gemv_group_workspace_size.argtypes = [P(P(Tensor)), i32, i32, P(sz)]
@@ -115,7 +116,7 @@ def lib():
     L.ecw_probe_stream_read.argtypes = [vp, vp, sz, vp, u32]
     L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
     for f in ("enc_build_tables", "enc_encode", "enc_e8_nearest", "dec_prepare", "dec_gemv_workspace_size",
-              "dec_gemv", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize", "dec_dequantize",
+              "dec_gemv", "dec_gemv_noalloc", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize", "dec_dequantize",
               "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []

@@ -1653,14 +1653,10 @@ static ecw_status check_group(const ecw_tensor* const* ts, int n, int batch, int
 }
 
 // Fused decode + GEMV of a group of tensors that read the same x: one launch.
-static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, int n, const void* x,
-                               int x_dtype, float* const* ys, int batch, void* workspace, size_t ws_bytes) {
-  ecw_status st = check_group(ts, n, batch, x_dtype, x, ys);
-  if (st != ECW_OK) return st;
-  uint64_t woff[kMaxGroup];
-  const uint64_t need = group_workspace(ts, n, batch, woff);
-  if (need && (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
-    return fail(ECW_E_INVALID_ARG, "workspace missing, too small or not 256-byte aligned");
+// tickets[i] / partials[i]: tensor i's arrival tickets and partial sums (used only
+// when its row groups span several blocks).  Arguments already checked.
+static ecw_status launch_core(ecw_stream stream, const ecw_tensor* const* ts, int n, const void* x, int x_dtype,
+                              float* const* ys, int batch, uint32_t* const* tickets, float* const* partials) {
   const int B = batch > 1 ? 4 : 1;
   const uint32_t W = ts[0]->waves_per_block;
   KArgs ka{};
@@ -1695,10 +1691,8 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
     blocks += a.n_blocks;
     lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false, x_dtype == ECW_DT_BF16));
     if (a.n_sg > 1) {
-      // tickets first: for one tensor they sit at the same place for every launch shape
-      uint8_t* base = static_cast<uint8_t*>(workspace) + woff[i];
-      a.tickets = reinterpret_cast<uint32_t*>(base);
-      a.partials = reinterpret_cast<float*>(base + ticket_bytes(t));
+      a.tickets = tickets[i];
+      a.partials = partials[i];
     }
     ++ka.nt;
   }
@@ -1717,6 +1711,89 @@ static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, i
   return ECW_OK;
 }
 
+// The same launch with a caller-provided workspace (group_workspace layout).
+static ecw_status launch_group(ecw_stream stream, const ecw_tensor* const* ts, int n, const void* x,
+                               int x_dtype, float* const* ys, int batch, void* workspace, size_t ws_bytes) {
+  ecw_status st = check_group(ts, n, batch, x_dtype, x, ys);
+  if (st != ECW_OK) return st;
+  uint64_t woff[kMaxGroup];
+  const uint64_t need = group_workspace(ts, n, batch, woff);
+  if (need && (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
+    return fail(ECW_E_INVALID_ARG, "workspace missing, too small or not 256-byte aligned");
+  uint32_t* tickets[kMaxGroup] = {};
+  float* partials[kMaxGroup] = {};
+  for (int i = 0; i < n; ++i) {
+    if (!workspace_bytes(ts[i], batch)) continue;
+    // tickets first: for one tensor they sit at the same place for every launch shape
+    uint8_t* base = static_cast<uint8_t*>(workspace) + woff[i];
+    tickets[i] = reinterpret_cast<uint32_t*>(base);
+    partials[i] = reinterpret_cast<float*>(base + ticket_bytes(ts[i]));
+  }
+  return launch_core(stream, ts, n, x, x_dtype, ys, batch, tickets, partials);
+}
+
+// ---- allocation-free variant of dec_gemv.  Its workspace is a file-scope device
+// array, one copy per GPU the library runs on, held until the process ends.  The
+// arrival tickets sit in a fixed region at its start (so they are back at zero
+// after every completed call, whatever the launch shape), the partial sums after
+// them.  Host code never uses the array's name as an address: the per-device
+// address comes from hipGetSymbolAddress, taken once per device.
+constexpr uint64_t kScratchBytes = ECW_NOALLOC_TICKET_BYTES + ECW_NOALLOC_PARTIAL_BYTES;   // per device
+constexpr uint64_t kScratchTicketBytes = ECW_NOALLOC_TICKET_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of `scratch`, set up on first use: its address, and its
+// ticket region cleared by a fill kernel on `stream` (a kernel, not a memset, so
+// a call under graph capture stays capturable).
+static ecw_status scratch_for_device(ecw_stream stream, uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(ECW_E_HIP, "hipGetDevice failed or device index out of range");
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(ECW_E_HIP, "hipGetSymbolAddress(scratch) failed");
+    }
+    const uint64_t words = kScratchTicketBytes / 4;
+    hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<float*>(ptr), words);
+    if (hipGetLastError() != hipSuccess) return fail(ECW_E_HIP, "scratch clear launch failed");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return ECW_OK;
+}
+
+static ecw_status launch_noalloc(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype, float* y,
+                                 int batch) {
+  ecw_status st = check_group(&t, 1, batch, x_dtype, x, &y);
+  if (st != ECW_OK) return st;
+  uint32_t* tickets[1] = {nullptr};
+  float* partials[1] = {nullptr};
+  const uint64_t pb = partial_bytes(t, batch);
+  if (pb) {
+    if (ticket_bytes(t) > kScratchTicketBytes || pb > kScratchBytes - kScratchTicketBytes)
+      return fail(ECW_E_UNSUPPORTED,
+                  "launch needs " + std::to_string(ticket_bytes(t)) + " bytes of tickets and " + std::to_string(pb) +
+                      " bytes of partial sums; the allocation-free entry point holds at most " +
+                      std::to_string(kScratchTicketBytes) + " and " + std::to_string(kScratchBytes - kScratchTicketBytes));
+    uint8_t* base = nullptr;
+    st = scratch_for_device(stream, &base);
+    if (st != ECW_OK) return st;
+    tickets[0] = reinterpret_cast<uint32_t*>(base);
+    partials[0] = reinterpret_cast<float*>(base + kScratchTicketBytes);
+  }
+  return launch_core(stream, &t, 1, x, x_dtype, &y, batch, tickets, partials);
+}
+
 }  // namespace ecw
 
 using namespace ecw;
@@ -1725,6 +1802,12 @@ extern "C" ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const voi
                                float* y, int batch, void* workspace, size_t ws_bytes) {
   clear_error();
   return launch_group(stream, &t, 1, x, x_dtype, &y, batch, workspace, ws_bytes);
+}
+
+extern "C" ecw_status dec_gemv_noalloc(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
+                                       float* y, int batch) {
+  clear_error();
+  return launch_noalloc(stream, t, x, x_dtype, y, batch);
 }
 
 extern "C" ecw_status dec_gemv_group_workspace_size(const ecw_tensor* const* t, int n, int batch,

@@ -2,8 +2,10 @@
  * ecw.h -- entropy-coded weights, decoded inside a batch-1 GEMV on MI355X (gfx950).
  *
  * Plain C ABI.  No C++ types, exceptions or HIP headers cross it.  Every buffer is
- * owned by the caller; the library allocates no device memory and keeps no device
- * state between calls.
+ * owned by the caller and the library calls no device allocator.  Device state that
+ * outlives a call: the arrival tickets in a caller's dec_gemv workspace (zero
+ * between completed calls, see dec_gemv_workspace_size) and the per-GPU scratch
+ * array of the allocation-free entry point dec_gemv_noalloc.
  *
  * The operation: a weight matrix W [rows][cols] is stored as independent rANS
  * tiles of 64 rows x tile_cols columns, 32-bit states and 16-bit payload words
@@ -36,6 +38,9 @@ extern "C" {
 #define ECW_MAX_TUPLES 4096
 #define ECW_MAX_TABLES 17
 #define ECW_MAX_ALPHABET 256
+/* device scratch of dec_gemv_noalloc, per GPU: arrival tickets, then partial sums */
+#define ECW_NOALLOC_TICKET_BYTES (64u << 10)
+#define ECW_NOALLOC_PARTIAL_BYTES ((8u << 20) - (64u << 10))
 
 typedef struct ihipStream_t* ecw_stream; /* same type as hipStream_t; NULL = default */
 
@@ -203,6 +208,23 @@ ecw_status dec_gemv_workspace_size(const ecw_tensor* t, int batch, size_t* bytes
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 ecw_status dec_gemv(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
                     float* y, int batch, void* workspace, size_t workspace_bytes);
+
+/* dec_gemv without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same operation, kernels, launch shape,
+ * bits and errors as dec_gemv; the arrival tickets and partial sums of row groups
+ * that span several blocks live in a file-scope device array of the library, one
+ * copy per GPU (held until the process ends): ECW_NOALLOC_TICKET_BYTES of tickets
+ * (one u32 per row group) and ECW_NOALLOC_PARTIAL_BYTES of partial sums.  A launch
+ * that needs more returns ECW_E_UNSUPPORTED before launching anything (choose a
+ * launch shape with fewer blocks per row group, or use dec_gemv).  The first call
+ * on a device that needs the array also enqueues a small kernel clearing its ticket
+ * region on `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams without ordering, concurrent graph
+ * replays) race and give wrong sums; calls ordered on one stream are safe.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ecw_status dec_gemv_noalloc(ecw_stream stream, const ecw_tensor* t, const void* x, int x_dtype,
+                            float* y, int batch);
 
 /* Grouped launch: several tensors that read the same activations, decoded and
  * multiplied in one kernel launch (MINE page, Section 4.2 "Launch": sections with
