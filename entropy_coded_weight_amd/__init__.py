@@ -115,9 +115,11 @@ def lib():
                                  P(ctypes.c_float)]
     L.ecw_probe_stream_read.argtypes = [vp, vp, sz, vp, u32]
     L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
+    L.ecw_probe_clock.argtypes = [vp, u32, u32, vp, P(u32)]
     for f in ("enc_build_tables", "enc_encode", "enc_e8_nearest", "dec_prepare", "dec_gemv_workspace_size",
               "dec_gemv", "dec_gemv_noalloc", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize", "dec_dequantize",
-              "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup"):
+              "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup",
+              "ecw_probe_clock"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []
     L.ecw_last_error.restype = ctypes.c_char_p
@@ -319,6 +321,29 @@ def probe_lds_lookup(log2_m: int, entry_bytes: int, steps: int = 4096, blocks: i
         times.append(e0.elapsed_time(e1))
     t = sorted(times[1:])[1]
     return blocks * waves * 64 * steps / (t * 1e-3)
+
+
+class ClockProbe:
+    """The shader clock while other work runs: start() launches ecw_probe_clock on a
+    side stream (blocks one-wave blocks busy for duration_us), mhz() waits for it and
+    returns the median clock over the blocks in MHz."""
+
+    def __init__(self, duration_us: int = 3000, blocks: int = 8):
+        self.duration_us, self.blocks = duration_us, blocks
+        self.sink = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+        self.stream = torch.cuda.Stream()
+        self.khz = ctypes.c_uint32(0)
+
+    def start(self):
+        self.stream.wait_stream(torch.cuda.current_stream())
+        _check(lib().ecw_probe_clock(ctypes.c_void_p(self.stream.cuda_stream), self.duration_us, self.blocks,
+                                     self.sink.data_ptr(), ctypes.byref(self.khz)), "ecw_probe_clock")
+
+    def mhz(self) -> float:
+        self.stream.synchronize()
+        v = self.sink.view(-1, 2).cpu().numpy().astype(np.float64)
+        f = v[:, 0] / np.maximum(v[:, 1], 1) * self.khz.value / 1e3
+        return float(np.median(f))
 
 
 # ------------------------------------------------------------------ device tensor

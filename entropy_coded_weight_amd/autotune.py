@@ -158,6 +158,9 @@ def time_group(cts, x: torch.Tensor, reps: int = 20, stream: torch.cuda.Stream |
     yarr = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
     us = ctypes.c_float(0)
     xd = DT_F16 if x.dtype == torch.float16 else DT_BF16
+    # the workspace's zero fill (and x) were enqueued on the current stream: the timed
+    # launches on `stream` must not start before them
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         _check(lib().dec_time_group(ctypes.c_void_p(stream.cuda_stream), _tensor_array([c.t for c in cts]),
                                     len(cts), x.data_ptr(), xd, yarr, x.shape[0],
@@ -168,10 +171,38 @@ def time_group(cts, x: torch.Tensor, reps: int = 20, stream: torch.cuda.Stream |
     return us.value
 
 
-def time_cold(launches, batch: int, steps: int, cold_bytes: float = 512e6):
+def burst_us(replay, stream, bursts: int = 5, min_burst_us: float = 400.0):
+    """Device microseconds per call of `replay` (a graph replay), by the MINE page's
+    timing protocol (Section 4.2 "Tuning Grid"): one warm-up call, then `bursts`
+    bursts, each repeating the call until it lasts at least min_burst_us; the median
+    burst's time per call.  Returns (us per call, [us per call of each burst], calls
+    per burst)."""
+    replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1) * 1e3, 1e-3)
+    reps = max(1, int(math.ceil(min_burst_us / one)))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(bursts + 1)]
+    evs[0].record(stream)
+    for b in range(bursts):
+        for _ in range(reps):
+            replay()
+        evs[b + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[b].elapsed_time(evs[b + 1]) * 1e3 / reps for b in range(bursts)]
+    return float(sorted(per)[len(per) // 2]), per, reps
+
+
+def time_cold(launches, batch: int, steps: int = 0, cold_bytes: float = 512e6):
     """Device microseconds per launch, cold: every launch is a group of compressed
     tensors sharing x; blobs are rotated over >= cold_bytes of device copies, and
-    each launch is captured as one graph over all copies and replayed.
+    each launch is captured as one graph over all copies and timed by burst_us (median
+    of 5 bursts of >= 400 us; `steps` is not used).
     launches: [(name, [(blob, (W, R, S, P)), ...], x_dev)].  Returns
     ({name: us}, {name: [y of the last copy per tensor]})."""
     from . import CompressedTensor, GemvGroup, gemv_group_raw, prepare
@@ -198,17 +229,7 @@ def time_cold(launches, batch: int, steps: int, cold_bytes: float = 512e6):
         with torch.cuda.graph(g):
             for c in range(copies):
                 gemv_group_raw([ct.t for ct in groups[c].tensors], x, ys, wss[c])
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(2, steps // copies)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us[name] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+        us[name] = burst_us(g.replay, stream)[0] / copies
         outs[name] = [y.cpu().numpy() for y in ys]
         del g, groups, wss
     return us, outs

@@ -41,8 +41,13 @@ ecw_status check_coding(const ecw_coding* c) {
   if (c->tile_rows != kLanes) return fail(ECW_E_UNSUPPORTED, "tile_rows must be 64");
   if (c->log2_m < kMinLog2M || c->log2_m > kMaxLog2M)
     return fail(ECW_E_UNSUPPORTED, "log2_m must be in [8, 13]");
-  if (c->tile_cols == 0 || c->tile_cols % 64)
-    return fail(ECW_E_INVALID_ARG, "tile_cols must be a positive multiple of 64");
+  // E8 blocks are 8 columns wide and their tiles are not cut into 16-step groups:
+  // any whole number of blocks per tile (so a tensor's tile count can be matched to
+  // the device's wave slots); the other payloads stage 64 columns at a time
+  const uint32_t tc_unit = c->payload == ECW_P_E8_LATTICE ? 8 : 64;
+  if (c->tile_cols == 0 || c->tile_cols % tc_unit)
+    return fail(ECW_E_INVALID_ARG, c->payload == ECW_P_E8_LATTICE ? "E8 tile_cols must be a positive multiple of 8"
+                                                                   : "tile_cols must be a positive multiple of 64");
   if (c->rows > (1u << 30) || c->cols > (1u << 30))
     return fail(ECW_E_INVALID_ARG, "rows/cols too large");
   const bool quads = quad_coding(c->payload, c->code_bits, c->weights_per_symbol);

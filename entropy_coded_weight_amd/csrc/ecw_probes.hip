@@ -57,6 +57,28 @@ __global__ void __launch_bounds__(1024) k_lds_lookup(uint32_t log2m, uint32_t st
   out[blockIdx.x * blockDim.x + threadIdx.x] = x;
 }
 
+// Shader clock under load: each one-wave block keeps a short dependent FMA chain
+// busy until `ticks` of the constant-rate real-time counter have passed, and records
+// how far the shader-clock counter moved meanwhile (lane 0: [cycles, ticks]).  Run
+// beside another kernel, it reads the clock that kernel runs at.  The loop ends on
+// the real-time bound or, should that counter not advance, after max_iters.
+__global__ void __launch_bounds__(64) k_clock(uint64_t ticks, uint64_t max_iters, uint64_t* out) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  float a = (float)threadIdx.x;
+  uint64_t r = r0;
+  for (uint64_t it = 0; it < max_iters && r - r0 < ticks; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a = fmaf(a, 0.999f, 0.25f);
+    r = __builtin_amdgcn_s_memrealtime();
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = (r - r0) + (a == 12345.0f ? 1u : 0u);
+  }
+}
+
 static ecw_status launch_error(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ECW_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -97,4 +119,22 @@ extern "C" ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, u
   }
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(waves_per_block * 64), lds, (hipStream_t)stream, log2_m, steps, sink);
   return launch_error("lookup probe launch failed");
+}
+
+extern "C" ecw_status ecw_probe_clock(ecw_stream stream, uint32_t duration_us, uint32_t blocks, uint64_t* sink,
+                                      uint32_t* wall_clock_khz) {
+  clear_error();
+  if (!sink || !wall_clock_khz || blocks == 0 || duration_us == 0 || duration_us > 1000000)
+    return fail(ECW_E_INVALID_ARG, "clock probe: bad arguments");
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      khz <= 0) {
+    (void)hipGetLastError();
+    return fail(ECW_E_HIP, "wall clock rate unavailable");
+  }
+  *wall_clock_khz = (uint32_t)khz;
+  const uint64_t ticks = (uint64_t)khz * duration_us / 1000u;
+  hipLaunchKernelGGL(k_clock, dim3(blocks), dim3(64), 0, (hipStream_t)stream, ticks, (uint64_t)duration_us * 1000u,
+                     sink);
+  return launch_error("clock probe launch failed");
 }

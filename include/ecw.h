@@ -76,7 +76,8 @@ typedef struct {
   uint32_t code_bits;          /* INT only: 2, 3 or 4; else 0 */
   uint32_t log2_m;             /* table size M = 2^log2_m, 8..13 */
   uint32_t tile_rows;          /* must be 64 (one wave64 lane per row) */
-  uint32_t tile_cols;          /* columns per tile: multiple of 64 (and of 8k) */
+  uint32_t tile_cols;          /* columns per tile: multiple of 64 (and of 8k);
+                                  E8: any multiple of 8 (whole 8-weight blocks) */
   uint32_t recon_dtype;        /* E8 only: ECW_DT_I8 (2v) or ECW_DT_FP8_E4M3 (v); else 0 */
   uint32_t stored_tuples;      /* INT, code_bits 4, k 4 only: t, the 4-tuples of codes
                                   the table stores, 1 .. min(M, ECW_MAX_TUPLES); else 0 */
@@ -151,7 +152,14 @@ typedef struct {
  * distinct symbols than M slots, alphabet > 256). */
 ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_tables* out);
 
-/* Encode `w` into a self-describing blob (format version 1, little-endian).
+/* Encode `w` into a self-describing blob (format version 1, little-endian): the
+ * symbols of each tile of 64 rows x tile_cols columns are rANS-coded as one
+ * independent stream per tile with 32-bit states and 16-bit words, and the blob
+ * stores what the EntroPack page lists as the stored representation (Section 3.6:
+ * payload words, offsets, terminal states, tables, row scales, layout; Section C.3:
+ * per tile the terminal states and a 32-bit payload offset, plus a final boundary
+ * offset).  rANS itself is the asymmetric numeral system of the MINE page's Section 3
+ * (Background).
  *   t: tables from enc_build_tables for the same w (or any tables with f > 0 for
  *      every occurring symbol); row_scales: host fp16 [rows] (NULL for BF16).
  *   Two-call protocol: blob == NULL -> *blob_bytes = required size, ECW_OK;
@@ -174,7 +182,12 @@ ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const void* w,
  * doubled coordinate outside [-127, 127]); nothing is written on error. */
 ecw_status enc_e8_nearest(const double* u, size_t n_blocks, int8_t* v2);
 
-/* Validate a blob and describe it.
+/* Validate a blob and describe it.  The checks follow the loader gates of the
+ * quantized-artifacts page (sections 0x05A "Parse Before Allocation": checked
+ * integer arithmetic before any size is trusted; 0x05B "Container Gates": versions,
+ * out-of-bounds, overlapping or misaligned intervals, lengths inconsistent with
+ * dtype and shape; 0x05C "Semantic Gates": shapes, layout version and the coding's
+ * own invariants).  Nothing is allocated.
  *   host_blob / blob_bytes: the blob in host memory (read only during the call).
  *   device_blob: the same bytes already copied to device memory, 256-byte aligned
  *   (may be NULL for host-only inspection; dec_gemv then refuses the tensor).
@@ -186,10 +199,16 @@ ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, const void* dev
                        ecw_tensor* out);
 
 /* Bytes of device workspace dec_gemv needs for this tensor, launch shape and batch
- * (0 when each row group fits one block).  The workspace holds the per-block
- * partial sums of row groups that span several blocks and one arrival ticket per
- * row group: the block that arrives last adds the partials in block order, inside
- * the same kernel.  The workspace must be zero-filled before its first use; every
+ * (0 when each row group fits one block).  The workspace is this library's addition
+ * to the plain call dec_gemv(stream, tensor, x, y, batch): a short row group split
+ * over several blocks (to keep every CU busy) needs a place for its partial sums and
+ * a counter for the last block to finish them in a fixed order, and the library does
+ * not allocate.  dec_gemv_noalloc is that plain call, with a library-held scratch.
+ * The workspace holds the per-block partial sums of row groups that span several
+ * blocks and one arrival ticket per row group: the block that arrives last adds the
+ * partials in block order, inside the same kernel.  The workspace must be
+ * zero-filled before its first use (from a nonzero ticket the wrong block finishes
+ * the row group, and its y is wrong or left unwritten, with ECW_OK); every
  * call that completes leaves its tickets at zero again, so later calls and graph
  * replays need no re-initialisation.  One tensor's tickets sit at the start of its
  * workspace for every launch shape; in a group (dec_gemv_group) they move with the
@@ -278,8 +297,21 @@ ecw_status ecw_probe_stream_read(ecw_stream stream, const void* buf, size_t byte
                                  uint32_t blocks);
 ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t entry_bytes, uint32_t steps,
                                 uint32_t blocks, uint32_t waves_per_block, uint32_t* sink);
+/* ecw_probe_clock: `blocks` one-wave blocks each keep a dependent FMA chain busy for
+ *   duration_us (by the constant-rate real-time counter, whose rate in kHz goes to
+ *   *wall_clock_khz) and write [shader-clock cycles, real-time ticks] elapsed, two u64
+ *   per block, to `sink` (device).  cycles / ticks * rate = the shader clock; launched
+ *   on a second stream beside a kernel, the clock that kernel runs at (the issue peak
+ *   of the VALU roofline is priced at it). */
+ecw_status ecw_probe_clock(ecw_stream stream, uint32_t duration_us, uint32_t blocks, uint64_t* sink,
+                           uint32_t* wall_clock_khz);
 
-/* Test hook: the same decode core, writing what dec_gemv keeps in registers.
+/* Test hook: the same decode core, writing what dec_gemv keeps in registers, so the
+ * GPU decode can be held to the parity levels of the quantized-artifacts page
+ * (section 0x09B "Pack/Unpack Parity": decoded codes equal the stored codes
+ * elementwise; 0x09C "Reference Reconstruction": reconstruction against a slow,
+ * explicit decoder) and to the rANS end-of-tile invariant (EntroPack page, Section
+ * C.3: each tile ends on its final boundary offset).
  *   symbols: nullable device uint16 [rows][symbols per row] (symbol indices; INT
  *          quads: the index of the stored tuple the symbol codes);
  *   w_out: nullable device [rows][cols] in the logical dtype (INT int8 codes, BF16

@@ -157,7 +157,9 @@ def e8_cases():
     """E8 variants for the GPU tests: both reconstruction routes, a ragged row group,
     wider tiles, a small table, and blocks covering every doubled coordinate."""
     out = [e8_case(4), e8_case(5), e8_case(4, rows=130, cols=384, m=10, tc=128, seed=2),
-           e8_case(5, rows=64, cols=512, m=9, tc=256, sigma=1.5, seed=3)]
+           e8_case(5, rows=64, cols=512, m=9, tc=256, sigma=1.5, seed=3),
+           # tiles of 10 and 9 blocks (widths not a multiple of 64), ragged last slices
+           e8_case(4, rows=100, cols=392, m=9, tc=80, seed=8), e8_case(5, rows=64, cols=200, m=10, tc=72, seed=9)]
     # every doubled coordinate -127..127 once, as blocks of 8 equal values (same
     # parity; sum of v = 4 * value is even)
     vals = np.arange(-127, 128)

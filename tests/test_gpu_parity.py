@@ -322,3 +322,43 @@ def test_split_row_groups_leave_tickets_at_zero(name, batch):
         assert torch.equal(yy, ys[0])
     ok, worst = gemv.check(ys[0].cpu().numpy(), wv, xv)
     assert ok, worst
+
+
+def test_group_workspace_zero_fill_precondition():
+    # dec_gemv_group's workspace through the C ABI.  Zero-filled once, every call
+    # leaves the tickets at zero.  A member's launch shape fixes the size of its part
+    # of the workspace, so changing it moves the later members' tickets onto bytes
+    # that held partial sums: used without a new zero fill, those row groups never see
+    # their last arrival and their y is not written (the call still returns OK).
+    # Zero-filled again, the group gives the bits of separate calls.
+    print("[gpu] group workspace precondition", flush=True)
+    a = cases._int("ga", 256, 2048, 2, 4, 11, 128, seed=51)
+    b = cases._int("gb", 192, 2048, 2, 4, 11, 128, seed=52)
+    cta = ecw.CompressedTensor(ecw.encode(a.lib_coding(), a.logical, a.scales), waves_per_block=1, tiles_per_wave=1)
+    ctb = ecw.CompressedTensor(ecw.encode(b.lib_coding(), b.logical, b.scales), waves_per_block=1, tiles_per_wave=1)
+    xd, xv = _x(a, 1)
+    big = ecw.group_workspace_size([cta.t, ctb.t], 1)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    ya = torch.full((1, a.rows), float("nan"), device="cuda")
+    yb = torch.full((1, b.rows), float("nan"), device="cuda")
+    ecw.gemv_group_raw([cta.t, ctb.t], xd, [ya, yb], ws)
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[:a.rows // 64].abs().sum()) == 0     # a's tickets
+    assert torch.equal(ya, cta.gemv(xd)) and torch.equal(yb, ctb.gemv(xd))
+    # a now takes two tiles per wave: its part shrinks and b's tickets move
+    cta.set_launch(1, 2)
+    assert ecw.group_workspace_size([cta.t, ctb.t], 1) < big
+    ya.fill_(float("nan"))
+    yb.fill_(float("nan"))
+    ecw.gemv_group_raw([cta.t, ctb.t], xd, [ya, yb], ws)         # stale workspace
+    torch.cuda.synchronize()
+    assert torch.equal(ya, cta.gemv(xd)), "a's tickets did not move"
+    assert bool(torch.isnan(yb).any()), "b's row groups finished on stale tickets"
+    ws.zero_()
+    yb.fill_(float("nan"))
+    ecw.gemv_group_raw([cta.t, ctb.t], xd, [ya, yb], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, cta.gemv(xd)) and torch.equal(yb, ctb.gemv(xd))
+    for y, c in ((ya, a), (yb, b)):      # same cols: both read x
+        ok, worst = gemv.check(y.cpu().numpy(), P.weight_values(c.oracle_coding(), c.logical, c.scales), xv)
+        assert ok, worst
