@@ -323,7 +323,7 @@ def stored_of(t) -> int:
     return t.bytes_words + t.bytes_raw + t.bytes_tile_meta + t.bytes_tables + t.bytes_scales
 
 
-def launch_grid(ts) -> int:
+def launch_grid(ts, x_bf16: bool = False) -> int:
     """Threads of the one kernel a grouped launch of tensor descriptors ts runs (the
     library's block count, rounded up to a multiple of 8 blocks, times the block
     size): how the profiler's dispatches are matched to launches."""
@@ -334,7 +334,7 @@ def launch_grid(ts) -> int:
             continue
         c = t.coding
         quads = c.payload == 1 and c.code_bits == 4 and c.weights_per_symbol == 4
-        two = t.streams_per_wave == 2 and c.payload not in (2, 4) and not quads
+        two = t.streams_per_wave == 2 and c.payload not in (2, 4) and not (quads and x_bf16)
         ns = 2 if two else 1
         per = t.waves_per_block * t.tiles_per_wave
         n_sg = (t.n_slices + per - 1) // per
@@ -355,7 +355,7 @@ LAUNCH_MAP = {}      # row -> launch -> [kernel template, grid threads]
 
 
 def note_launch(row: str, launch: str, ts, batch: int, x_bf16: bool):
-    LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), launch_grid(ts)]
+    LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), launch_grid(ts, x_bf16)]
 
 
 def bytes_row(us: float, stored: int, unc: float) -> dict:

@@ -105,11 +105,13 @@ def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks
     """Search the codings of one logical tensor `w` (host array as enc_encode takes it)
     with activations `x` (device [batch, cols]).  Returns the list of Candidates."""
     rows, cols = w.shape
-    # two row streams per wave exist for INT codes and FP8 only (not INT quads):
-    # elsewhere a shape asking for two runs as one and would only be timed twice
+    # two row streams per wave exist for INT codes and FP8 only (INT quads: with fp16
+    # activations only): elsewhere a shape asking for two runs as one and would only
+    # be timed twice
     one_stream = tuple(s for s in shapes if s[2] == 1)
     if payload not in (INT_CODES, FP8_E4M3):
         shapes = one_stream
+    quad_shapes = shapes if x.dtype == torch.float16 else one_stream
     stream = torch.cuda.Stream()
     out = []
     for k, m, tc, t in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols):
@@ -121,7 +123,7 @@ def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks
         ct = CompressedTensor(blob)
         cand = Candidate(k, m, tc, ct.stored_bytes(), stored_tuples=t)
         with torch.cuda.stream(stream):
-            cand.shape_us = _tune_launch(ct, x, one_stream if t else shapes, reps, stream)
+            cand.shape_us = _tune_launch(ct, x, quad_shapes if t else shapes, reps, stream)
         stream.synchronize()
         if log:
             us, s = cand.best()

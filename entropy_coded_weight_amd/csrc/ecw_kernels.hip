@@ -67,6 +67,13 @@ constexpr bool kBfSym2 = PAY == 2 && KW == 2;
 // stream.
 template <int PAY, int CB, int KW>
 constexpr bool kQuad = PAY == 1 && CB == 4 && KW == 4;
+// INT quads multiplied with fp16 activations (fused GEMV): the prologue rewrites each
+// decode entry as {f | bias << 16, the high bytes of the fp16 values of the stored
+// tuple's four codes}, so a step reads one table entry and rebuilds both fp16 code
+// pairs with byte permutes (an integer code |q| <= 8 has an fp16 value whose low byte
+// is zero) instead of reading a second, tuple-indexed table.
+template <int PAY, int CB, int KW, bool MAT, bool XBF>
+constexpr bool kQuadF = kQuad<PAY, CB, KW> && !MAT && !XBF;
 // Table entries whose high word is the bias alone (no payload bits beside it).
 template <int PAY, int CB, int KW>
 constexpr bool kCleanBias = (PAY == 1 && KW == 4 && CB != 4) || (PAY == 2 && KW == 1) || PAY == 4;
@@ -190,6 +197,20 @@ template <bool CLEAN>
 __device__ __forceinline__ uint2 decode_step(uint32_t& x, uint32_t lut, uint32_t m, uint32_t mmask) {
   const uint2 e = lds_load2(lut + ((x & mmask) << 3));
   x = mad_u24(x >> m, e.x, CLEAN ? e.y : (e.y & 0xFFFFu));
+  return e;
+}
+
+// A4 for the rewritten INT quad entries: x = f * (x >> m) + bias with f and bias the
+// two halves of the entry's low word, taken by sub-dword operand selection (two VALU
+// operations, as for the plain entries' mask and multiply-add).
+__device__ __forceinline__ uint2 decode_step_q(uint32_t& x, uint32_t lut, uint32_t m, uint32_t mmask) {
+  const uint2 e = lds_load2(lut + ((x & mmask) << 3));
+  const uint32_t xs = x >> m;
+  uint32_t r;
+  asm("v_mul_u32_u24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:DWORD\n\t"
+      "v_add_u32_sdwa %0, %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+      : "=&v"(r) : "v"(e.x), "v"(xs));
+  x = r;
   return e;
 }
 
@@ -525,6 +546,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
   constexpr int U = 16;
   constexpr bool BF2 = kBfSym2<PAY, KW>;               // bf16 exponent-pair symbols
   constexpr bool QD = kQuad<PAY, CB, KW>;              // INT quads over stored tuples
+  constexpr bool QF = kQuadF<PAY, CB, KW, MAT, XBF>;    // ... with rewritten entries (fp16 x)
   constexpr bool DOT = kDot<PAY, KW> || (BF2 && XBF);
   constexpr bool BFP = kBfPair<PAY, KW, XBF> && !MAT;   // bf16 weight pairs, two steps per dot
   constexpr int RG = BF2 ? 2 : 1;                      // raw 16-byte groups per U steps
@@ -595,7 +617,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
           const uint32_t step = j + u;
-          const uint2 e = decode_step<CLEAN>(x, lut, m, mmask);
+          const uint2 e = QF ? decode_step_q(x, lut, m, mmask) : decode_step<CLEAN>(x, lut, m, mmask);
           // BF16: the dword of raw bytes holding this step's (first) weight, at byte q
           uint32_t rdw;
           int q;
@@ -615,6 +637,10 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
             } else {
               ex0 = e.x;
             }
+          } else if constexpr (QF) {
+            // the codes' fp16 pairs (q0, q1) and (q2, q3): bytes [0, hi8 q, 0, hi8 q']
+            qwp.x = __builtin_amdgcn_perm(e.y, e.y, 0x010C000Cu);
+            qwp.y = __builtin_amdgcn_perm(e.y, e.y, 0x030C020Cu);
           } else if constexpr (QD && !MAT) {
             qwp = lds_load2(e.y >> 16);     // multiplied after the renormalisation's ring read
           } else if constexpr (!MAT) {
@@ -858,6 +884,8 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
                                                 uint32_t lane, bool activeB, float* accA, float* accB) {
   static_assert(PAY == 1 || PAY == 3, "two row streams per wave: INT codes and FP8 only");
   constexpr int U = 16;
+  constexpr bool QF = kQuadF<PAY, CB, KW, false, XBF>;   // INT quads (fp16 x): rewritten entries
+  static_assert(!kQuad<PAY, CB, KW> || QF, "two streams of INT quads: fp16 activations only");
   constexpr bool DOT = kDot<PAY, KW>;
   constexpr bool CLEAN = kCleanBias<PAY, CB, KW>;
   constexpr int XW = DOT ? (KW / 2) * B : KW * B;
@@ -895,18 +923,50 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
         for (int i = 0; i < XW; ++i) xq[i] = lds_load4(xg + (qtr * XW + i) * 16);
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
-          const uint2 eA = decode_step<CLEAN>(xA, lut, m, mmask);
-          const uint2 eB = decode_step<CLEAN>(xB, lut, m, mmask);
           const uint32_t* xw = reinterpret_cast<const uint32_t*>(xq) + u4 * XW;
-          mac<PAY, CB, KW, B, XBF>(eA, xw, 0u, 0, accA);
-          mac<PAY, CB, KW, B, XBF>(eB, xw, 0u, 0, accB);
-          pin<B>(accA);
-          pin<B>(accB);
-          const RenormRead rA = renorm_read<false>(xA, rposA, ringA, true);
-          const RenormRead rB = renorm_read<RAGGED>(xB, rposB, ringB, activeB);
-          renorm_apply2(rA, xA, rposA, rB, xB, rposB);
+          if constexpr (QF) {
+            // both streams' table reads, then both ring reads, with the codes'
+            // products issued while the ring reads are in flight
+            const uint2 eA = decode_step_q(xA, lut, m, mmask);
+            const uint2 eB = decode_step_q(xB, lut, m, mmask);
+            const RenormRead rA = renorm_read<false>(xA, rposA, ringA, true);
+            const RenormRead rB = renorm_read<RAGGED>(xB, rposB, ringB, activeB);
+            const uint32_t a01 = __builtin_amdgcn_perm(eA.y, eA.y, 0x010C000Cu);
+            const uint32_t a23 = __builtin_amdgcn_perm(eA.y, eA.y, 0x030C020Cu);
+            const uint32_t b01 = __builtin_amdgcn_perm(eB.y, eB.y, 0x010C000Cu);
+            const uint32_t b23 = __builtin_amdgcn_perm(eB.y, eB.y, 0x030C020Cu);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+              accA[b] = dot2<false>(a01, xw[b], accA[b]);
+              accA[b] = dot2<false>(a23, xw[B + b], accA[b]);
+              accB[b] = dot2<false>(b01, xw[b], accB[b]);
+              accB[b] = dot2<false>(b23, xw[B + b], accB[b]);
+            }
+            pin<B>(accA);
+            pin<B>(accB);
+            renorm_apply2(rA, xA, rposA, rB, xB, rposB);
+          } else {
+            const uint2 eA = decode_step<CLEAN>(xA, lut, m, mmask);
+            const uint2 eB = decode_step<CLEAN>(xB, lut, m, mmask);
+            mac<PAY, CB, KW, B, XBF>(eA, xw, 0u, 0, accA);
+            mac<PAY, CB, KW, B, XBF>(eB, xw, 0u, 0, accB);
+            pin<B>(accA);
+            pin<B>(accB);
+            const RenormRead rA = renorm_read<false>(xA, rposA, ringA, true);
+            const RenormRead rB = renorm_read<RAGGED>(xB, rposB, ringB, activeB);
+            renorm_apply2(rA, xA, rposA, rB, xB, rposB);
+          }
         }
       }
+    }
+    if constexpr (QF) {
+      // each stream's escaped codes, from its own correction stream
+      const uint64_t rowA = (uint64_t)rg * 64 + lane;
+      tile_corrections<B, kOutAcc, XBF, false, true>(a, rposA, haveA, ncA, preA, wl, srcA, nchA, lane, ringA, xs, col,
+                                                     KW * S, true, rowA * a.cols + (uint64_t)sl * a.tile_cols, accA);
+      tile_corrections<B, kOutAcc, XBF, false, true>(a, rposB, haveB, ncB, preB, wl + 2 * kRingStride, srcB, nchB,
+                                                     lane, ringB, xs, col, KW * S, activeB,
+                                                     (rowA + 64) * a.cols + (uint64_t)sl * a.tile_cols, accB);
     }
   }
 }
@@ -1160,6 +1220,7 @@ k_decode(const KArgs ka) {
   constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, KW, XBF> || (kBfSym2<PAY, KW> && XBF)) && !MAT;
   constexpr bool DEQ = MAT && XBF;
   constexpr bool QD = kQuad<PAY, CB, KW>;
+  constexpr bool QF = kQuadF<PAY, CB, KW, MAT, XBF>;
   constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT && !QD;
   const uint32_t W = ka.waves;
   const uint32_t tid = threadIdx.x;
@@ -1182,7 +1243,7 @@ k_decode(const KArgs ka) {
   constexpr bool E8 = PAY == 4;
   // streams per wave: 2 = the tiles of two adjacent row groups in lockstep (fused
   // GEMV of INT and FP8 payloads)
-  constexpr bool kTwoCapable = !MAT && !E8 && PAY != 2 && !QD;
+  constexpr bool kTwoCapable = !MAT && !E8 && PAY != 2 && (!QD || QF);
   const uint32_t NSr = (kTwoCapable && a.ns == 2) ? 2u : 1u;
   // the block's slice group and its run of row-group units [u_lo, u_hi); a unit is
   // NSr adjacent row groups, decoded by the waves' streams
@@ -1196,7 +1257,11 @@ k_decode(const KArgs ka) {
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
   constexpr bool E8F8 = E8 && CB == 1;            // E8: CB selects the FP8 reconstruction
-  const uint32_t pair_bytes = QD ? (a.quad_t * 8 + 15) & ~15u : PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
+  // (rewritten quad entries: the tuple table is only needed in the prologue and sits
+  // in the rings' space, which the streams fill after the rewrite)
+  const uint32_t pair_bytes = QF   ? 0
+                              : QD ? (a.quad_t * 8 + 15) & ~15u
+                                   : PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
   const uint32_t lut = pair_bytes;
   const uint32_t lut_bytes = a.lut_entries * (E8 ? 4 : 8);
   const uint32_t xs = lut + lut_bytes;
@@ -1298,8 +1363,10 @@ k_decode(const KArgs ka) {
   }
   if constexpr (QD) {
     // stored tuple i -> its four codes as two packed 16-bit floats of the
-    // activations' type (decode-only kernels: the tuple's digits), at byte 8 i
+    // activations' type (decode-only kernels: the tuple's digits), at byte 8 i (of the
+    // rings' space when the entries are rewritten)
     const uint16_t* tup = reinterpret_cast<const uint16_t*>(a.tables + sizeof(TableRecord));
+    const uint32_t tbase = QF ? rings : 0u;
     for (uint32_t i = tid; i < a.quad_t; i += bd) {
       const uint32_t v = tup[i];
       uint2 e = make_uint2(v, 0u);
@@ -1307,7 +1374,7 @@ k_decode(const KArgs ka) {
         e.x = small_int_bits<XBF>((int)(v & 15) - 8) | (small_int_bits<XBF>((int)((v >> 4) & 15) - 8) << 16);
         e.y = small_int_bits<XBF>((int)((v >> 8) & 15) - 8) | (small_int_bits<XBF>((int)(v >> 12) - 8) << 16);
       }
-      lds_store2(i * 8, e);
+      lds_store2(tbase + i * 8, e);
     }
   }
   if constexpr (PTAB) {
@@ -1328,6 +1395,17 @@ k_decode(const KArgs ka) {
     }
   }
   __syncthreads();
+  if constexpr (QF) {
+    // rewrite every decode entry: {f, bias | h16 << 16} -> {f | bias << 16, the high
+    // bytes of the fp16 values of the stored tuple's codes} (h16 = 8 x tuple index: the
+    // tuple's byte offset in the table staged at `rings`)
+    for (uint32_t i = tid; i < a.lut_entries; i += bd) {
+      const uint2 e = lds_load2(lut + i * 8);
+      const uint2 c = lds_load2(rings + (e.y >> 16));
+      lds_store2(lut + i * 8, make_uint2((e.x & 0xFFFFu) | (e.y << 16), __builtin_amdgcn_perm(c.y, c.x, 0x07050301u)));
+    }
+    __syncthreads();
+  }
 
   for (;;) {
   const uint32_t row = rg * 64 + lane;
@@ -1525,10 +1603,11 @@ static bool pair_table(const ecw_coding& c, bool xbf) {
 // and FP8; E8 and BF16 decode one stream per wave: the BF16 raw bytes of two streams
 // do not fit the 64-register budget beside the decode state, and exponent pairs and
 // INT quads would need a correction pass per stream).
-static bool two_streams(const ecw_tensor* t) {
+// Two row-group streams per wave: INT codes and FP8 (INT quads with fp16 activations).
+static bool two_streams(const ecw_tensor* t, bool xbf) {
   const ecw_coding& c = t->coding;
   return t->streams_per_wave == 2 && c.payload != ECW_P_E8_LATTICE && c.payload != ECW_P_BF16_EXP &&
-         !quad_coding(c.payload, c.code_bits, c.weights_per_symbol);
+         !(quad_coding(c.payload, c.code_bits, c.weights_per_symbol) && xbf);
 }
 
 // Dynamic LDS of one block: pair side table, decode table, staged activations,
@@ -1539,15 +1618,20 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   const bool e8 = t->coding.payload == ECW_P_E8_LATTICE;
   uint64_t pair = (!mat && pair_table(t->coding, xbf)) ? kPairTableBytes : 0;
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
-  if (quad_coding(t->coding.payload, t->coding.code_bits, t->coding.weights_per_symbol))
-    pair = (8ull * t->coding.stored_tuples + 15) / 16 * 16;
+  const bool quads = quad_coding(t->coding.payload, t->coding.code_bits, t->coding.weights_per_symbol);
+  const uint64_t tuples = (8ull * t->coding.stored_tuples + 15) / 16 * 16;
+  // fused quads with fp16 activations: the tuple table lives in the rings' space
+  const bool quad_rewrite = quads && !mat && !xbf;
+  if (quads) pair = quad_rewrite ? 0 : tuples;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
-  const bool two = !mat && two_streams(t);
+  const bool two = !mat && two_streams(t, xbf);
   (void)R;
   // dequantising decode: a 64-row tile per wave (lattice fields: 16 rows)
   const uint64_t stage = mat ? (uint64_t)W * (e8 ? 16 : 64) * kStagePitch : 0;
-  return pair + lut * 8 + xs + (uint64_t)W * (two ? 2 : 1) * kRingStride * 2 + stage;
+  uint64_t rings = (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
+  if (quad_rewrite) rings = std::max(rings, tuples);
+  return pair + lut * 8 + xs + rings + stage;
 }
 
 uint64_t launch_lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, int B, bool mat, bool xbf) {
@@ -1683,7 +1767,7 @@ static ecw_status launch_core(ecw_stream stream, const ecw_tensor* const* ts, in
     a.ns = t->streams_per_wave;
     a.rpb = std::max(1u, t->row_groups_per_block);
     a.n_sg = slice_groups(t);
-    const uint32_t ns = two_streams(t) ? 2u : 1u;
+    const uint32_t ns = two_streams(t, x_dtype == ECW_DT_BF16) ? 2u : 1u;
     const uint32_t units = (a.n_rg + ns - 1) / ns;
     a.n_blocks = (units + a.rpb - 1) / a.rpb * a.n_sg;
     ka.block_begin[ka.nt] = blocks;

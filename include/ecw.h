@@ -128,8 +128,9 @@ typedef struct {
   uint32_t streams_per_wave;         /* 1, or 2: each wave decodes the tiles of two
                                         adjacent row groups at the same slices in
                                         lockstep, sharing the activation reads
-                                        (fused GEMV of INT and FP8 payloads; BF16,
-                                        E8 and the decode-only calls use 1) */
+                                        (fused GEMV of INT and FP8 payloads, INT
+                                        quads with fp16 activations only; BF16, E8
+                                        and the decode-only calls use 1) */
   uint32_t row_groups_per_block;     /* >= 1: a block decodes this many row-group
                                         units (streams_per_wave adjacent row groups
                                         each) one after the other, staging the decode

@@ -121,7 +121,9 @@ def quad_cases():
             # 16 slices of a ragged row group, 48 KiB of tables
             q("quads_16_slices_m12", 70, 1024, 12, 64, 2048, 26),
             # a last slice narrower than the others (128, 128, 64 columns), bf16 x
-            q("quads_ragged_slice", 130, 320, 11, 128, 256, 27, "bf16")]
+            q("quads_ragged_slice", 130, 320, 11, 128, 256, 27, "bf16"),
+            # every nonzero code escaped, fp16 x, three row groups (two-stream waves)
+            q("quads_t1_m8_f16_two_streams", 150, 256, 8, 128, 1, 28)]
 
 
 def bf16_mixed(rows, cols, seed, frac=0.02):

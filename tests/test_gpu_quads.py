@@ -50,6 +50,31 @@ def test_quads_launch_shapes(name, shape):
         assert ok, f"batch {batch}: worst error / bound = {worst}"
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 1), (4, 2, 1), (8, 1, 2), (16, 1, 1), (2, 3, 2)])
+@pytest.mark.parametrize("name", ["quads_t64_m10_ragged", "quads_t2048_m12", "quads_t1_m8_f16_two_streams",
+                                  "quads_16_slices_m12"])
+def test_quads_two_row_streams(name, shape):
+    # fp16 activations: a wave decodes two adjacent row groups in lockstep, each with
+    # its own word stream and its own correction rounds (every nonzero code escaped
+    # in the t = 1 case); the same bits as one stream per wave, within the bound
+    W, R, P_ = shape
+    print(f"[gpu] quads two streams {name} W={W} R={R} P={P_}", flush=True)
+    case = _case(name)
+    blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
+    one = ecw.CompressedTensor(blob, waves_per_block=W, tiles_per_wave=R, row_groups_per_block=P_)
+    two = ecw.CompressedTensor(blob, waves_per_block=W, tiles_per_wave=R, streams_per_wave=2,
+                               row_groups_per_block=P_)
+    wv = P.weight_values(case.oracle_coding(), case.logical, case.scales)
+    for batch in (1, 4):
+        xd, xv = _x(case, batch)
+        y1 = one.gemv(xd)
+        y2 = two.gemv(xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+        ok, worst = gemv.check(y2.cpu().numpy(), wv, xv)
+        assert ok, f"batch {batch}: worst error / bound = {worst}"
+
+
 def test_quads_symbols_are_the_oracle_symbols():
     for case in cases.quad_cases():
         print(f"[gpu] quads symbols {case.name}", flush=True)
