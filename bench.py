@@ -347,15 +347,28 @@ def launch_grid(ts, x_bf16: bool = False) -> int:
 def kernel_sig(c, batch: int, x_bf16: bool) -> str:
     """The fused kernel's template arguments for a coding (PAY, CB, KW, B, MAT, XBF)."""
     cb = c.code_bits if c.payload == 1 else (1 if c.payload == 4 and c.recon_dtype == 5 else 0)
+    # the fused kernels are built per activation type only where they multiply packed
+    # 16-bit pairs (INT with several codes per symbol, BF16); the others stage fp32
+    xbf = x_bf16 and ((c.payload == 1 and c.weights_per_symbol >= 2) or c.payload == 2)
     return f"k_decode<{c.payload}, {cb}, {c.weights_per_symbol}, {1 if batch == 1 else 4}, false, " \
-           f"{'true' if x_bf16 else 'false'}>"
+           f"{'true' if xbf else 'false'}>"
 
 
-LAUNCH_MAP = {}      # row -> launch -> [kernel template, grid threads]
+LAUNCH_MAP = {}      # row -> launch -> [kernel template, grid threads, block threads, symbols]
+
+
+def launch_symbols(ts) -> int:
+    """rANS symbols a grouped launch decodes (E8: 9 per block of 8 weights)."""
+    n = 0
+    for t in ts:
+        c = t.coding
+        n += c.rows * (c.cols // 8 * 9 if c.payload == 4 else c.cols // max(1, c.weights_per_symbol))
+    return n
 
 
 def note_launch(row: str, launch: str, ts, batch: int, x_bf16: bool):
-    LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), launch_grid(ts, x_bf16)]
+    LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), launch_grid(ts, x_bf16),
+                                              ts[0].waves_per_block * 64, launch_symbols(ts)]
 
 
 def bytes_row(us: float, stored: int, unc: float) -> dict:
@@ -1054,7 +1067,9 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
         for r in csv.DictReader(open(path)):
             key = (path, r["Dispatch_Id"])
             per[key][r["Counter_Name"]] += float(r["Counter_Value"])
-            names[key] = (r["Kernel_Name"], int(r["Grid_Size"]))
+            names[key] = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            per[key]["VGPR_Count"] = float(r["VGPR_Count"])
+            per[key]["LDS_Block_Size"] = float(r["LDS_Block_Size"])
     lines = ["# Mean SQ counters per dispatch of every launch of every workload bench.py measures, MI355X.",
              "# Read by bench.py (VALU, LDS and bank-conflict fractions per launch, priced at the clock measured",
              "# in the same bench run); valid only while the kernel source and tune files hash to the values below.",
@@ -1063,12 +1078,15 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
     lines += [f"kernel_sha256 = {sha256(KERNEL_SRC)}",
               f"tune_sha256 = {sha256(os.path.relpath(TUNE_FILE, ROOT))}",
               f"secondary_tune_sha256 = {sha256(os.path.relpath(SECONDARY_TUNE_FILE, ROOT))}"]
+    table = ["| workload | launch | kernel | waves | VALU / wave-step | SALU / wave-step | LDS / wave-step | "
+             "bank-conflict share of LDS-active cycles | dependency waits / wave cycles |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for row, launches in lm.items():
-        for ln, (sig, grid) in launches.items():
+        for ln, (sig, grid, wg, nsym) in launches.items():
             agg = collections.defaultdict(list)
             for key, cs in per.items():
-                kname, g = names[key]
-                if g == grid and sig in kname:
+                kname, g, w = names[key]
+                if g == grid and w == wg and sig in kname:
                     for c, v in cs.items():
                         agg[c].append(v)
             if not agg:
@@ -1076,12 +1094,29 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
                 continue
             lines.append(f"{row}.{ln}.kernel = {sig}")
             lines.append(f"{row}.{ln}.grid = {grid}")
-            for c in sorted(agg):
-                lines.append(f"{row}.{ln}.{c} = {sum(agg[c]) / len(agg[c]):.1f}")
+            lines.append(f"{row}.{ln}.symbols = {nsym}")
+            mean = {c: sum(v) / len(v) for c, v in agg.items()}
+            for c in sorted(mean):
+                lines.append(f"{row}.{ln}.{c} = {mean[c]:.1f}")
             lines.append(f"{row}.{ln}.dispatches = {max(len(v) for v in agg.values())}")
+            ws = nsym / 64.0          # wave-steps: one symbol per lane
+            g = lambda c: mean.get(c, float("nan"))     # noqa: E731
+            table.append(f"| {row} | {ln} | `{sig}` | {int(g('SQ_WAVES'))} | {g('SQ_INSTS_VALU') / ws:.1f} | "
+                         f"{g('SQ_INSTS_SALU') / ws:.1f} | {g('SQ_INSTS_LDS') / ws:.2f} | "
+                         f"{g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):.2f} | "
+                         f"{g('SQ_WAIT_ANY') / g('SQ_WAVE_CYCLES'):.2f} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    log(f"wrote {out_path}")
+    md = os.path.splitext(out_path)[0] + ".md"
+    with open(md, "w") as f:
+        f.write("# SQ counters of every launch of every workload (k_decode), MI355X\n\n"
+                f"Derived from `{os.path.relpath(out_path, ROOT)}` (mean per dispatch; the commands that made it "
+                "are in its header).\nA wave-step is one decode step of one wave (64 lanes, one rANS symbol each). "
+                "Workload rows: 2 = the INT4 layer set in its tuned codings, k = the same with two codes per "
+                "symbol, 1 = the 1024x1024 Gaussian codes, 3 = BF16 exponent pairs, 4_batchB = the FP8 decode "
+                "step, 5_int8 / 5_fp8 = the E8 lattice fields.  bench.py turns the same record into VALU and LDS "
+                "fractions of each launch's measured time at the measured clock.\n\n" + "\n".join(table) + "\n")
+    log(f"wrote {out_path} and {md}")
 
 
 def read_counter_record(path: str):
