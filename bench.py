@@ -129,13 +129,30 @@ def run_tuner(path: str, batch: int):
     import torch
     import ecw_inputs as E
     from entropy_coded_weight_amd import autotune as A, INT_CODES
-    cands, specs, xs = {}, {}, {}
+    cands, specs, xs, ts = {}, {}, {}, {}
     for name in ORDER:
-        t = E.config2_tensor(name, layer=0, batch=batch)
+        ts[name] = E.config2_tensor(name, layer=0, batch=batch)
+    # stored tuples of the quad codings: the page's t search per launch (MINE page,
+    # Section 4.2 "Tuning t"), at each table size; each tensor is then timed at the t
+    # values of the search's first selections (the byte-optimal one and the next
+    # rounds of <= 1% more bytes)
+    quad_ts = {n: {} for n in ORDER}
+    t_trace = {}
+    for ln, names in LAUNCHES:
+        for m in A.DEFAULT_LOG2_M:
+            curves = {n: A.t_curve(ts[n].codes, ts[n].scales, m, 256) for n in names}
+            sels = A.t_search(curves)[:4]
+            t_trace.setdefault(ln, {})[str(m)] = sels
+            for n in names:
+                quad_ts[n][m] = tuple(sorted({s[n] for s in sels}))
+        log(f"t search {ln}: " + "; ".join(f"M=2^{m}: {v}" for m, v in t_trace[ln].items()))
+    for name in ORDER:
+        t = ts[name]
         xs[name] = torch.from_numpy(t.x).cuda()
         specs[name] = (INT_CODES, t.codes, t.scales, 4)
         log(f"tuning {name} {t.codes.shape}")
-        cands[name] = A.tune_tensor(INT_CODES, t.codes, t.scales, xs[name], code_bits=4, ks=(1, 2, 4), log=log)
+        cands[name] = A.tune_tensor(INT_CODES, t.codes, t.scales, xs[name], code_bits=4, ks=(1, 2, 4), log=log,
+                                    quad_ts=quad_ts[name])
     picks, fronts = {}, {}
     for ln, names in LAUNCHES:
         log(f"tuning launch {ln}")
@@ -154,7 +171,7 @@ def run_tuner(path: str, batch: int):
         json.dump({"workload": "Llama-3.1-8B-shaped layer set, 16-level Laplacian codes (H=2.2 bits), "
                                f"fp16 row scales, fp16 x, batch {batch}",
                    "device": torch.cuda.get_device_name(0), "picks": picks, "fronts": fronts,
-                   "candidates": table}, f, indent=1)
+                   "t_search": t_trace, "candidates": table}, f, indent=1)
     log(f"wrote {path}")
 
 

@@ -64,10 +64,87 @@ def stored_tuples_for(log2_m: int) -> tuple:
     return tuple(sorted({min(4096, M // 4), min(4096, M // 2), min(4096, 3 * M // 4)}))
 
 
+def t_grid(log2_m: int, steps: int = 32) -> tuple:
+    """Stored-tuple counts the t search walks over: M / steps apart, up to min(M, 4096)
+    (the page increments t one value at a time; M / 32 apart keeps the table builds
+    of a large tensor few)."""
+    M = 1 << log2_m
+    d = max(1, M // steps)
+    return tuple(range(d, min(M, 4096) + 1, d))
+
+
+def t_search(curves: dict, growth: float = 0.01, max_rounds: int = 64):
+    """The MINE page's search over the number t of stored values (Section 4.2
+    "Tuning t"), per section and jointly for the sections of one launch.
+    curves[name] = [(t, bytes, escapes), ...] ascending in t: the size bound (table
+    cross-entropy plus the 4-byte records) and the escape count of each t.  Start
+    from each section's byte-optimal t; then repeatedly increment the t of the
+    section with the most escapes saved per additional byte (a size that does not
+    grow counts as infinitely good) until one more increment would grow the launch's
+    transfer size by more than `growth` over the round's start, or every t is at its
+    cap; record that selection and start the next round from it.  Returns the
+    selections [{name: t}], the byte-optimal one first."""
+    pos = {n: min(range(len(c)), key=lambda i: (c[i][1], c[i][0])) for n, c in curves.items()}
+    total = lambda: sum(curves[n][pos[n]][1] for n in curves)   # noqa: E731
+    out = [{n: curves[n][pos[n]][0] for n in curves}]
+    for _ in range(max_rounds):
+        base = total()
+        moved = False
+        while True:
+            best, best_r = None, -1.0
+            for n, c in curves.items():
+                i = pos[n]
+                if i + 1 >= len(c):
+                    continue
+                db = c[i + 1][1] - c[i][1]
+                de = c[i][2] - c[i + 1][2]
+                r = math.inf if db <= 0 else de / db
+                if r > best_r or (r == best_r and best is not None and n < best):
+                    best, best_r = n, r
+            if best is None:
+                break
+            i = pos[best]
+            if total() + (curves[best][i + 1][1] - curves[best][i][1]) > base * (1.0 + growth):
+                break
+            pos[best] = i + 1
+            moved = True
+        if not moved:
+            # even one increment exceeds the growth allowance: take the best one anyway
+            # (the round's selection is then that single step), or stop at the caps
+            cand = [(n, pos[n]) for n in curves if pos[n] + 1 < len(curves[n])]
+            if not cand:
+                break
+            def ratio(n):
+                c, i = curves[n], pos[n]
+                db = c[i + 1][1] - c[i][1]
+                return math.inf if db <= 0 else (c[i][2] - c[i + 1][2]) / db
+            n = max(cand, key=lambda v: (ratio(v[0]), v[0]))[0]
+            pos[n] += 1
+        sel = {n: curves[n][pos[n]][0] for n in curves}
+        if sel != out[-1]:
+            out.append(sel)
+        if all(pos[n] + 1 >= len(curves[n]) for n in curves):
+            break
+    return out
+
+
+def t_curve(w, scales, log2_m: int, tile_cols: int, ts=None):
+    """(t, size bound in bytes, escapes) of INT quads of 4-bit codes over t stored
+    tuples, for each t of the grid: one table build each (enc_build_tables)."""
+    from . import build_tables
+    out = []
+    for t in (ts or t_grid(log2_m)):
+        c = Coding(INT_CODES, w.shape[0], w.shape[1], 4, 4, log2_m, tile_cols, stored_tuples=t)
+        tab = build_tables(c, w)
+        out.append((t, size_lower_bound_bytes(tab), int(tab.escapes)))
+    return out
+
+
 def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT_LOG2_M,
-                      tile_cols=DEFAULT_TILE_COLS):
+                      tile_cols=DEFAULT_TILE_COLS, quad_ts=None):
     """Every (k, m, tile width, stored tuples) the format accepts for this tensor
-    (stored tuples: INT quads of 4-bit codes, else 0)."""
+    (stored tuples: INT quads of 4-bit codes, else 0; quad_ts[m] overrides the
+    stored-tuple counts tried at table size 2^m, e.g. with the t search's values)."""
     for k in legal_ks(payload, code_bits, ks):
         quads = payload == INT_CODES and code_bits == 4 and k == 4
         for m in log2_ms:
@@ -78,7 +155,8 @@ def coding_candidates(payload, rows, cols, code_bits=0, ks=None, log2_ms=DEFAULT
                     continue
                 if quads and (cols % 64 or tc > 2048):
                     continue
-                for t in (stored_tuples_for(m) if quads else (0,)):
+                ts = (quad_ts.get(m, stored_tuples_for(m)) if quad_ts else stored_tuples_for(m)) if quads else (0,)
+                for t in ts:
                     yield k, m, tc, t
 
 
@@ -101,7 +179,7 @@ def _tune_launch(ct: CompressedTensor, x: torch.Tensor, shapes, reps: int, strea
 
 def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks=None,
                 log2_ms=DEFAULT_LOG2_M, tile_cols=DEFAULT_TILE_COLS, shapes=DEFAULT_SHAPES,
-                reps: int = 20, log=None):
+                reps: int = 20, log=None, quad_ts=None):
     """Search the codings of one logical tensor `w` (host array as enc_encode takes it)
     with activations `x` (device [batch, cols]).  Returns the list of Candidates."""
     rows, cols = w.shape
@@ -114,7 +192,7 @@ def tune_tensor(payload: int, w, scales, x: torch.Tensor, code_bits: int = 0, ks
     quad_shapes = shapes if x.dtype == torch.float16 else one_stream
     stream = torch.cuda.Stream()
     out = []
-    for k, m, tc, t in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols):
+    for k, m, tc, t in coding_candidates(payload, rows, cols, code_bits, ks, log2_ms, tile_cols, quad_ts):
         c = Coding(payload, rows, cols, k, code_bits if payload == INT_CODES else 0, m, tc, stored_tuples=t)
         try:
             blob = encode(c, w, scales)

@@ -154,3 +154,76 @@ def test_size_lower_bound_is_the_tables_cross_entropy():
         tt = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales, t))
         assert lb <= tt.bytes_words + tt.bytes_tile_meta
     assert escaped > 0
+
+
+# ------------------------------------------------------------------ the t search
+def _brute_best(curves, start, budget):
+    """Fewest total escapes over every selection with each section at or above its
+    start index and total bytes within budget (exhaustive)."""
+    import itertools
+    names = sorted(curves)
+    best = None
+    for idx in itertools.product(*[range(start[n], len(curves[n])) for n in names]):
+        b = sum(curves[n][i][1] for n, i in zip(names, idx))
+        if b > budget:
+            continue
+        e = sum(curves[n][i][2] for n, i in zip(names, idx))
+        if best is None or e < best:
+            best = e
+    return best
+
+
+def test_t_search_matches_brute_force_on_unit_steps():
+    # MINE page, Section 4.2 "Tuning t": from the byte-optimal t, increment the t with
+    # the most escapes saved per additional byte until the transfer would grow by more
+    # than 1%.  With every increment costing the same bytes and savings that shrink
+    # with t, the greedy choice is optimal: each round's selection has the fewest
+    # escapes of all selections (from the round's start) within the round's budget.
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        curves = {}
+        for n in ("gate", "up", "down")[: 1 + trial % 3]:
+            steps = int(rng.integers(3, 7))
+            saved = np.sort(rng.integers(1, 400, steps))[::-1]          # shrinking savings
+            esc = [int(5000 + saved.sum())]
+            for sv in saved:
+                esc.append(esc[-1] - int(sv))
+            base_bytes = float(rng.integers(80_000, 120_000))
+            # a few increments that shrink the size first (the byte-optimal start is
+            # past them), then equal steps of 250 bytes
+            lead = int(rng.integers(0, 3))
+            sizes = [base_bytes + 100 * (lead - i) for i in range(lead)] + \
+                    [base_bytes + 250 * i for i in range(steps + 1 - lead)]
+            curves[n] = [(64 * (i + 1), sizes[i], esc[i]) for i in range(steps + 1)]
+        sels = A.t_search(curves)
+        start = {n: min(range(len(c)), key=lambda i: (c[i][1], c[i][0])) for n, c in curves.items()}
+        assert sels[0] == {n: curves[n][start[n]][0] for n in curves}   # the byte-optimal start
+        pos = dict(start)
+        for sel in sels[1:]:
+            new = {n: [t for t, _, _ in curves[n]].index(sel[n]) for n in curves}
+            base = sum(curves[n][pos[n]][1] for n in curves)
+            got_b = sum(curves[n][new[n]][1] for n in curves)
+            got_e = sum(curves[n][new[n]][2] for n in curves)
+            assert all(new[n] >= pos[n] for n in curves)
+            if got_b <= base * 1.01:
+                assert got_e == _brute_best(curves, pos, base * 1.01)
+            else:
+                # no increment fits the allowance: the round takes exactly one step
+                assert sum(new[n] - pos[n] for n in curves) == 1
+            pos = new
+
+
+def test_t_curve_escapes_match_the_oracle():
+    # the size/escape curve the t search walks: the library's escape count for each t
+    # equals the number of codes the oracle's stored-tuple mapping sets to 0
+    from oracle import symbols as S
+    case = cases._int("tq", 128, 512, 4, 4, 10, 128, seed=61)
+    q = case.logical
+    tup = S.quad_tuples(q)
+    counts = np.bincount(tup.ravel(), minlength=1 << 16)
+    for t, nbytes, esc in A.t_curve(q, case.scales, 10, 128, ts=(1, 16, 128, 512, 1024)):
+        stored = S.quad_stored(counts, t)
+        ids, _ = S.quad_map(tup, stored)
+        coded = S.quad_join(ids, stored)
+        assert esc == int(np.count_nonzero(coded != q)), t
+        assert nbytes >= 4 * esc
