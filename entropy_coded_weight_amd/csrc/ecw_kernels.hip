@@ -1298,6 +1298,18 @@ k_decode(const KArgs ka) {
     const uint32_t idx = tid + (uint32_t)i * bd;
     if (idx < nl16) lv[i] = lsrc[idx];
   }
+  // INT quads: the first round of stored tuples goes out with the table, ahead of the
+  // word chunks, so the staging barrier does not wait for the chunks
+  constexpr int KT = QD ? 4 : 1;
+  const uint16_t* tup = reinterpret_cast<const uint16_t*>(a.tables + sizeof(TableRecord));
+  uint32_t tv[KT];
+  if constexpr (QD) {
+#pragma unroll
+    for (int i = 0; i < KT; ++i) {
+      const uint32_t idx = tid + (uint32_t)i * bd;
+      tv[i] = idx < a.quad_t ? tup[idx] : 0u;
+    }
+  }
   const uint32_t nvec = MAT ? 0 : a.xs_cols / 8;                 // activations, 8 columns per unit
   const uint32_t nxv = nvec * B;
   auto x_load = [&](uint32_t v) {
@@ -1365,17 +1377,21 @@ k_decode(const KArgs ka) {
     // stored tuple i -> its four codes as two packed 16-bit floats of the
     // activations' type (decode-only kernels: the tuple's digits), at byte 8 i (of the
     // rings' space when the entries are rewritten)
-    const uint16_t* tup = reinterpret_cast<const uint16_t*>(a.tables + sizeof(TableRecord));
     const uint32_t tbase = QF ? rings : 0u;
-    for (uint32_t i = tid; i < a.quad_t; i += bd) {
-      const uint32_t v = tup[i];
+    auto t_store = [&](uint32_t i, uint32_t v) {
       uint2 e = make_uint2(v, 0u);
       if constexpr (!MAT) {
         e.x = small_int_bits<XBF>((int)(v & 15) - 8) | (small_int_bits<XBF>((int)((v >> 4) & 15) - 8) << 16);
         e.y = small_int_bits<XBF>((int)((v >> 8) & 15) - 8) | (small_int_bits<XBF>((int)(v >> 12) - 8) << 16);
       }
       lds_store2(tbase + i * 8, e);
+    };
+#pragma unroll
+    for (int i = 0; i < KT; ++i) {
+      const uint32_t idx = tid + (uint32_t)i * bd;
+      if (idx < a.quad_t) t_store(idx, tv[i]);
     }
+    for (uint32_t i = tid + KT * bd; i < a.quad_t; i += bd) t_store(i, tup[i]);
   }
   if constexpr (PTAB) {
     // symbol -> its codes as 16-bit floats, packed two per word (digits low first)
@@ -1411,6 +1427,15 @@ k_decode(const KArgs ka) {
   const uint32_t row = rg * 64 + lane;
   const bool active = row < a.rows;
   const bool ragged = (rg + 1) * 64 > a.rows;     // wave-uniform
+  // the row scale of this thread's first output of the epilogue, requested now so the
+  // epilogue does not wait for it
+  float sc0 = 1.f;
+  if constexpr (!MAT && PAY != 2) {
+    if (tid < 64u * B * (hasB ? 2u : 1u)) {
+      const uint32_t r0 = (rg + tid / (64u * B)) * 64 + (tid & 63);
+      if (r0 < a.rows) sc0 = (float)__builtin_bit_cast(_Float16, a.scales[r0]);
+    }
+  }
   float acc[2][B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[0][b] = acc[1][b] = 0.f;
@@ -1484,7 +1509,7 @@ k_decode(const KArgs ka) {
         sum += *lds_ptr<const float>(rings + (w * NSr + s) * (2 * kRingStride) + (b * 64 + l) * 4);
       if (a.n_sg == 1) {
         if (r < a.rows && b < a.nb) {
-          const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]) * unit_scale;
+          const float sc = (PAY == 2) ? 1.f : (i == tid ? sc0 : (float)__builtin_bit_cast(_Float16, a.scales[r])) * unit_scale;
           a.y[(uint64_t)b * a.rows + r] = sum * sc;
         }
       } else {
@@ -1529,7 +1554,7 @@ k_decode(const KArgs ka) {
               if (g0 + k < a.n_sg) sum += v[k];
           }
           if (r < a.rows && b < a.nb) {
-            const float sc = (PAY == 2) ? 1.f : (float)__builtin_bit_cast(_Float16, a.scales[r]) * unit_scale;
+            const float sc = (PAY == 2) ? 1.f : (i == tid ? sc0 : (float)__builtin_bit_cast(_Float16, a.scales[r])) * unit_scale;
             a.y[(uint64_t)b * a.rows + r] = sum * sc;
           }
         }
