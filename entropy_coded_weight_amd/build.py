@@ -12,9 +12,12 @@ LIB = os.path.join(HERE, "libecw.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+# -amdgpu-kernarg-preload-count: the first 11 dwords of kernel arguments arrive in
+# scalar registers (k_decode's block-to-tensor fields); code objects keep a
+# load-based entry for firmware without preloading.
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-mcode-object-version=5", "-Wall", "-Wno-unused-result",
+             "-mcode-object-version=5", "-mllvm", "-amdgpu-kernarg-preload-count=11", "-Wall", "-Wno-unused-result",
              f"-I{ROOT}"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{ROOT}"]
 

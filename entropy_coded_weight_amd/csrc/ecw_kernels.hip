@@ -127,9 +127,11 @@ struct TArgs {
   uint32_t quad_t;         // INT quads: stored tuples (entries of the LDS tuple table), else 0
 };
 
-// Launch arguments.  The fields a block needs to find its tensor come first, so one
-// scalar load fetches them; the launch shape is passed here instead of being read
-// from the dispatch packet.
+// Launch arguments.  The fields a block needs to find its tensor are also passed as
+// the kernel's leading scalar arguments, which the build preloads into scalar
+// registers at wave launch (kernel-argument preloading of gfx950): a block finds its
+// tensor without a memory round trip, and only the tensor's own fields are loaded.
+// The launch shape is passed here instead of being read from the dispatch packet.
 struct KArgs {
   uint32_t n_blocks;                 // total logical blocks
   uint32_t nt;                       // tensors in the launch
@@ -1213,7 +1215,9 @@ constexpr int kKernelWaves = (MAT && (PAY == 2 || (PAY == 4 && XBF))) ? 4 : kWav
 // the dequantising decode's dense matrix.
 template <int PAY, int CB, int KW, int B, bool MAT, bool XBF>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kKernelWaves<PAY, B, MAT, XBF>)))
-k_decode(const KArgs ka) {
+k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const uint32_t grid,
+         const uint32_t bb1, const uint32_t bb2, const uint32_t bb3, const uint32_t bb4, const uint32_t bb5,
+         const uint32_t bb6, const uint32_t bb7, const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
   (void)smem;
   // activations staged as packed 16-bit pairs (dot-product paths), else as fp32
@@ -1222,24 +1226,26 @@ k_decode(const KArgs ka) {
   constexpr bool QD = kQuad<PAY, CB, KW>;
   constexpr bool QF = kQuadF<PAY, CB, KW, MAT, XBF>;
   constexpr bool PTAB = kPairTable<PAY, KW, XBF> && !MAT && !QD;
-  const uint32_t W = ka.waves;
+  const uint32_t W = waves;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Hardware block b runs on XCD b % 8.  Give each XCD a contiguous range of logical
-  // blocks (the slice groups of one row group are adjacent).  The grid (ka.grid) is
+  // blocks (the slice groups of one row group are adjacent).  The grid (`grid`) is
   // a multiple of 8; surplus blocks exit at once.
-  const uint32_t per = ka.grid >> 3;
+  const uint32_t per = grid >> 3;
   const uint32_t gl = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (gl >= ka.n_blocks) return;
+  if (gl >= n_blocks) return;
   // tensor of a grouped launch: blocks are numbered tensor by tensor
-  uint32_t ti = 0;
+  static_assert(kMaxGroup == 8, "one preloaded argument per group member after the first");
+  uint32_t ti = 0, bbt = 0;
+  const uint32_t bbs[kMaxGroup] = {0u, bb1, bb2, bb3, bb4, bb5, bb6, bb7};
 #pragma unroll
   for (uint32_t i = 1; i < kMaxGroup; ++i)
-    if (i < ka.nt && gl >= ka.block_begin[i]) ti = i;
+    if (i < nt && gl >= bbs[i]) { ti = i; bbt = bbs[i]; }
   const TArgs& a = ka.t[ti];
-  const uint32_t lb = gl - ka.block_begin[ti];
+  const uint32_t lb = gl - bbt;
   constexpr bool E8 = PAY == 4;
   // streams per wave: 2 = the tiles of two adjacent row groups in lockstep (fused
   // GEMV of INT and FP8 payloads)
@@ -1582,7 +1588,8 @@ __global__ void k_fill_zero(float* y, uint64_t n) {
 }
 
 // ------------------------------------------------------------------ host launch
-using KernelFn = void (*)(const KArgs);
+using KernelFn = void (*)(uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t,
+                         uint32_t, uint32_t, const KArgs);
 
 template <int B, bool MAT, bool XBF>
 static KernelFn pick_kernel(const ecw_coding& c) {
@@ -1814,7 +1821,9 @@ static ecw_status launch_core(ecw_stream stream, const ecw_tensor* const* ts, in
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   const uint32_t grid = (blocks + 7) / 8 * 8;
   ka.grid = grid;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka.n_blocks, ka.nt, ka.waves,
+                     ka.grid, ka.block_begin[1], ka.block_begin[2], ka.block_begin[3], ka.block_begin[4],
+                     ka.block_begin[5], ka.block_begin[6], ka.block_begin[7], ka);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
   return ECW_OK;
@@ -2058,7 +2067,9 @@ static ecw_status launch_decode_only(ecw_stream stream, const ecw_tensor* t, uin
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   const uint32_t grid = (ka.n_blocks + 7) / 8 * 8;
   ka.grid = grid;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(W * 64), (size_t)lds, (hipStream_t)stream, ka.n_blocks, ka.nt, ka.waves,
+                     ka.grid, ka.block_begin[1], ka.block_begin[2], ka.block_begin[3], ka.block_begin[4],
+                     ka.block_begin[5], ka.block_begin[6], ka.block_begin[7], ka);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(ECW_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
   return ECW_OK;
