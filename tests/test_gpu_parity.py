@@ -188,6 +188,31 @@ def test_grouped_launch_matches_separate_launches(batch):
         assert ok, worst
 
 
+@pytest.mark.parametrize("W", [1, 4])
+@pytest.mark.parametrize("batch", [1, 4])
+def test_largest_group_matches_separate_launches(batch, W):
+    # eight members, the most one launch takes: every member's first block reaches the
+    # kernel as a preloaded argument of its own; with one-wave blocks every member's
+    # row groups are split over blocks and finish through its own part of the
+    # workspace
+    print(f"[gpu] eight-member group batch={batch} W={W}", flush=True)
+    specs = [(64, 11, 128), (130, 12, 256), (200, 10, 128), (70, 11, 256),
+             (256, 12, 128), (96, 10, 256), (150, 11, 128), (65, 12, 128)]
+    cts, cs = [], []
+    for i, (n, m, tc) in enumerate(specs):
+        case = cases._int(f"g8_{i}", n, 1024, 2, 4, m, tc, seed=70 + i)
+        cts.append(ecw.CompressedTensor(ecw.encode(case.lib_coding(), case.logical, case.scales),
+                                        waves_per_block=W, tiles_per_wave=1))
+        cs.append(case)
+    xd, xv = _x(cs[0], batch)
+    ys = ecw.GemvGroup(cts).gemv(xd)
+    torch.cuda.synchronize()
+    for ct, case, y in zip(cts, cs, ys):
+        assert torch.equal(y, ct.gemv(xd))
+        ok, worst = gemv.check(y.cpu().numpy(), P.weight_values(case.oracle_coding(), case.logical, case.scales), xv)
+        assert ok, worst
+
+
 @pytest.mark.parametrize("case", cases.e8_cases(), ids=lambda c: c.name)
 def test_e8_materialize_bit_exact(case):
     # symbols, reconstructed weights (INT8 2v or E4M3 bytes) and tile ends vs the oracle
