@@ -58,7 +58,7 @@ def test_materialize_bit_exact(case):
     assert np.array_equal(sym.cpu().numpy().view(np.uint16).astype(np.int64), ref_sym)
 
 
-@pytest.mark.parametrize("batch", [1, 2, 4])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
 @pytest.mark.parametrize("case", cases.small_cases(), ids=lambda c: c.name)
 def test_gemv_within_bound(case, batch):
     print(f"[gpu] gemv {case.name} batch={batch}", flush=True)
