@@ -12,6 +12,11 @@ size as the tie-breaker).
 Tensors that share a launch (q/k/v, gate/up) must agree on waves per block;
 tune_group times the real grouped launch for combinations of each member's best
 single-tensor candidates at each common value.
+
+For INT quads the number t of stored tuples follows the page's search (Section 4.2,
+"Tuning t"; t_curve, t_search): from each tensor's byte-optimal t, the t that saves
+the most escapes per added byte is raised until the launch's bytes grow by more than
+1%, and each such selection becomes a candidate.
 """
 from __future__ import annotations
 
