@@ -500,6 +500,19 @@ __device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, 
 // phases so the loads overlap the block's table staging: head_begin issues the
 // tile offsets and start state, head_chunks (after staging, before the barrier)
 // the first chunk loads.
+// Wave priority by the work a wave has left in its tile.  Blocks sharing a CU start
+// about a microsecond apart and the later one stages its tables more slowly while the
+// first decodes; left alone it ends long after, with its CU half empty.  Waves with
+// more steps left take issue slots first (levels per 16-step group), so the blocks of
+// a CU end closer together.  Kernels enter at the top level, so a late block's
+// staging is not held back either.
+__device__ __forceinline__ void prio_by_steps_left(uint32_t left) {
+  if (left > 48) __builtin_amdgcn_s_setprio(3);
+  else if (left > 32) __builtin_amdgcn_s_setprio(2);
+  else if (left > 16) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 struct StreamHead {
   uint32_t gb, nch, rposb, st;
   uint2 c0, c1, pre;
@@ -586,6 +599,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
     const uint32_t col = sl * a.tile_cols - c_lo;
 
     for (uint32_t j = 0; j < S; j += U) {
+      prio_by_steps_left(S - j);
       uint4 rgp[RG];
 #pragma unroll
       for (int i = 0; i < RG; ++i) rgp[i] = zero4;
@@ -915,6 +929,7 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
     const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
     const uint32_t col = sl * a.tile_cols - c_lo;
     for (uint32_t j = 0; j < S; j += U) {
+      prio_by_steps_left(S - j);
       const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
@@ -1220,6 +1235,7 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
          const uint32_t bb6, const uint32_t bb7, const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
   (void)smem;
+  __builtin_amdgcn_s_setprio(3);           // see prio_by_steps_left
   // activations staged as packed 16-bit pairs (dot-product paths), else as fp32
   constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, KW, XBF> || (kBfSym2<PAY, KW> && XBF)) && !MAT;
   constexpr bool DEQ = MAT && XBF;
