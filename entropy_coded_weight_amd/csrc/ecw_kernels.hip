@@ -500,16 +500,17 @@ __device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, 
 // phases so the loads overlap the block's table staging: head_begin issues the
 // tile offsets and start state, head_chunks (after staging, before the barrier)
 // the first chunk loads.
-// Wave priority by the work a wave has left in its tile.  Blocks sharing a CU start
-// about a microsecond apart and the later one stages its tables more slowly while the
-// first decodes; left alone it ends long after, with its CU half empty.  Waves with
-// more steps left take issue slots first (levels per 16-step group), so the blocks of
-// a CU end closer together.  Kernels enter at the top level, so a late block's
-// staging is not held back either.
-__device__ __forceinline__ void prio_by_steps_left(uint32_t left) {
-  if (left > 48) __builtin_amdgcn_s_setprio(3);
-  else if (left > 32) __builtin_amdgcn_s_setprio(2);
-  else if (left > 16) __builtin_amdgcn_s_setprio(1);
+// Wave priority by the work a wave has left in its tile: `left` of `total` steps (or
+// lattice blocks), four levels by quarter.  Blocks sharing a CU start about a
+// microsecond apart and the later one stages its tables more slowly while the first
+// decodes; left alone it ends long after, with its CU half empty.  Waves with more
+// work left take issue slots first, so the blocks of a CU end closer together.
+// Kernels enter at the top level, so a late block's staging is not held back either.
+__device__ __forceinline__ void prio_by_work_left(uint32_t left, uint32_t total) {
+  const uint32_t q = total >> 2;
+  if (left > total - q) __builtin_amdgcn_s_setprio(3);
+  else if (left > 2 * q) __builtin_amdgcn_s_setprio(2);
+  else if (left > q) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
@@ -599,7 +600,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
     const uint32_t col = sl * a.tile_cols - c_lo;
 
     for (uint32_t j = 0; j < S; j += U) {
-      prio_by_steps_left(S - j);
+      prio_by_work_left(S - j, S);
       uint4 rgp[RG];
 #pragma unroll
       for (int i = 0; i < RG; ++i) rgp[i] = zero4;
@@ -797,6 +798,7 @@ __device__ __forceinline__ void wave_body_deq(const TArgs& a, const StreamHead& 
     const uint64_t colw = (uint64_t)sl * a.tile_cols;     // column of the tile's first weight
 
     for (uint32_t j = 0; j < S; j += U) {
+      prio_by_work_left(S - j, S);
       uint4 rgp[RG];
 #pragma unroll
       for (int i = 0; i < RG; ++i) rgp[i] = zero4;
@@ -929,7 +931,7 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
     const uint32_t S = (sl + 1 == a.n_sl) ? a.s_last : a.s_full;
     const uint32_t col = sl * a.tile_cols - c_lo;
     for (uint32_t j = 0; j < S; j += U) {
-      prio_by_steps_left(S - j);
+      prio_by_work_left(S - j, S);
       const uint32_t xg = xs + ((col + KW * j) * B / (DOT ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
@@ -1068,6 +1070,7 @@ __device__ __forceinline__ void wave_body_e8(const TArgs& a, const StreamHead& h
     const uint32_t col0 = sl * a.tile_cols - c_lo;
     const uint32_t nblk = S / 9;
     for (uint32_t blk = 0; blk < nblk; ++blk) {
+      prio_by_work_left(nblk - blk, nblk);
       const uint32_t step0 = blk * 9;
       // activations of the block's 8 columns: fp32 [col][B]
       float xv[MAT ? 1 : 8 * B];
@@ -1235,7 +1238,7 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
          const uint32_t bb6, const uint32_t bb7, const KArgs ka) {
   extern __shared__ __align__(16) unsigned char smem[];
   (void)smem;
-  __builtin_amdgcn_s_setprio(3);           // see prio_by_steps_left
+  __builtin_amdgcn_s_setprio(3);           // see prio_by_work_left
   // activations staged as packed 16-bit pairs (dot-product paths), else as fp32
   constexpr bool DOT = (kDot<PAY, KW> || kBfPair<PAY, KW, XBF> || (kBfSym2<PAY, KW> && XBF)) && !MAT;
   constexpr bool DEQ = MAT && XBF;
