@@ -1,4 +1,4 @@
-// Blob format version 1: layout shared by the host encoder, the validator and the
+// Blob format version 2: layout shared by the host encoder, the validator and the
 // device kernels of this library.  All integers little-endian.
 //
 //   [0, 256)        BlobHeader
@@ -38,7 +38,8 @@
 // holding the code as a bf16 number.
 //
 // Decode entry of slot i (table t), symbol s, as two u32 (MINE page, Section 4.1:
-// one table read yields both the state-update operands and the payload):
+// one table read yields both the state-update operands and the payload), every
+// coding but INT quads:
 //   lo = f | a8 << 24     f <= 2^13 sits in the low 24 bits, so the 24-bit multiply
 //                         f * (x >> m) ignores a8
 //   hi = bias | h16 << 16 bias = i - cum[s] < 2^13; next state = f * (x >> m) + bias
@@ -49,8 +50,6 @@
 //                     |q| <= 8 has a zero low byte, so the two high bytes are the
 //                     whole values)
 //   INT, k = 4:       a8 = symbol, h16 = 0
-//   INT quads:        a8 = 0, h16 = 8 * symbol (the byte offset of the symbol's
-//                     entry in the per-block table of its four codes)
 //   BF16:             a8 = exponent byte rotated right by one bit (bit 0 in bit 7),
 //                     h16 = 0.  With the raw byte (sign << 7 | mantissa) the bf16
 //                     value's high byte is then sign | a8[6:0] and its low byte
@@ -59,13 +58,19 @@
 //                     digits' exponents and rot the rotation above
 //   FP8 E4M3:         a8 = code byte, h16 = fp16(e4m3 value) (NaN codes: 0x7E00)
 //   E8:               a8 = field value (int8), h16 = 0
+// INT quads, with q0..q3 the four codes of the symbol's stored tuple:
+//   lo = f | bias << 16   (f <= 2^13, bias < 2^13: two clean 16-bit halves)
+//   hi = hi8(fp16(q0)) | hi8(fp16(q1)) << 8 | hi8(fp16(q2)) << 16 | hi8(fp16(q3)) << 24
+// so the fused product with fp16 activations takes the state update and all four
+// codes from one read; the other decoders recover the symbol index from the slot
+// order (a slot with bias 0 starts the next symbol's run).
 #pragma once
 #include <stdint.h>
 
 namespace ecw {
 
 constexpr uint32_t kMagic = 0x31574345u;   // "ECW1"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 constexpr uint32_t kHeaderBytes = 256;
 constexpr uint32_t kLanes = 64;
 constexpr uint32_t kStateL = 1u << 16;     // rANS lower bound L
@@ -156,6 +161,16 @@ inline uint16_t fp16_of_e4m3(uint8_t b) {
     return (uint16_t)(sign | ((uint32_t)(k - 9 + 15) << 10) | mant);
   }
   return (uint16_t)(sign | ((e - 7 + 15) << 10) | (m << 7));
+}
+
+// Decode entry of an INT quads slot: frequency f and bias of its symbol, whose stored
+// tuple holds digit q + 8 of code i at bits 4i..4i+3 (see the layout above).
+inline void quad_entry(uint32_t f, uint32_t bias, uint32_t tuple, uint32_t* lo, uint32_t* hi) {
+  *lo = f | (bias << 16);
+  uint32_t h = 0;
+  for (int i = 0; i < 4; ++i)
+    h |= (uint32_t)(fp16_of_int((int)((tuple >> (4 * i)) & 15) - 8) >> 8) << (8 * i);
+  *hi = h;
 }
 
 // Table entry payload of symbol s (see the layout above).  pair_values: the BF16 pair

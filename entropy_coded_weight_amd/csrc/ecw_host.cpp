@@ -862,10 +862,13 @@ extern "C" ecw_status enc_encode(const ecw_coding* c, const ecw_tables* t, const
     uint32_t slot = 0;
     for (uint32_t s = 0; s < A; ++s) {
       const uint32_t f = fr[k * A + s];
-      uint32_t a8 = 0, h16 = 8 * s;
-      if (!quads)
-        entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], t->pair_values, s, &a8,
-                      &h16);
+      if (quads) {
+        for (uint32_t i = 0; i < f; ++i, ++slot) quad_entry(f, i, t->tuples[s], &lut[2 * slot], &lut[2 * slot + 1]);
+        continue;
+      }
+      uint32_t a8 = 0, h16 = 0;
+      entry_payload(c->payload, c->code_bits, c->weights_per_symbol, t->value_offset[k], t->pair_values, s, &a8,
+                    &h16);
       for (uint32_t i = 0; i < f; ++i, ++slot) {
         lut[2 * slot] = f | (a8 << 24);
         lut[2 * slot + 1] = i | (h16 << 16);   // bias = slot - cum[s]
@@ -1030,9 +1033,12 @@ extern "C" ecw_status dec_prepare(const void* host_blob, size_t blob_bytes, cons
     if (sum == M) {
       uint32_t slot = 0;
       for (uint32_t s = 0; s < n; ++s)
-        for (uint32_t i = 0; i < fq[s]; ++i, ++slot)
-          if (lut[2 * slot] != fq[s] || lut[2 * slot + 1] != (i | ((8 * s) << 16)))
+        for (uint32_t i = 0; i < fq[s]; ++i, ++slot) {
+          uint32_t lo, hi;
+          quad_entry(fq[s], i, tup[s], &lo, &hi);
+          if (lut[2 * slot] != lo || lut[2 * slot + 1] != hi)
             return fail(ECW_E_CORRUPT, "decode table does not match the frequencies");
+        }
     }
   }
   for (uint32_t k = 0; k < g.n_tables && !quads; ++k) {

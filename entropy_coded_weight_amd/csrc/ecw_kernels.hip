@@ -67,11 +67,12 @@ constexpr bool kBfSym2 = PAY == 2 && KW == 2;
 // stream.
 template <int PAY, int CB, int KW>
 constexpr bool kQuad = PAY == 1 && CB == 4 && KW == 4;
-// INT quads multiplied with fp16 activations (fused GEMV): the prologue rewrites each
-// decode entry as {f | bias << 16, the high bytes of the fp16 values of the stored
-// tuple's four codes}, so a step reads one table entry and rebuilds both fp16 code
-// pairs with byte permutes (an integer code |q| <= 8 has an fp16 value whose low byte
-// is zero) instead of reading a second, tuple-indexed table.
+// INT quads multiplied with fp16 activations (fused GEMV): the blob's decode entries
+// are {f | bias << 16, the high bytes of the fp16 values of the stored tuple's four
+// codes}, so a step reads one table entry and rebuilds both fp16 code pairs with byte
+// permutes (an integer code |q| <= 8 has an fp16 value whose low byte is zero); the
+// table is staged as it is stored.  The other INT quad decoders turn the entries back
+// into symbol form in the prologue and read a tuple-indexed table.
 template <int PAY, int CB, int KW, bool MAT, bool XBF>
 constexpr bool kQuadF = kQuad<PAY, CB, KW> && !MAT && !XBF;
 // Table entries whose high word is the bias alone (no payload bits beside it).
@@ -202,7 +203,7 @@ __device__ __forceinline__ uint2 decode_step(uint32_t& x, uint32_t lut, uint32_t
   return e;
 }
 
-// A4 for the rewritten INT quad entries: x = f * (x >> m) + bias with f and bias the
+// A4 for the INT quad entries as stored: x = f * (x >> m) + bias with f and bias the
 // two halves of the entry's low word, taken by sub-dword operand selection (two VALU
 // operations, as for the plain entries' mask and multiply-add).
 __device__ __forceinline__ uint2 decode_step_q(uint32_t& x, uint32_t lut, uint32_t m, uint32_t mmask) {
@@ -494,12 +495,6 @@ __device__ __forceinline__ const uint8_t* raw_tile(const TArgs& a, uint32_t rg, 
   return a.raw + (uint64_t)rg * a.raw_rg_bytes + (uint64_t)sl * a.raw_full_bytes + lane * 16;
 }
 
-// Start of a wave's word stream over tiles [t0, t1): chunk-aligned word start gb,
-// chunk count nch, first read position rposb (bytes from gb), the first tile's
-// start state, the first two chunks and the one-ahead prefetch.  Filled in two
-// phases so the loads overlap the block's table staging: head_begin issues the
-// tile offsets and start state, head_chunks (after staging, before the barrier)
-// the first chunk loads.
 // Wave priority by the work a wave has left in its tile: `left` of `total` steps (or
 // lattice blocks), four levels by quarter.  Blocks sharing a CU start about a
 // microsecond apart and the later one stages its tables more slowly while the first
@@ -514,6 +509,12 @@ __device__ __forceinline__ void prio_by_work_left(uint32_t left, uint32_t total)
   else __builtin_amdgcn_s_setprio(0);
 }
 
+// Start of a wave's word stream over tiles [t0, t1): chunk-aligned word start gb,
+// chunk count nch, first read position rposb (bytes from gb), the first tile's
+// start state, the first two chunks and the one-ahead prefetch.  Filled in two
+// phases so the loads overlap the block's table staging: head_begin issues the
+// tile offsets and start state, head_chunks (after staging, before the barrier)
+// the first chunk loads.
 struct StreamHead {
   uint32_t gb, nch, rposb, st;
   uint2 c0, c1, pre;
@@ -562,7 +563,7 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
   constexpr int U = 16;
   constexpr bool BF2 = kBfSym2<PAY, KW>;               // bf16 exponent-pair symbols
   constexpr bool QD = kQuad<PAY, CB, KW>;              // INT quads over stored tuples
-  constexpr bool QF = kQuadF<PAY, CB, KW, MAT, XBF>;    // ... with rewritten entries (fp16 x)
+  constexpr bool QF = kQuadF<PAY, CB, KW, MAT, XBF>;    // ... codes in the entries (fp16 x)
   constexpr bool DOT = kDot<PAY, KW> || (BF2 && XBF);
   constexpr bool BFP = kBfPair<PAY, KW, XBF> && !MAT;   // bf16 weight pairs, two steps per dot
   constexpr int RG = BF2 ? 2 : 1;                      // raw 16-byte groups per U steps
@@ -818,11 +819,19 @@ __device__ __forceinline__ void wave_body_deq(const TArgs& a, const StreamHead& 
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
-          const uint2 e = decode_step<CLEAN>(x, lut, m, mmask);
+          const uint2 e = QD ? decode_step_q(x, lut, m, mmask) : decode_step<CLEAN>(x, lut, m, mmask);
           uint32_t v[KW];                                   // this step's weights, 16-bit
-          if constexpr (PAY == 1) {
-            // INT quads: the stored tuple's digits from the block's tuple table
-            const uint32_t aux = QD ? *lds_ptr<const uint32_t>(e.y >> 16) : e.x >> 24;
+          if constexpr (QD) {
+            // INT quads: the codes' fp16 values, rebuilt from the entry's high bytes
+            const uint32_t cp[2] = {__builtin_amdgcn_perm(e.y, e.y, 0x010C000Cu),
+                                    __builtin_amdgcn_perm(e.y, e.y, 0x030C020Cu)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float q = (float)__builtin_bit_cast(_Float16, (uint16_t)(cp[i >> 1] >> (16 * (i & 1))));
+              v[i] = to16<OBF>(exact_product(q, scale));
+            }
+          } else if constexpr (PAY == 1) {
+            const uint32_t aux = e.x >> 24;
             constexpr int half = 1 << (CB - 1);
 #pragma unroll
             for (int i = 0; i < KW; ++i) {
@@ -902,7 +911,7 @@ __device__ __forceinline__ void wave_body_rows2(const TArgs& a, const StreamHead
                                                 uint32_t lane, bool activeB, float* accA, float* accB) {
   static_assert(PAY == 1 || PAY == 3, "two row streams per wave: INT codes and FP8 only");
   constexpr int U = 16;
-  constexpr bool QF = kQuadF<PAY, CB, KW, false, XBF>;   // INT quads (fp16 x): rewritten entries
+  constexpr bool QF = kQuadF<PAY, CB, KW, false, XBF>;   // INT quads (fp16 x): codes in the entries
   static_assert(!kQuad<PAY, CB, KW> || QF, "two streams of INT quads: fp16 activations only");
   constexpr bool DOT = kDot<PAY, KW>;
   constexpr bool CLEAN = kCleanBias<PAY, CB, KW>;
@@ -1282,10 +1291,12 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
   const uint32_t c_lo = sl_blk * a.tile_cols;
   const uint32_t c_hi = min(sl_blk_end * a.tile_cols, a.cols);
   constexpr bool E8F8 = E8 && CB == 1;            // E8: CB selects the FP8 reconstruction
-  // (rewritten quad entries: the tuple table is only needed in the prologue and sits
-  // in the rings' space, which the streams fill after the rewrite)
-  const uint32_t pair_bytes = QF   ? 0
-                              : QD ? (a.quad_t * 8 + 15) & ~15u
+  // INT quads: the fused product with fp16 activations and the dequantising decode
+  // take the codes from the decode entries; the bf16 product and the decode-only
+  // hook read a tuple-indexed table (entries turned back into symbol form below)
+  constexpr bool QT = QD && !QF && !DEQ;
+  const uint32_t pair_bytes = QT   ? (a.quad_t * 8 + 15) & ~15u
+                              : QD ? 0
                                    : PTAB ? kPairTableBytes : (E8F8 ? kE8F8TableBytes : 0);
   const uint32_t lut = pair_bytes;
   const uint32_t lut_bytes = a.lut_entries * (E8 ? 4 : 8);
@@ -1323,12 +1334,13 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
     const uint32_t idx = tid + (uint32_t)i * bd;
     if (idx < nl16) lv[i] = lsrc[idx];
   }
-  // INT quads: the first round of stored tuples goes out with the table, ahead of the
-  // word chunks, so the staging barrier does not wait for the chunks
-  constexpr int KT = QD ? 4 : 1;
+  // INT quads in symbol form: the first round of stored tuples goes out with the
+  // table, ahead of the word chunks, so the staging barrier does not wait for the
+  // chunks
+  constexpr int KT = QT ? 4 : 1;
   const uint16_t* tup = reinterpret_cast<const uint16_t*>(a.tables + sizeof(TableRecord));
   uint32_t tv[KT];
-  if constexpr (QD) {
+  if constexpr (QT) {
 #pragma unroll
     for (int i = 0; i < KT; ++i) {
       const uint32_t idx = tid + (uint32_t)i * bd;
@@ -1398,18 +1410,16 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
     if (tid < nxv) x_store(tid, xv0);
     for (uint32_t v = tid + bd; v < nxv; v += bd) x_store(v, x_load(v));
   }
-  if constexpr (QD) {
-    // stored tuple i -> its four codes as two packed 16-bit floats of the
-    // activations' type (decode-only kernels: the tuple's digits), at byte 8 i (of the
-    // rings' space when the entries are rewritten)
-    const uint32_t tbase = QF ? rings : 0u;
+  if constexpr (QT) {
+    // stored tuple i -> its four codes as two packed bf16 numbers (decode-only
+    // kernels: the tuple's digits), at byte 8 i
     auto t_store = [&](uint32_t i, uint32_t v) {
       uint2 e = make_uint2(v, 0u);
       if constexpr (!MAT) {
         e.x = small_int_bits<XBF>((int)(v & 15) - 8) | (small_int_bits<XBF>((int)((v >> 4) & 15) - 8) << 16);
         e.y = small_int_bits<XBF>((int)((v >> 8) & 15) - 8) | (small_int_bits<XBF>((int)(v >> 12) - 8) << 16);
       }
-      lds_store2(tbase + i * 8, e);
+      lds_store2(i * 8, e);
     };
 #pragma unroll
     for (int i = 0; i < KT; ++i) {
@@ -1436,14 +1446,47 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
     }
   }
   __syncthreads();
-  if constexpr (QF) {
-    // rewrite every decode entry: {f, bias | h16 << 16} -> {f | bias << 16, the high
-    // bytes of the fp16 values of the stored tuple's codes} (h16 = 8 x tuple index: the
-    // tuple's byte offset in the table staged at `rings`)
-    for (uint32_t i = tid; i < a.lut_entries; i += bd) {
-      const uint2 e = lds_load2(lut + i * 8);
-      const uint2 c = lds_load2(rings + (e.y >> 16));
-      lds_store2(lut + i * 8, make_uint2((e.x & 0xFFFFu) | (e.y << 16), __builtin_amdgcn_perm(c.y, c.x, 0x07050301u)));
+  if constexpr (QT) {
+    // INT quad entries {f | bias << 16, the codes' fp16 high bytes} -> {f, bias | 8 s << 16}
+    // with s the slot's symbol: the symbols' runs of slots are in symbol order and
+    // each starts at bias 0, so s + 1 is the number of run starts up to the slot.
+    // Each thread takes a contiguous range of slots; a block-wide prefix sum of their
+    // start counts (wave totals in the rings' space, free until the streams start)
+    // gives each range its first s.
+    constexpr uint32_t KS = 16;                  // slots read per round, all in flight
+    constexpr uint32_t kNoStart = 1u << 16;      // stand-in past the range: bias 1, not a start
+    const uint32_t per = (a.lut_entries + bd - 1) / bd;
+    const uint32_t s0 = min(tid * per, a.lut_entries), s1 = min(s0 + per, a.lut_entries);
+    uint32_t cnt = 0;
+    for (uint32_t c = s0; c < s1; c += KS) {
+      uint32_t lo[KS];
+#pragma unroll
+      for (uint32_t k = 0; k < KS; ++k) lo[k] = c + k < s1 ? *lds_ptr<const uint32_t>(lut + (c + k) * 8) : kNoStart;
+#pragma unroll
+      for (uint32_t k = 0; k < KS; ++k) cnt += (lo[k] >> 16) == 0u ? 1u : 0u;
+    }
+    uint32_t incl = cnt;                         // inclusive prefix over the wave's lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_up((int)incl, (unsigned)d, 64);
+      if ((int)lane >= d) incl += v;
+    }
+    if (lane == 63) *lds_ptr<uint32_t>(rings + wid * 4) = incl;
+    __syncthreads();
+    uint32_t sym = incl - cnt - 1u;              // starts before s0, minus one
+    for (uint32_t w = 0; w < wid; ++w) sym += *lds_ptr<const uint32_t>(rings + w * 4);
+    for (uint32_t c = s0; c < s1; c += KS) {
+      uint32_t lo[KS];
+#pragma unroll
+      for (uint32_t k = 0; k < KS; ++k) lo[k] = c + k < s1 ? *lds_ptr<const uint32_t>(lut + (c + k) * 8) : kNoStart;
+#pragma unroll
+      for (uint32_t k = 0; k < KS; ++k) {
+        if (c + k < s1) {
+          const uint32_t bias = lo[k] >> 16;
+          sym += bias == 0u ? 1u : 0u;
+          lds_store2(lut + (c + k) * 8, make_uint2(lo[k] & 0xFFFFu, bias | ((8u * sym) << 16)));
+        }
+      }
     }
     __syncthreads();
   }
@@ -1671,17 +1714,17 @@ static uint64_t lds_bytes(const ecw_tensor* t, uint32_t W, uint32_t R, uint32_t 
   if (e8 && t->coding.recon_dtype == ECW_DT_FP8_E4M3) pair = kE8F8TableBytes;
   const bool quads = quad_coding(t->coding.payload, t->coding.code_bits, t->coding.weights_per_symbol);
   const uint64_t tuples = (8ull * t->coding.stored_tuples + 15) / 16 * 16;
-  // fused quads with fp16 activations: the tuple table lives in the rings' space
-  const bool quad_rewrite = quads && !mat && !xbf;
-  if (quads) pair = quad_rewrite ? 0 : tuples;
+  // the fused product with fp16 activations (!mat, !xbf) and the dequantising decode
+  // (mat, xbf) read the codes of INT quads from the decode entries
+  const bool quad_codes_in_entries = quads && mat == xbf;
+  if (quads) pair = quad_codes_in_entries ? 0 : tuples;
   const uint64_t lut = ((uint64_t)t->n_tables << t->coding.log2_m) * (e8 ? 4 : 8) / 8;
   const uint64_t xs = mat ? 0 : ((uint64_t)xs_cols * B * (dot ? 2 : 4) + 15) / 16 * 16;
   const bool two = !mat && two_streams(t, xbf);
   (void)R;
   // dequantising decode: a 64-row tile per wave (lattice fields: 16 rows)
   const uint64_t stage = mat ? (uint64_t)W * (e8 ? 16 : 64) * kStagePitch : 0;
-  uint64_t rings = (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
-  if (quad_rewrite) rings = std::max(rings, tuples);
+  const uint64_t rings = (uint64_t)W * (two ? 2 : 1) * kRingStride * 2;
   return pair + lut * 8 + xs + rings + stage;
 }
 
@@ -2081,7 +2124,7 @@ static ecw_status launch_decode_only(ecw_stream stream, const ecw_tensor* t, uin
   ka.block_begin[0] = 0;
   KernelFn fn = deq_out ? pick_kernel<1, true, true>(t->coding) : pick_kernel<1, true, false>(t->coding);
   if (!fn) return fail(ECW_E_UNSUPPORTED, "no kernel for this payload / code width");
-  const uint64_t lds = lds_bytes(t, W, 1, 0, 1, true, false);
+  const uint64_t lds = lds_bytes(t, W, 1, 0, 1, true, deq_out != nullptr);
   if (lds > 160 * 1024) return fail(ECW_E_UNSUPPORTED, "decode table needs more than 160 KiB of LDS");
   if (!lds_attribute_set(fn)) return fail(ECW_E_HIP, "hipFuncSetAttribute failed");
   const uint32_t grid = (ka.n_blocks + 7) / 8 * 8;

@@ -153,7 +153,7 @@ typedef struct {
  * distinct symbols than M slots, alphabet > 256). */
 ecw_status enc_build_tables(const ecw_coding* c, const void* w, ecw_tables* out);
 
-/* Encode `w` into a self-describing blob (format version 1, little-endian): the
+/* Encode `w` into a self-describing blob (format version 2, little-endian): the
  * symbols of each tile of 64 rows x tile_cols columns are rANS-coded as one
  * independent stream per tile with 32-bit states and 16-bit words, and the blob
  * stores what the EntroPack page lists as the stored representation (Section 3.6:

@@ -46,7 +46,7 @@ def test_byte_parity_with_oracle_and_oracle_decodes_library_blob(case):
     blob = ecw.encode(case.lib_coding(), case.logical, case.scales)
     comp = P.encode(case.oracle_coding(), case.logical, case.scales)
     bl = blobfmt.parse(blob)
-    assert bl.h["magic"] == 0x31574345 and bl.h["version"] == 1
+    assert bl.h["magic"] == 0x31574345 and bl.h["version"] == 2
     assert bl.h["total_bytes"] == blob.size
     alphabet, voff, freq = blobfmt.tables(bl)
     qt = blobfmt.quad_tables(bl)
@@ -215,7 +215,8 @@ def test_prepare_accepts_valid_blob():
 @pytest.mark.parametrize("name,fn,expect", [
     ("truncated", None, 3),
     ("bad_magic", lambda b: _u32(b, 0, 0xDEADBEEF), 3),
-    ("bad_version", lambda b: _u32(b, 4, 2), 2),
+    ("bad_version", lambda b: _u32(b, 4, 3), 2),
+    ("old_version", lambda b: _u32(b, 4, 1), 2),
     ("bad_section_count", lambda b: _u32(b, 12, 6), 3),
     ("bad_tile_rows", lambda b: _u32(b, 40, 32), 2),
     ("geometry_mismatch", lambda b: _u32(b, 64, 7), 3),
@@ -501,18 +502,27 @@ def test_quad_tables_match_oracle():
         assert (t.escapes > 0) == (case.stored_tuples < 1000)
 
 
-def test_quad_entry_payload_is_the_tuple_table_offset():
-    # a8 = 0; h16 = 8 * symbol, the byte offset of the stored tuple's entry in the
-    # per-block table of its four codes
-    case = [c for c in cases.quad_cases() if c.name == "quads_t64_m10_ragged"][0]
+@pytest.mark.parametrize("name", ["quads_t64_m10_ragged", "quads_t2048_m12"])
+def test_quad_entry_holds_state_update_and_fp16_codes(name):
+    # lo = f | bias << 16; hi = the high bytes of the fp16 values of the symbol's four
+    # codes (code i in byte i), all from the oracle's stored tuples and frequencies
+    case = [c for c in cases.quad_cases() if c.name == name][0]
     bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
-    tup, fq, _, _ = blobfmt.quad_tables(bl)
-    lut = blobfmt.lut(bl)[0]
-    sym = np.repeat(np.arange(tup.size), fq)
+    comp = P.encode(case.oracle_coding(), case.logical, case.scales)
+    n = comp.stored.size
+    fq = comp.freq[0, :n].astype(np.int64)
+    lut = blobfmt.lut(bl)[0].astype(np.int64)
+    sym = np.repeat(np.arange(n), fq)
     cum = np.concatenate([[0], np.cumsum(fq)[:-1]])
-    assert np.array_equal(lut[:, 0], fq[sym])
-    assert np.array_equal(lut[:, 1] & 0xFFFF, np.arange(lut.shape[0]) - cum[sym])
-    assert np.array_equal(lut[:, 1] >> 16, 8 * sym)
+    assert lut.shape[0] == sym.size
+    assert np.array_equal(lut[:, 0] & 0xFFFF, fq[sym])
+    assert np.array_equal(lut[:, 0] >> 16, np.arange(lut.shape[0]) - cum[sym])
+    tup = comp.stored.astype(np.int64)[sym]
+    for i in range(4):
+        code = ((tup >> (4 * i)) & 15) - 8
+        hb = code.astype(np.float16).view(np.uint16).astype(np.int64)
+        assert np.all(hb & 0xFF == 0)
+        assert np.array_equal((lut[:, 1] >> (8 * i)) & 0xFF, hb >> 8)
 
 
 def test_quad_coding_limits_and_validation():
