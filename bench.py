@@ -340,27 +340,6 @@ def stored_of(t) -> int:
     return t.bytes_words + t.bytes_raw + t.bytes_tile_meta + t.bytes_tables + t.bytes_scales
 
 
-def launch_grid(ts, x_bf16: bool = False) -> int:
-    """Threads of the one kernel a grouped launch of tensor descriptors ts runs (the
-    library's block count, rounded up to a multiple of 8 blocks, times the block
-    size): how the profiler's dispatches are matched to launches."""
-    blocks = 0
-    W = ts[0].waves_per_block
-    for t in ts:
-        if t.coding.rows == 0 or t.n_tiles == 0:
-            continue
-        c = t.coding
-        quads = c.payload == 1 and c.code_bits == 4 and c.weights_per_symbol == 4
-        two = t.streams_per_wave == 2 and c.payload not in (2, 4) and not (quads and x_bf16)
-        ns = 2 if two else 1
-        per = t.waves_per_block * t.tiles_per_wave
-        n_sg = (t.n_slices + per - 1) // per
-        units = (t.n_row_groups + ns - 1) // ns
-        rpb = max(1, t.row_groups_per_block)
-        blocks += (units + rpb - 1) // rpb * n_sg
-    return (blocks + 7) // 8 * 8 * W * 64
-
-
 def kernel_sig(c, batch: int, x_bf16: bool) -> str:
     """The fused kernel's template arguments for a coding (PAY, CB, KW, B, MAT, XBF)."""
     cb = c.code_bits if c.payload == 1 else (1 if c.payload == 4 and c.recon_dtype == 5 else 0)
@@ -371,7 +350,7 @@ def kernel_sig(c, batch: int, x_bf16: bool) -> str:
            f"{'true' if xbf else 'false'}>"
 
 
-LAUNCH_MAP = {}      # row -> launch -> [kernel template, grid threads, block threads, symbols]
+LAUNCH_MAP = {}      # row -> launch -> [kernel template, grid threads, block threads, symbols, LDS bytes]
 
 
 def launch_symbols(ts) -> int:
@@ -384,8 +363,26 @@ def launch_symbols(ts) -> int:
 
 
 def note_launch(row: str, launch: str, ts, batch: int, x_bf16: bool):
-    LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), launch_grid(ts, x_bf16),
-                                              ts[0].waves_per_block * 64, launch_symbols(ts)]
+    """Record how the profiler's dispatches of a launch are recognised: the kernel
+    template and the grid, block and LDS sizes the library reports for it."""
+    grid, block, lds = ecw.group_geometry(ts, batch, ecw.DT_BF16 if x_bf16 else ecw.DT_F16)
+    LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), grid, block,
+                                              launch_symbols(ts), lds]
+
+
+def dispatch_launches(lm: dict, kname: str, grid: int, wg: int, lds: int) -> list:
+    """The (row, launch) pairs of the launch map a profiled dispatch belongs to: same
+    kernel template, grid and block size; where several launches share those, the one
+    whose LDS size is nearest the dispatch's (launches of every row that match equally
+    well are all returned, so repeated workloads pool their dispatches)."""
+    cands = [(row, ln, e[4] if len(e) > 4 else None) for row, launches in lm.items()
+             for ln, e in launches.items() if e[1] == grid and e[2] == wg and e[0] in kname]
+    if not cands:
+        return []
+    if any(c[2] is None for c in cands) or lds is None:
+        return [(r, ln) for r, ln, _ in cands]
+    best = min(abs(c[2] - lds) for c in cands)
+    return [(r, ln) for r, ln, l in cands if abs(l - lds) == best]
 
 
 def bytes_row(us: float, stored: int, unc: float) -> dict:
@@ -1033,8 +1030,17 @@ def dequant_gemm(steps: int, cold_bytes: float):
     return out
 
 
+def _lds_of(r: dict) -> int:
+    """LDS bytes of a dispatch in a rocprofv3 CSV row (kernel traces name the column
+    after the group segment, counter collections after the LDS block)."""
+    for k in ("LDS_Block_Size", "Group_Segment_Size", "Lds_Size"):
+        if r.get(k) not in (None, ""):
+            return int(float(r[k]))
+    return 0
+
+
 def summarize_rocprof(directory: str):
-    """Print per-(kernel, grid size) averages from rocprofv3 CSV output under
+    """Print per-(kernel, grid size, LDS size) averages from rocprofv3 CSV output under
     `directory`: kernel durations from *_kernel_trace.csv and counter values from
     *_counter_collection.csv (one line per kernel and counter)."""
     import csv
@@ -1043,27 +1049,28 @@ def summarize_rocprof(directory: str):
     for path in sorted(glob.glob(os.path.join(directory, "**", "*_kernel_trace.csv"), recursive=True)):
         d = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
-            key = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size_X"]))
+            key = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size_X"]), _lds_of(r))
             d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         print(f"# kernel durations from {os.path.relpath(path, directory)}")
-        print(f"{'kernel':48s} {'grid':>8s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s}")
-        for (k, g), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{'kernel':48s} {'grid':>8s} {'lds':>7s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s}")
+        for (k, g, lds), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
             v.sort()
-            print(f"{k[:48]:48s} {g:8d} {len(v):6d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} {v[0]:8.2f}")
+            print(f"{k[:48]:48s} {g:8d} {lds:7d} {len(v):6d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} "
+                  f"{v[0]:8.2f}")
     for path in sorted(glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True)):
         per = collections.defaultdict(lambda: collections.defaultdict(float))
         names = {}
         for r in csv.DictReader(open(path)):
             per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
-            names[r["Dispatch_Id"]] = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size"]))
+            names[r["Dispatch_Id"]] = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size"]), _lds_of(r))
         agg = collections.defaultdict(lambda: collections.defaultdict(list))
         for did, cs in per.items():
             for c, v in cs.items():
                 agg[names[did]][c].append(v)
         print(f"# counters from {os.path.relpath(path, directory)} (mean per dispatch)")
-        for (k, g), cs in sorted(agg.items()):
+        for (k, g, lds), cs in sorted(agg.items()):
             for c, v in sorted(cs.items()):
-                print(f"{k[:48]:48s} {g:8d} {c:24s} n={len(v):4d} {sum(v) / len(v):16.1f}")
+                print(f"{k[:48]:48s} {g:8d} {lds:7d} {c:24s} n={len(v):4d} {sum(v) / len(v):16.1f}")
 
 
 
@@ -1084,9 +1091,10 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
         for r in csv.DictReader(open(path)):
             key = (path, r["Dispatch_Id"])
             per[key][r["Counter_Name"]] += float(r["Counter_Value"])
-            names[key] = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            names[key] = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]), _lds_of(r))
             per[key]["VGPR_Count"] = float(r["VGPR_Count"])
             per[key]["LDS_Block_Size"] = float(r["LDS_Block_Size"])
+    owners = {key: dispatch_launches(lm, *nm) for key, nm in names.items()}
     lines = ["# Mean SQ counters per dispatch of every launch of every workload bench.py measures, MI355X.",
              "# Read by bench.py (VALU, LDS and bank-conflict fractions per launch, priced at the clock measured",
              "# in the same bench run); valid only while the kernel source and tune files hash to the values below.",
@@ -1099,11 +1107,10 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
              "bank-conflict share of LDS-active cycles | dependency waits / wave cycles |",
              "|---|---|---|---|---|---|---|---|---|"]
     for row, launches in lm.items():
-        for ln, (sig, grid, wg, nsym) in launches.items():
+        for ln, (sig, grid, wg, nsym, *_) in launches.items():
             agg = collections.defaultdict(list)
             for key, cs in per.items():
-                kname, g, w = names[key]
-                if g == grid and w == wg and sig in kname:
+                if (row, ln) in owners[key]:
                     for c, v in cs.items():
                         agg[c].append(v)
             if not agg:

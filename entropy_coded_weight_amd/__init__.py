@@ -109,6 +109,7 @@ def lib():
     L.dec_dequantize.argtypes = [vp, P(Tensor), vp, i32]
     L.dec_gemv_group_workspace_size.argtypes = [P(P(Tensor)), i32, i32, P(sz)]
     L.dec_gemv_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz]
+    L.dec_gemv_group_geometry.argtypes = [P(P(Tensor)), i32, i32, i32, P(u32), P(u32), P(sz)]
     L.dec_tune_launch.argtypes = [vp, P(Tensor), vp, i32, vp, i32, vp, sz, P(u32), i32, i32,
                                   P(ctypes.c_float)]
     L.dec_time_group.argtypes = [vp, P(P(Tensor)), i32, vp, i32, P(vp), i32, vp, sz, i32,
@@ -117,7 +118,8 @@ def lib():
     L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
     L.ecw_probe_clock.argtypes = [vp, u32, u32, vp, P(u32)]
     for f in ("enc_build_tables", "enc_encode", "enc_e8_nearest", "dec_prepare", "dec_gemv_workspace_size",
-              "dec_gemv", "dec_gemv_noalloc", "dec_gemv_group_workspace_size", "dec_gemv_group", "dec_materialize", "dec_dequantize",
+              "dec_gemv", "dec_gemv_noalloc", "dec_gemv_group_workspace_size", "dec_gemv_group",
+              "dec_gemv_group_geometry", "dec_materialize", "dec_dequantize",
               "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup",
               "ecw_probe_clock"):
         getattr(L, f).restype = ctypes.c_int
@@ -228,6 +230,16 @@ def group_workspace_size(ts, batch: int) -> int:
     _check(lib().dec_gemv_group_workspace_size(_tensor_array(ts), len(ts), batch, ctypes.byref(n)),
            "dec_gemv_group_workspace_size")
     return n.value
+
+
+def group_geometry(ts, batch: int, x_dtype: int = None):
+    """dec_gemv_group_geometry: (grid threads, block threads, dynamic LDS bytes) of the
+    launch dec_gemv_group makes for tensors ts (no GPU needed)."""
+    g, b, l = ctypes.c_uint32(0), ctypes.c_uint32(0), ctypes.c_size_t(0)
+    _check(lib().dec_gemv_group_geometry(_tensor_array(ts), len(ts), batch, DT_F16 if x_dtype is None else x_dtype,
+                                         ctypes.byref(g), ctypes.byref(b), ctypes.byref(l)),
+           "dec_gemv_group_geometry")
+    return g.value, b.value, l.value
 
 
 def gemv_group_raw(ts, x: torch.Tensor, ys, workspace: torch.Tensor | None, stream=None):

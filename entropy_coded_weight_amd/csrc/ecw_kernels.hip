@@ -1830,6 +1830,16 @@ static ecw_status check_group(const ecw_tensor* const* ts, int n, int batch, int
   return ECW_OK;
 }
 
+// Blocks and dynamic LDS bytes per block of one member of a fused launch with W
+// waves per block.
+static void member_geometry(const ecw_tensor* t, uint32_t W, int B, bool xbf, uint32_t* n_blocks, uint64_t* lds) {
+  const uint32_t ns = two_streams(t, xbf) ? 2u : 1u;
+  const uint32_t units = (t->n_row_groups + ns - 1) / ns;
+  const uint32_t rpb = std::max(1u, t->row_groups_per_block);
+  *n_blocks = (units + rpb - 1) / rpb * slice_groups(t);
+  *lds = lds_bytes(t, W, t->tiles_per_wave, W * t->tiles_per_wave * t->coding.tile_cols, B, false, xbf);
+}
+
 // Fused decode + GEMV of a group of tensors that read the same x: one launch.
 // tickets[i] / partials[i]: tensor i's arrival tickets and partial sums (used only
 // when its row groups span several blocks).  Arguments already checked.
@@ -1861,13 +1871,12 @@ static ecw_status launch_core(ecw_stream stream, const ecw_tensor* const* ts, in
     a.ns = t->streams_per_wave;
     a.rpb = std::max(1u, t->row_groups_per_block);
     a.n_sg = slice_groups(t);
-    const uint32_t ns = two_streams(t, x_dtype == ECW_DT_BF16) ? 2u : 1u;
-    const uint32_t units = (a.n_rg + ns - 1) / ns;
-    a.n_blocks = (units + a.rpb - 1) / a.rpb * a.n_sg;
+    uint64_t member_lds = 0;
+    member_geometry(t, W, B, x_dtype == ECW_DT_BF16, &a.n_blocks, &member_lds);
     ka.block_begin[ka.nt] = blocks;
     a.xs_cols = W * t->tiles_per_wave * t->coding.tile_cols;
     blocks += a.n_blocks;
-    lds = std::max(lds, lds_bytes(t, W, t->tiles_per_wave, a.xs_cols, B, false, x_dtype == ECW_DT_BF16));
+    lds = std::max(lds, member_lds);
     if (a.n_sg > 1) {
       a.tickets = tickets[i];
       a.partials = partials[i];
@@ -1999,6 +2008,36 @@ extern "C" ecw_status dec_gemv_group_workspace_size(const ecw_tensor* const* t, 
     if (!t[i] || t[i]->waves_per_block < 1 || t[i]->waves_per_block > 16 || t[i]->tiles_per_wave < 1)
       return fail(ECW_E_INVALID_ARG, "bad tensor or launch shape");
   *bytes = (size_t)group_workspace(t, n, batch, nullptr);
+  return ECW_OK;
+}
+
+extern "C" ecw_status dec_gemv_group_geometry(const ecw_tensor* const* t, int n, int batch, int x_dtype,
+                                              uint32_t* grid_threads, uint32_t* block_threads, size_t* lds_bytes_out) {
+  clear_error();
+  if (!t || n < 1 || n > kMaxGroup || !grid_threads || !block_threads || !lds_bytes_out)
+    return fail(ECW_E_INVALID_ARG, "bad arguments");
+  if (batch < 1 || batch > 4) return fail(ECW_E_INVALID_ARG, "batch must be 1..4");
+  if (x_dtype != ECW_DT_F16 && x_dtype != ECW_DT_BF16) return fail(ECW_E_INVALID_ARG, "x dtype must be F16 or BF16");
+  for (int i = 0; i < n; ++i) {
+    if (!t[i] || t[i]->waves_per_block < 1 || t[i]->waves_per_block > 16 || t[i]->tiles_per_wave < 1)
+      return fail(ECW_E_INVALID_ARG, "bad tensor or launch shape");
+    if (t[i]->waves_per_block != t[0]->waves_per_block)
+      return fail(ECW_E_INVALID_ARG, "grouped tensors must share waves per block");
+  }
+  const uint32_t W = t[0]->waves_per_block;
+  uint32_t blocks = 0;
+  uint64_t lds = 0;
+  for (int i = 0; i < n; ++i) {
+    if (t[i]->coding.rows == 0 || t[i]->n_tiles == 0) continue;
+    uint32_t nb = 0;
+    uint64_t l = 0;
+    member_geometry(t[i], W, batch > 1 ? 4 : 1, x_dtype == ECW_DT_BF16, &nb, &l);
+    blocks += nb;
+    lds = std::max(lds, l);
+  }
+  *grid_threads = (blocks + 7) / 8 * 8 * W * 64;
+  *block_threads = W * 64;
+  *lds_bytes_out = (size_t)lds;
   return ECW_OK;
 }
 

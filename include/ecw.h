@@ -260,6 +260,17 @@ ecw_status dec_gemv_group(ecw_stream stream, const ecw_tensor* const* t, int n, 
                           int x_dtype, float* const* y, int batch, void* workspace,
                           size_t workspace_bytes);
 
+/* Geometry of the one kernel dec_gemv_group launches for these tensors at this
+ * batch and activation type, from their launch shapes: grid and block size in
+ * threads (grid_threads = 0 when no member has work) and the dynamic LDS bytes per
+ * block.  These are the values a profiler's dispatch record shows, so profiles can
+ * be matched to launches (two launches with the same kernel and grid differ in
+ * LDS); nothing is launched.  Host-only: callable without a GPU.
+ * Errors: INVALID_ARG (NULL pointers, n outside 1..8, batch outside 1..4, x_dtype
+ * not F16/BF16, a bad launch shape or members with different waves per block). */
+ecw_status dec_gemv_group_geometry(const ecw_tensor* const* t, int n, int batch, int x_dtype,
+                                   uint32_t* grid_threads, uint32_t* block_threads, size_t* lds_bytes);
+
 /* Launch-shape autotuning for one tensor (MINE page, Section 4.2: per-tensor
  * tuning of the kernel configuration by measured time).  For each candidate shape
  * shapes[4i..4i+3] = (waves_per_block, tiles_per_wave, streams_per_wave,

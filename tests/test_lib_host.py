@@ -525,6 +525,29 @@ def test_quad_entry_holds_state_update_and_fp16_codes(name):
         assert np.array_equal((lut[:, 1] >> (8 * i)) & 0xFF, hb >> 8)
 
 
+def test_group_geometry_is_the_launch_the_shape_defines():
+    # 130 x 512 INT quads, 256-wide tiles, t = 2048, M = 2^12
+    case = [c for c in cases.quad_cases() if c.name == "quads_t2048_m12"][0]
+    t = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    t.waves_per_block, t.tiles_per_wave = 2, 1
+    grid, block, lds16 = ecw.group_geometry([t], 1, ecw.DT_F16)
+    # 3 row groups x 1 slice group (2 slices on 2 waves): 3 blocks, rounded up to 8
+    assert (grid, block) == (8 * 2 * 64, 2 * 64)
+    # the bf16 product adds the tuple-indexed table (8 bytes per stored tuple); the
+    # fp16 product reads the codes from the decode entries (M x 8 bytes in both)
+    _, _, lds_bf = ecw.group_geometry([t], 1, ecw.DT_BF16)
+    assert lds_bf - lds16 == 8 * 2048 and lds16 > 8 * 4096
+    t.waves_per_block = 1
+    grid1, block1, _ = ecw.group_geometry([t], 4, ecw.DT_F16)
+    assert (grid1, block1) == (8 * 64, 64)          # 3 row groups x 2 slice groups = 6 blocks
+    u = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    u.waves_per_block = 2
+    with pytest.raises(ecw.EcwError):
+        ecw.group_geometry([t, u], 1, ecw.DT_F16)    # members must share waves per block
+    with pytest.raises(ecw.EcwError):
+        ecw.group_geometry([u], 5, ecw.DT_F16)
+
+
 def test_quad_coding_limits_and_validation():
     L = ecw.lib()
     w = np.zeros((64, 128), np.int8)
@@ -579,3 +602,37 @@ def test_quad_coding_limits_and_validation():
     b = base.copy()
     b[off_t + 520 + 2 * 63] = 1
     assert _prep_status(b) == 3
+
+
+def test_counter_record_separates_launches_by_lds(tmp_path, monkeypatch):
+    # two launches of one kernel template with the same grid and block size (the layer
+    # set's gate/up and down can be) are told apart by their LDS size
+    import csv
+    import json
+    import bench
+    sig = "k_decode<1, 4, 4, 1, false, false>"
+    lm = {"2": {"gate_up": [sig, 458752, 1024, 1000, 43008], "down": [sig, 458752, 1024, 2000, 38912]},
+          "k": {"gate_up": ["k_decode<1, 4, 2, 1, false, false>", 917504, 256, 3000, 20480]}}
+    assert bench.dispatch_launches(lm, f"void ecw::{sig}(unsigned int)", 458752, 1024, 43008) == [("2", "gate_up")]
+    assert bench.dispatch_launches(lm, f"void ecw::{sig}(unsigned int)", 458752, 1024, 39424) == [("2", "down")]
+    assert bench.dispatch_launches(lm, f"void ecw::{sig}(unsigned int)", 917504, 1024, 43008) == []
+    d = tmp_path / "sq0"
+    d.mkdir()
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "LDS_Block_Size", "VGPR_Count",
+              "Counter_Name", "Counter_Value"]
+    with open(d / "sq0_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for did, lds, valu in [(1, 43008, 100), (2, 38912, 40), (3, 43008, 120), (4, 38912, 60)]:
+            for name, v in [("SQ_INSTS_VALU", valu), ("SQ_WAVES", 7168)]:
+                w.writerow({"Dispatch_Id": did, "Kernel_Name": f"void ecw::{sig}(unsigned int)",
+                            "Grid_Size": 458752, "Workgroup_Size": 1024, "LDS_Block_Size": lds, "VGPR_Count": 64,
+                            "Counter_Name": name, "Counter_Value": v})
+    lmp = tmp_path / "launch_map.json"
+    lmp.write_text(json.dumps(lm))
+    out = tmp_path / "record.txt"
+    bench.write_counter_record(str(tmp_path), str(lmp), str(out), ["(test)"])
+    rec = {k.strip(): v.strip() for k, v in (l.split("=", 1) for l in out.read_text().splitlines()
+                                            if "=" in l and not l.startswith("#"))}
+    assert float(rec["2.gate_up.SQ_INSTS_VALU"]) == 110.0 and float(rec["2.down.SQ_INSTS_VALU"]) == 50.0
+    assert rec["2.gate_up.dispatches"] == "2" and "k.gate_up.SQ_INSTS_VALU" not in rec
