@@ -365,6 +365,7 @@ def launch_symbols(ts) -> int:
 def note_launch(row: str, launch: str, ts, batch: int, x_bf16: bool):
     """Record how the profiler's dispatches of a launch are recognised: the kernel
     template and the grid, block and LDS sizes the library reports for it."""
+    import entropy_coded_weight_amd as ecw
     grid, block, lds = ecw.group_geometry(ts, batch, ecw.DT_BF16 if x_bf16 else ecw.DT_F16)
     LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), grid, block,
                                               launch_symbols(ts), lds]

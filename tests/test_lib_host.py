@@ -636,3 +636,11 @@ def test_counter_record_separates_launches_by_lds(tmp_path, monkeypatch):
                                             if "=" in l and not l.startswith("#"))}
     assert float(rec["2.gate_up.SQ_INSTS_VALU"]) == 110.0 and float(rec["2.down.SQ_INSTS_VALU"]) == 50.0
     assert rec["2.gate_up.dispatches"] == "2" and "k.gate_up.SQ_INSTS_VALU" not in rec
+    # the launch map entry of a real tensor carries the library's geometry
+    case = [c for c in cases.quad_cases() if c.name == "quads_t2048_m12"][0]
+    t = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    monkeypatch.setattr(bench, "LAUNCH_MAP", {})
+    bench.note_launch("q", "w", [t], 1, False)
+    assert bench.LAUNCH_MAP["q"]["w"] == [bench.kernel_sig(t.coding, 1, False),
+                                          *ecw.group_geometry([t], 1, ecw.DT_F16)[:2],
+                                          130 * 512 // 4, ecw.group_geometry([t], 1, ecw.DT_F16)[2]]
