@@ -26,6 +26,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -362,13 +363,108 @@ def launch_symbols(ts) -> int:
     return n
 
 
+LAUNCH_KEYS = {}     # launch key (launch_key) -> [(row, launch), ...] registered by note_launch
+DISPATCH_LOG = None  # profiling runs: {"keys": [launch key, ...], "log": [key index per fused dispatch]}
+
+
+def launch_key(ts, batch: int, x_bf16: bool):
+    """What identifies a grouped launch: the kernel template, and each member's coding
+    and launch shape."""
+    return (kernel_sig(ts[0].coding, batch, x_bf16),
+            tuple((t.coding.payload, t.coding.rows, t.coding.cols, t.coding.weights_per_symbol, t.coding.log2_m,
+                   t.coding.tile_cols, t.coding.stored_tuples, t.coding.recon_dtype, t.waves_per_block,
+                   t.tiles_per_wave, t.streams_per_wave, t.row_groups_per_block) for t in ts))
+
+
 def note_launch(row: str, launch: str, ts, batch: int, x_bf16: bool):
     """Record how the profiler's dispatches of a launch are recognised: the kernel
-    template and the grid, block and LDS sizes the library reports for it."""
+    template and the grid, block and LDS sizes the library reports for it, and the
+    launch key the dispatch log uses."""
     import entropy_coded_weight_amd as ecw
     grid, block, lds = ecw.group_geometry(ts, batch, ecw.DT_BF16 if x_bf16 else ecw.DT_F16)
     LAUNCH_MAP.setdefault(row, {})[launch] = [kernel_sig(ts[0].coding, batch, x_bf16), grid, block,
                                               launch_symbols(ts), lds]
+    owners = LAUNCH_KEYS.setdefault(launch_key(ts, batch, x_bf16), [])
+    if [row, launch] not in owners:
+        owners.append([row, launch])
+
+
+def install_dispatch_log():
+    """Profiling runs: log the launch of every fused decode-GEMV dispatch in the order
+    it reaches the GPU (eager calls, and each graph replay expanded into the launches
+    its capture recorded).  Profiler records are then attributed to launches by
+    dispatch order, which also separates launches of one kernel with the same grid."""
+    global DISPATCH_LOG
+    import torch
+    import entropy_coded_weight_amd as ecw
+    DISPATCH_LOG = {"keys": [], "ids": {}, "log": []}
+    state = {"capture": None}
+
+    def record(ts, x):
+        if not any(t.coding.rows and t.n_tiles for t in ts):
+            return                                   # no decode kernel (K = 0: a fill)
+        key = launch_key(ts, x.shape[0], x.dtype == torch.bfloat16)
+        i = DISPATCH_LOG["ids"].get(key)
+        if i is None:
+            i = DISPATCH_LOG["ids"][key] = len(DISPATCH_LOG["keys"])
+            DISPATCH_LOG["keys"].append(key)
+        (state["capture"] if state["capture"] is not None else DISPATCH_LOG["log"]).append(i)
+
+    group_raw, single_raw = ecw.gemv_group_raw, ecw.gemv_raw
+
+    def gemv_group_raw(ts, x, ys, workspace, stream=None):
+        group_raw(ts, x, ys, workspace, stream)
+        record(list(ts), x)
+
+    def gemv_raw(t, x, y, workspace, stream=None):
+        single_raw(t, x, y, workspace, stream)
+        record([t], x)
+
+    ecw.gemv_group_raw, ecw.gemv_raw = gemv_group_raw, gemv_raw
+
+    class LoggedGraph(torch.cuda.CUDAGraph):
+        def capture_begin(self, *a, **k):
+            self._launches = []
+            state["capture"] = self._launches
+            return super().capture_begin(*a, **k)
+
+        def capture_end(self):
+            try:
+                return super().capture_end()
+            finally:
+                state["capture"] = None
+
+        def replay(self):
+            super().replay()
+            DISPATCH_LOG["log"].extend(getattr(self, "_launches", []))
+
+    torch.cuda.CUDAGraph = LoggedGraph
+
+
+def write_dispatch_log(path: str):
+    """The dispatch log beside the launch map: per logged launch key its (row, launch)
+    owners, then one key index per fused dispatch."""
+    keys = [LAUNCH_KEYS.get(k, []) for k in DISPATCH_LOG["keys"]]
+    with open(path, "w") as f:
+        json.dump({"owners": keys, "log": DISPATCH_LOG["log"]}, f)
+
+
+FUSED_KERNEL = re.compile(r"k_decode<\d+, \d+, \d+, \d+, false, (?:true|false)>")
+
+
+def attribute_dispatches(rows: dict, lm: dict, log_path: str):
+    """(row, launch) owners of every fused decode-GEMV dispatch of a profiler CSV.
+    rows: Dispatch_Id -> (kernel name, grid, block, LDS).  With the run's dispatch log
+    (same number of fused dispatches) the n-th dispatch belongs to the n-th logged
+    launch; otherwise dispatches are matched by kernel, grid, block and LDS."""
+    fused = sorted((d for d, r in rows.items() if FUSED_KERNEL.search(r[0])), key=int)
+    if log_path and os.path.exists(log_path):
+        lg = json.load(open(log_path))
+        if len(lg["log"]) == len(fused):
+            return {d: [tuple(o) for o in lg["owners"][i]] for d, i in zip(fused, lg["log"])}, "dispatch order"
+        log(f"dispatch log {log_path}: {len(lg['log'])} launches against {len(fused)} fused dispatches; "
+            "matching by kernel, grid and LDS")
+    return {d: dispatch_launches(lm, *rows[d]) for d in fused}, "kernel, grid and LDS"
 
 
 def dispatch_launches(lm: dict, kname: str, grid: int, wg: int, lds: int) -> list:
@@ -1043,27 +1139,52 @@ def _lds_of(r: dict) -> int:
 def summarize_rocprof(directory: str):
     """Print per-(kernel, grid size, LDS size) averages from rocprofv3 CSV output under
     `directory`: kernel durations from *_kernel_trace.csv and counter values from
-    *_counter_collection.csv (one line per kernel and counter)."""
+    *_counter_collection.csv (one line per kernel and counter).  Where the run that
+    made a CSV left its launch map and dispatch log beside it (--launch-map), the same
+    figures follow per launch (row.launch) of the fused decode-GEMV."""
     import csv
     import collections
     import glob
+
+    def by_launch(path, rows):
+        lmp = os.path.join(os.path.dirname(path), "launch_map.json")
+        if not os.path.exists(lmp):
+            return None, None
+        return attribute_dispatches(rows, json.load(open(lmp)), lmp + ".dispatches.json")
+
     for path in sorted(glob.glob(os.path.join(directory, "**", "*_kernel_trace.csv"), recursive=True)):
         d = collections.defaultdict(list)
+        rows, dur = {}, {}
         for r in csv.DictReader(open(path)):
             key = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size_X"]), _lds_of(r))
-            d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            d[key].append(us)
+            rows[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), _lds_of(r))
+            dur[r["Dispatch_Id"]] = us
         print(f"# kernel durations from {os.path.relpath(path, directory)}")
         print(f"{'kernel':48s} {'grid':>8s} {'lds':>7s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s}")
         for (k, g, lds), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
             v.sort()
             print(f"{k[:48]:48s} {g:8d} {lds:7d} {len(v):6d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} "
                   f"{v[0]:8.2f}")
+        att, how = by_launch(path, rows)
+        if att:
+            pl = collections.defaultdict(list)
+            for did, owners in att.items():
+                for o in owners:
+                    pl[".".join(o)].append(dur[did])
+            print(f"# per launch (dispatches attributed by {how})")
+            print(f"{'launch':24s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s}")
+            for ln, v in sorted(pl.items()):
+                v.sort()
+                print(f"{ln:24s} {len(v):6d} {sum(v) / len(v):9.2f} {v[len(v) // 2]:9.2f} {v[0]:8.2f}")
     for path in sorted(glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True)):
         per = collections.defaultdict(lambda: collections.defaultdict(float))
-        names = {}
+        names, rows = {}, {}
         for r in csv.DictReader(open(path)):
             per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
             names[r["Dispatch_Id"]] = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size"]), _lds_of(r))
+            rows[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]), _lds_of(r))
         agg = collections.defaultdict(lambda: collections.defaultdict(list))
         for did, cs in per.items():
             for c, v in cs.items():
@@ -1072,6 +1193,17 @@ def summarize_rocprof(directory: str):
         for (k, g, lds), cs in sorted(agg.items()):
             for c, v in sorted(cs.items()):
                 print(f"{k[:48]:48s} {g:8d} {lds:7d} {c:24s} n={len(v):4d} {sum(v) / len(v):16.1f}")
+        att, how = by_launch(path, rows)
+        if att:
+            pl = collections.defaultdict(lambda: collections.defaultdict(list))
+            for did, owners in att.items():
+                for o in owners:
+                    for c, v in per[did].items():
+                        pl[".".join(o)][c].append(v)
+            print(f"# per launch (dispatches attributed by {how}; mean per dispatch)")
+            for ln, cs in sorted(pl.items()):
+                for c, v in sorted(cs.items()):
+                    print(f"{ln:24s} {c:24s} n={len(v):4d} {sum(v) / len(v):16.1f}")
 
 
 
@@ -1087,21 +1219,28 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
     import glob
     lm = json.load(open(launch_map_path))
     per = collections.defaultdict(lambda: collections.defaultdict(float))
-    names = {}
+    owners, how = {}, set()
     for path in sorted(glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True)):
+        rows = {}
         for r in csv.DictReader(open(path)):
             key = (path, r["Dispatch_Id"])
             per[key][r["Counter_Name"]] += float(r["Counter_Value"])
-            names[key] = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]), _lds_of(r))
+            rows[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]), _lds_of(r))
             per[key]["VGPR_Count"] = float(r["VGPR_Count"])
-            per[key]["LDS_Block_Size"] = float(r["LDS_Block_Size"])
-    owners = {key: dispatch_launches(lm, *nm) for key, nm in names.items()}
+        # each profiled run leaves its own launch map and dispatch log beside its CSVs
+        local = os.path.join(os.path.dirname(path), "launch_map.json")
+        lmp = local if os.path.exists(local) else launch_map_path
+        att, h = attribute_dispatches(rows, json.load(open(lmp)), lmp + ".dispatches.json")
+        how.add(h)
+        for did, o in att.items():
+            owners[(path, did)] = o
     lines = ["# Mean SQ counters per dispatch of every launch of every workload bench.py measures, MI355X.",
              "# Read by bench.py (VALU, LDS and bank-conflict fractions per launch, priced at the clock measured",
              "# in the same bench run); valid only while the kernel source and tune files hash to the values below.",
              "#", "# Commands (repository root on the GPU host; cd /tmp && export TMPDIR=/tmp first):"]
     lines += [f"#   {c}" for c in commands]
-    lines += [f"kernel_sha256 = {sha256(KERNEL_SRC)}",
+    lines += [f"# dispatches attributed to launches by {' and '.join(sorted(how))}",
+              f"kernel_sha256 = {sha256(KERNEL_SRC)}",
               f"tune_sha256 = {sha256(os.path.relpath(TUNE_FILE, ROOT))}",
               f"secondary_tune_sha256 = {sha256(os.path.relpath(SECONDARY_TUNE_FILE, ROOT))}"]
     table = ["| workload | launch | kernel | waves | VALU / wave-step | SALU / wave-step | LDS / wave-step | "
@@ -1111,7 +1250,7 @@ def write_counter_record(directory: str, launch_map_path: str, out_path: str, co
         for ln, (sig, grid, wg, nsym, *_) in launches.items():
             agg = collections.defaultdict(list)
             for key, cs in per.items():
-                if (row, ln) in owners[key]:
+                if (row, ln) in owners.get(key, ()):
                     for c, v in cs.items():
                         agg[c].append(v)
             if not agg:
@@ -1235,8 +1374,9 @@ def main():
                     help="write the counter record from rocprofv3 counter CSVs under DIR and the launch map "
                          "(--launch-map) of the profiled run, and exit")
     ap.add_argument("--launch-map", metavar="PATH",
-                    help="write (or, with --write-counter-record, read) the kernel template and grid of every "
-                         "launch of the run")
+                    help="write (or, with --write-counter-record, read) the kernel template, grid and LDS of "
+                         "every launch of the run, and beside it (PATH.dispatches.json) the launch of every fused "
+                         "decode-GEMV dispatch in issue order, for attributing profiler records")
     ap.add_argument("--configs", default="1,3,4,5,k,p,d",
                     help="workloads measured after the layer set (1: Gaussian codes, 3: BF16 exponent coding, "
                          "4: 32-layer FP8 step + LM head at batch 1 and 4, 5: E8 lattice fields, INT8 and FP8 "
@@ -1254,10 +1394,13 @@ def main():
         write_counter_record(args.write_counter_record, args.launch_map, COUNTER_FILE,
                              [f"rocprofv3 --pmc {s} --output-format csv -d $R/gpurun_out/<dir>/sq{i} -o sq{i} -- "
                               f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --configs 1,3,4,5,k "
-                              f"--launch-map $R/gpurun_out/<dir>/launch_map.json" for i, s in enumerate(COUNTER_SETS)]
+                              f"--launch-map $R/gpurun_out/<dir>/sq{i}/launch_map.json"
+                              for i, s in enumerate(COUNTER_SETS)]
                              + ["python3 bench.py --write-counter-record gpurun_out/<dir> --launch-map "
-                                "gpurun_out/<dir>/launch_map.json"])
+                                "gpurun_out/<dir>/sq0/launch_map.json"])
         return
+    if args.launch_map:
+        install_dispatch_log()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the kernel measured here is one GPU's share; sharding over GPUs is not built)", file=sys.stderr)
@@ -1419,6 +1562,7 @@ def main():
     if args.launch_map:
         with open(args.launch_map, "w") as f:
             json.dump(LAUNCH_MAP, f, indent=1)
+        write_dispatch_log(args.launch_map + ".dispatches.json")
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -644,3 +644,67 @@ def test_counter_record_separates_launches_by_lds(tmp_path, monkeypatch):
     assert bench.LAUNCH_MAP["q"]["w"] == [bench.kernel_sig(t.coding, 1, False),
                                           *ecw.group_geometry([t], 1, ecw.DT_F16)[:2],
                                           130 * 512 // 4, ecw.group_geometry([t], 1, ecw.DT_F16)[2]]
+
+
+def test_counter_record_attributes_dispatches_by_order(tmp_path):
+    # the profiler shows no LDS size (0) and the same kernel and grid for gate/up and
+    # down; the run's dispatch log (one launch per fused dispatch in issue order)
+    # tells them apart
+    import csv
+    import json
+    import bench
+    sig = "k_decode<1, 4, 4, 1, false, false>"
+    d = tmp_path / "sq0"
+    d.mkdir()
+    lm = {"2": {"gate_up": [sig, 458752, 1024, 1000, 43008], "down": [sig, 458752, 1024, 2000, 38912]}}
+    (d / "launch_map.json").write_text(json.dumps(lm))
+    # issue order: gate_up, down, gate_up, gate_up (one per-launch graph), then a
+    # kernel that is not a fused GEMV (a dequantising decode) in between
+    (d / "launch_map.json.dispatches.json").write_text(json.dumps(
+        {"owners": [[["2", "gate_up"]], [["2", "down"]]], "log": [0, 1, 0, 0]}))
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "LDS_Block_Size", "VGPR_Count",
+              "Counter_Name", "Counter_Value"]
+    with open(d / "sq0_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for did, name, valu in [(7, sig, 100), (9, sig, 40), (10, "k_decode<1, 4, 4, 1, true, true>", 5),
+                                (12, sig, 120), (13, sig, 110)]:
+            for cname, v in [("SQ_INSTS_VALU", valu), ("SQ_WAVES", 7168)]:
+                w.writerow({"Dispatch_Id": did, "Kernel_Name": f"void ecw::{name}(unsigned int)",
+                            "Grid_Size": 458752, "Workgroup_Size": 1024, "LDS_Block_Size": 0, "VGPR_Count": 64,
+                            "Counter_Name": cname, "Counter_Value": v})
+    out = tmp_path / "record.txt"
+    bench.write_counter_record(str(tmp_path), str(d / "launch_map.json"), str(out), ["(test)"])
+    text = out.read_text()
+    rec = {k.strip(): v.strip() for k, v in (l.split("=", 1) for l in text.splitlines()
+                                            if "=" in l and not l.startswith("#"))}
+    assert float(rec["2.gate_up.SQ_INSTS_VALU"]) == 110.0 and rec["2.gate_up.dispatches"] == "3"
+    assert float(rec["2.down.SQ_INSTS_VALU"]) == 40.0
+    assert "attributed to launches by dispatch order" in text
+
+
+def test_dispatch_log_records_each_launch(monkeypatch, tmp_path):
+    # eager calls are logged in issue order under the launch key note_launch registered
+    import json
+    import torch
+    import bench
+    case = [c for c in cases.quad_cases() if c.name == "quads_t2048_m12"][0]
+    t = ecw.prepare(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    calls = []
+    monkeypatch.setattr(ecw, "gemv_group_raw", lambda ts, x, ys, ws, stream=None: calls.append(len(ts)))
+    monkeypatch.setattr(ecw, "gemv_raw", lambda t, x, y, ws, stream=None: calls.append(1))
+    monkeypatch.setattr(torch.cuda, "CUDAGraph", torch.cuda.CUDAGraph)
+    monkeypatch.setattr(bench, "LAUNCH_KEYS", {})
+    monkeypatch.setattr(bench, "LAUNCH_MAP", {})
+    monkeypatch.setattr(bench, "DISPATCH_LOG", None)
+    bench.note_launch("2", "w", [t], 1, False)
+    bench.install_dispatch_log()
+    x1 = torch.zeros((1, 512), dtype=torch.float16)
+    x4 = torch.zeros((4, 512), dtype=torch.float16)
+    ecw.gemv_group_raw([t], x1, [None], None)
+    ecw.gemv_raw(t, x4, None, None)              # batch 4: another kernel, not registered
+    ecw.gemv_raw(t, x1, None, None)
+    assert calls == [1, 1, 1]
+    bench.write_dispatch_log(str(tmp_path / "log.json"))
+    lg = json.loads((tmp_path / "log.json").read_text())
+    assert lg["log"] == [0, 1, 0] and lg["owners"] == [[["2", "w"]], []]
