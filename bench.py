@@ -1540,11 +1540,21 @@ def main():
     dev = torch.device("cuda:0")
     big = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     achievable = ecw.probe_stream_read(big)
+    # the same read, one launch of the dominant launch's size (each rep another, cold
+    # region): what a launch of that many bytes can reach at all
+    at_size = ecw.probe_stream_read(big, region_bytes=int(launch_bytes[dom]))
+    # per-wave streams shaped like the decode's plane reads (7168 waves, as the gate/up
+    # launch and the BF16 launches run): 2 KiB and 8 KiB per wave, 1 or 2 KiB in flight
+    tiles = {f"{kib}KiB_x7168_inflight{inf}": round(ecw.probe_tile_stream(big, kib, 7168, 16, inf), 1)
+             for kib in (2, 8) for inf in (1, 2)}
     del big
     lut_rate = {f"m{m}_{eb}B": round(ecw.probe_lds_lookup(m, eb) / 1e9, 1) for m in (11, 12) for eb in (4, 8, 16)}
     out["probes"] = {"hbm_read_gbs": round(achievable, 1),
                      "hbm_read_frac_of_peak": round(achievable / HBM_PEAK_GBS, 4),
                      "dominant_launch_frac_of_achievable": round(achieved / achievable, 4),
+                     "hbm_read_gbs_one_launch_of_dominant_size": round(at_size, 1),
+                     "dominant_launch_frac_of_achievable_at_its_size": round(achieved / at_size, 4),
+                     "tile_stream_gbs": tiles,
                      "lds_lookups_g_per_s": lut_rate}
     if args.calibrate_copy:
         src = torch.ones(64 << 18, dtype=torch.float32, device=dev)

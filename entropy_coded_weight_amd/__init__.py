@@ -116,11 +116,13 @@ def lib():
                                  P(ctypes.c_float)]
     L.ecw_probe_stream_read.argtypes = [vp, vp, sz, vp, u32]
     L.ecw_probe_lds_lookup.argtypes = [vp, u32, u32, u32, u32, u32, vp]
+    L.ecw_probe_tile_stream.argtypes = [vp, vp, sz, u32, u32, u32, u32, vp]
     L.ecw_probe_clock.argtypes = [vp, u32, u32, vp, P(u32)]
     for f in ("enc_build_tables", "enc_encode", "enc_e8_nearest", "dec_prepare", "dec_gemv_workspace_size",
               "dec_gemv", "dec_gemv_noalloc", "dec_gemv_group_workspace_size", "dec_gemv_group",
               "dec_gemv_group_geometry", "dec_materialize", "dec_dequantize",
               "dec_tune_launch", "dec_time_group", "ecw_probe_stream_read", "ecw_probe_lds_lookup",
+              "ecw_probe_tile_stream",
               "ecw_probe_clock"):
         getattr(L, f).restype = ctypes.c_int
     L.ecw_last_error.argtypes = []
@@ -297,23 +299,56 @@ def dequantize_raw(t: Tensor, w_out: torch.Tensor, stream=None):
 
 
 # ------------------------------------------------------------------ roofline probes
-def probe_stream_read(buf: torch.Tensor, blocks: int = 2048, reps: int = 5) -> float:
-    """Achievable streaming-read GB/s over the device buffer `buf` (median of reps)."""
+def probe_stream_read(buf: torch.Tensor, blocks: int = 2048, reps: int = 5, region_bytes: int | None = None) -> float:
+    """Achievable streaming-read GB/s over the device buffer `buf` (median of reps).
+    With region_bytes, each rep reads another region of that size of `buf`, so that
+    no rep finds its bytes cached: the rate one launch of that size can reach."""
     sink = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
-    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    total = buf.numel() * buf.element_size() // 16 * 16
+    nbytes = total if region_bytes is None else region_bytes // 16 * 16
+    if nbytes <= 0 or nbytes > total:
+        raise ValueError("region larger than the buffer")
+    nreg = total // nbytes
     s = torch.cuda.current_stream()
     times = []
-    for _ in range(reps + 1):
+    for r in range(reps + 1):
+        base = buf.data_ptr() + (r % nreg) * nbytes
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(s)
-        _check(lib().ecw_probe_stream_read(_stream(None), buf.data_ptr(), nbytes, sink.data_ptr(), blocks),
+        _check(lib().ecw_probe_stream_read(_stream(None), base, nbytes, sink.data_ptr(), blocks),
                "ecw_probe_stream_read")
         e1.record(s)
         e1.synchronize()
         times.append(e0.elapsed_time(e1))
     t = sorted(times[1:])[len(times[1:]) // 2]
     return nbytes / (t * 1e-3) / 1e9
+
+
+def probe_tile_stream(buf: torch.Tensor, kib_per_wave: int, waves: int, waves_per_block: int = 16,
+                      inflight: int = 1, reps: int = 5) -> float:
+    """GB/s of `waves` per-wave streams of kib_per_wave KiB each (ecw_probe_tile_stream),
+    median of reps; every rep reads another region of `buf`, so none is cached."""
+    region = waves * kib_per_wave * 1024
+    total = buf.numel() * buf.element_size()
+    if region > total:
+        raise ValueError("buffer smaller than one region")
+    nreg = total // region
+    sink = torch.empty(waves * 64, dtype=torch.int32, device=buf.device)
+    s = torch.cuda.current_stream()
+    times = []
+    for r in range(reps + 1):
+        base = buf.data_ptr() + (r % nreg) * region
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        _check(lib().ecw_probe_tile_stream(_stream(None), base, region, kib_per_wave, waves, waves_per_block,
+                                           inflight, sink.data_ptr()), "ecw_probe_tile_stream")
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    t = sorted(times[1:])[len(times[1:]) // 2]
+    return region / (t * 1e-3) / 1e9
 
 
 def probe_lds_lookup(log2_m: int, entry_bytes: int, steps: int = 4096, blocks: int = 512,

@@ -26,6 +26,30 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p
   out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Per-wave tile streams, shaped like the decode's reads of its word and raw-byte
+// planes: wave w reads its own contiguous region of `kib` KiB as 1 KiB wave-wide
+// loads (16 bytes per lane), INFL of them in flight, with the decode's XCD-contiguous
+// block order, and folds them into one word per lane so the loads cannot be dropped.
+template <int INFL>
+__global__ void __launch_bounds__(1024) k_tile_stream(const uint4* __restrict__ p, uint32_t kib, uint32_t n_waves,
+                                                      uint32_t grid, uint32_t* out) {
+  const uint32_t per = grid >> 3;
+  const uint32_t gl = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const uint32_t w = gl * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (w >= n_waves) return;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint4* q = p + (uint64_t)w * kib * 64 + lane;
+  uint32_t acc = 0;
+  for (uint32_t k = 0; k < kib; k += INFL) {
+    uint4 v[INFL];
+#pragma unroll
+    for (int i = 0; i < INFL; ++i) v[i] = k + i < kib ? q[(uint64_t)(k + i) * 64] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < INFL; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  }
+  out[(uint64_t)w * 64 + lane] = acc;
+}
+
 // LDS random lookups shaped like the decode: a table of 2^m entries of 4, 8, 12 or 16 bytes,
 // and per lane a dependent chain idx -> entry -> next idx (the state update of the
 // decode is a multiply-add on the entry).  Every wave of the chip runs `steps` steps.
@@ -97,6 +121,22 @@ extern "C" ecw_status ecw_probe_stream_read(ecw_stream stream, const void* buf, 
   hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const uint4*>(buf), (uint64_t)(bytes / 16), sink);
   return launch_error("stream probe launch failed");
+}
+
+extern "C" ecw_status ecw_probe_tile_stream(ecw_stream stream, const void* buf, size_t bytes, uint32_t kib_per_wave,
+                                            uint32_t waves, uint32_t waves_per_block, uint32_t inflight,
+                                            uint32_t* sink) {
+  clear_error();
+  if (!buf || !sink || reinterpret_cast<uintptr_t>(buf) % 16 || kib_per_wave == 0 || waves == 0 ||
+      waves_per_block == 0 || waves_per_block > 16 || (inflight != 1 && inflight != 2 && inflight != 4) ||
+      (uint64_t)waves * kib_per_wave * 1024u > bytes)
+    return fail(ECW_E_INVALID_ARG, "tile stream probe: bad buffer, sink or shape");
+  const uint32_t blocks = (waves + waves_per_block - 1) / waves_per_block;
+  const uint32_t grid = (blocks + 7) / 8 * 8;
+  auto fn = inflight == 4 ? k_tile_stream<4> : inflight == 2 ? k_tile_stream<2> : k_tile_stream<1>;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(waves_per_block * 64), 0, (hipStream_t)stream,
+                     static_cast<const uint4*>(buf), kib_per_wave, waves, grid, sink);
+  return launch_error("tile stream probe launch failed");
 }
 
 extern "C" ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t entry_bytes,

@@ -309,6 +309,14 @@ ecw_status ecw_probe_stream_read(ecw_stream stream, const void* buf, size_t byte
                                  uint32_t blocks);
 ecw_status ecw_probe_lds_lookup(ecw_stream stream, uint32_t log2_m, uint32_t entry_bytes, uint32_t steps,
                                 uint32_t blocks, uint32_t waves_per_block, uint32_t* sink);
+/* ecw_probe_tile_stream: `waves` waves, `waves_per_block` per block, each read their
+ *   own contiguous kib_per_wave KiB of `buf` (16-byte aligned; bytes must cover
+ *   waves x kib_per_wave KiB) as 1 KiB wave-wide loads (16 bytes per lane) with
+ *   `inflight` (1, 2 or 4) loads in flight, in the decode's block order: the read
+ *   pattern of the decode's word and raw-byte planes, one stream per tile.  Writes
+ *   one word per lane to `sink` (device, waves x 64 u32). */
+ecw_status ecw_probe_tile_stream(ecw_stream stream, const void* buf, size_t bytes, uint32_t kib_per_wave,
+                                 uint32_t waves, uint32_t waves_per_block, uint32_t inflight, uint32_t* sink);
 /* ecw_probe_clock: `blocks` one-wave blocks each keep a dependent FMA chain busy for
  *   duration_us (by the constant-rate real-time counter, whose rate in kHz goes to
  *   *wall_clock_khz) and write [shader-clock cycles, real-time ticks] elapsed, two u64

@@ -378,6 +378,12 @@ def test_probe_entry_points_reject_bad_arguments():
     assert L.ecw_probe_stream_read(None, None, 16, None, 1) == 1
     assert L.ecw_probe_lds_lookup(None, 14, 8, 10, 1, 1, None) == 1
     assert L.ecw_probe_lds_lookup(None, 11, 6, 10, 1, 1, ctypes.c_void_p(16)) == 1
+    p16 = ctypes.c_void_p(16)
+    assert L.ecw_probe_tile_stream(None, None, 1 << 20, 1, 8, 4, 1, p16) == 1          # no buffer
+    assert L.ecw_probe_tile_stream(None, p16, 1 << 20, 1, 8, 4, 3, p16) == 1           # 3 in flight
+    assert L.ecw_probe_tile_stream(None, p16, 1 << 20, 1, 8, 17, 1, p16) == 1          # 17 waves per block
+    assert L.ecw_probe_tile_stream(None, p16, 8 * 1024 - 1, 1, 8, 4, 1, p16) == 1      # buffer too short
+    assert L.ecw_probe_tile_stream(None, ctypes.c_void_p(8), 1 << 20, 1, 8, 4, 1, p16) == 1   # misaligned
 
 
 def test_bench_lattice_inputs_match_the_test_recipe():
