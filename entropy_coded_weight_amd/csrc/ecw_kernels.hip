@@ -82,7 +82,7 @@ constexpr bool kCleanBias = (PAY == 1 && KW == 4 && CB != 4) || (PAY == 2 && KW 
 #define ECW_LDS __attribute__((address_space(3)))
 template <typename T>
 __device__ __forceinline__ ECW_LDS T* lds_ptr(uint32_t addr) {
-  return (ECW_LDS T*)addr;
+  return (ECW_LDS T*)(size_t)addr;
 }
 // 8- and 16-byte LDS accesses (clang vector types: HIP's vector classes cannot be
 // addressed in LDS address space)
@@ -1347,8 +1347,10 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
       tv[i] = idx < a.quad_t ? tup[idx] : 0u;
     }
   }
-  const uint32_t nvec = MAT ? 0 : a.xs_cols / 8;                 // activations, 8 columns per unit
-  const uint32_t nxv = nvec * B;
+  // activations, 8 columns per unit (none for the materialising hook; nvec stays a
+  // valid divisor there)
+  const uint32_t nvec = MAT ? 1u : a.xs_cols / 8;
+  const uint32_t nxv = MAT ? 0u : nvec * B;
   auto x_load = [&](uint32_t v) {
     const uint32_t b = v / nvec, c8 = v - b * nvec, col = c_lo + 8 * c8;
     uint4 raw = {0u, 0u, 0u, 0u};
