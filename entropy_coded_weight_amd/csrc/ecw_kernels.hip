@@ -40,6 +40,14 @@ constexpr uint32_t kRing = 512;            // words per wave ring (two chunks)
 constexpr uint32_t kMirror = 64;           // copy of the ring head for reads that wrap
 constexpr uint32_t kRingStride = kRing + kMirror;   // 1152 bytes per stream
 constexpr uint32_t kPairTableBytes = 2048; // 256 symbols x up to 8 bytes
+// BF16 raw-byte groups of the next 16 steps are loaded after the refill of this
+// quarter of the current 16 steps, i.e. 8 steps before their first use.  Vector
+// loads complete in order, and the refill's wait for its prefetched chunk is a wait
+// for every load in flight (the compiler cannot count loads issued under
+// data-dependent conditions).  Raw groups issued at the top of the 16 steps made
+// every refill that followed soon after wait for them; issued here, only the last
+// quarter's refill does.
+constexpr int kRawQuarter = 2;
 
 constexpr int kMaxGroup = 8;
 
@@ -605,22 +613,25 @@ __device__ __forceinline__ void wave_body(const TArgs& a, const StreamHead& h, u
       uint4 rgp[RG];
 #pragma unroll
       for (int i = 0; i < RG; ++i) rgp[i] = zero4;
+      bool more = false;            // raw groups of the next U steps to prefetch
       if constexpr (PAY == 2) {
 #pragma unroll
         for (int i = 0; i < RG; ++i) rgp[i] = rnext[i];
         // the next groups: of this tile, else the first of the wave's next tile
-        const bool more = j + U < S || t + 1 < t1;          // wave-uniform
+        more = j + U < S || t + 1 < t1;                     // wave-uniform
         rawp = j + U < S ? rawp + 1024 * RG : raw_tile(a, rg, sl + 1, lane);
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < RG; ++i) rnext[i] = *reinterpret_cast<const uint4*>(rawp + 1024 * i);
-        }
       }
       // activation words of step j: fp32 [col][B], or packed pairs [col / 2][B]
       const uint32_t xg = xs + ((col + KW * j) * B / (PK ? 2 : 1)) * 4;
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
         refill(rposb, haveb, nc, pre, wl, src, nch, lane);
+        if constexpr (PAY == 2) {
+          if (qtr == kRawQuarter && more) {
+#pragma unroll
+            for (int i = 0; i < RG; ++i) rnext[i] = *reinterpret_cast<const uint4*>(rawp + 1024 * i);
+          }
+        }
         uint4 xq[MAT || BFP ? 1 : XW];
         uint32_t xp[BFP ? 2 * B : 1];     // bf16 pairs: two pair words per batch row
         if constexpr (BFP) {
@@ -803,19 +814,22 @@ __device__ __forceinline__ void wave_body_deq(const TArgs& a, const StreamHead& 
       uint4 rgp[RG];
 #pragma unroll
       for (int i = 0; i < RG; ++i) rgp[i] = zero4;
+      bool more = false;            // raw groups of the next U steps to prefetch
       if constexpr (PAY == 2) {
 #pragma unroll
         for (int i = 0; i < RG; ++i) rgp[i] = rnext[i];
-        const bool more = j + U < S || t + 1 < t1;          // wave-uniform
+        more = j + U < S || t + 1 < t1;                     // wave-uniform
         rawp = j + U < S ? rawp + 1024 * RG : raw_tile(a, rg, sl + 1, lane);
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < RG; ++i) rnext[i] = *reinterpret_cast<const uint4*>(rawp + 1024 * i);
-        }
       }
 #pragma unroll
       for (int qtr = 0; qtr < U / 4; ++qtr) {
         refill(rposb, haveb, nc, pre, wl, src, nch, lane);
+        if constexpr (PAY == 2) {
+          if (qtr == kRawQuarter && more) {
+#pragma unroll
+            for (int i = 0; i < RG; ++i) rnext[i] = *reinterpret_cast<const uint4*>(rawp + 1024 * i);
+          }
+        }
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           const int u = qtr * 4 + u4;
