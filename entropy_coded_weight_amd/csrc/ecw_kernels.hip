@@ -316,8 +316,9 @@ __device__ __forceinline__ float exact_product(float a, float b) {
 // w_out; kOutCode: the int8 code into w_out; kOutF16 / kOutBf16: the value, times
 // the row scale with SC, into deq_out).  Rounds end when every lane
 // has read its row's last record, or after `width` rounds (a row has at most
-// `width` escapes) so that a damaged stream still ends.  Records are read as two
-// 16-bit halves, each wrapped into the ring.  col: staged column of the tile's first
+// `width` escapes) so that a damaged stream still ends.  The general rounds read a
+// record as two 16-bit halves, each wrapped into the ring (the fused product's own
+// rounds are described there).  col: staged column of the tile's first
 // weight; width: weights per row in the tile; wrow: output index of this row's first
 // weight in the tile.
 constexpr int kOutAcc = 0, kOutBits = 1, kOutF16 = 2, kOutBf16 = 3, kOutCode = 4;
@@ -348,6 +349,42 @@ __device__ __forceinline__ void tile_corrections(const TArgs& a, uint32_t& rposb
   bool has = active && ((mw >> (lane & 15)) & 1u);
   rposb += 2 * kEscMaskWords;
   uint64_t act = __ballot(has);
+  if constexpr (OUT == kOutAcc) {
+    // The fused product's rounds, written for few instructions (the launches are
+    // issue-bound): both halves of a record from one ring address (a record that
+    // starts on the ring's last word reads its high half from the mirror of the ring
+    // head), the column clamped into the tile instead of an exec branch, the
+    // activation read as one 16-bit value, and the multiply-add kept by a select.
+    // The same multiply-adds in the same order as the general rounds below.
+    const uint32_t wmax = width - 1;
+    for (uint32_t round = 0; act != 0 && round < width; ++round) {
+      refill(rposb, haveb, nc, pre, wl, src, nch, lane);
+      const uint32_t ra = ring + ((rposb + 4 * lanes_below(act)) & kWrap);
+      const uint32_t rec = (uint32_t)*lds_ptr<const uint16_t>(ra) |
+                           ((uint32_t)*lds_ptr<const uint16_t>(ra + 2) << 16);
+      rposb += 4 * (uint32_t)__popcll(act);
+      const uint32_t c = (rec >> 16) & 0x7FFu;
+      const bool use = has && c < width;
+      const uint32_t cx = col + (c < wmax ? c : wmax);
+      const float w = __uint_as_float(rec << 16);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float xv;
+        if constexpr (PKX) {
+          // packed pairs [column / 2][B]; the tile starts on an even column
+          const uint32_t h = *lds_ptr<const uint16_t>(xs + ((cx >> 1) * B + b) * 4 + (cx & 1u) * 2);
+          xv = XBF ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        } else {
+          xv = *lds_ptr<const float>(xs + (cx * B + b) * 4);
+        }
+        const float f = fmaf(w, xv, acc[b]);
+        acc[b] = use ? f : acc[b];
+      }
+      has = has && !(rec & kEscLast);
+      act = __ballot(has);
+    }
+    return;
+  }
   for (uint32_t round = 0; act != 0 && round < width; ++round) {
     refill(rposb, haveb, nc, pre, wl, src, nch, lane);
     const uint32_t pos = rposb + 4 * lanes_below(act);
