@@ -1625,7 +1625,11 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
     for (uint32_t i = tid; i < 64u * B * nrg; i += W * 64) {
       const uint32_t s = i / (64u * B), bi = i - s * (64u * B);
       const uint32_t b = bi >> 6, l = bi & 63, rgs = rg + s, r = rgs * 64 + l;
+      // the block's wave slots added in wave order; unrolled so that eight reads are
+      // in flight at a time instead of one read per add (16 waves were 16 dependent
+      // LDS round trips at the end of every block)
       float sum = 0.f;
+#pragma unroll 8
       for (uint32_t w = 0; w < W; ++w)
         sum += *lds_ptr<const float>(rings + (w * NSr + s) * (2 * kRingStride) + (b * 64 + l) * 4);
       if (a.n_sg == 1) {
