@@ -1437,11 +1437,24 @@ k_decode(const uint32_t n_blocks, const uint32_t nt, const uint32_t waves, const
   if (kTwoCapable && hasB) head_chunks(a, lane, hB);
 
   if constexpr (E8) {
-    // E8 tables are packed to 4-byte entries on the way
+    // E8 tables are packed to 4-byte entries on the way.  The 17 tables take several
+    // rounds of the block, so the entries go in batches of eight rounds: eight loads
+    // in flight (indices clamped into the table), then the eight LDS writes.
     const uint2* src = a.lut;
-    for (uint32_t i = tid; i < a.lut_entries; i += bd) {
-      const uint2 e = src[i];
-      *lds_ptr<uint32_t>(lut + i * 4) = (e.x & 0xFFFu) | ((e.y & 0x7FFu) << 12) | (e.x & 0xFF000000u);
+    const uint32_t ne = a.lut_entries;
+    for (uint32_t i0 = 0; i0 < ne; i0 += 8 * bd) {       // wave-uniform
+      uint2 e[8];
+#pragma unroll
+      for (uint32_t k = 0; k < 8; ++k) {
+        const uint32_t i = i0 + k * bd + tid;
+        e[k] = src[i < ne ? i : ne - 1];
+      }
+#pragma unroll
+      for (uint32_t k = 0; k < 8; ++k) {
+        const uint32_t i = i0 + k * bd + tid;
+        if (i < ne)
+          *lds_ptr<uint32_t>(lut + i * 4) = (e[k].x & 0xFFFu) | ((e[k].y & 0x7FFu) << 12) | (e[k].x & 0xFF000000u);
+      }
     }
     if constexpr (E8F8) {
       for (uint32_t i = tid; i < 256; i += bd) {
