@@ -383,48 +383,36 @@ __device__ __forceinline__ void tile_corrections(const TArgs& a, uint32_t& rposb
       has = has && !(rec & kEscLast);
       act = __ballot(has);
     }
-    return;
-  }
-  for (uint32_t round = 0; act != 0 && round < width; ++round) {
-    refill(rposb, haveb, nc, pre, wl, src, nch, lane);
-    const uint32_t pos = rposb + 4 * lanes_below(act);
-    const uint32_t lo = *lds_ptr<const uint16_t>(ring + (pos & kWrap));
-    const uint32_t hi = *lds_ptr<const uint16_t>(ring + ((pos + 2) & kWrap));
-    rposb += 4 * (uint32_t)__popcll(act);
-    if (has) {
-      const uint32_t rec = lo | (hi << 16);
-      const uint32_t c = (rec >> 16) & 0x7FFu;
-      if (c < width) {
-        if constexpr (OUT == kOutBits) {
-          if (a.w_out) static_cast<uint16_t*>(a.w_out)[wrow + c] = (uint16_t)rec;
-        } else if constexpr (OUT == kOutCode) {
-          if (a.w_out) static_cast<int8_t*>(a.w_out)[wrow + c] = (int8_t)(int)__uint_as_float(rec << 16);
-        } else if constexpr (OUT == kOutBf16 && !SC) {
-          static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)rec;
-        } else if constexpr (OUT == kOutBf16 || OUT == kOutF16) {
-          float v = __uint_as_float(rec << 16);
-          if constexpr (SC) v = exact_product(v, scale);
-          static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)to16<OUT == kOutBf16>(v);
-        } else {
-          const float w = __uint_as_float(rec << 16);
-#pragma unroll
-          for (int b = 0; b < B; ++b) {
-            float xv;
-            if constexpr (PKX) {
-              // packed pairs [column / 2][B]; the tile starts on an even column
-              const uint32_t xw = *lds_ptr<const uint32_t>(xs + (((col + c) >> 1) * B + b) * 4);
-              const uint32_t h = (c & 1u) ? (xw >> 16) : (xw & 0xFFFFu);
-              xv = XBF ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-            } else {
-              xv = *lds_ptr<const float>(xs + ((col + c) * B + b) * 4);
-            }
-            acc[b] = fmaf(w, xv, acc[b]);
+  } else {
+    // the general rounds: the decode-only hook and the dequantising decode store
+    // each escaped weight
+    for (uint32_t round = 0; act != 0 && round < width; ++round) {
+      refill(rposb, haveb, nc, pre, wl, src, nch, lane);
+      const uint32_t pos = rposb + 4 * lanes_below(act);
+      const uint32_t lo = *lds_ptr<const uint16_t>(ring + (pos & kWrap));
+      const uint32_t hi = *lds_ptr<const uint16_t>(ring + ((pos + 2) & kWrap));
+      rposb += 4 * (uint32_t)__popcll(act);
+      if (has) {
+        const uint32_t rec = lo | (hi << 16);
+        const uint32_t c = (rec >> 16) & 0x7FFu;
+        if (c < width) {
+          if constexpr (OUT == kOutBits) {
+            if (a.w_out) static_cast<uint16_t*>(a.w_out)[wrow + c] = (uint16_t)rec;
+          } else if constexpr (OUT == kOutCode) {
+            if (a.w_out) static_cast<int8_t*>(a.w_out)[wrow + c] = (int8_t)(int)__uint_as_float(rec << 16);
+          } else if constexpr (OUT == kOutBf16 && !SC) {
+            static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)rec;
+          } else {
+            static_assert(OUT == kOutBf16 || OUT == kOutF16, "unknown correction output");
+            float v = __uint_as_float(rec << 16);
+            if constexpr (SC) v = exact_product(v, scale);
+            static_cast<uint16_t*>(a.deq_out)[wrow + c] = (uint16_t)to16<OUT == kOutBf16>(v);
           }
         }
+        if (rec & kEscLast) has = false;
       }
-      if (rec & kEscLast) has = false;
+      act = __ballot(has);
     }
-    act = __ballot(has);
   }
 }
 
