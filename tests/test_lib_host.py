@@ -714,3 +714,36 @@ def test_dispatch_log_records_each_launch(monkeypatch, tmp_path):
     bench.write_dispatch_log(str(tmp_path / "log.json"))
     lg = json.loads((tmp_path / "log.json").read_text())
     assert lg["log"] == [0, 1, 0] and lg["owners"] == [[["2", "w"]], []]
+
+
+def test_quad_case_has_records_on_the_ring_mirror():
+    # The fused product's correction rounds read a record's two halves from one ring
+    # address; a record that starts on the ring's last word (of 512) takes its high
+    # half from the mirror of the ring head.  With one tile per wave a wave's ring
+    # position of word w is (w - the tile's chunk-aligned start) mod 512.  The model is
+    # checked first: each tile's correction stream (a 4-word lane mask, then two words
+    # per record) ends at the next tile's offset and its mask is the oracle's rows with
+    # escapes.  Then the case the quad GEMV tests run at one tile per wave
+    # (fp16 activations) must hold such records, so those tests cover the mirror read.
+    from oracle import symbols as S
+    case = [c for c in cases.quad_cases() if c.name == "quads_t64_m10_ragged"][0]
+    assert case.x_dtype == "f16"
+    bl = blobfmt.parse(ecw.encode(case.lib_coding(), case.logical, case.scales))
+    offs, words = blobfmt.offsets(bl), blobfmt.words(bl)
+    stored = blobfmt.quad_tables(bl)[0]
+    _, esc = S.quad_map(S.quad_tuples(case.logical), np.asarray(stored))
+    n, k = case.logical.shape
+    tc, nsl, nrg = bl.h["tile_cols"], bl.h["n_slices"], bl.h["n_row_groups"]
+    on_last_word = 0
+    for rg in range(nrg):
+        for sl in range(nsl):
+            t = rg * nsl + sl
+            e = esc[rg * 64:min(n, rg * 64 + 64), sl * tc:min(k, sl * tc + tc)]
+            recs = int(e.sum())
+            cs = int(offs[t + 1]) - (4 + 2 * recs)
+            mask = sum(int(words[cs + i]) << (16 * i) for i in range(4))
+            want = sum(1 << lane for lane in range(e.shape[0]) if e[lane].any())
+            assert mask == want, (t, hex(mask), hex(want))
+            gb = int(offs[t]) & ~255
+            on_last_word += sum(1 for r in range(recs) if (cs + 4 + 2 * r - gb) % 512 == 511)
+    assert on_last_word > 0
